@@ -1,0 +1,232 @@
+"""fp64 oracle of fused CSR graph attention (forward and recompute backward).
+
+Test infrastructure only (see the package docstring).
+
+Definition followed: "On Efficient Scaling of GNNs via IO-Aware Layers
+Implementations", Technical Summary > Methodology, attention-based layers.  For every
+destination node i of a CSR graph and every head h:
+
+    e_k   = score(i, J_k)                      over the neighbour multiset J of row i
+    alpha = softmax_k(e)                       (two passes: max, then exp / sum)
+    out_i = sum_k alpha_k v_{J_k}
+    lse_i = max_k e_k + ln sum_k exp(e_k - max)
+
+Score forms (the pages name Graph Transformer and GAT-style layers but print no
+formula; these are the standard definitions):
+    dot:  e = scale * <q_i, k_j>               (scale = 1/sqrt(d) unless given)
+    gat:  e = scale * LeakyReLU_a(s_i + t_j)   (per-node, per-head scalars; scale = 1)
+
+The backward (Methodology, "Backward Pass": cached per-node log-sum-exp, weights
+recomputed) is written out from the chain rule of the same definition, row by row:
+    dp_k  = <dOut_i, v_{J_k}>,  D = sum_k alpha_k dp_k,  dS_k = alpha_k (dp_k - D)
+    dq_i  = scale sum_k dS_k k_{J_k};  dk_{J_k} += scale dS_k q_i;  dv_{J_k} += alpha_k dOut_i
+
+Conventions: CSR row = destination; parallel edges count with multiplicity; a row with
+no neighbours gives out = 0 and lse = -inf and no gradient.  All arithmetic is fp64;
+bf16 inputs arrive as uint16 bit patterns and are widened exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "widen", "leaky_relu", "row_scores", "row_softmax", "forward_rows", "forward",
+    "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
+]
+
+
+def widen(x) -> np.ndarray:
+    """Exact fp64 value of a stored tensor: float arrays as-is, uint16 = bf16 bits."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def leaky_relu(x: np.ndarray, neg_slope: float) -> np.ndarray:
+    return np.where(x >= 0.0, x, neg_slope * x)
+
+
+def _neighbours(indptr, indices, i):
+    return indices[int(indptr[i]):int(indptr[i + 1])]
+
+
+def row_scores(i, indptr, indices, a, b, score="dot", scale=None, neg_slope=0.2):
+    """Scores e[k, h] of row i, materialised ([deg, H], fp64).
+
+    dot: a = q [N,H,d], b = k [N,H,d].   gat: a = s [N,H], b = t [N,H].
+    ``scale`` and ``neg_slope`` are used at their given (fp32) values, widened.
+    """
+    J = _neighbours(indptr, indices, i)
+    if score == "dot":
+        qi = widen(a[i])                       # [H, d]
+        kj = widen(b[J])                       # [deg, H, d]
+        if scale is None:
+            scale = 1.0 / np.sqrt(qi.shape[-1])
+        return float(scale) * np.einsum("hc,khc->kh", qi, kj)
+    if score == "gat":
+        si = widen(a[i])                       # [H]
+        tj = widen(b[J])                       # [deg, H]
+        sc = 1.0 if scale is None else float(scale)
+        return sc * leaky_relu(si[None, :] + tj, float(neg_slope))
+    raise ValueError(score)
+
+
+def row_softmax(e: np.ndarray):
+    """Two-pass softmax over axis 0 of e [deg, H]: returns (alpha, lse)."""
+    m = e.max(axis=0)
+    w = np.exp(e - m[None, :])
+    l = w.sum(axis=0)
+    return w / l[None, :], m + np.log(l)
+
+
+def forward_rows(indptr, indices, a, b, v, rows, score="dot", scale=None, neg_slope=0.2):
+    """out [R, H, d] and lse [R, H] (fp64) for the listed rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = v.shape[1], v.shape[2]
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    for r, i in enumerate(rows):
+        J = _neighbours(indptr, indices, i)
+        if J.size == 0:
+            continue
+        e = row_scores(i, indptr, indices, a, b, score, scale, neg_slope)
+        alpha, lse[r] = row_softmax(e)
+        out[r] = np.einsum("kh,khc->hc", alpha, widen(v[J]))
+    return out, lse
+
+
+def forward(indptr, indices, a, b, v, score="dot", scale=None, neg_slope=0.2):
+    n = indptr.size - 1
+    return forward_rows(indptr, indices, a, b, v, np.arange(n), score, scale, neg_slope)
+
+
+def _row_backward(i, indptr, indices, q, k, v, dout, scale):
+    """Per-row pieces of the dot-score backward: (J, alpha [deg,H], dS [deg,H])."""
+    J = _neighbours(indptr, indices, i)
+    e = row_scores(i, indptr, indices, q, k, "dot", scale)
+    alpha, _ = row_softmax(e)
+    dp = np.einsum("hc,khc->kh", widen(dout[i]), widen(v[J]))
+    D = (alpha * dp).sum(axis=0)
+    return J, alpha, alpha * (dp - D[None, :])
+
+
+def _scale_of(q, scale):
+    return 1.0 / np.sqrt(q.shape[-1]) if scale is None else float(scale)
+
+
+def backward(indptr, indices, q, k, v, dout, scale=None):
+    """dq, dk, dv [N, H, d] (fp64) by rows, scattering dK/dV in CSR order."""
+    sc = _scale_of(q, scale)
+    n = indptr.size - 1
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for i in range(n):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        J, alpha, dS = _row_backward(i, indptr, indices, q, k, v, dout, sc)
+        dq[i] = sc * np.einsum("kh,khc->hc", dS, widen(k[J]))
+        np.add.at(dk, J, sc * dS[:, :, None] * widen(q[i])[None])
+        np.add.at(dv, J, alpha[:, :, None] * widen(dout[i])[None])
+    return dq, dk, dv
+
+
+def backward_by_columns(indptr, indices, q, k, v, dout, scale=None):
+    """Same gradients, but dK/dV gathered per source column (a CSC-ordered formulation
+    with its own transpose), dQ per row.  Agrees with ``backward`` to rounding."""
+    sc = _scale_of(q, scale)
+    n = indptr.size - 1
+    deg = np.diff(indptr)
+    edge_row = np.repeat(np.arange(n), deg)
+    dS_all = np.zeros((indices.size, q.shape[1]))
+    al_all = np.zeros((indices.size, q.shape[1]))
+    dq = np.zeros(q.shape)
+    for i in range(n):
+        if deg[i] == 0:
+            continue
+        J, alpha, dS = _row_backward(i, indptr, indices, q, k, v, dout, sc)
+        dq[i] = sc * np.einsum("kh,khc->hc", dS, widen(k[J]))
+        dS_all[indptr[i]:indptr[i + 1]] = dS
+        al_all[indptr[i]:indptr[i + 1]] = alpha
+    order = np.argsort(indices, kind="stable")
+    col_start = np.searchsorted(indices[order], np.arange(n + 1))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for j in range(n):
+        es = order[col_start[j]:col_start[j + 1]]
+        if es.size == 0:
+            continue
+        rows = edge_row[es]
+        dk[j] = sc * np.einsum("eh,ehc->hc", dS_all[es], widen(q[rows]))
+        dv[j] = np.einsum("eh,ehc->hc", al_all[es], widen(dout[rows]))
+    return dq, dk, dv
+
+
+def grad_q_rows(indptr, indices, q, k, v, dout, rows, scale=None):
+    """dq [R, H, d] for the listed rows only."""
+    sc = _scale_of(q, scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((rows.size,) + tuple(q.shape[1:]))
+    for r, i in enumerate(rows):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        J, _, dS = _row_backward(i, indptr, indices, q, k, v, dout, sc)
+        dq[r] = sc * np.einsum("kh,khc->hc", dS, widen(k[J]))
+    return dq
+
+
+def grad_kv_cols(indptr, indices, q, k, v, dout, cols, scale=None):
+    """dk, dv [C, H, d] for the listed source columns only: every edge (i -> j) with j in
+    ``cols`` contributes its row's dS and alpha."""
+    sc = _scale_of(q, scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    slot = {int(j): c for c, j in enumerate(cols)}
+    dk = np.zeros((cols.size,) + tuple(k.shape[1:]))
+    dv = np.zeros((cols.size,) + tuple(v.shape[1:]))
+    pos = np.flatnonzero(np.isin(indices, cols))
+    rows = np.searchsorted(indptr, pos, side="right") - 1
+    for i in np.unique(rows):
+        J, alpha, dS = _row_backward(i, indptr, indices, q, k, v, dout, sc)
+        qi, doi = widen(q[i]), widen(dout[i])
+        for kk in np.flatnonzero(np.isin(J, cols)):
+            c = slot[int(J[kk])]
+            dk[c] += sc * dS[kk][:, None] * qi
+            dv[c] += alpha[kk][:, None] * doi
+    return dk, dv
+
+
+def train_step_rows(indptr, indices, q, k, v, dout, rows, scale=None):
+    """Forward and backward of the listed rows, each row's work done once.
+
+    Returns (out [R,H,d], lse [R,H], dq [R,H,d], cols, dk_part [C,H,d], dv_part [C,H,d])
+    where ``cols`` are the source columns the rows touch (ascending) and dk_part/dv_part
+    hold those rows' contributions to dK/dV.  With rows = all rows this is exactly
+    ``forward`` plus ``backward``.
+    """
+    sc = _scale_of(q, scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = q.shape[1], q.shape[2]
+    segs = [indices[int(indptr[i]):int(indptr[i + 1])] for i in rows]
+    cols = np.unique(np.concatenate(segs)) if segs else np.zeros(0, np.int64)
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    dq = np.zeros((rows.size, H, d))
+    dk = np.zeros((cols.size, H, d))
+    dv = np.zeros((cols.size, H, d))
+    for r, i in enumerate(rows):
+        J = segs[r]
+        if J.size == 0:
+            continue
+        e = row_scores(i, indptr, indices, q, k, "dot", sc)
+        alpha, lse[r] = row_softmax(e)
+        vj, kj = widen(v[J]), widen(k[J])
+        out[r] = np.einsum("kh,khc->hc", alpha, vj)
+        dp = np.einsum("hc,khc->kh", widen(dout[i]), vj)
+        D = (alpha * dp).sum(axis=0)
+        dS = alpha * (dp - D[None, :])
+        dq[r] = sc * np.einsum("kh,khc->hc", dS, kj)
+        slot = np.searchsorted(cols, J)
+        np.add.at(dk, slot, sc * dS[:, :, None] * widen(q[i])[None])
+        np.add.at(dv, slot, alpha[:, :, None] * widen(dout[i])[None])
+    return out, lse, dq, cols, dk, dv

@@ -1,0 +1,155 @@
+"""Pins of the fp64 oracle's backward (dot score).
+
+* hand-derived closed forms (tests/golden/worked_example.json),
+* central finite differences of the oracle's own forward (loss = <out, dOut>),
+* torch fp64 autograd through dense masked attention (boolean / log-count mask),
+* invariants: sum_j dK_j = 0 per head, sum_j dV_j = sum of dOut over non-empty rows,
+  dQ = 0 on single-neighbour rows and on rows whose neighbour keys are all equal,
+* agreement of the CSR-scatter, CSC-gather, sampled and per-row training-step forms.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import graphgen as gg
+from oracle import attention as A
+
+
+def _graph(seed, n, m):
+    rng = np.random.default_rng(seed)
+    ip, ix = gg.random_multigraph(n, m, rng)
+    return rng, ip, ix
+
+
+def test_worked_example_backward(golden_dir):
+    with open(os.path.join(golden_dir, "worked_example.json")) as f:
+        g = json.load(f)
+    arr = lambda key: np.array(g[key], dtype=np.float64)
+    ip = np.array(g["indptr"], np.int32)
+    ix = np.array(g["indices"], np.int32)
+    dq, dk, dv = A.backward(ip, ix, arr("q"), arr("k"), arr("v"), arr("dout"), g["scale"])
+    ex = g["expected"]
+    np.testing.assert_allclose(dq, np.array(ex["dq"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk, np.array(ex["dk"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dv, np.array(ex["dv"]), rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_matches_central_finite_differences(seed):
+    rng, ip, ix = _graph(seed, 9, 30)
+    H, d = 2, 3
+    q, k, v, do = (rng.standard_normal((9, H, d)) for _ in range(4))
+    scale = 0.61
+    dq, dk, dv = A.backward(ip, ix, q, k, v, do, scale)
+
+    def loss(q_, k_, v_):
+        out, _ = A.forward(ip, ix, q_, k_, v_, "dot", scale)
+        return float((out * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}; args_p[name] = xp
+            args_m = {"q": q, "k": k, "v": v}; args_m[name] = xm
+            num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) -
+                        loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def _torch_dense_grads(ip, ix, q, k, v, do, scale):
+    n = ip.size - 1
+    c = np.zeros((n, n))
+    np.add.at(c, (np.repeat(np.arange(n), np.diff(ip)), ix), 1.0)
+    add = torch.from_numpy(np.where(c > 0, np.log(np.maximum(c, 1)), -np.inf))
+    T = lambda x: torch.from_numpy(x).permute(1, 0, 2).contiguous().requires_grad_(True)
+    tq, tk, tv = T(q), T(k), T(v)
+    S = scale * torch.matmul(tq, tk.transpose(1, 2).contiguous()) + add  # [H, n, n]
+    has = torch.from_numpy(c.sum(1) > 0)
+    P = torch.softmax(S[:, has], dim=-1)
+    out = torch.zeros(q.shape[1], n, q.shape[2], dtype=torch.float64)
+    out[:, has] = torch.matmul(P, tv)
+    (out * torch.from_numpy(do).permute(1, 0, 2)).sum().backward()
+    back = lambda t: t.grad.permute(1, 0, 2).numpy()
+    return back(tq), back(tk), back(tv)
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_backward_matches_torch_autograd_dense(seed):
+    rng, ip, ix = _graph(seed, 30, 400)
+    # one empty row
+    dst = np.repeat(np.arange(30), np.diff(ip))
+    ip, ix = gg.csr_from_edges(30, ix[dst != 4], dst[dst != 4])
+    H, d = 3, 4
+    q, k, v, do = (rng.standard_normal((30, H, d)) for _ in range(4))
+    dq, dk, dv = A.backward(ip, ix, q, k, v, do, 0.5)
+    rq, rk, rv = _torch_dense_grads(ip, ix, q, k, v, do, 0.5)
+    np.testing.assert_allclose(dq, rq, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, rk, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, rv, rtol=1e-11, atol=1e-12)
+
+
+def test_gradient_invariants():
+    rng, ip, ix = _graph(5, 80, 900)
+    n, H, d = 80, 4, 8
+    q, k, v, do = (rng.standard_normal((n, H, d)) for _ in range(4))
+    dq, dk, dv = A.backward(ip, ix, q, k, v, do, None)
+    # shifting every key by a constant vector shifts a row's scores uniformly
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-12)
+    nonempty = np.diff(ip) > 0
+    np.testing.assert_allclose(dv.sum(axis=0), do[nonempty].sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_dq_vanishes_on_single_neighbour_and_equal_key_rows():
+    rng = np.random.default_rng(6)
+    n, H, d = 30, 2, 5
+    src = np.r_[rng.integers(0, n, n), [0, 1, 2]]
+    dst = np.r_[np.arange(n), [3, 3, 3]]         # row 3 gets 4 neighbours
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    q, k, v, do = (rng.standard_normal((n, H, d)) for _ in range(4))
+    k[ix[ip[3]:ip[4]]] = k[0]                    # all of row 3's keys equal
+    dq, _, _ = A.backward(ip, ix, q, k, v, do, None)
+    single = np.flatnonzero(np.diff(ip) == 1)
+    assert single.size > 10
+    assert np.all(dq[single] == 0.0)
+    np.testing.assert_allclose(dq[3], 0.0, atol=1e-14)
+
+
+def test_formulations_agree():
+    rng, ip, ix = _graph(7, 60, 700)
+    n, H, d = 60, 2, 6
+    q, k, v, do = (rng.standard_normal((n, H, d)) for _ in range(4))
+    a = A.backward(ip, ix, q, k, v, do, None)
+    b = A.backward_by_columns(ip, ix, q, k, v, do, None)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-12)
+    rows = np.arange(n)
+    out, lse, dq, cols, dkp, dvp = A.train_step_rows(ip, ix, q, k, v, do, rows, None)
+    fo, fl = A.forward(ip, ix, q, k, v, "dot", None)
+    np.testing.assert_allclose(out, fo, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dq, a[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dkp, a[1][cols], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dvp, a[2][cols], rtol=1e-12, atol=1e-12)
+    sel = rng.choice(n, 12, replace=False)
+    np.testing.assert_allclose(A.grad_q_rows(ip, ix, q, k, v, do, sel, None), a[0][sel],
+                               rtol=1e-12, atol=1e-12)
+    gk, gv = A.grad_kv_cols(ip, ix, q, k, v, do, sel, None)
+    np.testing.assert_allclose(gk, a[1][sel], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gv, a[2][sel], rtol=1e-12, atol=1e-12)
+
+
+def test_gat_scale_is_a_temperature():
+    """LeakyReLU is positively homogeneous, so scale * LeakyReLU(s + t) equals the score
+    of (scale * s, scale * t) at scale 1."""
+    rng, ip, ix = _graph(8, 40, 300)
+    s, t = rng.standard_normal((40, 2)), rng.standard_normal((40, 2))
+    v = rng.standard_normal((40, 2, 3))
+    a, la = A.forward(ip, ix, s, t, v, "gat", 2.5, 0.2)
+    b, lb = A.forward(ip, ix, 2.5 * s, 2.5 * t, v, "gat", 1.0, 0.2)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=1e-13, atol=1e-14)

@@ -1,0 +1,77 @@
+"""Pins of the reference planner: scipy's CSR->CSC conversion, partition invariants,
+chunk tiling and CSR validation."""
+import numpy as np
+import pytest
+import scipy.sparse as sp
+
+import graphgen as gg
+from oracle import planner as P
+
+
+def _graphs():
+    rng = np.random.default_rng(0)
+    yield "multigraph", gg.random_multigraph(200, 3000, rng, hub_rows=(3, 77), hub_deg=700)
+    yield "empty_rows", gg.csr_from_edges(50, rng.integers(0, 50, 80), rng.integers(0, 10, 80))
+    yield "no_edges", (np.zeros(6, np.int32), np.zeros(0, np.int32))
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    yield "chunglu20k", gg.make_graph(w, n=20_000)
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+def test_transpose_matches_scipy(name, g):
+    ip, ix = g
+    n = ip.size - 1
+    colptr, rowidx = P.transpose(ip, ix)
+    eid = np.arange(ix.size, dtype=np.int64)
+    m = sp.csr_matrix((eid, ix, ip), shape=(n, n)).tocsc()
+    assert np.array_equal(colptr, m.indptr)
+    assert np.array_equal(rowidx, m.indices)
+    # each CSC slot names the CSR edge it came from: same (row, col) and stable order
+    edge_row = np.repeat(np.arange(n), np.diff(ip))
+    assert np.array_equal(edge_row[m.data], rowidx)
+    # stable: within a column, CSR edge ids (hence destinations) ascend
+    col_of_slot = np.repeat(np.arange(n), np.diff(colptr))
+    same_col = col_of_slot[1:] == col_of_slot[:-1]
+    assert np.all(np.diff(m.data)[same_col] > 0)
+    assert np.all(np.diff(rowidx)[same_col] >= 0)
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("tl,th,c", [(16, 256, 128), (1, 1, 1), (0, 100, 37), (32, 1024, 1024)])
+def test_bins_partition_and_chunks_tile(name, g, tl, th, c):
+    ip, ix = g
+    n = ip.size - 1
+    plan = P.plan(ip, ix, tl, th, c)
+    deg = np.diff(ip.astype(np.int64))
+    allrows = np.concatenate([plan["row_light"], plan["row_medium"], plan["row_hub"]])
+    assert np.array_equal(np.sort(allrows), np.arange(n))
+    assert np.all(deg[plan["row_light"]] <= tl)
+    assert np.all((deg[plan["row_medium"]] > tl) & (deg[plan["row_medium"]] <= th))
+    assert np.all(deg[plan["row_hub"]] > th)
+    for b in ("row_light", "row_medium", "row_hub"):
+        r = plan[b].astype(np.int64)
+        key = -deg[r] * (n + 1) + r          # degree descending, then id ascending
+        assert np.all(np.diff(key) > 0)
+    ptr = plan["row_hub_chunk_ptr"]
+    assert ptr.size == plan["row_hub"].size + 1 and ptr[0] == 0
+    for h, i in enumerate(plan["row_hub"]):
+        b, e = plan["row_chunk_begin"][ptr[h]:ptr[h + 1]], plan["row_chunk_end"][ptr[h]:ptr[h + 1]]
+        assert np.all(plan["row_chunk_row"][ptr[h]:ptr[h + 1]] == i)
+        assert b[0] == ip[i] and e[-1] == ip[i + 1]
+        assert np.array_equal(b[1:], e[:-1]) and np.all(e - b <= c) and np.all(e > b)
+    odeg = np.bincount(ix, minlength=n)
+    assert np.array_equal(np.sort(np.concatenate(
+        [plan["col_light"], plan["col_medium"], plan["col_hub"]])), np.arange(n))
+    assert np.all(odeg[plan["col_hub"]] > th)
+    assert plan["col_chunk_end"].sum() - plan["col_chunk_begin"].sum() == odeg[plan["col_hub"]].sum()
+
+
+def test_validate_csr():
+    ip = np.array([0, 2, 3], np.int32)
+    ix = np.array([1, 0, 1], np.int32)
+    assert P.validate_csr(ip, ix)
+    assert not P.validate_csr(np.array([1, 2, 3]), ix)           # indptr[0] != 0
+    assert not P.validate_csr(np.array([0, 3, 2]), ix[:2])       # not monotone
+    assert not P.validate_csr(np.array([0, 2, 4]), ix)           # indptr[N] != E
+    assert not P.validate_csr(ip, np.array([1, 0, 2], np.int32))  # index out of range
+    assert not P.validate_csr(ip, np.array([1, -1, 0], np.int32))
