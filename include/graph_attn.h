@@ -1,0 +1,206 @@
+/*
+ * graph_attn.h -- C ABI of the fused CSR graph-attention library for AMD MI355X (gfx950).
+ *
+ * What the library computes is the attention-based layer family of "On Efficient Scaling
+ * of GNNs via IO-Aware Layers Implementations" (gist.science explainer of arXiv
+ * 2605.31500), Technical Summary > Methodology: for every destination node of a CSR
+ * graph, score each neighbour edge, normalise the scores with an online softmax whose
+ * running statistics stay in registers, and accumulate the weighted neighbour values in
+ * one streaming pass, so no edge-sized score or probability tensor is ever stored. The
+ * backward keeps one log-sum-exp per node and head and recomputes the attention weights;
+ * it reads a cached transpose of the adjacency (same section, SpMM paragraph: transposed
+ * adjacency precomputed for the backward pass), so dK/dV need no atomics. Rows are
+ * binned by degree (same section, reduction paragraph: light / heavy split by a degree
+ * threshold, heavy rows reduced over edge chunks in parallel).
+ *
+ * Score forms (dot: Graph-Transformer layer; gat: GAT-style layer), per head h:
+ *     dot:  e_ij = scale * sum_c q[i,h,c] k[j,h,c]
+ *     gat:  e_ij = scale * LeakyReLU_{neg_slope}(s[i,h] + t[j,h])
+ *     out[i,h,:] = sum_j softmax_j(e_ij) v[j,h,:],   lse[i,h] = ln sum_j exp(e_ij)
+ * A row with no neighbours gives out = 0 and lse = -inf.
+ *
+ * Conventions shared by every call
+ *   Graph: CSR with int32 indptr [N+1] and indices [E], row i = destination, indices =
+ *     its sources. Parallel edges count with multiplicity. N, E < 2^31.
+ *   Features: node-major, contiguous [N, H, d] in the call's dtype (fp32 or bf16), each
+ *     pointer 16-byte aligned, H*d*sizeof(dtype) a multiple of 16 bytes and at most 1024
+ *     bytes, d*sizeof(dtype) a power of two between 32 and 1024 bytes dividing the row.
+ *     lse is fp32 [N, H].  GAT mode: s and t are fp32 [N, H] (4-byte aligned).
+ *   Ownership: the caller allocates and frees every device buffer (features, outputs,
+ *     the plan's device copy, workspaces). The library never calls hipMalloc/hipFree;
+ *     it owns only the host-side plan metadata.
+ *   Streams: `stream` is a hipStream_t (NULL = the default stream). fwd/bwd only enqueue
+ *     work and return; results are ready when the stream reaches them.
+ *   Errors: every call returns a ga_status; nothing throws or aborts across the ABI.
+ *     Argument checks run before any HIP call, so an invalid call enqueues nothing.
+ *   Determinism: no atomics anywhere; partial states merge in a fixed order, so two runs
+ *     on the same inputs are bitwise identical.
+ */
+#ifndef GRAPH_ATTN_H
+#define GRAPH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GA_OK = 0,
+  GA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misaligned pointer, bad enum */
+  GA_ERR_BAD_GRAPH = 2,    /* CSR fails validation (indptr[0]!=0, not monotone,
+                              indptr[N]!=E, index outside [0,N)) */
+  GA_ERR_UNSUPPORTED = 3,  /* feature geometry or mode this build does not implement */
+  GA_ERR_WORKSPACE = 4,    /* workspace pointer null or smaller than required */
+  GA_ERR_NOT_READY = 5,    /* plan not uploaded, or transpose missing for backward */
+  GA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
+  GA_ERR_HOST_ALLOC = 7    /* host memory for the plan could not be allocated */
+} ga_status;
+
+typedef enum { GA_F32 = 0, GA_BF16 = 1 } ga_dtype;
+typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
+
+/* Degree-binning thresholds. Rows (and, for the transpose, columns) with degree
+ * <= light_max_deg are "light" (one lane group per row); degree in
+ * (light_max_deg, hub_min_deg_exclusive] is "medium" (one wavefront per row); larger
+ * rows are "hubs", cut into chunks of hub_chunk edges that separate wavefronts reduce,
+ * merged in ascending chunk order. build_csc != 0 also builds the transpose needed by
+ * graph_attn_bwd. Constraints: 0 <= light_max_deg <= hub_min_deg_exclusive,
+ * hub_chunk >= 1. */
+typedef struct {
+  int32_t light_max_deg;
+  int32_t hub_min_deg_exclusive;
+  int32_t hub_chunk;
+  int32_t build_csc;
+} ga_plan_opts;
+
+/* Counts describing a built plan (all int64 so the struct has no padding). */
+typedef struct {
+  int64_t n_nodes, n_edges;
+  int64_t n_row_light, n_row_medium, n_row_hub, n_row_chunks;
+  int64_t has_csc;
+  int64_t n_col_light, n_col_medium, n_col_hub, n_col_chunks;
+  int64_t max_in_degree, max_out_degree;
+  int64_t light_max_deg, hub_min_deg_exclusive, hub_chunk;
+  int64_t device_bytes;
+  int64_t uploaded;
+} ga_plan_info;
+
+typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */
+
+/* Library version string, e.g. "graph_attn 0.1 gfx950". Never NULL. */
+const char* graph_attn_version(void);
+
+/* Human-readable name of a status code. Never NULL. */
+const char* graph_attn_status_string(ga_status status);
+
+/* Fill *opts with the default thresholds. */
+ga_status graph_attn_plan_opts_default(ga_plan_opts* opts);
+
+/* Build a plan from a host CSR graph (the planner of the degree-aware tiling; runs on the
+ * host, O(N + E), no HIP calls). The CSR is always validated; GA_ERR_BAD_GRAPH on failure.
+ * Bins: each bin lists its rows by degree descending, ties by ascending row id. Hub row
+ * chunks: [indptr[i] + k*C, min(indptr[i] + (k+1)*C, indptr[i+1])), listed hub by hub.
+ * Transpose (build_csc): colptr [N+1] and rowidx [E], destinations ascending within each
+ * column (the order a stable scatter over rows produces); column bins/chunks follow the
+ * same rules on out-degree. indptr_host/indices_host are only read during the call
+ * (indices_host may be NULL when n_edges == 0). opts NULL = defaults. On success *out
+ * receives a plan to be released with graph_attn_plan_destroy. */
+ga_status graph_attn_plan_create(const int32_t* indptr_host, const int32_t* indices_host,
+                                 int64_t n_nodes, int64_t n_edges, const ga_plan_opts* opts,
+                                 ga_plan** out);
+
+/* Counts of a plan. */
+ga_status graph_attn_plan_get_info(const ga_plan* plan, ga_plan_info* info);
+
+/* Bytes of device memory the plan's device copy needs (the CSR, bins, chunk tables and,
+ * if built, the transpose; each array 256-byte aligned). */
+ga_status graph_attn_plan_device_bytes(const ga_plan* plan, size_t* bytes);
+
+/* Copy the plan to caller-owned device memory `dev_buf` (256-byte aligned, `bytes` >=
+ * graph_attn_plan_device_bytes) with hipMemcpyAsync on `stream`, then wait for the copy.
+ * The plan keeps pointers into dev_buf: the buffer must outlive every fwd/bwd call that
+ * uses the plan. Uploading again re-targets the plan to the new buffer. */
+ga_status graph_attn_plan_upload(ga_plan* plan, void* dev_buf, size_t bytes, void* stream);
+
+/* Host views of the plan's arrays, for tests and tools. Names: "indptr", "indices",
+ * "row_light", "row_medium", "row_hub", "row_chunk_row", "row_chunk_begin",
+ * "row_chunk_end", "row_hub_chunk_ptr", and with the transpose "colptr", "rowidx",
+ * "col_light", "col_medium", "col_hub", "col_chunk_row", "col_chunk_begin",
+ * "col_chunk_end", "col_hub_chunk_ptr". *data stays valid until the plan is destroyed
+ * (it may be NULL when *count == 0). GA_ERR_INVALID_ARG for an unknown name,
+ * GA_ERR_NOT_READY for a transpose array of a plan built without it. */
+ga_status graph_attn_plan_array(const ga_plan* plan, const char* name, const int32_t** data,
+                                int64_t* count);
+
+/* Number of exported array names and the i-th name (NULL if out of range). */
+int32_t graph_attn_plan_array_count(void);
+const char* graph_attn_plan_array_name(int32_t index);
+
+/* Release a plan's host memory (the caller frees the device copy). NULL is a no-op. */
+void graph_attn_plan_destroy(ga_plan* plan);
+
+/* Workspace the forward needs: fp32 (m, l, acc) partial states of the hub-row chunks,
+ * n_row_chunks * (H*d + 2*H) * 4 bytes, 256-byte aligned sections (0 if no hub rows). */
+ga_status graph_attn_fwd_workspace_bytes(const ga_plan* plan, int32_t heads, int32_t dim,
+                                         size_t* bytes);
+
+/* Forward (Methodology, attention-based layers, forward pass: fused score -> online
+ * softmax -> weighted value sum; per-node log-sum-exp kept for the backward).
+ *   dot: q_or_s = q, k_or_t = k, both [N,H,d] of `dtype`;  gat: q_or_s = s,
+ *   k_or_t = t, both fp32 [N,H]. v [N,H,d] of `dtype`. out [N,H,d] of `dtype` (bf16 by
+ *   round-to-nearest-even), lse fp32 [N,H] (natural log). scale multiplies the score
+ *   (1/sqrt(d) is the usual dot value, 1 the GAT value); neg_slope is the LeakyReLU
+ *   slope (gat only). workspace: graph_attn_fwd_workspace_bytes bytes (NULL allowed when
+ *   that is 0). All computation in fp32. The plan must be uploaded. */
+ga_status graph_attn_fwd(const ga_plan* plan, ga_score score, ga_dtype dtype, int32_t heads,
+                         int32_t dim, float scale, float neg_slope, const void* q_or_s,
+                         const void* k_or_t, const void* v, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace the backward needs: per-node (lse*log2 e, D) records N*H*8 bytes, fp32 dQ
+ * partials of hub-row chunks n_row_chunks*(2*H*d + 4*ceil(H/4))*4 bytes and fp32 (dK, dV)
+ * partials of hub-column chunks n_col_chunks*2*H*d*4 bytes, each section 256-byte
+ * aligned. */
+ga_status graph_attn_bwd_workspace_bytes(const ga_plan* plan, int32_t heads, int32_t dim,
+                                         size_t* bytes);
+
+/* Backward of the dot-score layer by recomputation (Methodology, attention-based layers,
+ * backward pass: attention weights recomputed from the cached per-node log-sum-exp).
+ * With P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, v_j>, D_i = sum_j P_ij dp_ij (per head),
+ * dS_ij = P_ij (dp_ij - D_i):
+ *   dq_i = scale sum_j dS_ij k_j   (over CSR rows; D_i is accumulated in the same pass
+ *          from the recomputed weights, so the forward output is not needed)
+ *   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i   (over the cached transpose)
+ * Inputs: q, k, v, dout [N,H,d] of `dtype`, lse fp32 [N,H] as produced by graph_attn_fwd.
+ * Outputs dq, dk, dv [N,H,d] of `dtype`, each fully written (rows and columns with no
+ * edges get zeros). Needs a plan built with build_csc and uploaded (else
+ * GA_ERR_NOT_READY). GA_SCORE_GAT returns GA_ERR_UNSUPPORTED in this version. */
+ga_status graph_attn_bwd(const ga_plan* plan, ga_score score, ga_dtype dtype, int32_t heads,
+                         int32_t dim, float scale, const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel timers (tracing). When enabled, every kernel the library launches is bracketed
+ * by two hipEvents recorded on its stream; graph_attn_timer_read synchronises those
+ * events and reports, per kernel name, the number of launches and their summed duration
+ * in milliseconds. Process-wide, thread-safe. Disabled by default. */
+ga_status graph_attn_timer_enable(int32_t enable);
+ga_status graph_attn_timer_reset(void);
+/* Number of distinct kernel names recorded since the last reset. */
+int32_t graph_attn_timer_count(void);
+/* The index-th record: name (static string), launches and total milliseconds. */
+ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launches,
+                                double* total_ms);
+
+/* Device-to-device copy of `bytes` bytes with the library's streaming copy kernel (16-byte
+ * vector loads/stores). Both pointers 16-byte aligned, bytes a multiple of 16. Used to
+ * measure copy bandwidth and to calibrate traffic counters against a known byte count. */
+ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRAPH_ATTN_H */

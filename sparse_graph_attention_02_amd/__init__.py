@@ -1,0 +1,280 @@
+"""Fused CSR graph attention for AMD MI355X (gfx950): Python binding.
+
+Every step of the computation runs in the HIP kernels of ``libgraph_attn.so``; this module
+only marshals arguments: it takes tensors' device pointers, allocates outputs and
+workspaces with torch (the library never allocates device memory) and passes torch's
+current HIP stream.  ``capi`` holds the raw C entry points under their C names.
+
+    plan = Plan(indptr, indices)          # host planner: bins, hub chunks, transpose
+    plan.upload("cuda")                   # one device copy, caller-owned (torch)
+    out, lse = fwd(plan, q, k, v)         # dot score, scale 1/sqrt(d)
+    dq, dk, dv = bwd(plan, q, k, v, dout, lse)
+    out, lse = fwd(plan, s, t, v, score="gat")
+
+Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
+Summary > Methodology, attention-based layers (fused score -> online softmax ->
+aggregation; backward recomputes weights from the per-node log-sum-exp).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from ctypes import POINTER, byref, c_int32, c_int64, c_size_t, c_void_p
+
+import numpy as np
+
+from . import capi
+from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,  # noqa: F401
+                   graph_attn_bwd, graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
+                   graph_attn_fwd, graph_attn_fwd_workspace_bytes, graph_attn_plan_array,
+                   graph_attn_plan_array_count, graph_attn_plan_array_name,
+                   graph_attn_plan_create, graph_attn_plan_destroy,
+                   graph_attn_plan_device_bytes, graph_attn_plan_get_info,
+                   graph_attn_plan_opts_default, graph_attn_plan_upload,
+                   graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
+                   graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
+
+__all__ = ["Plan", "fwd", "bwd", "graph_attention", "copy_probe", "timers", "default_opts",
+           "GraphAttnError", "capi"]
+
+
+def default_opts() -> dict:
+    o = capi.ga_plan_opts()
+    graph_attn_plan_opts_default(byref(o))
+    return {n: int(getattr(o, n)) for n, _ in o._fields_}
+
+
+class Plan:
+    """A graph's cached metadata: degree bins, hub chunks and (optionally) the transpose,
+    built on the host by the library's planner; ``upload`` copies it to the GPU."""
+
+    def __init__(self, indptr, indices, *, light_max_deg=None, hub_min_deg_exclusive=None,
+                 hub_chunk=None, build_csc=True):
+        ip = np.ascontiguousarray(indptr, dtype=np.int32)
+        ix = np.ascontiguousarray(indices, dtype=np.int32)
+        opts = capi.ga_plan_opts()
+        graph_attn_plan_opts_default(byref(opts))
+        for k, v in (("light_max_deg", light_max_deg),
+                     ("hub_min_deg_exclusive", hub_min_deg_exclusive),
+                     ("hub_chunk", hub_chunk)):
+            if v is not None:
+                setattr(opts, k, int(v))
+        opts.build_csc = 1 if build_csc else 0
+        h = c_void_p()
+        graph_attn_plan_create(ip.ctypes.data_as(POINTER(c_int32)),
+                               ix.ctypes.data_as(POINTER(c_int32)) if ix.size else None,
+                               ip.size - 1, ix.size, byref(opts), byref(h))
+        self._h = h
+        self.n_nodes = ip.size - 1
+        self.n_edges = ix.size
+        self.device_buffer = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        i = capi.ga_plan_info()
+        graph_attn_plan_get_info(self._h, byref(i))
+        return i.as_dict()
+
+    def array(self, name: str) -> np.ndarray:
+        """Copy of one of the plan's host arrays (see graph_attn_plan_array)."""
+        p = POINTER(c_int32)()
+        n = c_int64()
+        graph_attn_plan_array(self._h, name.encode(), byref(p), byref(n))
+        if n.value == 0:
+            return np.zeros(0, np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
+
+    def device_bytes(self) -> int:
+        b = c_size_t()
+        graph_attn_plan_device_bytes(self._h, byref(b))
+        return int(b.value)
+
+    def upload(self, device="cuda", stream=None):
+        import torch
+        nbytes = self.device_bytes()
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        with torch.cuda.device(buf.device):
+            graph_attn_plan_upload(self._h, c_void_p(buf.data_ptr()), nbytes, _stream(stream))
+        self.device_buffer = buf
+        return self
+
+    def fwd_workspace_bytes(self, heads: int, dim: int) -> int:
+        b = c_size_t()
+        graph_attn_fwd_workspace_bytes(self._h, heads, dim, byref(b))
+        return int(b.value)
+
+    def bwd_workspace_bytes(self, heads: int, dim: int) -> int:
+        b = c_size_t()
+        graph_attn_bwd_workspace_bytes(self._h, heads, dim, byref(b))
+        return int(b.value)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                graph_attn_plan_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return GA_F32
+    if t.dtype == torch.bfloat16:
+        return GA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _ptr(t):
+    return c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {tuple(shape)} {dtype}, got "
+                         f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()}")
+
+
+def _workspace(nbytes, device, ws):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2, out=None,
+        lse=None, workspace=None, stream=None):
+    """Forward of the fused layer; returns (out [N,H,d], lse [N,H] fp32).
+
+    dot: q, k, v [N,H,d] (fp32 or bf16), scale defaults to 1/sqrt(d).
+    gat: s, t fp32 [N,H], v [N,H,d], scale defaults to 1, neg_slope to 0.2.
+    """
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    N, H, d = v.shape
+    dev = v.device
+    if N != plan.n_nodes:
+        raise ValueError("feature rows != plan nodes")
+    sc = GA_SCORE_DOT if score == "dot" else GA_SCORE_GAT if score == "gat" else None
+    if sc is None:
+        raise ValueError(score)
+    if sc == GA_SCORE_DOT:
+        _need(q_or_s, "q", (N, H, d), v.dtype, dev)
+        _need(k_or_t, "k", (N, H, d), v.dtype, dev)
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+    else:
+        _need(q_or_s, "s", (N, H), torch.float32, dev)
+        _need(k_or_t, "t", (N, H), torch.float32, dev)
+        scale = 1.0 if scale is None else scale
+    _need(v, "v", (N, H, d), v.dtype, dev)
+    out = torch.empty_like(v) if out is None else out
+    lse = torch.empty((N, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", (N, H, d), v.dtype, dev)
+    _need(lse, "lse", (N, H), torch.float32, dev)
+    ws, wsb = _workspace(plan.fwd_workspace_bytes(H, d), dev, workspace)
+    with torch.cuda.device(dev):
+        graph_attn_fwd(plan.handle, sc, _dtype_code(v), H, d, float(scale), float(neg_slope),
+                       _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+                       wsb, _stream(stream))
+    return out, lse
+
+
+def bwd(plan: Plan, q, k, v, dout, lse, *, scale=None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Backward of the dot-score layer from the forward's lse; returns (dq, dk, dv), each
+    [N,H,d] like q."""
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    N, H, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _need(t, name, (N, H, d), q.dtype, dev)
+    _need(lse, "lse", (N, H), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    ws, wsb = _workspace(plan.bwd_workspace_bytes(H, d), dev, workspace)
+    with torch.cuda.device(dev):
+        graph_attn_bwd(plan.handle, GA_SCORE_DOT, _dtype_code(q), H, d, float(scale),
+                       _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
+                       _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(stream))
+    return dq, dk, dv
+
+
+def _autograd_fn():
+    import torch
+
+    class _GraphAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, plan, scale):
+            out, lse = fwd(plan, q.contiguous(), k.contiguous(), v.contiguous(), scale=scale)
+            ctx.save_for_backward(q, k, v, lse)
+            ctx.plan, ctx.scale = plan, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, g):
+            q, k, v, lse = ctx.saved_tensors
+            dq, dk, dv = bwd(ctx.plan, q.contiguous(), k.contiguous(), v.contiguous(),
+                             g.contiguous(), lse, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    return _GraphAttention
+
+
+_FN = None
+
+
+def graph_attention(plan: Plan, q, k, v, scale=None):
+    """Dot-score graph attention as a differentiable torch op (forward saves lse; backward
+    recomputes the weights)."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    return _FN.apply(q, k, v, plan, scale)
+
+
+def copy_probe(dst, src, stream=None):
+    import torch
+    nbytes = src.numel() * src.element_size()
+    with torch.cuda.device(src.device):
+        graph_attn_copy_probe(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def timers(enable=None, reset=False) -> dict:
+    """Per-kernel {name: (launches, total_ms)} from the library's event timers.
+    ``enable`` switches recording, ``reset`` clears the records (after reading)."""
+    if enable is not None:
+        graph_attn_timer_enable(1 if enable else 0)
+    n = graph_attn_timer_count()
+    res = {}
+    for i in range(n):
+        name = ctypes.c_char_p()
+        launches = c_int64()
+        ms = ctypes.c_double()
+        graph_attn_timer_read(i, byref(name), byref(launches), byref(ms))
+        res[name.value.decode()] = (int(launches.value), float(ms.value))
+    if reset:
+        graph_attn_timer_reset()
+    return res

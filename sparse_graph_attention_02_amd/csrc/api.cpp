@@ -1,0 +1,477 @@
+// C-ABI layer: argument validation, plan lifetime and upload, workspace sizing, kernel
+// dispatch and kernel timers. Every check that can fail does so before the first HIP
+// call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ga_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- timers
+struct TimerRec {
+  const char* name;
+  hipEvent_t begin, end;
+};
+
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+std::vector<TimerRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+struct Agg {
+  const char* name;
+  int64_t launches;
+  double ms;
+};
+std::vector<Agg> g_agg;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void timer_hook(const char* name, void* stream, int begin) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  hipEvent_t e = pool_get();
+  if (!e) return;
+  hipEventRecord(e, static_cast<hipStream_t>(stream));
+  if (begin) {
+    g_recs.push_back(TimerRec{name, e, nullptr});
+  } else {
+    for (auto it = g_recs.rbegin(); it != g_recs.rend(); ++it)
+      if (it->end == nullptr && std::strcmp(it->name, name) == 0) {
+        it->end = e;
+        return;
+      }
+    g_pool.push_back(e);
+  }
+}
+
+ga::TimerHook active_hook() {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  return g_timer_on ? timer_hook : nullptr;
+}
+
+// ---------------------------------------------------------------- plan arrays
+struct ArrayRef {
+  const char* name;
+  const std::vector<int32_t>* (*get)(const ga_plan*);
+  bool csc;
+};
+
+#define GA_REF(NAME, EXPR, CSC) \
+  {NAME, [](const ga_plan* p) -> const std::vector<int32_t>* { return &(EXPR); }, CSC}
+const ArrayRef kArrays[] = {
+    GA_REF("indptr", p->indptr, false),
+    GA_REF("indices", p->indices, false),
+    GA_REF("row_light", p->rows.light, false),
+    GA_REF("row_medium", p->rows.medium, false),
+    GA_REF("row_hub", p->rows.hub, false),
+    GA_REF("row_chunk_row", p->rows.chunk_row, false),
+    GA_REF("row_chunk_begin", p->rows.chunk_begin, false),
+    GA_REF("row_chunk_end", p->rows.chunk_end, false),
+    GA_REF("row_hub_chunk_ptr", p->rows.hub_chunk_ptr, false),
+    GA_REF("colptr", p->colptr, true),
+    GA_REF("rowidx", p->rowidx, true),
+    GA_REF("col_light", p->cols.light, true),
+    GA_REF("col_medium", p->cols.medium, true),
+    GA_REF("col_hub", p->cols.hub, true),
+    GA_REF("col_chunk_row", p->cols.chunk_row, true),
+    GA_REF("col_chunk_begin", p->cols.chunk_begin, true),
+    GA_REF("col_chunk_end", p->cols.chunk_end, true),
+    GA_REF("col_hub_chunk_ptr", p->cols.hub_chunk_ptr, true),
+};
+#undef GA_REF
+constexpr int kNumArrays = sizeof(kArrays) / sizeof(kArrays[0]);
+
+size_t device_layout(const ga_plan* p, std::vector<size_t>* offsets) {
+  size_t off = 0;
+  for (int i = 0; i < kNumArrays; ++i) {
+    const bool present = !kArrays[i].csc || p->has_csc;
+    const size_t n = present ? kArrays[i].get(p)->size() : 0;
+    if (offsets) offsets->push_back(off);
+    off += align_up(n * sizeof(int32_t));
+  }
+  return off;
+}
+
+// ---------------------------------------------------------------- argument checks
+ga_status make_geometry(ga_dtype dt, int32_t heads, int32_t dim, ga::Geometry* g) {
+  if (dt != GA_F32 && dt != GA_BF16) return GA_ERR_INVALID_ARG;
+  if (heads < 1 || dim < 1) return GA_ERR_INVALID_ARG;
+  const int64_t eb = dt == GA_F32 ? 4 : 2;
+  const int64_t head_bytes = dim * eb, row_bytes = head_bytes * heads;
+  if (head_bytes % 16 || row_bytes > 1024 || row_bytes % 16) return GA_ERR_UNSUPPORTED;
+  g->heads = heads;
+  g->dim = dim;
+  g->elem_bytes = static_cast<int>(eb);
+  g->G = static_cast<int>(row_bytes / 16);
+  g->LH = static_cast<int>(head_bytes / 16);
+  return GA_OK;
+}
+
+ga_status check_ptr(const void* p, size_t align) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  return aligned(p, align) ? GA_OK : GA_ERR_INVALID_ARG;
+}
+
+size_t fwd_ws_bytes(const ga_plan* p, const ga::Geometry& g) {
+  const size_t nc = p->rows.chunk_row.size();
+  if (nc == 0) return 0;
+  return align_up(nc * g.heads * 2 * sizeof(float)) +
+         align_up(nc * size_t(g.heads) * g.dim * sizeof(float));
+}
+
+size_t bwd_ws_bytes(const ga_plan* p, const ga::Geometry& g) {
+  const size_t F = size_t(g.heads) * g.dim;
+  return align_up(size_t(p->n) * g.heads * 2 * sizeof(float)) +
+         align_up(p->rows.chunk_row.size() * ga::dq_partial_floats(g.heads, g.dim) *
+                  sizeof(float)) +
+         align_up(p->cols.chunk_row.size() * 2 * F * sizeof(float));
+}
+
+ga_status check_device(const ga_plan* p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
+  return dev == p->device ? GA_OK : GA_ERR_INVALID_ARG;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* graph_attn_version(void) { return "graph_attn 0.1 gfx950"; }
+
+const char* graph_attn_status_string(ga_status s) {
+  switch (s) {
+    case GA_OK: return "GA_OK";
+    case GA_ERR_INVALID_ARG: return "GA_ERR_INVALID_ARG: invalid argument";
+    case GA_ERR_BAD_GRAPH: return "GA_ERR_BAD_GRAPH: CSR failed validation";
+    case GA_ERR_UNSUPPORTED: return "GA_ERR_UNSUPPORTED: unsupported geometry or mode";
+    case GA_ERR_WORKSPACE: return "GA_ERR_WORKSPACE: workspace missing or too small";
+    case GA_ERR_NOT_READY: return "GA_ERR_NOT_READY: plan not uploaded or transpose missing";
+    case GA_ERR_HIP: return "GA_ERR_HIP: HIP runtime error";
+    case GA_ERR_HOST_ALLOC: return "GA_ERR_HOST_ALLOC: host allocation failed";
+  }
+  return "unknown ga_status";
+}
+
+ga_status graph_attn_plan_opts_default(ga_plan_opts* o) {
+  if (!o) return GA_ERR_INVALID_ARG;
+  o->light_max_deg = 16;
+  o->hub_min_deg_exclusive = 1024;
+  o->hub_chunk = 512;
+  o->build_csc = 1;
+  return GA_OK;
+}
+
+ga_status graph_attn_plan_create(const int32_t* indptr, const int32_t* indices, int64_t n,
+                                 int64_t e, const ga_plan_opts* opts, ga_plan** out) {
+  if (!out) return GA_ERR_INVALID_ARG;
+  *out = nullptr;
+  ga_plan_opts o;
+  if (opts)
+    o = *opts;
+  else
+    graph_attn_plan_opts_default(&o);
+  ga_plan* p = new (std::nothrow) ga_plan();
+  if (!p) return GA_ERR_HOST_ALLOC;
+  const ga_status s = ga::build_plan(indptr, indices, n, e, o, p);
+  if (s != GA_OK) {
+    delete p;
+    return s;
+  }
+  *out = p;
+  return GA_OK;
+}
+
+ga_status graph_attn_plan_get_info(const ga_plan* p, ga_plan_info* info) {
+  if (!p || !info) return GA_ERR_INVALID_ARG;
+  info->n_nodes = p->n;
+  info->n_edges = p->e;
+  info->n_row_light = static_cast<int64_t>(p->rows.light.size());
+  info->n_row_medium = static_cast<int64_t>(p->rows.medium.size());
+  info->n_row_hub = static_cast<int64_t>(p->rows.hub.size());
+  info->n_row_chunks = static_cast<int64_t>(p->rows.chunk_row.size());
+  info->has_csc = p->has_csc;
+  info->n_col_light = static_cast<int64_t>(p->cols.light.size());
+  info->n_col_medium = static_cast<int64_t>(p->cols.medium.size());
+  info->n_col_hub = static_cast<int64_t>(p->cols.hub.size());
+  info->n_col_chunks = static_cast<int64_t>(p->cols.chunk_row.size());
+  info->max_in_degree = p->max_in;
+  info->max_out_degree = p->max_out;
+  info->light_max_deg = p->opts.light_max_deg;
+  info->hub_min_deg_exclusive = p->opts.hub_min_deg_exclusive;
+  info->hub_chunk = p->opts.hub_chunk;
+  info->device_bytes = static_cast<int64_t>(device_layout(p, nullptr));
+  info->uploaded = p->uploaded;
+  return GA_OK;
+}
+
+ga_status graph_attn_plan_device_bytes(const ga_plan* p, size_t* bytes) {
+  if (!p || !bytes) return GA_ERR_INVALID_ARG;
+  *bytes = device_layout(p, nullptr);
+  return GA_OK;
+}
+
+ga_status graph_attn_plan_upload(ga_plan* p, void* dev_buf, size_t bytes, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  std::vector<size_t> off;
+  const size_t need = device_layout(p, &off);
+  if (need > 0 && (!dev_buf || !aligned(dev_buf, kAlign))) return GA_ERR_INVALID_ARG;
+  if (bytes < need) return GA_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(dev_buf);
+  const int32_t* ptrs[kNumArrays];
+  for (int i = 0; i < kNumArrays; ++i) {
+    ptrs[i] = reinterpret_cast<const int32_t*>(base + off[i]);
+    const bool present = !kArrays[i].csc || p->has_csc;
+    if (!present) continue;
+    const std::vector<int32_t>& v = *kArrays[i].get(p);
+    if (v.empty()) continue;
+    if (hipMemcpyAsync(base + off[i], v.data(), v.size() * sizeof(int32_t), hipMemcpyHostToDevice,
+                       s) != hipSuccess)
+      return GA_ERR_HIP;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return GA_ERR_HIP;
+  auto bins = [&](int first, const ga::Bins& b) {
+    ga::DevBins d;
+    d.light = ptrs[first];
+    d.medium = ptrs[first + 1];
+    d.hub = ptrs[first + 2];
+    d.chunk_row = ptrs[first + 3];
+    d.chunk_begin = ptrs[first + 4];
+    d.chunk_end = ptrs[first + 5];
+    d.hub_chunk_ptr = ptrs[first + 6];
+    d.n_light = static_cast<int32_t>(b.light.size());
+    d.n_medium = static_cast<int32_t>(b.medium.size());
+    d.n_hub = static_cast<int32_t>(b.hub.size());
+    d.n_chunks = static_cast<int32_t>(b.chunk_row.size());
+    return d;
+  };
+  p->d_indptr = ptrs[0];
+  p->d_indices = ptrs[1];
+  p->d_rows = bins(2, p->rows);
+  p->d_colptr = ptrs[9];
+  p->d_rowidx = ptrs[10];
+  p->d_cols = p->has_csc ? bins(11, p->cols) : ga::DevBins{};
+  p->device = dev;
+  p->uploaded = true;
+  return GA_OK;
+}
+
+int32_t graph_attn_plan_array_count(void) { return kNumArrays; }
+
+const char* graph_attn_plan_array_name(int32_t i) {
+  return (i >= 0 && i < kNumArrays) ? kArrays[i].name : nullptr;
+}
+
+ga_status graph_attn_plan_array(const ga_plan* p, const char* name, const int32_t** data,
+                                int64_t* count) {
+  if (!p || !name || !data || !count) return GA_ERR_INVALID_ARG;
+  for (int i = 0; i < kNumArrays; ++i) {
+    if (std::strcmp(name, kArrays[i].name) != 0) continue;
+    if (kArrays[i].csc && !p->has_csc) return GA_ERR_NOT_READY;
+    const std::vector<int32_t>* v = kArrays[i].get(p);
+    *data = v->empty() ? nullptr : v->data();
+    *count = static_cast<int64_t>(v->size());
+    return GA_OK;
+  }
+  return GA_ERR_INVALID_ARG;
+}
+
+void graph_attn_plan_destroy(ga_plan* p) { delete p; }
+
+ga_status graph_attn_fwd_workspace_bytes(const ga_plan* p, int32_t heads, int32_t dim,
+                                         size_t* bytes) {
+  if (!p || !bytes || heads < 1 || dim < 1) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  g.heads = heads;
+  g.dim = dim;
+  *bytes = fwd_ws_bytes(p, g);
+  return GA_OK;
+}
+
+ga_status graph_attn_bwd_workspace_bytes(const ga_plan* p, int32_t heads, int32_t dim,
+                                         size_t* bytes) {
+  if (!p || !bytes || heads < 1 || dim < 1) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  g.heads = heads;
+  g.dim = dim;
+  *bytes = bwd_ws_bytes(p, g);
+  return GA_OK;
+}
+
+ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads,
+                         int32_t dim, float scale, float neg_slope, const void* a, const void* b,
+                         const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  if (score != GA_SCORE_DOT && score != GA_SCORE_GAT) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (!ga::fwd_supported(dtype, score, g)) return GA_ERR_UNSUPPORTED;
+  if (p->n > 0) {
+    const size_t score_align = score == GA_SCORE_DOT ? 16 : 4;
+    if ((s = check_ptr(a, score_align)) != GA_OK || (s = check_ptr(b, score_align)) != GA_OK ||
+        (s = check_ptr(v, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
+        (s = check_ptr(lse, 4)) != GA_OK)
+      return s;
+  }
+  const size_t need = fwd_ws_bytes(p, g);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+
+  ga::FwdArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.bins = p->d_rows;
+  args.a = a;
+  args.b = b;
+  args.v = v;
+  args.out = out;
+  args.lse = lse;
+  const size_t nc = p->rows.chunk_row.size();
+  args.ws_ml = static_cast<float*>(ws);
+  args.ws_acc = nc ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align_up(nc * heads * 2 * sizeof(float)))
+                   : nullptr;
+  args.sc2 = scale * 1.4426950408889634f;
+  args.neg_slope = neg_slope;
+  const int rc = ga::launch_fwd(dtype, score, g, args, p->n, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads,
+                         int32_t dim, float scale, const void* q, const void* k, const void* v,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  if (score != GA_SCORE_DOT && score != GA_SCORE_GAT) return GA_ERR_INVALID_ARG;
+  if (score == GA_SCORE_GAT) return GA_ERR_UNSUPPORTED;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (!ga::bwd_supported(dtype, g)) return GA_ERR_UNSUPPORTED;
+  if (p->n > 0) {
+    const void* f[] = {q, k, v, dout, dq, dk, dv};
+    for (const void* x : f)
+      if ((s = check_ptr(x, 16)) != GA_OK) return s;
+    if ((s = check_ptr(lse, 4)) != GA_OK) return s;
+  }
+  if (!p->has_csc) return GA_ERR_NOT_READY;
+  const size_t need = bwd_ws_bytes(p, g);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+
+  ga::BwdArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.colptr = p->d_colptr;
+  args.rowidx = p->d_rowidx;
+  args.rows = p->d_rows;
+  args.cols = p->d_cols;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.dout = dout;
+  args.lse = lse;
+  args.dq = dq;
+  args.dk = dk;
+  args.dv = dv;
+  const size_t F = size_t(heads) * dim;
+  char* w = static_cast<char*>(ws);
+  args.ws_ld = reinterpret_cast<float*>(w);
+  w += align_up(size_t(p->n) * heads * 2 * sizeof(float));
+  args.ws_dq = reinterpret_cast<float*>(w);
+  w += align_up(p->rows.chunk_row.size() * ga::dq_partial_floats(heads, dim) * sizeof(float));
+  args.ws_dkv = reinterpret_cast<float*>(w);
+  args.scale = scale;
+  args.sc2 = scale * 1.4426950408889634f;
+  const int rc = ga::launch_bwd(dtype, g, args, p->n, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_timer_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timer_on = enable != 0;
+  return GA_OK;
+}
+
+ga_status graph_attn_timer_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  for (auto& r : g_recs) {
+    if (r.begin) g_pool.push_back(r.begin);
+    if (r.end) g_pool.push_back(r.end);
+  }
+  g_recs.clear();
+  g_agg.clear();
+  return GA_OK;
+}
+
+int32_t graph_attn_timer_count(void) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_agg.clear();
+  for (const auto& r : g_recs) {
+    if (!r.end) continue;
+    if (hipEventSynchronize(r.end) != hipSuccess) continue;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.begin, r.end) != hipSuccess) continue;
+    bool found = false;
+    for (auto& a : g_agg)
+      if (std::strcmp(a.name, r.name) == 0) {
+        a.launches++;
+        a.ms += ms;
+        found = true;
+        break;
+      }
+    if (!found) g_agg.push_back(Agg{r.name, 1, ms});
+  }
+  return static_cast<int32_t>(g_agg.size());
+}
+
+ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launches,
+                                double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (index < 0 || index >= static_cast<int32_t>(g_agg.size()) || !name || !launches ||
+      !total_ms)
+    return GA_ERR_INVALID_ARG;
+  *name = g_agg[index].name;
+  *launches = g_agg[index].launches;
+  *total_ms = g_agg[index].ms;
+  return GA_OK;
+}
+
+ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes % 16) return GA_ERR_INVALID_ARG;
+  if (bytes == 0) return GA_OK;
+  if (!dst || !src || !aligned(dst, 16) || !aligned(src, 16)) return GA_ERR_INVALID_ARG;
+  const int rc = ga::launch_copy(dst, src, bytes, stream, active_hook());
+  return rc == 0 ? GA_OK : GA_ERR_HIP;
+}
+
+}  // extern "C"

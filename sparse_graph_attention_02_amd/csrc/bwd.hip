@@ -1,0 +1,425 @@
+// Backward kernels of fused CSR graph attention (dot score) for gfx950.
+//
+// Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
+// Summary > Methodology, attention-based layers, backward pass: only a compact per-node
+// statistic (the log-sum-exp) is kept from the forward and the attention weights are
+// recomputed on the fly; the transposed adjacency is precomputed once (same section, SpMM
+// paragraph) so that dK/dV are gathered per source column instead of scattered with
+// atomics.
+//
+// With P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, v_j>, D_i = sum_j P_ij dp_ij (per head),
+// dS_ij = P_ij (dp_ij - D_i):
+//   bwd_dq_main     over CSR rows (same bins / item order as the forward), one pass:
+//                   A_i = sum_j P_ij dp_ij k_j, B_i = sum_j P_ij k_j, D_i = sum_j P_ij dp_ij,
+//                   then dq_i = scale (A_i - D_i B_i) = scale sum_j dS_ij k_j, and the
+//                   record (lse_i log2 e, D_i) is stored for the column pass. D comes from
+//                   the recomputed weights, not from the rounded stored output, so it is
+//                   the exact row statistic (hub rows: fp32 chunk partials of A, B, D)
+//   bwd_dq_merge    hub rows: sum chunk partials in ascending chunk order
+//   bwd_dkdv_main   over transpose columns (column bins by out-degree):
+//                   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+//   bwd_dkdv_merge  hub columns: sum chunk partials in ascending chunk order
+// Every sum runs in fp32 in a fixed order; no atomics.
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+template <typename T, int G, int LH, int U>
+struct Bwd {
+  using L16 = Lane16<T>;
+  using raw_t = typename L16::raw_t;
+  static constexpr int VEC = L16::VEC;
+  static constexpr int NG = kWave / G;
+  static constexpr int H = G / LH;
+  static constexpr int F = G * VEC;
+  static constexpr int kDqStride = 2 * F + (H + 3) / 4 * 4;
+
+  __device__ __forceinline__ static const raw_t* R(const void* p) {
+    return static_cast<const raw_t*>(p);
+  }
+
+  __device__ __forceinline__ static float dot(const float* x, const float* y) {
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) d = fmaf(x[c], y[c], d);
+    return d;
+  }
+
+  // Sum a per-lane vector over the NGS groups of a segment (butterfly, fixed order).
+  template <int NGS>
+  __device__ __forceinline__ static void group_sum(float* x) {
+#pragma unroll
+    for (int off = G; off < NGS * G; off <<= 1)
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) x[c] += __shfl_xor(x[c], off);
+  }
+
+  // ---- dQ over CSR rows ------------------------------------------------------------
+  // Accumulates A += P dp k, B += P k and D += P dp over edges [e0, e1).
+  template <int NGS>
+  __device__ __forceinline__ static void run_dq(const BwdArgs& a, int e0, int e1, int seg0,
+                                                int gs, int r, const float* qf, const float* dof,
+                                                float lse2, float* A, float* Bk, float& D) {
+    constexpr int L = NGS * G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const raw_t* __restrict__ Kr = R(a.k);
+    const raw_t* __restrict__ Vr = R(a.v);
+    for (int base = e0; base < e1; base += L) {
+      const int nb = min(L, e1 - base);
+      const int li = lane - seg0;
+      const int my_j = (li < nb) ? a.indices[base + li] : 0;
+      for (int t = 0; t < nb; t += NGS * U) {
+        int jj[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pos = t + u * NGS + gs;
+          ok[u] = pos < nb;
+          jj[u] = __shfl(my_j, seg0 + (ok[u] ? pos : t));
+        }
+        raw_t kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          kr[u] = Kr[static_cast<size_t>(jj[u]) * G + r];
+          vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float kf[VEC], vf[VEC];
+          L16::unpack(kr[u], kf);
+          L16::unpack(vr[u], vf);
+          const float s2 = head_sum<LH>(dot(qf, kf)) * a.sc2;
+          const float dp = head_sum<LH>(dot(dof, vf));
+          const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
+          const float pdp = p * dp;
+          D += pdp;
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            A[c] = fmaf(pdp, kf[c], A[c]);
+            Bk[c] = fmaf(p, kf[c], Bk[c]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- dK / dV over transpose columns ----------------------------------------------
+  template <int NGS>
+  __device__ __forceinline__ static void run_dkdv(const BwdArgs& a, int e0, int e1, int seg0,
+                                                  int gs, int r, int h, const float* kf,
+                                                  const float* vf, float* dk, float* dv) {
+    constexpr int L = NGS * G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const raw_t* __restrict__ Qr = R(a.q);
+    const raw_t* __restrict__ Or = R(a.dout);
+    const float2* __restrict__ LD = reinterpret_cast<const float2*>(a.ws_ld);
+    for (int base = e0; base < e1; base += L) {
+      const int nb = min(L, e1 - base);
+      const int li = lane - seg0;
+      const int my_i = (li < nb) ? a.rowidx[base + li] : 0;
+      for (int t = 0; t < nb; t += NGS * U) {
+        int ii[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pos = t + u * NGS + gs;
+          ok[u] = pos < nb;
+          ii[u] = __shfl(my_i, seg0 + (ok[u] ? pos : t));
+        }
+        raw_t qr[U], dr[U];
+        float2 ld[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          qr[u] = Qr[static_cast<size_t>(ii[u]) * G + r];
+          dr[u] = Or[static_cast<size_t>(ii[u]) * G + r];
+          ld[u] = LD[static_cast<size_t>(ii[u]) * H + h];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float qf[VEC], df[VEC];
+          L16::unpack(qr[u], qf);
+          L16::unpack(dr[u], df);
+          const float s2 = head_sum<LH>(dot(qf, kf)) * a.sc2;
+          const float dp = head_sum<LH>(dot(df, vf));
+          const float p = ok[u] ? fast_exp2(s2 - ld[u].x) : 0.f;
+          const float ds = p * (dp - ld[u].y);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            dk[c] = fmaf(ds, qf[c], dk[c]);
+            dv[c] = fmaf(p, df[c], dv[c]);
+          }
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ static void store(void* base, int row, int r, const float* x,
+                                               float mul) {
+    float o[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) o[c] = x[c] * mul;
+    static_cast<raw_t*>(base)[static_cast<size_t>(row) * G + r] = L16::pack(o);
+  }
+
+  __device__ __forceinline__ static void store_f32(float* base, int r, const float* x) {
+    float4* p = reinterpret_cast<float4*>(base + r * VEC);
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c)
+      p[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+  }
+
+  __device__ __forceinline__ static void add_f32(const float* base, int r, float* x) {
+    const float4* p = reinterpret_cast<const float4*>(base + r * VEC);
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c) {
+      const float4 y = p[c];
+      x[4 * c] += y.x;
+      x[4 * c + 1] += y.y;
+      x[4 * c + 2] += y.z;
+      x[4 * c + 3] += y.w;
+    }
+  }
+
+  // Row prologue of the dQ pass: q and dout slices, lse in log2 units.
+  __device__ __forceinline__ static void row_prologue(const BwdArgs& a, int row, int r, int h,
+                                                      float* qf, float* dof, float& lse2) {
+    const size_t off = static_cast<size_t>(row) * G + r;
+    L16::unpack(R(a.q)[off], qf);
+    L16::unpack(R(a.dout)[off], dof);
+    lse2 = a.lse[static_cast<size_t>(row) * H + h] * kLog2e;
+  }
+
+  // dq = scale (A - D B), written in the feature dtype.
+  __device__ __forceinline__ static void store_dq(const BwdArgs& a, int row, int r,
+                                                  const float* A, const float* Bk, float D) {
+    float x[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) x[c] = fmaf(-D, Bk[c], A[c]);
+    store(a.dq, row, r, x, a.scale);
+  }
+
+  template <int NGS>
+  __device__ __forceinline__ static void group_sum1(float& x) {
+#pragma unroll
+    for (int off = G; off < NGS * G; off <<= 1) x += __shfl_xor(x, off);
+  }
+};
+
+// dQ pass. Hub-row chunk partial layout in ws_dq: [chunk][A: F | B: F | D: H, padded to 4]
+// fp32 (kDqStride floats per chunk, a multiple of 4 so the float4 stores stay aligned).
+template <typename T, int G, int LH, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
+  using K = Bwd<T, G, LH, U>;
+  constexpr int NG = K::NG, VEC = K::VEC, H = K::H, F = K::F;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int g = lane / G, r = lane % G, h = r / LH;
+  const DevBins& B = a.rows;
+  float qf[VEC], dof[VEC], A[VEC], Bk[VEC], lse2, D = 0.f;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
+  float2* LD = reinterpret_cast<float2*>(a.ws_ld);
+  if (item < B.n_chunks + B.n_medium) {
+    int row, e0, e1;
+    const bool chunk = item < B.n_chunks;
+    if (chunk) {
+      row = B.chunk_row[item];
+      e0 = B.chunk_begin[item];
+      e1 = B.chunk_end[item];
+    } else {
+      row = B.medium[item - B.n_chunks];
+      e0 = a.indptr[row];
+      e1 = a.indptr[row + 1];
+    }
+    K::row_prologue(a, row, r, h, qf, dof, lse2);
+    K::template run_dq<NG>(a, e0, e1, 0, g, r, qf, dof, lse2, A, Bk, D);
+    K::template group_sum<NG>(A);
+    K::template group_sum<NG>(Bk);
+    K::template group_sum1<NG>(D);
+    if (g != 0) return;
+    if (chunk) {
+      float* p = a.ws_dq + static_cast<size_t>(item) * K::kDqStride;
+      K::store_f32(p, r, A);
+      K::store_f32(p + F, r, Bk);
+      if (r % LH == 0) p[2 * F + h] = D;
+    } else {
+      if (r % LH == 0) LD[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+      K::store_dq(a, row, r, A, Bk, D);
+    }
+    return;
+  }
+  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  if (li >= B.n_light) return;
+  const int row = B.light[li];
+  const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
+  K::row_prologue(a, row, r, h, qf, dof, lse2);
+  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qf, dof, lse2, A, Bk, D);
+  if (r % LH == 0) LD[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+  K::store_dq(a, row, r, A, Bk, D);
+}
+
+template <typename T, int G, int LH>
+__global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
+  using K = Bwd<T, G, LH, 1>;
+  constexpr int VEC = K::VEC, F = K::F, H = K::H;
+  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
+  const int r = threadIdx.x % G, h = r / LH;
+  if (hub >= a.rows.n_hub) return;
+  const int row = a.rows.hub[hub];
+  const int c0 = a.rows.hub_chunk_ptr[hub], c1 = a.rows.hub_chunk_ptr[hub + 1];
+  float A[VEC], Bk[VEC], D = 0.f;
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const float* p = a.ws_dq + static_cast<size_t>(c) * K::kDqStride;
+    K::add_f32(p, r, A);
+    K::add_f32(p + F, r, Bk);
+    D += p[2 * F + h];
+  }
+  if (r % LH == 0) {
+    const float lse2 = a.lse[static_cast<size_t>(row) * H + h] * kLog2e;
+    reinterpret_cast<float2*>(a.ws_ld)[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+  }
+  K::store_dq(a, row, r, A, Bk, D);
+}
+
+template <typename T, int G, int LH, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
+  using K = Bwd<T, G, LH, U>;
+  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int g = lane / G, r = lane % G, h = r / LH;
+  const DevBins& B = a.cols;
+  float kf[VEC], vf[VEC], dk[VEC], dv[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
+  if (item < B.n_chunks + B.n_medium) {
+    int col, e0, e1;
+    const bool chunk = item < B.n_chunks;
+    if (chunk) {
+      col = B.chunk_row[item];
+      e0 = B.chunk_begin[item];
+      e1 = B.chunk_end[item];
+    } else {
+      col = B.medium[item - B.n_chunks];
+      e0 = a.colptr[col];
+      e1 = a.colptr[col + 1];
+    }
+    const size_t off = static_cast<size_t>(col) * G + r;
+    K::L16::unpack(K::R(a.k)[off], kf);
+    K::L16::unpack(K::R(a.v)[off], vf);
+    K::template run_dkdv<NG>(a, e0, e1, 0, g, r, h, kf, vf, dk, dv);
+    K::template group_sum<NG>(dk);
+    K::template group_sum<NG>(dv);
+    if (g != 0) return;
+    if (chunk) {
+      float* p = a.ws_dkv + static_cast<size_t>(item) * 2 * F;
+      K::store_f32(p, r, dk);
+      K::store_f32(p + F, r, dv);
+    } else {
+      K::store(a.dk, col, r, dk, a.scale);
+      K::store(a.dv, col, r, dv, 1.f);
+    }
+    return;
+  }
+  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  if (li >= B.n_light) return;
+  const int col = B.light[li];
+  const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
+  const size_t off = static_cast<size_t>(col) * G + r;
+  K::L16::unpack(K::R(a.k)[off], kf);
+  K::L16::unpack(K::R(a.v)[off], vf);
+  K::template run_dkdv<1>(a, e0, e1, g * G, 0, r, h, kf, vf, dk, dv);
+  K::store(a.dk, col, r, dk, a.scale);
+  K::store(a.dv, col, r, dv, 1.f);
+}
+
+template <typename T, int G, int LH>
+__global__ __launch_bounds__(kBlock) void bwd_dkdv_merge(BwdArgs a) {
+  using K = Bwd<T, G, LH, 1>;
+  constexpr int VEC = K::VEC, F = K::F;
+  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
+  const int r = threadIdx.x % G;
+  if (hub >= a.cols.n_hub) return;
+  const int col = a.cols.hub[hub];
+  const int c0 = a.cols.hub_chunk_ptr[hub], c1 = a.cols.hub_chunk_ptr[hub + 1];
+  float dk[VEC], dv[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
+  for (int c = c0; c < c1; ++c) {
+    const float* p = a.ws_dkv + static_cast<size_t>(c) * 2 * F;
+    K::add_f32(p, r, dk);
+    K::add_f32(p + F, r, dv);
+  }
+  K::store(a.dk, col, r, dk, a.scale);
+  K::store(a.dv, col, r, dv, 1.f);
+}
+
+template <typename T, int G, int LH>
+int launch(const BwdArgs& a, void* stream, TimerHook hook) {
+  constexpr int U = 4;
+  constexpr int NG = kWave / G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto items_of = [](const DevBins& B) {
+    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  };
+  auto go = [&](const char* name, auto kernel, int64_t blocks) -> int {
+    if (blocks <= 0) return 0;
+    if (hook) hook(name, stream, 1);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    if (hook) hook(name, stream, 0);
+    return static_cast<int>(hipGetLastError());
+  };
+  const int per_block = kBlock / G;
+  int e;
+  if ((e = go("bwd_dq_main", bwd_dq_main<T, G, LH, U>,
+              (items_of(a.rows) + kWavesPerBlock - 1) / kWavesPerBlock)))
+    return e;
+  if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>, (a.rows.n_hub + per_block - 1) / per_block)))
+    return e;
+  if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, U>,
+              (items_of(a.cols) + kWavesPerBlock - 1) / kWavesPerBlock)))
+    return e;
+  if ((e = go("bwd_dkdv_merge", bwd_dkdv_merge<T, G, LH>,
+              (a.cols.n_hub + per_block - 1) / per_block)))
+    return e;
+  return 0;
+}
+
+#define GA_GEOMS(X)                                                                       \
+  X(4, 2) X(4, 4) X(8, 2) X(8, 4) X(8, 8) X(16, 2) X(16, 4) X(16, 8) X(16, 16) X(32, 2) \
+  X(32, 4) X(32, 8) X(32, 16) X(32, 32) X(64, 2) X(64, 4) X(64, 8) X(64, 16) X(64, 32) \
+  X(64, 64)
+
+template <typename T>
+int dispatch(const Geometry& g, const BwdArgs& a, void* stream, TimerHook hook) {
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return launch<T, GG, LL>(a, stream, hook);
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  return -1;
+}
+
+bool geom_ok(const Geometry& g) {
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return true;
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  return false;
+}
+
+}  // namespace
+
+bool bwd_supported(ga_dtype dt, const Geometry& g) {
+  return (dt == GA_F32 || dt == GA_BF16) && geom_ok(g);
+}
+
+int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t, void* stream,
+               TimerHook hook) {
+  return dt == GA_F32 ? dispatch<float>(g, a, stream, hook) : dispatch<bf16_t>(g, a, stream, hook);
+}
+
+}  // namespace ga

@@ -1,0 +1,327 @@
+// Forward kernels of fused CSR graph attention for gfx950.
+//
+// Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
+// Summary > Methodology, attention-based layers, forward pass: score computation, softmax
+// normalisation and value aggregation fused in one streaming pass over a row's
+// neighbours, with the running softmax statistics held in registers (online softmax), so
+// no edge-wise logits are materialised. Degree-aware work split after the same section's
+// reduction paragraph (light rows feature-parallel, heavy rows as parallel edge chunks).
+//
+// One launch (fwd_main) covers every row. Its wavefront work items are, in order:
+//   [0, n_chunks)                hub-row chunks: one wavefront per chunk -> fp32 partial
+//                                (m, l, acc) in the workspace
+//   [.., + n_medium)             medium rows: one wavefront per row
+//   [.., + ceil(n_light / NG))   light rows: one G-lane group per row, NG rows per wave
+// Bins are sorted by degree descending, so the longest items start first. A second
+// launch (fwd_hub_merge) folds each hub row's chunk partials in ascending chunk order.
+//
+// Per edge a lane group gathers the neighbour's K and V rows with 16-byte loads per lane
+// (coalesced across the group), reduces the per-head dot product with DPP adds, and folds
+// U edges at a time into the running (m, l, acc) state: one rescale per U edges. Scores
+// are kept in log2 units (scale * log2 e folded into one multiplier) so every exponential
+// is a single v_exp_f32. No atomics: results are bitwise reproducible.
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+template <typename T, int G, int LH, bool GAT, int U>
+struct Fwd {
+  using L16 = Lane16<T>;
+  using raw_t = typename L16::raw_t;
+  static constexpr int VEC = L16::VEC;
+  static constexpr int NG = kWave / G;  // lane groups per wavefront
+  static constexpr int H = G / LH;      // heads
+  static constexpr int F = G * VEC;     // elements per feature row
+
+  struct State {
+    float m, l;
+    float acc[VEC];
+  };
+
+  __device__ __forceinline__ static void init(State& s) {
+    s.m = kEmptyMax;
+    s.l = 0.f;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) s.acc[c] = 0.f;
+  }
+
+  // Row-side operand of the score: the query row slice (dot) or s[i, h] (gat).
+  struct RowOp {
+    float qf[VEC];
+    float si;
+  };
+
+  __device__ __forceinline__ static void load_row(const FwdArgs& a, int row, int r, int h,
+                                                  RowOp& q) {
+    if constexpr (GAT) {
+      q.si = static_cast<const float*>(a.a)[static_cast<size_t>(row) * H + h];
+    } else {
+      const raw_t x = static_cast<const raw_t*>(a.a)[static_cast<size_t>(row) * G + r];
+      L16::unpack(x, q.qf);
+    }
+  }
+
+  // Stream edges [e0, e1) through the state with NGS lane groups cooperating. seg0 is the
+  // segment's first lane in the wave, gs this lane's group within the segment.
+  template <int NGS>
+  __device__ __forceinline__ static void run(const FwdArgs& a, int e0, int e1, int seg0, int gs,
+                                             int r, int h, const RowOp& q, State& st) {
+    constexpr int L = NGS * G;  // lanes of the segment = indices fetched per batch
+    const int lane = threadIdx.x & (kWave - 1);
+    const raw_t* __restrict__ Kr = static_cast<const raw_t*>(a.b);
+    const float* __restrict__ Tt = static_cast<const float*>(a.b);
+    const raw_t* __restrict__ Vr = static_cast<const raw_t*>(a.v);
+    for (int base = e0; base < e1; base += L) {
+      const int nb = min(L, e1 - base);
+      const int li = lane - seg0;
+      const int my_j = (li < nb) ? a.indices[base + li] : 0;
+      for (int t = 0; t < nb; t += NGS * U) {
+        int jj[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pos = t + u * NGS + gs;
+          ok[u] = pos < nb;
+          // out-of-range slots re-read this step's first edge (valid, cached) and are
+          // masked out of the softmax below
+          jj[u] = __shfl(my_j, seg0 + (ok[u] ? pos : t));
+        }
+        raw_t kr[U], vr[U];
+        float tv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (GAT)
+            tv[u] = Tt[static_cast<size_t>(jj[u]) * H + h];
+          else
+            kr[u] = Kr[static_cast<size_t>(jj[u]) * G + r];
+          vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
+        }
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float x;
+          if constexpr (GAT) {
+            x = q.si + tv[u];
+            x = (x >= 0.f ? x : x * a.neg_slope) * a.sc2;
+          } else {
+            float kf[VEC];
+            L16::unpack(kr[u], kf);
+            float d = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) d = fmaf(q.qf[c], kf[c], d);
+            x = head_sum<LH>(d) * a.sc2;
+          }
+          s[u] = ok[u] ? x : -INFINITY;
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mt = fmaxf(mt, s[u]);
+        const float mn = fmaxf(st.m, mt);
+        const float corr = fast_exp2(st.m - mn);
+        st.l *= corr;
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) st.acc[c] *= corr;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = fast_exp2(s[u] - mn);
+          float vf[VEC];
+          L16::unpack(vr[u], vf);
+          st.l += p;
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) st.acc[c] = fmaf(p, vf[c], st.acc[c]);
+        }
+        st.m = mn;
+      }
+    }
+  }
+
+  // Fold the states of the NGS groups of a segment (butterfly over lane distance G..).
+  template <int NGS>
+  __device__ __forceinline__ static void combine(State& st) {
+#pragma unroll
+    for (int off = G; off < NGS * G; off <<= 1) {
+      const float m2 = __shfl_xor(st.m, off);
+      const float l2 = __shfl_xor(st.l, off);
+      const float mn = fmaxf(st.m, m2);
+      const float c1 = fast_exp2(st.m - mn);
+      const float c2 = fast_exp2(m2 - mn);
+      st.l = st.l * c1 + l2 * c2;
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) {
+        const float a2 = __shfl_xor(st.acc[c], off);
+        st.acc[c] = st.acc[c] * c1 + a2 * c2;
+      }
+      st.m = mn;
+    }
+  }
+
+  __device__ __forceinline__ static void write_row(const FwdArgs& a, int row, int r, int h,
+                                                   const State& st) {
+    const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
+    float o[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) o[c] = st.acc[c] * inv;
+    static_cast<raw_t*>(a.out)[static_cast<size_t>(row) * G + r] = L16::pack(o);
+    if (r % LH == 0)
+      a.lse[static_cast<size_t>(row) * H + h] =
+          st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY;
+  }
+
+  __device__ __forceinline__ static void write_partial(const FwdArgs& a, int chunk, int r, int h,
+                                                       const State& st) {
+    if (r % LH == 0) {
+      float2* ml = reinterpret_cast<float2*>(a.ws_ml);
+      ml[static_cast<size_t>(chunk) * H + h] = make_float2(st.m, st.l);
+    }
+    float4* acc = reinterpret_cast<float4*>(a.ws_acc + static_cast<size_t>(chunk) * F + r * VEC);
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c)
+      acc[c] = make_float4(st.acc[4 * c], st.acc[4 * c + 1], st.acc[4 * c + 2], st.acc[4 * c + 3]);
+  }
+};
+
+template <typename T, int G, int LH, bool GAT, int U>
+__global__ __launch_bounds__(kBlock) void fwd_main(FwdArgs a) {
+  using K = Fwd<T, G, LH, GAT, U>;
+  constexpr int NG = K::NG;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int g = lane / G, r = lane % G, h = r / LH;
+  const DevBins& B = a.bins;
+  typename K::State st;
+  typename K::RowOp q;
+  K::init(st);
+  if (item < B.n_chunks + B.n_medium) {
+    int row, e0, e1;
+    const bool chunk = item < B.n_chunks;
+    if (chunk) {
+      row = B.chunk_row[item];
+      e0 = B.chunk_begin[item];
+      e1 = B.chunk_end[item];
+    } else {
+      row = B.medium[item - B.n_chunks];
+      e0 = a.indptr[row];
+      e1 = a.indptr[row + 1];
+    }
+    K::load_row(a, row, r, h, q);
+    K::template run<NG>(a, e0, e1, 0, g, r, h, q, st);
+    K::template combine<NG>(st);
+    if (g != 0) return;
+    if (chunk)
+      K::write_partial(a, item, r, h, st);
+    else
+      K::write_row(a, row, r, h, st);
+    return;
+  }
+  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  if (li >= B.n_light) return;
+  const int row = B.light[li];
+  const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
+  K::load_row(a, row, r, h, q);
+  K::template run<1>(a, e0, e1, g * G, 0, r, h, q, st);
+  K::write_row(a, row, r, h, st);
+}
+
+// One G-lane group per hub row: fold its chunk partials in ascending chunk order.
+template <typename T, int G, int LH>
+__global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
+  using K = Fwd<T, G, LH, false, 1>;
+  constexpr int H = K::H, F = K::F, VEC = K::VEC;
+  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
+  const int r = threadIdx.x % G, h = r / LH;
+  if (hub >= a.bins.n_hub) return;
+  const int row = a.bins.hub[hub];
+  const int c0 = a.bins.hub_chunk_ptr[hub], c1 = a.bins.hub_chunk_ptr[hub + 1];
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  typename K::State st;
+  K::init(st);
+  for (int c = c0; c < c1; ++c) {
+    const float2 p = ml[static_cast<size_t>(c) * H + h];
+    const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + static_cast<size_t>(c) * F + r * VEC);
+    const float mn = fmaxf(st.m, p.x);
+    const float f1 = fast_exp2(st.m - mn);
+    const float f2 = fast_exp2(p.x - mn);
+    st.l = st.l * f1 + p.y * f2;
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) {
+      const float4 x = acc[k];
+      st.acc[4 * k] = st.acc[4 * k] * f1 + x.x * f2;
+      st.acc[4 * k + 1] = st.acc[4 * k + 1] * f1 + x.y * f2;
+      st.acc[4 * k + 2] = st.acc[4 * k + 2] * f1 + x.z * f2;
+      st.acc[4 * k + 3] = st.acc[4 * k + 3] * f1 + x.w * f2;
+    }
+    st.m = mn;
+  }
+  K::write_row(a, row, r, h, st);
+}
+
+template <typename T, int G, int LH, bool GAT>
+int launch(const FwdArgs& a, void* stream, TimerHook hook) {
+  constexpr int U = 4;
+  constexpr int NG = kWave / G;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DevBins& B = a.bins;
+  const int64_t items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  if (items > 0) {
+    const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (hook) hook("fwd_main", stream, 1);
+    hipLaunchKernelGGL((fwd_main<T, G, LH, GAT, U>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, s, a);
+    if (hook) hook("fwd_main", stream, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  if (B.n_hub > 0) {
+    const int per_block = kBlock / G;
+    const int blocks = (B.n_hub + per_block - 1) / per_block;
+    if (hook) hook("fwd_hub_merge", stream, 1);
+    hipLaunchKernelGGL((fwd_hub_merge<T, G, LH>), dim3(blocks), dim3(kBlock), 0, s, a);
+    if (hook) hook("fwd_hub_merge", stream, 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  return 0;
+}
+
+// (G, LH) pairs with compiled kernels: rows of 64..1024 bytes, heads of 32..1024 bytes.
+#define GA_GEOMS(X)                                                                       \
+  X(4, 2) X(4, 4) X(8, 2) X(8, 4) X(8, 8) X(16, 2) X(16, 4) X(16, 8) X(16, 16) X(32, 2) \
+  X(32, 4) X(32, 8) X(32, 16) X(32, 32) X(64, 2) X(64, 4) X(64, 8) X(64, 16) X(64, 32) \
+  X(64, 64)
+
+template <typename T, bool GAT>
+int dispatch(const Geometry& g, const FwdArgs& a, void* stream, TimerHook hook) {
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return launch<T, GG, LL, GAT>(a, stream, hook);
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  return -1;
+}
+
+bool geom_ok(const Geometry& g) {
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return true;
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  return false;
+}
+
+}  // namespace
+
+bool fwd_supported(ga_dtype dt, ga_score sc, const Geometry& g) {
+  return (dt == GA_F32 || dt == GA_BF16) && (sc == GA_SCORE_DOT || sc == GA_SCORE_GAT) &&
+         geom_ok(g);
+}
+
+int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, int64_t,
+               void* stream, TimerHook hook) {
+  if (dt == GA_F32)
+    return sc == GA_SCORE_DOT ? dispatch<float, false>(g, a, stream, hook)
+                              : dispatch<float, true>(g, a, stream, hook);
+  return sc == GA_SCORE_DOT ? dispatch<bf16_t, false>(g, a, stream, hook)
+                            : dispatch<bf16_t, true>(g, a, stream, hook);
+}
+
+}  // namespace ga

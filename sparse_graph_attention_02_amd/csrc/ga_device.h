@@ -1,0 +1,97 @@
+// Device helpers for the gfx950 (CDNA4) kernels: 16-byte lane vectors, bf16 conversion,
+// cross-lane sums within a head (DPP / ds_swizzle), work-item decoding.
+//
+// Lane layout used by every kernel: a feature row of H*d elements is split into G lanes
+// of 16 bytes each (lane r holds elements [r*VEC, (r+1)*VEC)); a head spans LH = G/H
+// consecutive lanes. A 64-lane wavefront holds NG = 64/G such lane groups.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ga {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maximum of an empty state: finite, so exp2(m_old - m_new) never sees inf - inf.
+constexpr float kEmptyMax = -1.0e30f;
+
+// bf16 is carried as raw 16-bit patterns.
+using bf16_t = uint16_t;
+
+template <typename T>
+struct Lane16;
+
+template <>
+struct Lane16<float> {
+  using raw_t = float4;
+  static constexpr int VEC = 4;
+  __device__ __forceinline__ static void unpack(const raw_t& x, float* f) {
+    f[0] = x.x;
+    f[1] = x.y;
+    f[2] = x.z;
+    f[3] = x.w;
+  }
+  __device__ __forceinline__ static raw_t pack(const float* f) {
+    return make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+
+// fp32 -> bf16 by round-to-nearest-even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <>
+struct Lane16<bf16_t> {
+  using raw_t = uint4;
+  static constexpr int VEC = 8;
+  __device__ __forceinline__ static void unpack(const raw_t& x, float* f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      f[2 * c] = __uint_as_float(w[c] << 16);
+      f[2 * c + 1] = __uint_as_float(w[c] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static raw_t pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = bf16_rne(f[2 * c]) | (bf16_rne(f[2 * c + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+// DPP move within rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the LH consecutive lanes of a head (LH a power of two, head-aligned); every
+// lane of the head receives the sum. The summation tree is fixed, so results are
+// deterministic.
+template <int LH>
+__device__ __forceinline__ float head_sum(float x) {
+  static_assert(LH >= 1 && LH <= 64 && (LH & (LH - 1)) == 0, "LH must be a power of two");
+  if constexpr (LH >= 2) x += dpp_mov<0xb1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (LH >= 4) x += dpp_mov<0x4e>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LH >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror: other quad of 8
+  if constexpr (LH >= 16) x += dpp_mov<0x140>(x); // row_mirror: other half of 16
+  if constexpr (LH >= 32)                          // lane ^ 16 within 32 (bitmask swizzle)
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401f));
+  if constexpr (LH >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace ga

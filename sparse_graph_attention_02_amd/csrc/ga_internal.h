@@ -1,0 +1,127 @@
+// Internal declarations shared by the host planner, the C-ABI layer and the kernel
+// launchers. Not part of the public interface (include/graph_attn.h is).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "graph_attn.h"
+
+namespace ga {
+
+// One degree-binned view of a CSR-like structure (the CSR itself, or its transpose).
+struct Bins {
+  std::vector<int32_t> light, medium, hub;               // ids, degree desc / id asc
+  std::vector<int32_t> chunk_row, chunk_begin, chunk_end;  // hub chunks, hub by hub
+  std::vector<int32_t> hub_chunk_ptr;                      // [n_hub + 1]
+};
+
+// Device pointers of one Bins (into the caller's plan buffer).
+struct DevBins {
+  const int32_t* light = nullptr;
+  const int32_t* medium = nullptr;
+  const int32_t* hub = nullptr;
+  const int32_t* chunk_row = nullptr;
+  const int32_t* chunk_begin = nullptr;
+  const int32_t* chunk_end = nullptr;
+  const int32_t* hub_chunk_ptr = nullptr;
+  int32_t n_light = 0, n_medium = 0, n_hub = 0, n_chunks = 0;
+};
+
+}  // namespace ga
+
+struct ga_plan {
+  int64_t n = 0, e = 0;
+  ga_plan_opts opts{};
+  std::vector<int32_t> indptr, indices;
+  ga::Bins rows;
+  bool has_csc = false;
+  std::vector<int32_t> colptr, rowidx;
+  ga::Bins cols;
+  int64_t max_in = 0, max_out = 0;
+
+  // device copy (caller-owned memory)
+  bool uploaded = false;
+  int device = -1;
+  const int32_t* d_indptr = nullptr;
+  const int32_t* d_indices = nullptr;
+  const int32_t* d_colptr = nullptr;
+  const int32_t* d_rowidx = nullptr;
+  ga::DevBins d_rows, d_cols;
+};
+
+namespace ga {
+
+// Planner (plan.cpp). Validates and builds every host array.
+ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, int64_t e,
+                     const ga_plan_opts& opts, ga_plan* p);
+
+// Feature geometry shared by the launchers: a "row" is H*d elements = G lanes x 16 bytes,
+// a head spans LH lanes.
+struct Geometry {
+  int heads = 0, dim = 0, elem_bytes = 0;
+  int G = 0;   // lanes per feature row (row bytes / 16)
+  int LH = 0;  // lanes per head (head bytes / 16)
+};
+
+// Forward kernels (fwd.hip).
+struct FwdArgs {
+  const int32_t* indptr;
+  const int32_t* indices;
+  DevBins bins;
+  const void* a;  // q (dot) or s (gat)
+  const void* b;  // k (dot) or t (gat)
+  const void* v;
+  void* out;
+  float* lse;
+  float* ws_ml;   // [n_chunks][H][2]  (m in log2 units, l)
+  float* ws_acc;  // [n_chunks][H*d]
+  float sc2;      // scale * log2(e)
+  float neg_slope;
+};
+
+// Backward kernels (bwd.hip).
+struct BwdArgs {
+  const int32_t* indptr;
+  const int32_t* indices;
+  const int32_t* colptr;
+  const int32_t* rowidx;
+  DevBins rows, cols;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws_ld;    // [N][H][2]: (lse * log2 e, D)
+  float* ws_dq;    // [n_row_chunks][dq_partial_floats(H, d)]
+  float* ws_dkv;   // [n_col_chunks][2][H*d]
+  float scale;
+  float sc2;       // scale * log2(e)
+};
+
+// fp32 floats per hub-row chunk partial of the dQ pass: A [H*d], B [H*d], D [H] padded
+// to a multiple of 4.
+inline int64_t dq_partial_floats(int64_t heads, int64_t dim) {
+  return 2 * heads * dim + (heads + 3) / 4 * 4;
+}
+
+// Returns false when the geometry/dtype/score combination has no compiled kernels.
+bool fwd_supported(ga_dtype dt, ga_score sc, const Geometry& g);
+bool bwd_supported(ga_dtype dt, const Geometry& g);
+
+// Enqueue the forward / backward kernels. A non-null hook is called before (begin = 1)
+// and after (begin = 0) each launch with the kernel's name (the library's event timers).
+// Both return hipSuccess or the first launch error (as int to keep HIP headers out).
+typedef void (*TimerHook)(const char* name, void* stream, int begin);
+int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, int64_t n,
+               void* stream, TimerHook hook);
+int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t n, void* stream,
+               TimerHook hook);
+int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
+
+}  // namespace ga

@@ -1,0 +1,358 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by
+element on the same seeded inputs; at full workload sizes on sampled rows/columns.
+
+Criteria are in tests/gpu_util.py. Each test prints the case it is about to run.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import graphgen as gg
+from oracle import attention as A
+from sparse_graph_attention_02_amd import Plan, bwd, fwd, graph_attention
+from tests.gpu_util import check, check_lse, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def run_fwd(ip, ix, a, b, v, score="dot", scale=None, neg_slope=0.2, **plan_kw):
+    plan = Plan(ip, ix, **plan_kw).upload()
+    out, lse = fwd(plan, dev(a), dev(b), dev(v), score=score, scale=scale, neg_slope=neg_slope)
+    torch.cuda.synchronize()
+    return plan, out, lse
+
+
+def fwd_parity(tag, ip, ix, a, b, v, dtype, score="dot", scale=None, neg_slope=0.2, rows=None,
+               **plan_kw):
+    d = v.shape[2]
+    if scale is None:
+        scale = f32(1 / math.sqrt(d)) if score == "dot" else 1.0
+    say(tag, "N", ip.size - 1, "E", ix.size, "H", v.shape[1], "d", d, dtype, score, plan_kw)
+    plan, out, lse = run_fwd(ip, ix, a, b, v, score, scale, neg_slope, **plan_kw)
+    rows = np.arange(ip.size - 1) if rows is None else np.asarray(rows)
+    ro, rl = A.forward_rows(ip, ix, a, b, v, rows, score, scale, f32(neg_slope))
+    rt = torch.from_numpy(rows).cuda()
+    err = check(f"{tag} out", host64(out[rt]), ro, dtype)
+    check_lse(f"{tag} lse", host64(lse[rt]), rl)
+    return plan, out, lse, err
+
+
+# ------------------------------------------------------------------ forward, small sizes
+
+def test_er2k_f32_forward_every_row():
+    w = gg.WORKLOADS["er2k_dot_f32"]
+    ip, ix = gg.make_graph(w)
+    q, k, v = gg.make_features(w)
+    fwd_parity("er2k f32 dot", ip, ix, q, k, v, "f32")
+    # same graph with every bin populated, including multi-chunk hubs
+    fwd_parity("er2k f32 dot small bins", ip, ix, q, k, v, "f32", light_max_deg=4,
+               hub_min_deg_exclusive=9, hub_chunk=3)
+
+
+@pytest.mark.parametrize("tl,th,c", [(8, 64, 32), (16, 1024, 512), (0, 0, 5)])
+def test_chunglu20k_bf16_forward_every_row(tl, th, c):
+    w = gg.WORKLOADS["chunglu1m_dot_bf16"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    q, k, v = gg.make_features(w, n=20_000)
+    plan, *_ = fwd_parity("chunglu20k bf16 dot", ip, ix, q, k, v, "bf16", light_max_deg=tl,
+                          hub_min_deg_exclusive=th, hub_chunk=c)
+    info = plan.info()
+    assert info["n_row_hub"] > 0 and info["n_row_chunks"] > info["n_row_hub"]
+
+
+def test_gat_chunglu100k_f32_forward_every_row():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w)
+    s, t, v = gg.make_features(w)
+    plan, *_ = fwd_parity("chunglu100k f32 gat", ip, ix, s, t, v, "f32", score="gat",
+                          scale=1.0, neg_slope=0.2)
+    assert plan.info()["n_row_hub"] > 0
+
+
+def test_gat_scale_and_slope_bf16():
+    rng = np.random.default_rng(4)
+    ip, ix = gg.random_multigraph(3000, 60000, rng, hub_rows=(7,), hub_deg=5000)
+    s = rng.standard_normal((3000, 2)).astype(np.float32)
+    t = rng.standard_normal((3000, 2)).astype(np.float32)
+    v = gg.f32_to_bf16_bits(rng.standard_normal((3000, 2, 64)).astype(np.float32))
+    fwd_parity("gat bf16 scale 1.7 slope 0.05", ip, ix, s, t, v, "bf16", score="gat",
+               scale=1.7, neg_slope=0.05, light_max_deg=8, hub_min_deg_exclusive=32, hub_chunk=64)
+
+
+def test_rmat16k_bf16_d128_forward_every_row():
+    w = gg.WORKLOADS["rmat21_dot_bf16"]
+    ip, ix = gg.make_graph(w, n=1 << 14)
+    q, k, v = gg.make_features(w, n=1 << 14)
+    fwd_parity("rmat 2^14 bf16 d128", ip, ix, q, k, v, "bf16", light_max_deg=8,
+               hub_min_deg_exclusive=256, hub_chunk=128)
+
+
+GEOMS = [(G, LH) for G in (4, 8, 16, 32, 64) for LH in (2, 4, 8, 16, 32, 64) if LH <= G]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G,LH", GEOMS)
+def test_every_compiled_geometry(dtype, G, LH):
+    eb = 4 if dtype == "f32" else 2
+    H, d = G // LH, LH * 16 // eb
+    rng = np.random.default_rng(G * 100 + LH)
+    n = 400
+    ip, ix = gg.random_multigraph(n, 3000, rng, hub_rows=(3,), hub_deg=700)
+    feats = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(3)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    fwd_parity(f"geometry G{G} LH{LH}", ip, ix, *feats, dtype, light_max_deg=6,
+               hub_min_deg_exclusive=20, hub_chunk=16)
+    if G in (8, 64):
+        s = rng.standard_normal((n, H)).astype(np.float32)
+        t = rng.standard_normal((n, H)).astype(np.float32)
+        fwd_parity(f"geometry G{G} LH{LH} gat", ip, ix, s, t, feats[2], dtype, score="gat",
+                   light_max_deg=6, hub_min_deg_exclusive=20, hub_chunk=16)
+
+
+def test_empty_rows_single_neighbours_and_parallel_edges():
+    rng = np.random.default_rng(9)
+    n, H, d = 500, 4, 32
+    dst = np.r_[np.arange(100, 200),                   # rows 100..199: exactly one edge
+                np.repeat(np.arange(200, 300), 5),     # 5 edges each
+                np.full(40, 300), np.full(3000, 301)]  # a medium row and a hub row
+    src = rng.integers(0, n, dst.size)
+    src[np.flatnonzero(dst == 300)[:20]] = 17          # 20 parallel 17 -> 300 edges
+    ip, ix = gg.csr_from_edges(n, src, dst)           # rows 0..99 and 302..499 are empty
+    q, k, v = (gg.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
+               for _ in range(3))
+    plan, out, lse, _ = fwd_parity("empty/single/parallel", ip, ix, q, k, v, "bf16",
+                                   light_max_deg=4, hub_min_deg_exclusive=64, hub_chunk=100)
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    empty = np.diff(ip) == 0
+    assert np.all(o[empty] == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()[empty]))
+    single = np.flatnonzero(np.diff(ip) == 1)
+    assert np.array_equal(o[single], v[ix[ip[single]]])   # bitwise: weight exactly 1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_star_hub_row_200k(dtype):
+    """One destination with 200,000 in-edges (hundreds of chunks, ordered merge)."""
+    rng = np.random.default_rng(11)
+    n, H, d = 250_000, 2, 64
+    src = rng.integers(0, n, 200_000)
+    ip, ix = gg.csr_from_edges(n, np.r_[src, np.arange(n)], np.r_[np.zeros(200_000, np.int64),
+                                                                  np.arange(n)])
+    feats = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(3)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    rows = np.r_[0, rng.integers(1, n, 50)]
+    plan, *_ = fwd_parity(f"star 200k {dtype}", ip, ix, *feats, dtype, rows=rows)
+    assert plan.info()["max_in_degree"] == 200_001
+
+
+# ------------------------------------------------------------------ backward
+
+def bwd_case(tag, ip, ix, q, k, v, dout, dtype, rows=None, cols=None, **plan_kw):
+    d = q.shape[2]
+    scale = f32(1 / math.sqrt(d))
+    say(tag, "N", ip.size - 1, "E", ix.size, "H", q.shape[1], "d", d, dtype, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    tq, tk, tv, tdo = dev(q), dev(k), dev(v), dev(dout)
+    out, lse = fwd(plan, tq, tk, tv, scale=scale)
+    dq, dk, dv = bwd(plan, tq, tk, tv, tdo, lse, scale=scale)
+    torch.cuda.synchronize()
+    if rows is None:
+        rq, rk, rv = A.backward(ip, ix, q, k, v, dout, scale)
+        errs = [check(f"{tag} dq", host64(dq), rq, dtype),
+                check(f"{tag} dk", host64(dk), rk, dtype),
+                check(f"{tag} dv", host64(dv), rv, dtype)]
+    else:
+        rq = A.grad_q_rows(ip, ix, q, k, v, dout, rows, scale)
+        rk, rv = A.grad_kv_cols(ip, ix, q, k, v, dout, cols, scale)
+        rt, ct = torch.from_numpy(np.asarray(rows)).cuda(), torch.from_numpy(np.asarray(cols)).cuda()
+        errs = [check(f"{tag} dq", host64(dq[rt]), rq, dtype),
+                check(f"{tag} dk", host64(dk[ct]), rk, dtype),
+                check(f"{tag} dv", host64(dv[ct]), rv, dtype)]
+    say(tag, "max abs / norm-rel errors", errs)
+    return plan, (out, lse, dq, dk, dv)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_chunglu5k_every_element(dtype):
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    n = 5000
+    ip, ix = gg.make_graph(w, n=n)
+    rng = np.random.default_rng(21)
+    feats = [rng.standard_normal((n, 8, 32)).astype(np.float32) for _ in range(4)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    plan, _ = bwd_case(f"bwd chunglu5k {dtype}", ip, ix, *feats, dtype, light_max_deg=8,
+                       hub_min_deg_exclusive=64, hub_chunk=32)
+    info = plan.info()
+    assert info["n_col_hub"] > 0 and info["n_col_chunks"] > info["n_col_hub"]
+    assert info["n_row_hub"] > 0
+
+
+@pytest.mark.parametrize("G,LH,dtype", [(8, 8, "f32"), (16, 16, "bf16"), (64, 16, "f32"),
+                                        (4, 2, "bf16"), (64, 64, "bf16"), (32, 32, "f32")])
+def test_backward_geometries(G, LH, dtype):
+    eb = 4 if dtype == "f32" else 2
+    H, d = G // LH, LH * 16 // eb
+    rng = np.random.default_rng(G + LH)
+    n = 300
+    src = np.r_[rng.integers(0, n, 2500), np.full(600, 5)]       # column hub 5
+    dst = np.r_[rng.integers(0, n, 2500), rng.integers(0, n, 600)]
+    dst[:500] = 9                                               # row hub 9
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    feats = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(4)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    bwd_case(f"bwd geometry G{G} LH{LH} {dtype}", ip, ix, *feats, dtype, light_max_deg=4,
+             hub_min_deg_exclusive=40, hub_chunk=16)
+
+
+def test_backward_empty_rows_and_star_column():
+    rng = np.random.default_rng(31)
+    n, H, d = 60_000, 2, 32
+    src = np.r_[np.zeros(50_000, np.int64), rng.integers(0, n, 20_000)]   # node 0: source hub
+    dst = np.r_[rng.integers(0, 30_000, 50_000), rng.integers(0, 30_000, 20_000)]
+    ip, ix = gg.csr_from_edges(n, src, dst)          # rows >= 30000 are empty
+    feats = [gg.f32_to_bf16_bits(rng.standard_normal((n, H, d)).astype(np.float32))
+             for _ in range(4)]
+    rows = np.r_[rng.integers(0, 30_000, 100), rng.integers(30_000, n, 20)]
+    cols = np.r_[0, rng.integers(1, n, 60)]
+    plan, (out, lse, dq, dk, dv) = bwd_case("bwd star column", ip, ix, *feats, "bf16",
+                                            rows=rows, cols=cols)
+    assert plan.info()["max_out_degree"] >= 50_000
+    empty = torch.from_numpy(np.flatnonzero(np.diff(ip) == 0)).cuda()
+    assert torch.all(dq[empty] == 0)
+
+
+def test_autograd_wrapper_matches_direct_calls():
+    w = gg.WORKLOADS["chunglu1m_dot_bf16"]
+    ip, ix = gg.make_graph(w, n=3000)
+    q, k, v = gg.make_features(w, n=3000)
+    say("autograd wrapper")
+    plan = Plan(ip, ix).upload()
+    tq, tk, tv = (dev(x).requires_grad_(True) for x in (q, k, v))
+    out = graph_attention(plan, tq, tk, tv)
+    g = torch.randn_like(out)
+    out.backward(g)
+    o2, lse = fwd(plan, tq.detach(), tk.detach(), tv.detach())
+    d2 = bwd(plan, tq.detach(), tk.detach(), tv.detach(), g, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2)
+    for a, b in zip((tq.grad, tk.grad, tv.grad), d2):
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ determinism, memory
+
+def test_bitwise_deterministic_fwd_bwd():
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    ip, ix = gg.make_graph(w, n=50_000)
+    q, k, v = gg.make_features(w, n=50_000)
+    dout = gg.make_dout(w, n=50_000)
+    say("determinism chunglu50k")
+    plan = Plan(ip, ix, light_max_deg=8, hub_min_deg_exclusive=128, hub_chunk=64).upload()
+    tq, tk, tv, td = dev(q), dev(k), dev(v), dev(dout)
+    res = []
+    for _ in range(2):
+        out, lse = fwd(plan, tq, tk, tv)
+        res.append((out, lse) + bwd(plan, tq, tk, tv, td, lse))
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_no_edge_sized_allocation():
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    n = 200_000
+    ip, ix = gg.make_graph(w, n=n)
+    q, k, v = gg.make_features(w, n=n)
+    dout = gg.make_dout(w, n=n)
+    say("memory chunglu200k E", ix.size)
+    plan = Plan(ip, ix).upload()
+    tq, tk, tv, td = dev(q), dev(k), dev(v), dev(dout)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    out, lse = fwd(plan, tq, tk, tv)
+    dq, dk, dv = bwd(plan, tq, tk, tv, td, lse)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    feat = tq.numel() * tq.element_size()
+    ws = plan.fwd_workspace_bytes(8, 32) + plan.bwd_workspace_bytes(8, 32)
+    expected = 4 * feat + lse.numel() * 4 + ws       # out, dq, dk, dv + lse + workspaces
+    e_scores = ix.size * 8 * 4                         # an E x H fp32 score tensor
+    say("peak delta", peak, "expected", expected, "E*H*4", e_scores)
+    assert peak <= expected + (4 << 20)
+    assert ws < e_scores / 4
+
+
+# ------------------------------------------------------------------ full workload sizes
+
+def _sample_rows(ip, rng, k=256):
+    deg = np.diff(ip)
+    top = np.argsort(-deg, kind="stable")[:8]
+    ones = np.flatnonzero(deg == 1)[:8]
+    return np.unique(np.r_[top, ones, rng.choice(ip.size - 1, k, replace=False)])
+
+
+@pytest.mark.slow
+def test_full_chunglu1m_bf16_forward_sampled():
+    w = gg.WORKLOADS["chunglu1m_dot_bf16"]
+    ip, ix = gg.make_graph(w)
+    q, k, v = gg.make_features(w)
+    rows = _sample_rows(ip, np.random.default_rng(3))
+    fwd_parity("full chunglu1m bf16 dot (sampled rows)", ip, ix, q, k, v, "bf16", rows=rows)
+
+
+@pytest.mark.slow
+def test_full_rmat21_bf16_forward_sampled():
+    w = gg.WORKLOADS["rmat21_dot_bf16"]
+    ip, ix = gg.make_graph(w)
+    q, k, v = gg.make_features(w)
+    rows = _sample_rows(ip, np.random.default_rng(4))
+    plan, *_ = fwd_parity("full rmat21 bf16 dot (sampled rows)", ip, ix, q, k, v, "bf16",
+                          rows=rows)
+    assert plan.info()["max_in_degree"] > 100_000
+
+
+@pytest.mark.slow
+def test_full_chunglu100k_gat_f32_default_plan():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w)
+    s, t, v = gg.make_features(w)
+    rows = _sample_rows(ip, np.random.default_rng(5), k=2000)
+    fwd_parity("full chunglu100k gat (sampled rows)", ip, ix, s, t, v, "f32", score="gat",
+               scale=1.0, rows=rows)
+
+
+@pytest.mark.slow
+def test_full_chunglu1m_training_step_sampled():
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    ip, ix = gg.make_graph(w)
+    q, k, v = gg.make_features(w)
+    dout = gg.make_dout(w)
+    rng = np.random.default_rng(6)
+    rows = _sample_rows(ip, rng, k=128)
+    odeg = np.bincount(ix, minlength=w.n)
+    cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3],
+                           np.flatnonzero(odeg == 1)[:4], rng.choice(w.n, 48, replace=False)])
+    bwd_case("full chunglu1m training step (sampled rows/cols)", ip, ix, q, k, v, dout, "bf16",
+             rows=rows, cols=cols)

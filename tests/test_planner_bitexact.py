@@ -1,0 +1,71 @@
+"""The library's C++ planner (through the C ABI, host only) against the numpy reference
+planner of the oracle: every plan array must be identical."""
+import numpy as np
+import pytest
+
+import graphgen as gg
+from oracle import planner as P
+from sparse_graph_attention_02_amd import Plan, capi
+
+NAMES = None
+
+
+def _names():
+    return [capi.graph_attn_plan_array_name(i).decode()
+            for i in range(capi.graph_attn_plan_array_count())]
+
+
+def _graphs():
+    rng = np.random.default_rng(1)
+    yield "star", gg.csr_from_edges(300, np.arange(300), np.zeros(300, np.int64))
+    yield "multigraph_hubs", gg.random_multigraph(500, 4000, rng, hub_rows=(0, 17, 499),
+                                                  hub_deg=1500)
+    yield "empty_rows", gg.csr_from_edges(40, rng.integers(0, 40, 50), rng.integers(0, 5, 50))
+    yield "no_edges", (np.zeros(9, np.int32), np.zeros(0, np.int32))
+    yield "no_nodes", (np.zeros(1, np.int32), np.zeros(0, np.int32))
+    yield "chunglu30k", gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=30_000)
+    yield "rmat2^14", gg.make_graph(gg.WORKLOADS["rmat21_dot_bf16"], n=1 << 14)
+
+
+THRESH = [(16, 1024, 512), (0, 0, 1), (2, 3, 2), (31, 32, 33), (8, 64, 64)]
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("tl,th,c", THRESH)
+def test_cpp_planner_equals_reference(name, g, tl, th, c):
+    ip, ix = g
+    ref = P.plan(ip, ix, tl, th, c, build_csc=True)
+    p = Plan(ip, ix, light_max_deg=tl, hub_min_deg_exclusive=th, hub_chunk=c)
+    for nm in _names():
+        got = p.array(nm)
+        want = {"indptr": ip, "indices": ix}.get(nm, ref.get(nm))
+        assert got.dtype == np.int32
+        assert np.array_equal(got, np.asarray(want, np.int32)), nm
+    info = p.info()
+    n = ip.size - 1
+    assert info["n_row_hub"] == ref["row_hub"].size
+    assert info["max_in_degree"] == (int(np.diff(ip).max()) if n else 0)
+
+
+def test_threshold_edges_and_chunk_multiples():
+    """Rows with degree exactly at, below and above the thresholds; hub rows whose degree
+    is a multiple of the chunk and one more / one less."""
+    tl, th, c = 4, 16, 8
+    degs = [0, 1, tl - 1, tl, tl + 1, th - 1, th, th + 1, 2 * c + 16, 3 * c, 3 * c - 1,
+            3 * c + 1, 5 * c]
+    n = len(degs)
+    rng = np.random.default_rng(2)
+    dst = np.repeat(np.arange(n), degs)
+    src = rng.integers(0, n, dst.size)
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    ref = P.plan(ip, ix, tl, th, c)
+    p = Plan(ip, ix, light_max_deg=tl, hub_min_deg_exclusive=th, hub_chunk=c)
+    for nm in _names():
+        want = {"indptr": ip, "indices": ix}.get(nm, ref.get(nm))
+        assert np.array_equal(p.array(nm), want), nm
+    assert sorted(p.array("row_light").tolist()) == [0, 1, 2, 3]
+    assert sorted(p.array("row_medium").tolist()) == [4, 5, 6]
+    chunks = np.diff(p.array("row_hub_chunk_ptr"))
+    hub = p.array("row_hub")
+    expect = {i: -(-degs[i] // c) for i in hub}
+    assert [expect[i] for i in hub] == chunks.tolist()
