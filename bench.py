@@ -1,0 +1,315 @@
+"""Benchmark of the fused CSR graph-attention layer on one MI355X.
+
+A step is one training step of the layer on the 1M-node Chung-Lu workload (gamma 2.1,
+average in-degree 50 plus self-loops, H = 8, d = 32, bf16 with fp32 accumulation): the
+forward (scores -> online softmax -> weighted V, saving the per-row log-sum-exp), then
+the backward (dQ over CSR, dK/dV over the cached transpose).  The graph plan is built
+once per graph, before the timed region, as the method caches graph metadata.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+
+Prints one JSON line.  ``value`` is edges/s of the whole step (E / step time) with
+inputs resident in HBM; ``roofline`` is the dominant kernel's algorithmic bytes per
+launch over its measured average duration (HIP events recorded by the library on the
+launch stream); ``cpu_baseline`` is the fp64 oracle timed on this host on a time-boxed
+uniform sample of rows (same edges/s unit).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import graphgen as gg  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def algorithmic_bytes(kernel, N, E, H, d, b):
+    """Bytes a launch must move at minimum: the CSR (or transpose) once, one read of each
+    gathered row per edge, each per-node operand once and each output once."""
+    F = H * d
+    if kernel == "fwd_main":       # indptr, indices, K_j + V_j per edge, Q, out, lse
+        return 4 * (N + 1) + 4 * E + 2 * E * F * b + N * F * b + N * F * b + 4 * N * H
+    if kernel == "bwd_dq_main":    # indptr, indices, K_j + V_j per edge, Q, dOut, lse, dQ,
+        return (4 * (N + 1) + 4 * E + 2 * E * F * b + 2 * N * F * b + 4 * N * H
+                + N * F * b + 8 * N * H)  # + (lse, D) record written
+    if kernel == "bwd_dkdv_main":  # colptr, rowidx, Q_i + dOut_i + (lse, D)_i per edge, K, V, dK, dV
+        return 4 * (N + 1) + 4 * E + E * (2 * F * b + 8 * H) + 2 * N * F * b + 2 * N * F * b
+    return None
+
+
+def step_bytes(N, E, H, d, b, backward):
+    tot = algorithmic_bytes("fwd_main", N, E, H, d, b)
+    if backward:
+        tot += algorithmic_bytes("bwd_dq_main", N, E, H, d, b)
+        tot += algorithmic_bytes("bwd_dkdv_main", N, E, H, d, b)
+    return tot
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+
+_SHARED = {}
+
+
+def _cpu_worker(args):
+    rows, deadline_s, backward = args
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as A
+    g = _SHARED
+    t0 = time.perf_counter()
+    done_rows = done_edges = 0
+    with threadpool_limits(1):
+        for s in range(0, rows.size, 128):
+            batch = rows[s:s + 128]
+            if backward:
+                A.train_step_rows(g["ip"], g["ix"], g["q"], g["k"], g["v"], g["dout"], batch,
+                                  g["scale"])
+            else:
+                A.forward_rows(g["ip"], g["ix"], g["q"], g["k"], g["v"], batch, g["score"],
+                               g["scale"], g["slope"])
+            done_rows += batch.size
+            done_edges += int((g["ip"][batch + 1] - g["ip"][batch]).sum())
+            if time.perf_counter() - t0 > deadline_s:
+                break
+    return done_rows, done_edges, time.perf_counter() - t0
+
+
+def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
+    import multiprocessing as mp
+    cores = min(16, len(os.sched_getaffinity(0)))
+    _SHARED.update(ip=ip, ix=ix, q=feats[0], k=feats[1], v=feats[2], dout=dout, scale=scale,
+                   score=w.score, slope=0.2)
+    rng = np.random.default_rng(12345)
+    n = ip.size - 1
+    rows = rng.permutation(n)[: min(n, 400_000)]
+    parts = np.array_split(rows, cores)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        res = pool.map(_cpu_worker, [(p, budget_s, w.backward) for p in parts])
+    wall = time.perf_counter() - t0
+    r = sum(x[0] for x in res)
+    e = sum(x[1] for x in res)
+    longest = max(x[2] for x in res)
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    what = "forward+backward" if w.backward else "forward"
+    return {
+        "value": e / longest, "unit": "edges/s", "cores": cores, "kind": "oracle",
+        "sample": f"{what} of {r} uniformly sampled rows ({e} edges) of the same graph, "
+                  f"time-boxed to {budget_s:.0f} s per worker on {cores} fork workers "
+                  f"(fp64 numpy per-row oracle, 1 BLAS thread each); wall {wall:.1f} s; "
+                  f"cpu: {cpu}",
+    }
+
+
+# ---------------------------------------------------------------- GPU
+
+def to_dev(x):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_graph_attention_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources (else None)."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="chunglu1m_train_bf16", choices=sorted(gg.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds per worker for the oracle baseline (0 = skip)")
+    ap.add_argument("--light", type=int, default=None)
+    ap.add_argument("--hub", type=int, default=None)
+    ap.add_argument("--chunk", type=int, default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the fused layer is measured on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    w = gg.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    ip, ix = gg.make_graph(w)
+    feats = gg.make_features(w)
+    dout = gg.make_dout(w) if w.backward else None
+    gen_s = time.perf_counter() - t0
+    N, E, H, d = ip.size - 1, ix.size, w.heads, w.dim
+    b = 2 if w.dtype == "bf16" else 4
+    scale = float(np.float32(1 / math.sqrt(d))) if w.score == "dot" else 1.0
+    print(f"[bench] {w.name}: N={N} E={E} H={H} d={d} {w.dtype} {w.score} "
+          f"backward={w.backward} (inputs {gen_s:.1f}s)", file=sys.stderr, flush=True)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(ip, ix, feats, dout, w, scale, args.cpu_budget)
+        print(f"[bench] cpu oracle: {cpu['value']:.3g} edges/s on {cpu['cores']} cores",
+              file=sys.stderr, flush=True)
+
+    # ---- GPU from here on
+    import torch
+    import sparse_graph_attention_02_amd as ga
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    plan = ga.Plan(ip, ix, light_max_deg=args.light, hub_min_deg_exclusive=args.hub,
+                   hub_chunk=args.chunk, build_csc=w.backward)
+    plan_host_s = time.perf_counter() - t0
+    plan.upload("cuda")
+    torch.cuda.synchronize()
+    plan_s = time.perf_counter() - t0
+    info = plan.info()
+    tens = [to_dev(x) for x in feats]
+    tdo = to_dev(dout) if dout is not None else None
+    stream = torch.cuda.current_stream()
+
+    # copy-kernel bandwidth on this device (the measured ceiling next to the 8 TB/s spec)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        ga.copy_probe(dst, src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        ga.copy_probe(dst, src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    out = torch.empty_like(tens[2])
+    lse = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    fws = torch.empty(max(plan.fwd_workspace_bytes(H, d), 1), dtype=torch.uint8, device="cuda")
+    if w.backward:
+        dq, dk, dv = (torch.empty_like(tens[0]) for _ in range(3))
+        bws = torch.empty(plan.bwd_workspace_bytes(H, d), dtype=torch.uint8, device="cuda")
+
+    def step(backward=w.backward):
+        ga.fwd(plan, *tens, score=w.score, scale=scale, out=out, lse=lse, workspace=fws)
+        if backward:
+            ga.bwd(plan, *tens, tdo, lse, scale=scale, dq=dq, dk=dk, dv=dv, workspace=bws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn, k):
+        ga.timers(enable=True, reset=True)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        z.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(z) / k
+        kt = ga.timers(enable=False, reset=True)
+        return ms, kt
+
+    ms_step, kt = timed(step, args.steps)
+    ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
+
+    kernels = {}
+    for name, (launches, tot) in kt.items():
+        per = tot / launches
+        ab = algorithmic_bytes(name, N, E, H, d, b)
+        kernels[name] = {"launches_per_step": launches / args.steps, "avg_ms": per,
+                         "share": tot / (ms_step * args.steps)}
+        if ab is not None:
+            kernels[name].update(algorithmic_bytes=ab, GBps=ab / (per * 1e-3) / 1e9)
+    dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
+              key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
+    dk_ = kernels[dom]
+    ach = dk_["GBps"]
+    traffic = measured_traffic(w.name, dom)
+    fwd_bytes = step_bytes(N, E, H, d, b, False)
+    tot_bytes = step_bytes(N, E, H, d, b, w.backward)
+    fwd_main_ms = kt_fwd["fwd_main"][1] / kt_fwd["fwd_main"][0]
+    rec = {
+        "metric": "fused graph-attn fwd/bwd edges/sec + achieved HBM GB/s (% of MI355X peak)",
+        "value": E / (ms_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "graph": w.graph, "nodes": N, "edges": E, "heads": H, "dim": d,
+            "score": w.score, "step": "forward+backward" if w.backward else "forward",
+            "plan": {k: info[k] for k in ("light_max_deg", "hub_min_deg_exclusive", "hub_chunk",
+                                          "n_row_light", "n_row_medium", "n_row_hub",
+                                          "n_row_chunks", "n_col_hub", "n_col_chunks",
+                                          "max_in_degree", "max_out_degree")},
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "step_GBps_algorithmic": tot_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": tot_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "fwd": {"ms": ms_fwd, "edges_per_s": E / (ms_fwd * 1e-3),
+                "GBps_algorithmic": fwd_bytes / (ms_fwd * 1e-3) / 1e9,
+                "frac_of_peak": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "fwd_main_ms": fwd_main_ms},
+        "kernels": kernels,
+        "copy_probe_GBps": copy_gbps,
+        "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,
+        "workspace_bytes": {"fwd": plan.fwd_workspace_bytes(H, d),
+                            "bwd": plan.bwd_workspace_bytes(H, d) if w.backward else 0,
+                            "edge_score_tensor_would_be": E * H * 4},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
