@@ -69,7 +69,7 @@ struct Bwd {
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      const int my_j = (li < nb) ? a.indices[base + li] : 0;
+      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
@@ -114,11 +114,11 @@ struct Bwd {
     const int lane = threadIdx.x & (kWave - 1);
     const raw_t* __restrict__ Qr = R(a.q);
     const raw_t* __restrict__ Or = R(a.dout);
-    const float2* __restrict__ LD = reinterpret_cast<const float2*>(a.ws_ld);
+    const f32x2* __restrict__ LD = reinterpret_cast<const f32x2*>(a.ws_ld);
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      const int my_i = (li < nb) ? a.rowidx[base + li] : 0;
+      const int my_i = (li < nb) ? ld_stream(a.rowidx + base + li) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int ii[U];
         bool ok[U];
@@ -129,7 +129,7 @@ struct Bwd {
           ii[u] = __shfl(my_i, seg0 + (ok[u] ? pos : t));
         }
         raw_t qr[U], dr[U];
-        float2 ld[U];
+        f32x2 ld[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           qr[u] = Qr[static_cast<size_t>(ii[u]) * G + r];
@@ -160,21 +160,21 @@ struct Bwd {
     float o[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) o[c] = x[c] * mul;
-    static_cast<raw_t*>(base)[static_cast<size_t>(row) * G + r] = L16::pack(o);
+    st_stream(static_cast<raw_t*>(base) + static_cast<size_t>(row) * G + r, L16::pack(o));
   }
 
   __device__ __forceinline__ static void store_f32(float* base, int r, const float* x) {
-    float4* p = reinterpret_cast<float4*>(base + r * VEC);
+    f32x4* p = reinterpret_cast<f32x4*>(base + r * VEC);
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c)
-      p[c] = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
+      st_stream(p + c, f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]});
   }
 
   __device__ __forceinline__ static void add_f32(const float* base, int r, float* x) {
-    const float4* p = reinterpret_cast<const float4*>(base + r * VEC);
+    const f32x4* p = reinterpret_cast<const f32x4*>(base + r * VEC);
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c) {
-      const float4 y = p[c];
+      const f32x4 y = ld_stream(p + c);
       x[4 * c] += y.x;
       x[4 * c + 1] += y.y;
       x[4 * c + 2] += y.z;
@@ -186,9 +186,9 @@ struct Bwd {
   __device__ __forceinline__ static void row_prologue(const BwdArgs& a, int row, int r, int h,
                                                       float* qf, float* dof, float& lse2) {
     const size_t off = static_cast<size_t>(row) * G + r;
-    L16::unpack(R(a.q)[off], qf);
-    L16::unpack(R(a.dout)[off], dof);
-    lse2 = a.lse[static_cast<size_t>(row) * H + h] * kLog2e;
+    L16::unpack(ld_stream(R(a.q) + off), qf);
+    L16::unpack(ld_stream(R(a.dout) + off), dof);
+    lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
   }
 
   // dq = scale (A - D B), written in the feature dtype.
@@ -208,7 +208,7 @@ struct Bwd {
 };
 
 // dQ pass. Hub-row chunk partial layout in ws_dq: [chunk][A: F | B: F | D: H, padded to 4]
-// fp32 (kDqStride floats per chunk, a multiple of 4 so the float4 stores stay aligned).
+// fp32 (kDqStride floats per chunk, a multiple of 4 so the 16-byte stores stay aligned).
 template <typename T, int G, int LH, int U>
 __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
   using K = Bwd<T, G, LH, U>;
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
   float qf[VEC], dof[VEC], A[VEC], Bk[VEC], lse2, D = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
-  float2* LD = reinterpret_cast<float2*>(a.ws_ld);
+  f32x2* LD = reinterpret_cast<f32x2*>(a.ws_ld);
   if (item < B.n_chunks + B.n_medium) {
     int row, e0, e1;
     const bool chunk = item < B.n_chunks;
@@ -243,9 +243,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
       float* p = a.ws_dq + static_cast<size_t>(item) * K::kDqStride;
       K::store_f32(p, r, A);
       K::store_f32(p + F, r, Bk);
-      if (r % LH == 0) p[2 * F + h] = D;
+      if (r % LH == 0) st_stream(p + 2 * F + h, D);
     } else {
-      if (r % LH == 0) LD[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+      if (r % LH == 0) st_stream(LD + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
       K::store_dq(a, row, r, A, Bk, D);
     }
     return;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
   K::row_prologue(a, row, r, h, qf, dof, lse2);
   K::template run_dq<1>(a, e0, e1, g * G, 0, r, qf, dof, lse2, A, Bk, D);
-  if (r % LH == 0) LD[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+  if (r % LH == 0) st_stream(LD + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
   K::store_dq(a, row, r, A, Bk, D);
 }
 
@@ -276,11 +276,11 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
     const float* p = a.ws_dq + static_cast<size_t>(c) * K::kDqStride;
     K::add_f32(p, r, A);
     K::add_f32(p + F, r, Bk);
-    D += p[2 * F + h];
+    D += ld_stream(p + 2 * F + h);
   }
   if (r % LH == 0) {
-    const float lse2 = a.lse[static_cast<size_t>(row) * H + h] * kLog2e;
-    reinterpret_cast<float2*>(a.ws_ld)[static_cast<size_t>(row) * H + h] = make_float2(lse2, D);
+    const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
+    st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
   }
   K::store_dq(a, row, r, A, Bk, D);
 }
@@ -309,8 +309,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
       e1 = a.colptr[col + 1];
     }
     const size_t off = static_cast<size_t>(col) * G + r;
-    K::L16::unpack(K::R(a.k)[off], kf);
-    K::L16::unpack(K::R(a.v)[off], vf);
+    K::L16::unpack(ld_stream(K::R(a.k) + off), kf);
+    K::L16::unpack(ld_stream(K::R(a.v) + off), vf);
     K::template run_dkdv<NG>(a, e0, e1, 0, g, r, h, kf, vf, dk, dv);
     K::template group_sum<NG>(dk);
     K::template group_sum<NG>(dv);

@@ -56,9 +56,9 @@ struct Fwd {
   __device__ __forceinline__ static void load_row(const FwdArgs& a, int row, int r, int h,
                                                   RowOp& q) {
     if constexpr (GAT) {
-      q.si = static_cast<const float*>(a.a)[static_cast<size_t>(row) * H + h];
+      q.si = ld_stream(static_cast<const float*>(a.a) + static_cast<size_t>(row) * H + h);
     } else {
-      const raw_t x = static_cast<const raw_t*>(a.a)[static_cast<size_t>(row) * G + r];
+      const raw_t x = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * G + r);
       L16::unpack(x, q.qf);
     }
   }
@@ -76,7 +76,7 @@ struct Fwd {
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      const int my_j = (li < nb) ? a.indices[base + li] : 0;
+      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
@@ -163,22 +163,23 @@ struct Fwd {
     float o[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) o[c] = st.acc[c] * inv;
-    static_cast<raw_t*>(a.out)[static_cast<size_t>(row) * G + r] = L16::pack(o);
+    st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * G + r, L16::pack(o));
     if (r % LH == 0)
-      a.lse[static_cast<size_t>(row) * H + h] =
-          st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY;
+      st_stream(a.lse + static_cast<size_t>(row) * H + h,
+                st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY);
   }
 
   __device__ __forceinline__ static void write_partial(const FwdArgs& a, int chunk, int r, int h,
                                                        const State& st) {
     if (r % LH == 0) {
-      float2* ml = reinterpret_cast<float2*>(a.ws_ml);
-      ml[static_cast<size_t>(chunk) * H + h] = make_float2(st.m, st.l);
+      f32x2* ml = reinterpret_cast<f32x2*>(a.ws_ml);
+      st_stream(ml + static_cast<size_t>(chunk) * H + h, f32x2{st.m, st.l});
     }
-    float4* acc = reinterpret_cast<float4*>(a.ws_acc + static_cast<size_t>(chunk) * F + r * VEC);
+    f32x4* acc = reinterpret_cast<f32x4*>(a.ws_acc + static_cast<size_t>(chunk) * F + r * VEC);
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c)
-      acc[c] = make_float4(st.acc[4 * c], st.acc[4 * c + 1], st.acc[4 * c + 2], st.acc[4 * c + 3]);
+      st_stream(acc + c, f32x4{st.acc[4 * c], st.acc[4 * c + 1], st.acc[4 * c + 2],
+                               st.acc[4 * c + 3]});
   }
 };
 
@@ -234,19 +235,19 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   if (hub >= a.bins.n_hub) return;
   const int row = a.bins.hub[hub];
   const int c0 = a.bins.hub_chunk_ptr[hub], c1 = a.bins.hub_chunk_ptr[hub + 1];
-  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml);
+  const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml);
   typename K::State st;
   K::init(st);
   for (int c = c0; c < c1; ++c) {
-    const float2 p = ml[static_cast<size_t>(c) * H + h];
-    const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + static_cast<size_t>(c) * F + r * VEC);
+    const f32x2 p = ld_stream(ml + static_cast<size_t>(c) * H + h);
+    const f32x4* acc = reinterpret_cast<const f32x4*>(a.ws_acc + static_cast<size_t>(c) * F + r * VEC);
     const float mn = fmaxf(st.m, p.x);
     const float f1 = fast_exp2(st.m - mn);
     const float f2 = fast_exp2(p.x - mn);
     st.l = st.l * f1 + p.y * f2;
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k) {
-      const float4 x = acc[k];
+      const f32x4 x = ld_stream(acc + k);
       st.acc[4 * k] = st.acc[4 * k] * f1 + x.x * f2;
       st.acc[4 * k + 1] = st.acc[4 * k + 1] * f1 + x.y * f2;
       st.acc[4 * k + 2] = st.acc[4 * k + 2] * f1 + x.z * f2;

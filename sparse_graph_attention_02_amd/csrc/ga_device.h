@@ -22,12 +22,29 @@ constexpr float kEmptyMax = -1.0e30f;
 // bf16 is carried as raw 16-bit patterns.
 using bf16_t = uint16_t;
 
+// 16-byte lane vectors as clang ext-vector types (accepted by the non-temporal builtins).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Loads/stores of data a pass touches exactly once (index batches, the row-side operand,
+// outputs, partials) carry the non-temporal hint so they do not evict the gathered
+// neighbour rows, which power-law graphs re-read from L2.
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename V>
+__device__ __forceinline__ void st_stream(V* p, V x) {
+  __builtin_nontemporal_store(x, p);
+}
+
 template <typename T>
 struct Lane16;
 
 template <>
 struct Lane16<float> {
-  using raw_t = float4;
+  using raw_t = f32x4;
   static constexpr int VEC = 4;
   __device__ __forceinline__ static void unpack(const raw_t& x, float* f) {
     f[0] = x.x;
@@ -36,7 +53,7 @@ struct Lane16<float> {
     f[3] = x.w;
   }
   __device__ __forceinline__ static raw_t pack(const float* f) {
-    return make_float4(f[0], f[1], f[2], f[3]);
+    return raw_t{f[0], f[1], f[2], f[3]};
   }
 };
 
@@ -50,7 +67,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 
 template <>
 struct Lane16<bf16_t> {
-  using raw_t = uint4;
+  using raw_t = u32x4;
   static constexpr int VEC = 8;
   __device__ __forceinline__ static void unpack(const raw_t& x, float* f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -64,7 +81,7 @@ struct Lane16<bf16_t> {
     uint32_t w[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[c] = bf16_rne(f[2 * c]) | (bf16_rne(f[2 * c + 1]) << 16);
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return raw_t{w[0], w[1], w[2], w[3]};
   }
 };
 
