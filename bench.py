@@ -252,6 +252,12 @@ def main():
 
     ms_step, kt = timed(step, args.steps)
     ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
+    # gather floor: the forward's neighbour gathers alone (same graph, same lane pattern)
+    sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    kv = (tens[1], tens[2]) if w.score == "dot" else (tens[2], tens[2])
+    ga.gather_probe(plan, *kv, sink=sink)
+    ms_gather, _ = timed(lambda: ga.gather_probe(plan, *kv, sink=sink), args.steps)
+    gather_bytes = 2 * E * H * d * b + 4 * E
 
     kernels = {}
     for name, (launches, tot) in kt.items():
@@ -301,6 +307,12 @@ def main():
                 "GBps_algorithmic": fwd_bytes / (ms_fwd * 1e-3) / 1e9,
                 "frac_of_peak": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "fwd_main_ms": fwd_main_ms},
+        "gather_floor": {
+            "ms": ms_gather, "GBps_algorithmic": gather_bytes / (ms_gather * 1e-3) / 1e9,
+            "fwd_main_frac_of_floor": ms_gather / fwd_main_ms,
+            "note": "K and V rows of every edge gathered with the forward's lane pattern and "
+                    "no arithmetic (graph_attn_gather_probe); the memory system's floor for "
+                    "the forward's gathers on this graph"},
         "kernels": kernels,
         "copy_probe_GBps": copy_gbps,
         "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,

@@ -199,6 +199,16 @@ ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launc
  * measure copy bandwidth and to calibrate traffic counters against a known byte count. */
 ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Gather-only pass over the plan's CSR: for every edge, load the source's K and V rows with
+ * the forward's lane pattern (16 bytes per lane, G = H*d*sizeof(dtype)/16 lanes per row)
+ * and do no arithmetic. Its duration is the memory system's floor for the forward's
+ * neighbour gathers on this graph (the roofline of a gather-bound kernel, measured rather
+ * than assumed). k, v as for graph_attn_fwd; sink: 1 KiB of device memory, 16-byte aligned,
+ * that the probe may write. The plan must be uploaded. */
+ga_status graph_attn_gather_probe(const ga_plan* plan, ga_dtype dtype, int32_t heads,
+                                  int32_t dim, const void* k, const void* v, void* sink,
+                                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ import numpy as np
 from . import capi
 from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,  # noqa: F401
                    graph_attn_bwd, graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
-                   graph_attn_fwd, graph_attn_fwd_workspace_bytes, graph_attn_plan_array,
+                   graph_attn_fwd, graph_attn_fwd_workspace_bytes, graph_attn_gather_probe,
+                   graph_attn_plan_array,
                    graph_attn_plan_array_count, graph_attn_plan_array_name,
                    graph_attn_plan_create, graph_attn_plan_destroy,
                    graph_attn_plan_device_bytes, graph_attn_plan_get_info,
@@ -260,6 +261,19 @@ def copy_probe(dst, src, stream=None):
     nbytes = src.numel() * src.element_size()
     with torch.cuda.device(src.device):
         graph_attn_copy_probe(_ptr(dst), _ptr(src), nbytes, _stream(stream))
+
+
+def gather_probe(plan: Plan, k, v, sink=None, stream=None):
+    """Gather-only pass over the plan's CSR with the forward's lane pattern (see
+    graph_attn_gather_probe); returns the sink tensor."""
+    import torch
+    if sink is None:
+        sink = torch.empty(1024, dtype=torch.uint8, device=k.device)
+    N, H, d = k.shape
+    with torch.cuda.device(k.device):
+        graph_attn_gather_probe(plan.handle, _dtype_code(k), H, d, _ptr(k), _ptr(v), _ptr(sink),
+                                _stream(stream))
+    return sink
 
 
 def timers(enable=None, reset=False) -> dict:

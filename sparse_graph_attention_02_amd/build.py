@@ -57,19 +57,35 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, out: str | None = None, defines=()) -> str:
+    """Compile and link; ``out`` and ``defines`` (e.g. ["GA_UNROLL=8"]) build a variant
+    library elsewhere (tuning); the default is the in-tree libgraph_attn.so."""
+    global OBJ
+    lib = out or LIB
+    obj_dir = OBJ if out is None else os.path.splitext(out)[0] + "_obj"
+    os.makedirs(obj_dir, exist_ok=True)
+    saved = OBJ, list(COMMON)
+    OBJ = obj_dir
+    COMMON.extend(f"-D{d}" for d in defines)
+    try:
+        return _build(verbose, lib)
+    finally:
+        OBJ = saved[0]
+        COMMON[:] = saved[1]
+
+
+def _build(verbose: bool, lib: str) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -11,7 +11,9 @@ import os
 from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int32, c_int64,
                     c_size_t, c_void_p)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgraph_attn.so")
+# GRAPH_ATTN_LIB selects another build of the same library (tuning variants).
+LIB_PATH = os.environ.get("GRAPH_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libgraph_attn.so")
 
 GA_OK, GA_ERR_INVALID_ARG, GA_ERR_BAD_GRAPH, GA_ERR_UNSUPPORTED = 0, 1, 2, 3
 GA_ERR_WORKSPACE, GA_ERR_NOT_READY, GA_ERR_HIP, GA_ERR_HOST_ALLOC = 4, 5, 6, 7
@@ -69,6 +71,8 @@ _SIGS = {
     "graph_attn_timer_read": (c_int32, [c_int32, POINTER(c_char_p), POINTER(c_int64),
                                         POINTER(c_double)]),
     "graph_attn_copy_probe": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
+    "graph_attn_gather_probe": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                          c_void_p, c_void_p]),
 }
 
 _lib = None
@@ -135,6 +139,7 @@ graph_attn_timer_reset = _wrap("graph_attn_timer_reset")
 graph_attn_timer_count = _wrap("graph_attn_timer_count")
 graph_attn_timer_read = _wrap("graph_attn_timer_read")
 graph_attn_copy_probe = _wrap("graph_attn_copy_probe")
+graph_attn_gather_probe = _wrap("graph_attn_gather_probe")
 
 
 def raw_status(name: str, *args) -> int:

@@ -466,6 +466,22 @@ ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launc
   return GA_OK;
 }
 
+ga_status graph_attn_gather_probe(const ga_plan* p, ga_dtype dtype, int32_t heads, int32_t dim,
+                                  const void* k, const void* v, void* sink, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (g.G < 4) return GA_ERR_UNSUPPORTED;
+  if (p->n > 0 && ((s = check_ptr(k, 16)) != GA_OK || (s = check_ptr(v, 16)) != GA_OK)) return s;
+  if ((s = check_ptr(sink, 16)) != GA_OK) return s;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->e == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+  const int rc = ga::launch_gather_probe(p->d_indices, p->e, g.G, k, v, sink, stream, active_hook());
+  return rc == 0 ? GA_OK : GA_ERR_HIP;
+}
+
 ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
   if (bytes % 16) return GA_ERR_INVALID_ARG;
   if (bytes == 0) return GA_OK;

@@ -40,13 +40,6 @@ struct Bwd {
     return static_cast<const raw_t*>(p);
   }
 
-  __device__ __forceinline__ static float dot(const float* x, const float* y) {
-    float d = 0.f;
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) d = fmaf(x[c], y[c], d);
-    return d;
-  }
-
   // Sum a per-lane vector over the NGS groups of a segment (butterfly, fixed order).
   template <int NGS>
   __device__ __forceinline__ static void group_sum(float* x) {
@@ -60,7 +53,7 @@ struct Bwd {
   // Accumulates A += P dp k, B += P k and D += P dp over edges [e0, e1).
   template <int NGS>
   __device__ __forceinline__ static void run_dq(const BwdArgs& a, int e0, int e1, int seg0,
-                                                int gs, int r, const float* qf, const float* dof,
+                                                int gs, int r, const raw_t& qr, const raw_t& dor,
                                                 float lse2, float* A, float* Bk, float& D) {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
@@ -87,11 +80,10 @@ struct Bwd {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          float kf[VEC], vf[VEC];
+          float kf[VEC];
           L16::unpack(kr[u], kf);
-          L16::unpack(vr[u], vf);
-          const float s2 = head_sum<LH>(dot(qf, kf)) * a.sc2;
-          const float dp = head_sum<LH>(dot(dof, vf));
+          const float s2 = head_sum<LH>(L16::dot(qr, kr[u])) * a.sc2;
+          const float dp = head_sum<LH>(L16::dot(dor, vr[u]));
           const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
           const float pdp = p * dp;
           D += pdp;
@@ -108,8 +100,8 @@ struct Bwd {
   // ---- dK / dV over transpose columns ----------------------------------------------
   template <int NGS>
   __device__ __forceinline__ static void run_dkdv(const BwdArgs& a, int e0, int e1, int seg0,
-                                                  int gs, int r, int h, const float* kf,
-                                                  const float* vf, float* dk, float* dv) {
+                                                  int gs, int r, int h, const raw_t& kr,
+                                                  const raw_t& vr, float* dk, float* dv) {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
     const raw_t* __restrict__ Qr = R(a.q);
@@ -141,8 +133,8 @@ struct Bwd {
           float qf[VEC], df[VEC];
           L16::unpack(qr[u], qf);
           L16::unpack(dr[u], df);
-          const float s2 = head_sum<LH>(dot(qf, kf)) * a.sc2;
-          const float dp = head_sum<LH>(dot(df, vf));
+          const float s2 = head_sum<LH>(L16::dot(qr[u], kr)) * a.sc2;
+          const float dp = head_sum<LH>(L16::dot(dr[u], vr));
           const float p = ok[u] ? fast_exp2(s2 - ld[u].x) : 0.f;
           const float ds = p * (dp - ld[u].y);
 #pragma unroll
@@ -184,10 +176,10 @@ struct Bwd {
 
   // Row prologue of the dQ pass: q and dout slices, lse in log2 units.
   __device__ __forceinline__ static void row_prologue(const BwdArgs& a, int row, int r, int h,
-                                                      float* qf, float* dof, float& lse2) {
+                                                      raw_t& qr, raw_t& dor, float& lse2) {
     const size_t off = static_cast<size_t>(row) * G + r;
-    L16::unpack(ld_stream(R(a.q) + off), qf);
-    L16::unpack(ld_stream(R(a.dout) + off), dof);
+    qr = ld_stream(R(a.q) + off);
+    dor = ld_stream(R(a.dout) + off);
     lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
   }
 
@@ -210,14 +202,15 @@ struct Bwd {
 // dQ pass. Hub-row chunk partial layout in ws_dq: [chunk][A: F | B: F | D: H, padded to 4]
 // fp32 (kDqStride floats per chunk, a multiple of 4 so the 16-byte stores stay aligned).
 template <typename T, int G, int LH, int U>
-__global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
   using K = Bwd<T, G, LH, U>;
   constexpr int NG = K::NG, VEC = K::VEC, H = K::H, F = K::F;
   const int lane = threadIdx.x & (kWave - 1);
   const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.rows;
-  float qf[VEC], dof[VEC], A[VEC], Bk[VEC], lse2, D = 0.f;
+  typename K::raw_t qr, dor;
+  float A[VEC], Bk[VEC], lse2, D = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
   f32x2* LD = reinterpret_cast<f32x2*>(a.ws_ld);
@@ -233,8 +226,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
       e0 = a.indptr[row];
       e1 = a.indptr[row + 1];
     }
-    K::row_prologue(a, row, r, h, qf, dof, lse2);
-    K::template run_dq<NG>(a, e0, e1, 0, g, r, qf, dof, lse2, A, Bk, D);
+    K::row_prologue(a, row, r, h, qr, dor, lse2);
+    K::template run_dq<NG>(a, e0, e1, 0, g, r, qr, dor, lse2, A, Bk, D);
     K::template group_sum<NG>(A);
     K::template group_sum<NG>(Bk);
     K::template group_sum1<NG>(D);
@@ -254,30 +247,38 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_main(BwdArgs a) {
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
-  K::row_prologue(a, row, r, h, qf, dof, lse2);
-  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qf, dof, lse2, A, Bk, D);
+  K::row_prologue(a, row, r, h, qr, dor, lse2);
+  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qr, dor, lse2, A, Bk, D);
   if (r % LH == 0) st_stream(LD + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
   K::store_dq(a, row, r, A, Bk, D);
 }
 
+// One wavefront per hub row: lane group g sums chunks c0+g, c0+g+NG, ... in ascending
+// order, then the group sums are added by the fixed butterfly (deterministic).
 template <typename T, int G, int LH>
 __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
   using K = Bwd<T, G, LH, 1>;
-  constexpr int VEC = K::VEC, F = K::F, H = K::H;
-  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
-  const int r = threadIdx.x % G, h = r / LH;
+  constexpr int VEC = K::VEC, F = K::F, H = K::H, NG = K::NG;
+  const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G, r = lane % G, h = r / LH;
   if (hub >= a.rows.n_hub) return;
   const int row = a.rows.hub[hub];
   const int c0 = a.rows.hub_chunk_ptr[hub], c1 = a.rows.hub_chunk_ptr[hub + 1];
   float A[VEC], Bk[VEC], D = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
-  for (int c = c0; c < c1; ++c) {
+#pragma unroll 4
+  for (int c = c0 + g; c < c1; c += NG) {
     const float* p = a.ws_dq + static_cast<size_t>(c) * K::kDqStride;
     K::add_f32(p, r, A);
     K::add_f32(p + F, r, Bk);
     D += ld_stream(p + 2 * F + h);
   }
+  K::template group_sum<NG>(A);
+  K::template group_sum<NG>(Bk);
+  K::template group_sum1<NG>(D);
+  if (g != 0) return;
   if (r % LH == 0) {
     const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
     st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
@@ -286,14 +287,15 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
 }
 
 template <typename T, int G, int LH, int U>
-__global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) {
   using K = Bwd<T, G, LH, U>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
   const int lane = threadIdx.x & (kWave - 1);
   const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.cols;
-  float kf[VEC], vf[VEC], dk[VEC], dv[VEC];
+  typename K::raw_t kr, vr;
+  float dk[VEC], dv[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
   if (item < B.n_chunks + B.n_medium) {
@@ -309,9 +311,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
       e1 = a.colptr[col + 1];
     }
     const size_t off = static_cast<size_t>(col) * G + r;
-    K::L16::unpack(ld_stream(K::R(a.k) + off), kf);
-    K::L16::unpack(ld_stream(K::R(a.v) + off), vf);
-    K::template run_dkdv<NG>(a, e0, e1, 0, g, r, h, kf, vf, dk, dv);
+    kr = ld_stream(K::R(a.k) + off);
+    vr = ld_stream(K::R(a.v) + off);
+    K::template run_dkdv<NG>(a, e0, e1, 0, g, r, h, kr, vr, dk, dv);
     K::template group_sum<NG>(dk);
     K::template group_sum<NG>(dv);
     if (g != 0) return;
@@ -330,9 +332,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
   const size_t off = static_cast<size_t>(col) * G + r;
-  K::L16::unpack(K::R(a.k)[off], kf);
-  K::L16::unpack(K::R(a.v)[off], vf);
-  K::template run_dkdv<1>(a, e0, e1, g * G, 0, r, h, kf, vf, dk, dv);
+  kr = ld_stream(K::R(a.k) + off);
+  vr = ld_stream(K::R(a.v) + off);
+  K::template run_dkdv<1>(a, e0, e1, g * G, 0, r, h, kr, vr, dk, dv);
   K::store(a.dk, col, r, dk, a.scale);
   K::store(a.dv, col, r, dv, 1.f);
 }
@@ -340,27 +342,31 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_main(BwdArgs a) {
 template <typename T, int G, int LH>
 __global__ __launch_bounds__(kBlock) void bwd_dkdv_merge(BwdArgs a) {
   using K = Bwd<T, G, LH, 1>;
-  constexpr int VEC = K::VEC, F = K::F;
-  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
-  const int r = threadIdx.x % G;
+  constexpr int VEC = K::VEC, F = K::F, NG = K::NG;
+  const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G, r = lane % G;
   if (hub >= a.cols.n_hub) return;
   const int col = a.cols.hub[hub];
   const int c0 = a.cols.hub_chunk_ptr[hub], c1 = a.cols.hub_chunk_ptr[hub + 1];
   float dk[VEC], dv[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
-  for (int c = c0; c < c1; ++c) {
+#pragma unroll 4
+  for (int c = c0 + g; c < c1; c += NG) {
     const float* p = a.ws_dkv + static_cast<size_t>(c) * 2 * F;
     K::add_f32(p, r, dk);
     K::add_f32(p + F, r, dv);
   }
+  K::template group_sum<NG>(dk);
+  K::template group_sum<NG>(dv);
+  if (g != 0) return;
   K::store(a.dk, col, r, dk, a.scale);
   K::store(a.dv, col, r, dv, 1.f);
 }
 
 template <typename T, int G, int LH>
 int launch(const BwdArgs& a, void* stream, TimerHook hook) {
-  constexpr int U = 4;
   constexpr int NG = kWave / G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto items_of = [](const DevBins& B) {
@@ -373,18 +379,18 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
     if (hook) hook(name, stream, 0);
     return static_cast<int>(hipGetLastError());
   };
-  const int per_block = kBlock / G;
   int e;
-  if ((e = go("bwd_dq_main", bwd_dq_main<T, G, LH, U>,
+  if ((e = go("bwd_dq_main", bwd_dq_main<T, G, LH, GA_UNROLL_DQ>,
               (items_of(a.rows) + kWavesPerBlock - 1) / kWavesPerBlock)))
     return e;
-  if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>, (a.rows.n_hub + per_block - 1) / per_block)))
+  if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>,
+              (a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock)))
     return e;
-  if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, U>,
+  if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, GA_UNROLL_DKDV>,
               (items_of(a.cols) + kWavesPerBlock - 1) / kWavesPerBlock)))
     return e;
   if ((e = go("bwd_dkdv_merge", bwd_dkdv_merge<T, G, LH>,
-              (a.cols.n_hub + per_block - 1) / per_block)))
+              (a.cols.n_hub + kWavesPerBlock - 1) / kWavesPerBlock)))
     return e;
   return 0;
 }

@@ -49,7 +49,7 @@ struct Fwd {
 
   // Row-side operand of the score: the query row slice (dot) or s[i, h] (gat).
   struct RowOp {
-    float qf[VEC];
+    raw_t q;
     float si;
   };
 
@@ -58,8 +58,7 @@ struct Fwd {
     if constexpr (GAT) {
       q.si = ld_stream(static_cast<const float*>(a.a) + static_cast<size_t>(row) * H + h);
     } else {
-      const raw_t x = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * G + r);
-      L16::unpack(x, q.qf);
+      q.q = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * G + r);
     }
   }
 
@@ -106,12 +105,7 @@ struct Fwd {
             x = q.si + tv[u];
             x = (x >= 0.f ? x : x * a.neg_slope) * a.sc2;
           } else {
-            float kf[VEC];
-            L16::unpack(kr[u], kf);
-            float d = 0.f;
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) d = fmaf(q.qf[c], kf[c], d);
-            x = head_sum<LH>(d) * a.sc2;
+            x = head_sum<LH>(L16::dot(q.q, kr[u])) * a.sc2;
           }
           s[u] = ok[u] ? x : -INFINITY;
         }
@@ -184,7 +178,7 @@ struct Fwd {
 };
 
 template <typename T, int G, int LH, bool GAT, int U>
-__global__ __launch_bounds__(kBlock) void fwd_main(FwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a) {
   using K = Fwd<T, G, LH, GAT, U>;
   constexpr int NG = K::NG;
   const int lane = threadIdx.x & (kWave - 1);
@@ -225,42 +219,48 @@ __global__ __launch_bounds__(kBlock) void fwd_main(FwdArgs a) {
   K::write_row(a, row, r, h, st);
 }
 
-// One G-lane group per hub row: fold its chunk partials in ascending chunk order.
+// One wavefront per hub row: lane group g folds chunks c0+g, c0+g+NG, ... in ascending
+// order, then the NG group states are combined by the fixed butterfly (deterministic).
 template <typename T, int G, int LH>
 __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   using K = Fwd<T, G, LH, false, 1>;
-  constexpr int H = K::H, F = K::F, VEC = K::VEC;
-  const int hub = blockIdx.x * (kBlock / G) + threadIdx.x / G;
-  const int r = threadIdx.x % G, h = r / LH;
+  constexpr int H = K::H, F = K::F, VEC = K::VEC, NG = K::NG;
+  const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G, r = lane % G, h = r / LH;
   if (hub >= a.bins.n_hub) return;
   const int row = a.bins.hub[hub];
   const int c0 = a.bins.hub_chunk_ptr[hub], c1 = a.bins.hub_chunk_ptr[hub + 1];
   const f32x2* ml = reinterpret_cast<const f32x2*>(a.ws_ml);
   typename K::State st;
   K::init(st);
-  for (int c = c0; c < c1; ++c) {
+#pragma unroll 4
+  for (int c = c0 + g; c < c1; c += NG) {
     const f32x2 p = ld_stream(ml + static_cast<size_t>(c) * H + h);
     const f32x4* acc = reinterpret_cast<const f32x4*>(a.ws_acc + static_cast<size_t>(c) * F + r * VEC);
+    f32x4 x[VEC / 4];
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) x[k] = ld_stream(acc + k);
     const float mn = fmaxf(st.m, p.x);
     const float f1 = fast_exp2(st.m - mn);
     const float f2 = fast_exp2(p.x - mn);
     st.l = st.l * f1 + p.y * f2;
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k) {
-      const f32x4 x = ld_stream(acc + k);
-      st.acc[4 * k] = st.acc[4 * k] * f1 + x.x * f2;
-      st.acc[4 * k + 1] = st.acc[4 * k + 1] * f1 + x.y * f2;
-      st.acc[4 * k + 2] = st.acc[4 * k + 2] * f1 + x.z * f2;
-      st.acc[4 * k + 3] = st.acc[4 * k + 3] * f1 + x.w * f2;
+      st.acc[4 * k] = st.acc[4 * k] * f1 + x[k].x * f2;
+      st.acc[4 * k + 1] = st.acc[4 * k + 1] * f1 + x[k].y * f2;
+      st.acc[4 * k + 2] = st.acc[4 * k + 2] * f1 + x[k].z * f2;
+      st.acc[4 * k + 3] = st.acc[4 * k + 3] * f1 + x[k].w * f2;
     }
     st.m = mn;
   }
-  K::write_row(a, row, r, h, st);
+  K::template combine<NG>(st);
+  if (g == 0) K::write_row(a, row, r, h, st);
 }
 
 template <typename T, int G, int LH, bool GAT>
 int launch(const FwdArgs& a, void* stream, TimerHook hook) {
-  constexpr int U = 4;
+  constexpr int U = GA_UNROLL_FWD;
   constexpr int NG = kWave / G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const DevBins& B = a.bins;
@@ -275,8 +275,7 @@ int launch(const FwdArgs& a, void* stream, TimerHook hook) {
     if (e != hipSuccess) return static_cast<int>(e);
   }
   if (B.n_hub > 0) {
-    const int per_block = kBlock / G;
-    const int blocks = (B.n_hub + per_block - 1) / per_block;
+    const int blocks = (B.n_hub + kWavesPerBlock - 1) / kWavesPerBlock;
     if (hook) hook("fwd_hub_merge", stream, 1);
     hipLaunchKernelGGL((fwd_hub_merge<T, G, LH>), dim3(blocks), dim3(kBlock), 0, s, a);
     if (hook) hook("fwd_hub_merge", stream, 0);

@@ -39,6 +39,27 @@ __device__ __forceinline__ void st_stream(V* p, V x) {
   __builtin_nontemporal_store(x, p);
 }
 
+// Edges folded per lane group per step (independent gathers in flight per lane), per pass.
+#ifndef GA_UNROLL_FWD
+#define GA_UNROLL_FWD 8
+#endif
+#ifndef GA_UNROLL_DQ
+#define GA_UNROLL_DQ 4
+#endif
+#ifndef GA_UNROLL_DKDV
+#define GA_UNROLL_DKDV 4
+#endif
+// Minimum waves per SIMD requested from the register allocator for the main kernels
+// (0 = compiler default).
+#ifndef GA_WAVES_PER_EU
+#define GA_WAVES_PER_EU 0
+#endif
+#if GA_WAVES_PER_EU > 0
+#define GA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(GA_WAVES_PER_EU)))
+#else
+#define GA_OCCUPANCY
+#endif
+
 template <typename T>
 struct Lane16;
 
@@ -54,6 +75,10 @@ struct Lane16<float> {
   }
   __device__ __forceinline__ static raw_t pack(const float* f) {
     return raw_t{f[0], f[1], f[2], f[3]};
+  }
+  // <x, y> over the lane's 4 elements, fp32 FMA chain.
+  __device__ __forceinline__ static float dot(const raw_t& x, const raw_t& y) {
+    return fmaf(x.w, y.w, fmaf(x.z, y.z, fmaf(x.y, y.y, x.x * y.x)));
   }
 };
 
@@ -82,6 +107,17 @@ struct Lane16<bf16_t> {
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[c] = bf16_rne(f[2 * c]) | (bf16_rne(f[2 * c + 1]) << 16);
     return raw_t{w[0], w[1], w[2], w[3]};
+  }
+  // <x, y> over the lane's 8 bf16 elements (unpack + fp32 FMA chain; a v_dot2_f32_bf16
+  // chain measured slower on gfx950 for these gather-bound passes).
+  __device__ __forceinline__ static float dot(const raw_t& x, const raw_t& y) {
+    float a[8], b[8];
+    unpack(x, a);
+    unpack(y, b);
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) d = fmaf(a[c], b[c], d);
+    return d;
   }
 };
 

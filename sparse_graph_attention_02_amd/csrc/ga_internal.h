@@ -123,5 +123,7 @@ int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, in
 int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t n, void* stream,
                TimerHook hook);
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
+int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
+                        void* sink, void* stream, TimerHook hook);
 
 }  // namespace ga

@@ -188,6 +188,18 @@ def test_timers_and_copy_probe_host_paths():
                            None) == capi.GA_ERR_INVALID_ARG
 
 
+def test_gather_probe_argument_checks():
+    p, _, _ = _hub_plan()
+    call = lambda plan, H=8, d=32, k=FAKE, v=FAKE, sink=FAKE: capi.raw_status(
+        "graph_attn_gather_probe", plan.handle if plan else None, capi.GA_BF16, H, d,
+        c_void_p(k), c_void_p(v), c_void_p(sink), None)
+    assert call(None) == capi.GA_ERR_INVALID_ARG
+    assert call(p, d=12) == capi.GA_ERR_UNSUPPORTED
+    assert call(p, k=0) == capi.GA_ERR_INVALID_ARG
+    assert call(p, sink=FAKE + 4) == capi.GA_ERR_INVALID_ARG
+    assert call(p) == capi.GA_ERR_NOT_READY
+
+
 def test_default_opts():
     o = default_opts()
     assert o["light_max_deg"] <= o["hub_min_deg_exclusive"] and o["hub_chunk"] >= 1

@@ -356,3 +356,16 @@ def test_full_chunglu1m_training_step_sampled():
                            np.flatnonzero(odeg == 1)[:4], rng.choice(w.n, 48, replace=False)])
     bwd_case("full chunglu1m training step (sampled rows/cols)", ip, ix, q, k, v, dout, "bf16",
              rows=rows, cols=cols)
+
+
+def test_gather_probe_runs_on_the_plan_graph():
+    w = gg.WORKLOADS["chunglu1m_dot_bf16"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    q, k, v = gg.make_features(w, n=20_000)
+    say("gather probe chunglu20k")
+    from sparse_graph_attention_02_amd import gather_probe
+    plan = Plan(ip, ix).upload()
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    gather_probe(plan, dev(k), dev(v), sink=sink)
+    torch.cuda.synchronize()
+    assert int(sink.sum()) == 0   # the probe writes its sink only on a 64-bit XOR collision
