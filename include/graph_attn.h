@@ -159,28 +159,35 @@ ga_status graph_attn_fwd(const ga_plan* plan, ga_score score, ga_dtype dtype, in
                          const void* k_or_t, const void* v, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace the backward needs: per-node (lse*log2 e, D) records N*H*8 bytes, fp32 dQ
- * partials of hub-row chunks n_row_chunks*(2*H*d + 4*ceil(H/4))*4 bytes and fp32 (dK, dV)
- * partials of hub-column chunks n_col_chunks*2*H*d*4 bytes, each section 256-byte
- * aligned. */
+/* Workspace the backward needs (either score): per-node (lse*log2 e, D) records N*H*8
+ * bytes, fp32 row-chunk partials n_row_chunks*(2*H*d + 4*ceil(2H/4))*4 bytes and fp32
+ * column-chunk partials n_col_chunks*2*H*d*4 bytes, each section 256-byte aligned. */
 ga_status graph_attn_bwd_workspace_bytes(const ga_plan* plan, int32_t heads, int32_t dim,
                                          size_t* bytes);
 
-/* Backward of the dot-score layer by recomputation (Methodology, attention-based layers,
- * backward pass: attention weights recomputed from the cached per-node log-sum-exp).
- * With P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, v_j>, D_i = sum_j P_ij dp_ij (per head),
- * dS_ij = P_ij (dp_ij - D_i):
- *   dq_i = scale sum_j dS_ij k_j   (over CSR rows; D_i is accumulated in the same pass
- *          from the recomputed weights, so the forward output is not needed)
- *   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i   (over the cached transpose)
- * Inputs: q, k, v, dout [N,H,d] of `dtype`, lse fp32 [N,H] as produced by graph_attn_fwd.
- * Outputs dq, dk, dv [N,H,d] of `dtype`, each fully written (rows and columns with no
- * edges get zeros). Needs a plan built with build_csc and uploaded (else
- * GA_ERR_NOT_READY). GA_SCORE_GAT returns GA_ERR_UNSUPPORTED in this version. */
+/* Backward by recomputation (Methodology, attention-based layers, backward pass: attention
+ * weights recomputed from the cached per-node log-sum-exp). With P_ij = exp(e_ij - lse_i),
+ * dp_ij = <dout_i, v_j>, D_i = sum_j P_ij dp_ij (per head), dS_ij = P_ij (dp_ij - D_i):
+ *   dot: dq_i = scale sum_j dS_ij k_j             (over CSR rows)
+ *        dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i   (over the transpose)
+ *   gat: with x_ij = s_i + t_j and g_ij = 1 if x_ij >= 0 else neg_slope,
+ *        ds_i = scale sum_j dS_ij g_ij             (over CSR rows)
+ *        dt_j = scale sum_i dS_ij g_ij,  dv_j = sum_i P_ij dout_i   (over the transpose)
+ * D_i is accumulated in the row pass from the recomputed weights, so the forward output
+ * is not needed; the row pass also sums the recomputed weights (1 up to the rounding of
+ * the stored lse) and divides by that sum, so both passes use weights that sum to 1.
+ * Arguments by score:
+ *   dot: q, k, v, dout, dq, dk, dv are [N,H,d] of `dtype` (16-byte aligned).
+ *   gat: q = s, k = t, dq = ds, dk = dt are fp32 [N,H] (4-byte aligned); v, dout, dv are
+ *        [N,H,d] of `dtype`. neg_slope is the forward's LeakyReLU slope (ignored for dot).
+ * lse: fp32 [N,H] as produced by graph_attn_fwd with the same scale (and slope). Every
+ * output is fully written (rows and columns with no edges get zeros). Needs a plan built
+ * with build_csc and uploaded (else GA_ERR_NOT_READY). */
 ga_status graph_attn_bwd(const ga_plan* plan, ga_score score, ga_dtype dtype, int32_t heads,
-                         int32_t dim, float scale, const void* q, const void* k, const void* v,
-                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int32_t dim, float scale, float neg_slope, const void* q,
+                         const void* k, const void* v, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Kernel timers (tracing). When enabled, every kernel the library launches is bracketed
  * by two hipEvents recorded on its stream; graph_attn_timer_read synchronises those

@@ -21,6 +21,11 @@ recomputed) is written out from the chain rule of the same definition, row by ro
     dp_k  = <dOut_i, v_{J_k}>,  D = sum_k alpha_k dp_k,  dS_k = alpha_k (dp_k - D)
     dq_i  = scale sum_k dS_k k_{J_k};  dk_{J_k} += scale dS_k q_i;  dv_{J_k} += alpha_k dOut_i
 
+GAT-style backward, x_ij = s_i + t_j, LeakyReLU'(x) = 1 for x >= 0 else neg_slope (the
+branch the forward takes at 0), same dS:
+    ds_i += scale dS_ij LeakyReLU'(x_ij);  dt_j += scale dS_ij LeakyReLU'(x_ij);
+    dv_j += alpha_ij dOut_i
+
 Conventions: CSR row = destination; parallel edges count with multiplicity; a row with
 no neighbours gives out = 0 and lse = -inf and no gradient.  All arithmetic is fp64;
 bf16 inputs arrive as uint16 bit patterns and are widened exactly.
@@ -32,6 +37,7 @@ import numpy as np
 __all__ = [
     "widen", "leaky_relu", "row_scores", "row_softmax", "forward_rows", "forward",
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
+    "backward_gat", "grad_s_rows", "grad_tv_cols",
 ]
 
 
@@ -230,3 +236,68 @@ def train_step_rows(indptr, indices, q, k, v, dout, rows, scale=None):
         np.add.at(dk, slot, sc * dS[:, :, None] * widen(q[i])[None])
         np.add.at(dv, slot, alpha[:, :, None] * widen(dout[i])[None])
     return out, lse, dq, cols, dk, dv
+
+
+def leaky_relu_grad(x: np.ndarray, neg_slope: float) -> np.ndarray:
+    return np.where(x >= 0.0, 1.0, neg_slope)
+
+
+def _row_backward_gat(i, indptr, indices, s, t, v, dout, scale, neg_slope):
+    """Per-row pieces of the GAT-style backward: (J, alpha, dS, LeakyReLU'(x)) [deg, H]."""
+    J = _neighbours(indptr, indices, i)
+    e = row_scores(i, indptr, indices, s, t, "gat", scale, neg_slope)
+    alpha, _ = row_softmax(e)
+    dp = np.einsum("hc,khc->kh", widen(dout[i]), widen(v[J]))
+    D = (alpha * dp).sum(axis=0)
+    x = widen(s[i])[None, :] + widen(t[J])
+    return J, alpha, alpha * (dp - D[None, :]), leaky_relu_grad(x, float(neg_slope))
+
+
+def backward_gat(indptr, indices, s, t, v, dout, scale=1.0, neg_slope=0.2):
+    """ds [N,H], dt [N,H], dv [N,H,d] (fp64) of the GAT-style layer, by rows with a
+    sequential scatter into dt and dv."""
+    sc = float(scale)
+    n = indptr.size - 1
+    ds = np.zeros(s.shape)
+    dt = np.zeros(t.shape)
+    dv = np.zeros(v.shape)
+    for i in range(n):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        J, alpha, dS, g = _row_backward_gat(i, indptr, indices, s, t, v, dout, sc, neg_slope)
+        ds[i] = sc * (dS * g).sum(axis=0)
+        np.add.at(dt, J, sc * dS * g)
+        np.add.at(dv, J, alpha[:, :, None] * widen(dout[i])[None])
+    return ds, dt, dv
+
+
+def grad_s_rows(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slope=0.2):
+    """ds [R, H] for the listed rows only."""
+    sc = float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    ds = np.zeros((rows.size, s.shape[1]))
+    for r, i in enumerate(rows):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        _, _, dS, g = _row_backward_gat(i, indptr, indices, s, t, v, dout, sc, neg_slope)
+        ds[r] = sc * (dS * g).sum(axis=0)
+    return ds
+
+
+def grad_tv_cols(indptr, indices, s, t, v, dout, cols, scale=1.0, neg_slope=0.2):
+    """dt [C, H] and dv [C, H, d] for the listed source columns only."""
+    sc = float(scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    slot = {int(j): c for c, j in enumerate(cols)}
+    dt = np.zeros((cols.size, t.shape[1]))
+    dv = np.zeros((cols.size,) + tuple(v.shape[1:]))
+    pos = np.flatnonzero(np.isin(indices, cols))
+    rows = np.searchsorted(indptr, pos, side="right") - 1
+    for i in np.unique(rows):
+        J, alpha, dS, g = _row_backward_gat(i, indptr, indices, s, t, v, dout, sc, neg_slope)
+        doi = widen(dout[i])
+        for kk in np.flatnonzero(np.isin(J, cols)):
+            c = slot[int(J[kk])]
+            dt[c] += sc * dS[kk] * g[kk]
+            dv[c] += alpha[kk][:, None] * doi
+    return dt, dv

@@ -199,26 +199,42 @@ def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2
     return out, lse
 
 
-def bwd(plan: Plan, q, k, v, dout, lse, *, scale=None, dq=None, dk=None, dv=None,
-        workspace=None, stream=None):
-    """Backward of the dot-score layer from the forward's lse; returns (dq, dk, dv), each
-    [N,H,d] like q."""
+def bwd(plan: Plan, q_or_s, k_or_t, v, dout, lse, *, score="dot", scale=None, neg_slope=0.2,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward from the forward's lse.
+
+    dot: returns (dq, dk, dv), each [N,H,d] like q; scale defaults to 1/sqrt(d).
+    gat: q_or_s = s, k_or_t = t (fp32 [N,H]); returns (ds, dt fp32 [N,H], dv [N,H,d]);
+    scale defaults to 1 and neg_slope to 0.2 (use the forward's values).
+    """
     import torch
     if plan.device_buffer is None:
         raise RuntimeError("plan is not uploaded")
-    N, H, d = q.shape
-    dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _need(t, name, (N, H, d), q.dtype, dev)
+    N, H, d = v.shape
+    dev = v.device
+    sc = GA_SCORE_DOT if score == "dot" else GA_SCORE_GAT if score == "gat" else None
+    if sc is None:
+        raise ValueError(score)
+    for name, t in (("v", v), ("dout", dout)):
+        _need(t, name, (N, H, d), v.dtype, dev)
+    if sc == GA_SCORE_DOT:
+        _need(q_or_s, "q", (N, H, d), v.dtype, dev)
+        _need(k_or_t, "k", (N, H, d), v.dtype, dev)
+        dq = torch.empty_like(q_or_s) if dq is None else dq
+        dk = torch.empty_like(k_or_t) if dk is None else dk
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+    else:
+        _need(q_or_s, "s", (N, H), torch.float32, dev)
+        _need(k_or_t, "t", (N, H), torch.float32, dev)
+        dq = torch.empty((N, H), dtype=torch.float32, device=dev) if dq is None else dq
+        dk = torch.empty((N, H), dtype=torch.float32, device=dev) if dk is None else dk
+        scale = 1.0 if scale is None else scale
     _need(lse, "lse", (N, H), torch.float32, dev)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dv = torch.empty_like(v) if dv is None else dv
     ws, wsb = _workspace(plan.bwd_workspace_bytes(H, d), dev, workspace)
     with torch.cuda.device(dev):
-        graph_attn_bwd(plan.handle, GA_SCORE_DOT, _dtype_code(q), H, d, float(scale),
-                       _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
+        graph_attn_bwd(plan.handle, sc, _dtype_code(v), H, d, float(scale), float(neg_slope),
+                       _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
                        _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(stream))
     return dq, dk, dv
 

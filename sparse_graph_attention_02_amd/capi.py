@@ -63,8 +63,8 @@ _SIGS = {
                                  c_size_t, c_void_p]),
     "graph_attn_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_size_t)]),
     "graph_attn_bwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
-                                 c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+                                 c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "graph_attn_timer_enable": (c_int32, [c_int32]),
     "graph_attn_timer_reset": (c_int32, []),
     "graph_attn_timer_count": (c_int32, []),

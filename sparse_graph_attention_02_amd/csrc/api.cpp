@@ -365,20 +365,24 @@ ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
 }
 
 ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads,
-                         int32_t dim, float scale, const void* q, const void* k, const void* v,
-                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         int32_t dim, float scale, float neg_slope, const void* q, const void* k,
+                         const void* v, const void* dout, const float* lse, void* dq, void* dk,
+                         void* dv, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return GA_ERR_INVALID_ARG;
   if (score != GA_SCORE_DOT && score != GA_SCORE_GAT) return GA_ERR_INVALID_ARG;
-  if (score == GA_SCORE_GAT) return GA_ERR_UNSUPPORTED;
   ga::Geometry g;
   ga_status s = make_geometry(dtype, heads, dim, &g);
   if (s != GA_OK) return s;
   if (!ga::bwd_supported(dtype, g)) return GA_ERR_UNSUPPORTED;
   if (p->n > 0) {
-    const void* f[] = {q, k, v, dout, dq, dk, dv};
-    for (const void* x : f)
+    // dot: q, k, dq, dk are [N,H,d] feature rows; gat: s, t, ds, dt are fp32 [N,H]
+    const size_t qk_align = score == GA_SCORE_DOT ? 16 : 4;
+    const void* f16[] = {v, dout, dv};
+    const void* fqk[] = {q, k, dq, dk};
+    for (const void* x : f16)
       if ((s = check_ptr(x, 16)) != GA_OK) return s;
+    for (const void* x : fqk)
+      if ((s = check_ptr(x, qk_align)) != GA_OK) return s;
     if ((s = check_ptr(lse, 4)) != GA_OK) return s;
   }
   if (!p->has_csc) return GA_ERR_NOT_READY;
@@ -412,7 +416,9 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.ws_dkv = reinterpret_cast<float*>(w);
   args.scale = scale;
   args.sc2 = scale * 1.4426950408889634f;
-  const int rc = ga::launch_bwd(dtype, g, args, p->n, stream, active_hook());
+  args.neg_slope = neg_slope;
+  const int rc = score == GA_SCORE_DOT ? ga::launch_bwd(dtype, g, args, p->n, stream, active_hook())
+                                       : ga::launch_bwd_gat(dtype, g, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
 

@@ -10,11 +10,15 @@
 // With P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, v_j>, D_i = sum_j P_ij dp_ij (per head),
 // dS_ij = P_ij (dp_ij - D_i):
 //   bwd_dq_main     over CSR rows (same bins / item order as the forward), one pass:
-//                   A_i = sum_j P_ij dp_ij k_j, B_i = sum_j P_ij k_j, D_i = sum_j P_ij dp_ij,
-//                   then dq_i = scale (A_i - D_i B_i) = scale sum_j dS_ij k_j, and the
-//                   record (lse_i log2 e, D_i) is stored for the column pass. D comes from
-//                   the recomputed weights, not from the rounded stored output, so it is
-//                   the exact row statistic (hub rows: fp32 chunk partials of A, B, D)
+//                   L_i = sum_j P_ij, A_i = sum_j P_ij dp_ij k_j, B_i = sum_j P_ij k_j,
+//                   D_i = sum_j P_ij dp_ij. L is 1 up to the rounding of the stored lse;
+//                   dividing by it makes the recomputed weights sum to 1, so with
+//                   D^ = D / L:  dq_i = scale (A_i - D^_i B_i) / L_i = scale sum_j dS_ij k_j
+//                   (single-neighbour rows give dq = 0 up to one rounding). The record
+//                   (lse_i log2 e + log2 L_i, D^_i) goes to the column pass, whose weights
+//                   are then normalised the same way. D comes from the recomputed weights,
+//                   not from the rounded stored output (hub rows: fp32 chunk partials of
+//                   A, B, D, L)
 //   bwd_dq_merge    hub rows: sum chunk partials in ascending chunk order
 //   bwd_dkdv_main   over transpose columns (column bins by out-degree):
 //                   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
@@ -27,34 +31,26 @@ namespace ga {
 namespace {
 
 template <typename T, int G, int LH, int U>
-struct Bwd {
-  using L16 = Lane16<T>;
-  using raw_t = typename L16::raw_t;
-  static constexpr int VEC = L16::VEC;
-  static constexpr int NG = kWave / G;
-  static constexpr int H = G / LH;
-  static constexpr int F = G * VEC;
-  static constexpr int kDqStride = 2 * F + (H + 3) / 4 * 4;
-
-  __device__ __forceinline__ static const raw_t* R(const void* p) {
-    return static_cast<const raw_t*>(p);
-  }
-
-  // Sum a per-lane vector over the NGS groups of a segment (butterfly, fixed order).
-  template <int NGS>
-  __device__ __forceinline__ static void group_sum(float* x) {
-#pragma unroll
-    for (int off = G; off < NGS * G; off <<= 1)
-#pragma unroll
-      for (int c = 0; c < VEC; ++c) x[c] += __shfl_xor(x[c], off);
-  }
+struct Bwd : RowIO<T, G, LH> {
+  using IO = RowIO<T, G, LH>;
+  using typename IO::L16;
+  using typename IO::raw_t;
+  using IO::F;
+  using IO::H;
+  using IO::NG;
+  using IO::R;
+  using IO::VEC;
+  using IO::store;
+  using typename IO::acc_t;
+  static constexpr int kDqStride = 2 * F + (2 * H + 3) / 4 * 4;
 
   // ---- dQ over CSR rows ------------------------------------------------------------
-  // Accumulates A += P dp k, B += P k and D += P dp over edges [e0, e1).
+  // Accumulates A += P dp k, B += P k, D += P dp and L += P over edges [e0, e1).
   template <int NGS>
   __device__ __forceinline__ static void run_dq(const BwdArgs& a, int e0, int e1, int seg0,
                                                 int gs, int r, const raw_t& qr, const raw_t& dor,
-                                                float lse2, float* A, float* Bk, float& D) {
+                                                float lse2, float* A, float* Bk, float& D,
+                                                float& Lp) {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
     const raw_t* __restrict__ Kr = R(a.k);
@@ -87,6 +83,7 @@ struct Bwd {
           const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
           const float pdp = p * dp;
           D += pdp;
+          Lp += p;
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
             A[c] = fmaf(pdp, kf[c], A[c]);
@@ -101,7 +98,7 @@ struct Bwd {
   template <int NGS>
   __device__ __forceinline__ static void run_dkdv(const BwdArgs& a, int e0, int e1, int seg0,
                                                   int gs, int r, int h, const raw_t& kr,
-                                                  const raw_t& vr, float* dk, float* dv) {
+                                                  const raw_t& vr, acc_t* dk, acc_t* dv) {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
     const raw_t* __restrict__ Qr = R(a.q);
@@ -139,38 +136,11 @@ struct Bwd {
           const float ds = p * (dp - ld[u].y);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
-            dk[c] = fmaf(ds, qf[c], dk[c]);
-            dv[c] = fmaf(p, df[c], dv[c]);
+            dk[c] = fma(static_cast<acc_t>(ds), static_cast<acc_t>(qf[c]), dk[c]);
+            dv[c] = fma(static_cast<acc_t>(p), static_cast<acc_t>(df[c]), dv[c]);
           }
         }
       }
-    }
-  }
-
-  __device__ __forceinline__ static void store(void* base, int row, int r, const float* x,
-                                               float mul) {
-    float o[VEC];
-#pragma unroll
-    for (int c = 0; c < VEC; ++c) o[c] = x[c] * mul;
-    st_stream(static_cast<raw_t*>(base) + static_cast<size_t>(row) * G + r, L16::pack(o));
-  }
-
-  __device__ __forceinline__ static void store_f32(float* base, int r, const float* x) {
-    f32x4* p = reinterpret_cast<f32x4*>(base + r * VEC);
-#pragma unroll
-    for (int c = 0; c < VEC / 4; ++c)
-      st_stream(p + c, f32x4{x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]});
-  }
-
-  __device__ __forceinline__ static void add_f32(const float* base, int r, float* x) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(base + r * VEC);
-#pragma unroll
-    for (int c = 0; c < VEC / 4; ++c) {
-      const f32x4 y = ld_stream(p + c);
-      x[4 * c] += y.x;
-      x[4 * c + 1] += y.y;
-      x[4 * c + 2] += y.z;
-      x[4 * c + 3] += y.w;
     }
   }
 
@@ -183,20 +153,22 @@ struct Bwd {
     lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
   }
 
-  // dq = scale (A - D B), written in the feature dtype.
-  __device__ __forceinline__ static void store_dq(const BwdArgs& a, int row, int r,
-                                                  const float* A, const float* Bk, float D) {
+  // Row-pass epilogue: dq = scale (A - D^ B) / L in the feature dtype, and the record
+  // (lse2 + log2 L, D^) with D^ = D / L (one lane per head writes it).
+  __device__ __forceinline__ static void finish_row(const BwdArgs& a, int row, int r, int h,
+                                                    float lse2, const float* A, const float* Bk,
+                                                    float D, float Lp) {
+    const float inv = Lp > 0.f ? 1.f / Lp : 0.f;
+    const float Dn = D * inv;
     float x[VEC];
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) x[c] = fmaf(-D, Bk[c], A[c]);
-    store(a.dq, row, r, x, a.scale);
+    for (int c = 0; c < VEC; ++c) x[c] = fmaf(-Dn, Bk[c], A[c]);
+    store(a.dq, row, r, x, a.scale * inv);
+    if (r % LH == 0)
+      st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h,
+                f32x2{Lp > 0.f ? lse2 + __log2f(Lp) : lse2, Dn});
   }
 
-  template <int NGS>
-  __device__ __forceinline__ static void group_sum1(float& x) {
-#pragma unroll
-    for (int off = G; off < NGS * G; off <<= 1) x += __shfl_xor(x, off);
-  }
 };
 
 // dQ pass. Hub-row chunk partial layout in ws_dq: [chunk][A: F | B: F | D: H, padded to 4]
@@ -210,10 +182,9 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.rows;
   typename K::raw_t qr, dor;
-  float A[VEC], Bk[VEC], lse2, D = 0.f;
+  float A[VEC], Bk[VEC], lse2, D = 0.f, Lp = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
-  f32x2* LD = reinterpret_cast<f32x2*>(a.ws_ld);
   if (item < B.n_chunks + B.n_medium) {
     int row, e0, e1;
     const bool chunk = item < B.n_chunks;
@@ -227,19 +198,22 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
       e1 = a.indptr[row + 1];
     }
     K::row_prologue(a, row, r, h, qr, dor, lse2);
-    K::template run_dq<NG>(a, e0, e1, 0, g, r, qr, dor, lse2, A, Bk, D);
+    K::template run_dq<NG>(a, e0, e1, 0, g, r, qr, dor, lse2, A, Bk, D, Lp);
     K::template group_sum<NG>(A);
     K::template group_sum<NG>(Bk);
     K::template group_sum1<NG>(D);
+    K::template group_sum1<NG>(Lp);
     if (g != 0) return;
     if (chunk) {
       float* p = a.ws_dq + static_cast<size_t>(item) * K::kDqStride;
       K::store_f32(p, r, A);
       K::store_f32(p + F, r, Bk);
-      if (r % LH == 0) st_stream(p + 2 * F + h, D);
+      if (r % LH == 0) {
+        st_stream(p + 2 * F + h, D);
+        st_stream(p + 2 * F + H + h, Lp);
+      }
     } else {
-      if (r % LH == 0) st_stream(LD + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
-      K::store_dq(a, row, r, A, Bk, D);
+      K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
     }
     return;
   }
@@ -248,9 +222,8 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
   K::row_prologue(a, row, r, h, qr, dor, lse2);
-  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qr, dor, lse2, A, Bk, D);
-  if (r % LH == 0) st_stream(LD + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
-  K::store_dq(a, row, r, A, Bk, D);
+  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qr, dor, lse2, A, Bk, D, Lp);
+  K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
 }
 
 // One wavefront per hub row: lane group g sums chunks c0+g, c0+g+NG, ... in ascending
@@ -265,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
   if (hub >= a.rows.n_hub) return;
   const int row = a.rows.hub[hub];
   const int c0 = a.rows.hub_chunk_ptr[hub], c1 = a.rows.hub_chunk_ptr[hub + 1];
-  float A[VEC], Bk[VEC], D = 0.f;
+  float A[VEC], Bk[VEC], D = 0.f, Lp = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
 #pragma unroll 4
@@ -274,16 +247,15 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
     K::add_f32(p, r, A);
     K::add_f32(p + F, r, Bk);
     D += ld_stream(p + 2 * F + h);
+    Lp += ld_stream(p + 2 * F + H + h);
   }
   K::template group_sum<NG>(A);
   K::template group_sum<NG>(Bk);
   K::template group_sum1<NG>(D);
+  K::template group_sum1<NG>(Lp);
   if (g != 0) return;
-  if (r % LH == 0) {
-    const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
-    st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h, f32x2{lse2, D});
-  }
-  K::store_dq(a, row, r, A, Bk, D);
+  const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
+  K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
 }
 
 template <typename T, int G, int LH, int U>
@@ -295,9 +267,9 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) 
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.cols;
   typename K::raw_t kr, vr;
-  float dk[VEC], dv[VEC];
+  typename K::acc_t dk[VEC], dv[VEC];
 #pragma unroll
-  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
+  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0;
   if (item < B.n_chunks + B.n_medium) {
     int col, e0, e1;
     const bool chunk = item < B.n_chunks;
@@ -349,9 +321,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_merge(BwdArgs a) {
   if (hub >= a.cols.n_hub) return;
   const int col = a.cols.hub[hub];
   const int c0 = a.cols.hub_chunk_ptr[hub], c1 = a.cols.hub_chunk_ptr[hub + 1];
-  float dk[VEC], dv[VEC];
+  typename K::acc_t dk[VEC], dv[VEC];
 #pragma unroll
-  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0.f;
+  for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0;
 #pragma unroll 4
   for (int c = c0 + g; c < c1; c += NG) {
     const float* p = a.ws_dkv + static_cast<size_t>(c) * 2 * F;

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ga {
 
 constexpr int kWave = 64;
@@ -144,6 +146,70 @@ __device__ __forceinline__ float head_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row-slice I/O shared by the backward kernels: a lane owns VEC elements of a feature row
+// (G lanes per row, LH lanes per head, NG lane groups per wavefront).
+template <typename T, int G, int LH>
+struct RowIO {
+  using L16 = Lane16<T>;
+  using raw_t = typename L16::raw_t;
+  static constexpr int VEC = L16::VEC;
+  static constexpr int NG = kWave / G;
+  static constexpr int H = G / LH;
+  static constexpr int F = G * VEC;
+  // Accumulator of the column-pass sums (dK, dV, dt). A source column's weights are not
+  // normalised and its sum can cancel heavily (thousands of terms for a hub column), so
+  // fp32 features accumulate in fp64 to keep fp32-level accuracy in the result; bf16
+  // features keep fp32 accumulation.
+  using acc_t = std::conditional_t<std::is_same_v<T, float>, double, float>;
+
+  __device__ __forceinline__ static const raw_t* R(const void* p) {
+    return static_cast<const raw_t*>(p);
+  }
+  // x * mul, converted to T, into row `row` of a [N, H*d] array (streamed store).
+  template <typename X>
+  __device__ __forceinline__ static void store(void* base, int row, int r, const X* x,
+                                               float mul) {
+    float o[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) o[c] = static_cast<float>(x[c] * static_cast<X>(mul));
+    st_stream(static_cast<raw_t*>(base) + static_cast<size_t>(row) * G + r, L16::pack(o));
+  }
+  // fp32 row-slice store / accumulate (chunk partials are fp32; X is the accumulator).
+  template <typename X>
+  __device__ __forceinline__ static void store_f32(float* base, int r, const X* x) {
+    f32x4* p = reinterpret_cast<f32x4*>(base + r * VEC);
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c)
+      st_stream(p + c, f32x4{static_cast<float>(x[4 * c]), static_cast<float>(x[4 * c + 1]),
+                             static_cast<float>(x[4 * c + 2]), static_cast<float>(x[4 * c + 3])});
+  }
+  template <typename X>
+  __device__ __forceinline__ static void add_f32(const float* base, int r, X* x) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base + r * VEC);
+#pragma unroll
+    for (int c = 0; c < VEC / 4; ++c) {
+      const f32x4 y = ld_stream(p + c);
+      x[4 * c] += y.x;
+      x[4 * c + 1] += y.y;
+      x[4 * c + 2] += y.z;
+      x[4 * c + 3] += y.w;
+    }
+  }
+  // Sums over the NGS lane groups of a segment (butterfly over lane distance G, fixed order).
+  template <int NGS, typename X>
+  __device__ __forceinline__ static void group_sum(X* x) {
+#pragma unroll
+    for (int off = G; off < NGS * G; off <<= 1)
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) x[c] += __shfl_xor(x[c], off);
+  }
+  template <int NGS, typename X>
+  __device__ __forceinline__ static void group_sum1(X& x) {
+#pragma unroll
+    for (int off = G; off < NGS * G; off <<= 1) x += __shfl_xor(x, off);
+  }
+};
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -102,12 +102,13 @@ struct BwdArgs {
   float* ws_dkv;   // [n_col_chunks][2][H*d]
   float scale;
   float sc2;       // scale * log2(e)
+  float neg_slope; // LeakyReLU slope (GAT score only)
 };
 
-// fp32 floats per hub-row chunk partial of the dQ pass: A [H*d], B [H*d], D [H] padded
-// to a multiple of 4.
+// fp32 floats per hub-row chunk partial of the row pass: A [H*d], B [H*d], D [H], L [H]
+// (D and L padded together to a multiple of 4).
 inline int64_t dq_partial_floats(int64_t heads, int64_t dim) {
-  return 2 * heads * dim + (heads + 3) / 4 * 4;
+  return 2 * heads * dim + (2 * heads + 3) / 4 * 4;
 }
 
 // Returns false when the geometry/dtype/score combination has no compiled kernels.
@@ -122,6 +123,9 @@ int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, in
                void* stream, TimerHook hook);
 int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t n, void* stream,
                TimerHook hook);
+// GAT-style score: q/k/dq/dk carry s/t/ds/dt (fp32 [N, H]).
+int launch_bwd_gat(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
+                   TimerHook hook);
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
 int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
                         void* sink, void* stream, TimerHook hook);

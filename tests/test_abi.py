@@ -121,13 +121,21 @@ def _bwd(p, score=capi.GA_SCORE_DOT, dtype=capi.GA_BF16, H=8, d=32, ptrs=None, w
          wsb=1 << 30):
     ptrs = ptrs or [FAKE] * 8
     return capi.raw_status("graph_attn_bwd", p.handle, score, dtype, H, d, ctypes.c_float(0.1),
-                           *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb, None)
+                           ctypes.c_float(0.2), *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb,
+                           None)
 
 
 def test_bwd_argument_checks_before_any_hip_call():
     p, ip, ix = _hub_plan()
-    assert _bwd(p, score=capi.GA_SCORE_GAT) == capi.GA_ERR_UNSUPPORTED
+    assert _bwd(p, score=5) == capi.GA_ERR_INVALID_ARG
     assert _bwd(p, d=8, dtype=capi.GA_BF16) == capi.GA_ERR_UNSUPPORTED
+    # GAT: s, t, ds, dt only need 4-byte alignment; v, dout, dv 16
+    assert _bwd(p, score=capi.GA_SCORE_GAT, ptrs=[FAKE + 4, FAKE + 8, FAKE, FAKE, FAKE,
+                                                  FAKE + 4, FAKE + 12, FAKE]) == capi.GA_ERR_NOT_READY
+    assert _bwd(p, score=capi.GA_SCORE_GAT, ptrs=[FAKE, FAKE, FAKE + 4, FAKE, FAKE,
+                                                  FAKE, FAKE, FAKE]) == capi.GA_ERR_INVALID_ARG
+    assert _bwd(p, score=capi.GA_SCORE_DOT, ptrs=[FAKE + 4, FAKE, FAKE, FAKE, FAKE,
+                                                  FAKE, FAKE, FAKE]) == capi.GA_ERR_INVALID_ARG
     for i in range(8):
         ptrs = [FAKE] * 8
         ptrs[i] = 0
@@ -151,9 +159,11 @@ def test_workspace_sizes_follow_the_declared_formulas():
     assert p.fwd_workspace_bytes(H, d) == al(info["n_row_chunks"] * H * 8) + \
         al(info["n_row_chunks"] * H * d * 4)
     assert p.bwd_workspace_bytes(H, d) == al(64 * H * 8) + \
-        al(info["n_row_chunks"] * (2 * H * d + 4) * 4) + al(info["n_col_chunks"] * 2 * H * d * 4)
+        al(info["n_row_chunks"] * (2 * H * d + 8) * 4) + al(info["n_col_chunks"] * 2 * H * d * 4)
     assert p.bwd_workspace_bytes(8, 32) == al(64 * 8 * 8) + \
-        al(info["n_row_chunks"] * (2 * 256 + 8) * 4) + al(info["n_col_chunks"] * 2 * 256 * 4)
+        al(info["n_row_chunks"] * (2 * 256 + 16) * 4) + al(info["n_col_chunks"] * 2 * 256 * 4)
+    assert p.bwd_workspace_bytes(1, 64) == al(64 * 1 * 8) + \
+        al(info["n_row_chunks"] * (2 * 64 + 4) * 4) + al(info["n_col_chunks"] * 2 * 64 * 4)
     # no hub rows -> no forward workspace
     q = Plan(*gg.csr_from_edges(4, [0, 1], [1, 2]))
     assert q.fwd_workspace_bytes(8, 32) == 0

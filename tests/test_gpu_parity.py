@@ -369,3 +369,95 @@ def test_gather_probe_runs_on_the_plan_graph():
     gather_probe(plan, dev(k), dev(v), sink=sink)
     torch.cuda.synchronize()
     assert int(sink.sum()) == 0   # the probe writes its sink only on a 64-bit XOR collision
+
+
+# ------------------------------------------------------------------ GAT-style backward
+
+def gat_bwd_case(tag, ip, ix, s, t, v, dout, dtype, scale=1.0, slope=0.2, rows=None, cols=None,
+                 **plan_kw):
+    say(tag, "N", ip.size - 1, "E", ix.size, "H", v.shape[1], "d", v.shape[2], dtype, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    ts, tt, tv, td = dev(s), dev(t), dev(v), dev(dout)
+    out, lse = fwd(plan, ts, tt, tv, score="gat", scale=scale, neg_slope=slope)
+    ds, dt, dv = bwd(plan, ts, tt, tv, td, lse, score="gat", scale=scale, neg_slope=slope)
+    torch.cuda.synchronize()
+    if rows is None:
+        rs, rt, rv = A.backward_gat(ip, ix, s, t, v, dout, scale, f32(slope))
+        errs = [check(f"{tag} ds", host64(ds), rs, dtype), check(f"{tag} dt", host64(dt), rt, dtype),
+                check(f"{tag} dv", host64(dv), rv, dtype)]
+    else:
+        rs = A.grad_s_rows(ip, ix, s, t, v, dout, rows, scale, f32(slope))
+        rt, rv = A.grad_tv_cols(ip, ix, s, t, v, dout, cols, scale, f32(slope))
+        r_t, c_t = torch.from_numpy(np.asarray(rows)).cuda(), torch.from_numpy(np.asarray(cols)).cuda()
+        errs = [check(f"{tag} ds", host64(ds[r_t]), rs, dtype),
+                check(f"{tag} dt", host64(dt[c_t]), rt, dtype),
+                check(f"{tag} dv", host64(dv[c_t]), rv, dtype)]
+    say(tag, "max abs / norm-rel errors", errs)
+    return plan, (ds, dt, dv)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gat_backward_every_element(dtype):
+    rng = np.random.default_rng(41)
+    n, H, d = 3000, 4, 64
+    src = np.r_[rng.integers(0, n, 40_000), np.full(3000, 11)]      # column hub 11
+    dst = np.r_[rng.integers(0, n, 40_000), rng.integers(0, n, 3000)]
+    dst[:4000] = 7                                                  # row hub 7
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    s = rng.standard_normal((n, H)).astype(np.float32)
+    t = rng.standard_normal((n, H)).astype(np.float32)
+    v, do = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    if dtype == "bf16":
+        v, do = gg.f32_to_bf16_bits(v), gg.f32_to_bf16_bits(do)
+    plan, _ = gat_bwd_case(f"gat bwd {dtype}", ip, ix, s, t, v, do, dtype, scale=1.3, slope=0.1,
+                           light_max_deg=8, hub_min_deg_exclusive=64, hub_chunk=100)
+    info = plan.info()
+    assert info["n_row_chunks"] > info["n_row_hub"] > 0
+    assert info["n_col_chunks"] > info["n_col_hub"] > 0
+
+
+@pytest.mark.parametrize("G,LH,dtype", [(8, 8, "f32"), (16, 2, "bf16"), (64, 64, "bf16"),
+                                        (4, 4, "f32"), (32, 8, "f32")])
+def test_gat_backward_geometries(G, LH, dtype):
+    eb = 4 if dtype == "f32" else 2
+    H, d = G // LH, LH * 16 // eb
+    rng = np.random.default_rng(G * 7 + LH)
+    n = 400
+    ip, ix = gg.random_multigraph(n, 4000, rng, hub_rows=(3,), hub_deg=500)
+    s, t = (rng.standard_normal((n, H)).astype(np.float32) for _ in range(2))
+    v, do = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    if dtype == "bf16":
+        v, do = gg.f32_to_bf16_bits(v), gg.f32_to_bf16_bits(do)
+    gat_bwd_case(f"gat bwd geometry G{G} LH{LH} {dtype}", ip, ix, s, t, v, do, dtype,
+                 light_max_deg=4, hub_min_deg_exclusive=30, hub_chunk=16)
+
+
+def test_gat_backward_deterministic():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    s, t, v = gg.make_features(w, n=20_000)
+    do = np.random.default_rng(3).standard_normal(v.shape).astype(np.float32)
+    say("gat bwd determinism")
+    plan = Plan(ip, ix, light_max_deg=8, hub_min_deg_exclusive=128, hub_chunk=64).upload()
+    ts, tt, tv, td = dev(s), dev(t), dev(v), dev(do)
+    res = []
+    for _ in range(2):
+        out, lse = fwd(plan, ts, tt, tv, score="gat")
+        res.append(bwd(plan, ts, tt, tv, td, lse, score="gat"))
+    torch.cuda.synchronize()
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_full_chunglu100k_gat_backward_sampled():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w)
+    s, t, v = gg.make_features(w)
+    rng = np.random.default_rng(8)
+    do = rng.standard_normal(v.shape).astype(np.float32)
+    rows = _sample_rows(ip, rng, k=500)
+    odeg = np.bincount(ix, minlength=w.n)
+    cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3], rng.choice(w.n, 200, replace=False)])
+    gat_bwd_case("full chunglu100k gat bwd (sampled)", ip, ix, s, t, v, do, "f32", rows=rows,
+                 cols=cols)

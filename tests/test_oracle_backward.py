@@ -153,3 +153,82 @@ def test_gat_scale_is_a_temperature():
     b, lb = A.forward(ip, ix, 2.5 * s, 2.5 * t, v, "gat", 1.0, 0.2)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(la, lb, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------------------ GAT-style backward
+
+def _gat_inputs(seed, n, m, H=2, d=3):
+    rng, ip, ix = _graph(seed, n, m)
+    s, t = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    v, do = rng.standard_normal((n, H, d)), rng.standard_normal((n, H, d))
+    return ip, ix, s, t, v, do
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gat_backward_matches_central_finite_differences(seed):
+    ip, ix, s, t, v, do = _gat_inputs(seed, 9, 30)
+    scale, a = 1.3, 0.2
+    ds, dt, dv = A.backward_gat(ip, ix, s, t, v, do, scale, a)
+
+    def loss(s_, t_, v_):
+        out, _ = A.forward(ip, ix, s_, t_, v_, "gat", scale, a)
+        return float((out * do).sum())
+
+    h = 1e-6
+    for name, x, g in (("s", s, ds), ("t", t, dt), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            ap = {"s": s, "t": t, "v": v}; ap[name] = xp
+            am = {"s": s, "t": t, "v": v}; am[name] = xm
+            num[idx] = (loss(ap["s"], ap["t"], ap["v"]) - loss(am["s"], am["t"], am["v"])) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_gat_backward_matches_torch_autograd_dense():
+    ip, ix, s, t, v, do = _gat_inputs(5, 30, 400, H=3, d=4)
+    n, H = 30, 3
+    dst = np.repeat(np.arange(n), np.diff(ip))
+    ip, ix = gg.csr_from_edges(n, ix[dst != 6], dst[dst != 6])          # row 6 empty
+    ds, dt, dv = A.backward_gat(ip, ix, s, t, v, do, 0.9, 0.1)
+    c = np.zeros((n, n))
+    np.add.at(c, (np.repeat(np.arange(n), np.diff(ip)), ix), 1.0)
+    add = torch.from_numpy(np.where(c > 0, np.log(np.maximum(c, 1)), -np.inf))
+    ts = torch.from_numpy(s.T.copy()).requires_grad_(True)           # [H, n]
+    tt = torch.from_numpy(t.T.copy()).requires_grad_(True)
+    tv = torch.from_numpy(v).permute(1, 0, 2).contiguous().requires_grad_(True)
+    x = ts[:, :, None] + tt[:, None, :]
+    S = 0.9 * torch.nn.functional.leaky_relu(x, 0.1) + add
+    has = torch.from_numpy(c.sum(1) > 0)
+    P = torch.softmax(S[:, has], dim=-1)
+    out = torch.zeros(H, n, 4, dtype=torch.float64)
+    out[:, has] = torch.matmul(P, tv)
+    (out * torch.from_numpy(do).permute(1, 0, 2)).sum().backward()
+    np.testing.assert_allclose(ds, ts.grad.T.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dt, tt.grad.T.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_gat_backward_linear_regime_closed_forms():
+    """With every s_i + t_j >= 0 the score is scale (s_i + t_j): each row's softmax ignores
+    s_i (ds = 0), and shifting every t by a constant shifts rows uniformly (sum dt = 0)."""
+    ip, ix, s, t, v, do = _gat_inputs(7, 50, 500, H=3, d=4)
+    s = s + 50.0
+    ds, dt, dv = A.backward_gat(ip, ix, s, t, v, do, 1.0, 0.2)
+    np.testing.assert_allclose(ds, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dt.sum(axis=0), 0.0, atol=1e-12)
+    nonempty = np.diff(ip) > 0
+    np.testing.assert_allclose(dv.sum(axis=0), do[nonempty].sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_gat_backward_sampled_forms_agree():
+    ip, ix, s, t, v, do = _gat_inputs(8, 70, 800, H=2, d=5)
+    ds, dt, dv = A.backward_gat(ip, ix, s, t, v, do, 1.0, 0.2)
+    rng = np.random.default_rng(0)
+    sel = rng.choice(70, 15, replace=False)
+    np.testing.assert_allclose(A.grad_s_rows(ip, ix, s, t, v, do, sel, 1.0, 0.2), ds[sel],
+                               rtol=1e-12, atol=1e-13)
+    gt, gv = A.grad_tv_cols(ip, ix, s, t, v, do, sel, 1.0, 0.2)
+    np.testing.assert_allclose(gt, dt[sel], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(gv, dv[sel], rtol=1e-12, atol=1e-13)
