@@ -122,6 +122,22 @@ def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     }
 
 
+def relabel_by_out_degree(ip, ix, feats, dout):
+    """Node order ablation: new id = rank by out-degree (descending, ties by old id). The
+    graph is the same up to relabelling; features move with their nodes."""
+    n = ip.size - 1
+    odeg = np.bincount(ix, minlength=n)
+    old_of_new = np.lexsort((np.arange(n), -odeg))
+    new_of_old = np.empty(n, np.int64)
+    new_of_old[old_of_new] = np.arange(n)
+    dst = new_of_old[np.repeat(np.arange(n), np.diff(ip))]
+    src = new_of_old[ix]
+    ip2, ix2 = gg.csr_from_edges(n, src, dst)
+    feats = tuple(np.ascontiguousarray(f[old_of_new]) for f in feats)
+    dout = None if dout is None else np.ascontiguousarray(dout[old_of_new])
+    return ip2, ix2, feats, dout
+
+
 # ---------------------------------------------------------------- GPU
 
 def to_dev(x):
@@ -166,6 +182,9 @@ def main():
     ap.add_argument("--light", type=int, default=None)
     ap.add_argument("--hub", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--order", choices=["as-generated", "out-degree"], default="as-generated",
+                    help="node order ablation: relabel nodes by descending out-degree (hot "
+                         "source rows contiguous) before the run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -177,6 +196,8 @@ def main():
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)
     dout = gg.make_dout(w) if w.backward else None
+    if args.order == "out-degree":
+        ip, ix, feats, dout = relabel_by_out_degree(ip, ix, feats, dout)
     gen_s = time.perf_counter() - t0
     N, E, H, d = ip.size - 1, ix.size, w.heads, w.dim
     b = 2 if w.dtype == "bf16" else 4
@@ -292,6 +313,7 @@ def main():
             "workload": w.name,
             "graph": w.graph, "nodes": N, "edges": E, "heads": H, "dim": d,
             "score": w.score, "step": "forward+backward" if w.backward else "forward",
+            "node_order": args.order,
             "plan": {k: info[k] for k in ("light_max_deg", "hub_min_deg_exclusive", "hub_chunk",
                                           "n_row_light", "n_row_medium", "n_row_hub",
                                           "n_row_chunks", "n_col_hub", "n_col_chunks",
