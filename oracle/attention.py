@@ -26,6 +26,14 @@ branch the forward takes at 0), same dS:
     ds_i += scale dS_ij LeakyReLU'(x_ij);  dt_j += scale dS_ij LeakyReLU'(x_ij);
     dv_j += alpha_ij dOut_i
 
+GATv2 score (Brody et al., the GATv2 the pages name; destination projection xd, source
+projection xs, which is also the message, attention vector a [H, d]):
+    z_ij = xd_i + xs_j,  e_ij = scale * sum_c a[h,c] LeakyReLU(z_ij[h,c]),
+    out_i = sum_j softmax_j(e)_ij xs_j
+Its backward, with g = LeakyReLU'(z) elementwise and dS as above (dp_ij = <dOut_i, xs_j>):
+    dxd_i += scale dS_ij (a * g_ij);  dxs_j += scale dS_ij (a * g_ij) + alpha_ij dOut_i;
+    da    += scale dS_ij LeakyReLU(z_ij)   (summed over every edge)
+
 Conventions: CSR row = destination; parallel edges count with multiplicity; a row with
 no neighbours gives out = 0 and lse = -inf and no gradient.  All arithmetic is fp64;
 bf16 inputs arrive as uint16 bit patterns and are widened exactly.
@@ -37,7 +45,8 @@ import numpy as np
 __all__ = [
     "widen", "leaky_relu", "row_scores", "row_softmax", "forward_rows", "forward",
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
-    "backward_gat", "grad_s_rows", "grad_tv_cols",
+    "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
+    "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
 ]
 
 
@@ -301,3 +310,99 @@ def grad_tv_cols(indptr, indices, s, t, v, dout, cols, scale=1.0, neg_slope=0.2)
             dt[c] += sc * dS[kk] * g[kk]
             dv[c] += alpha[kk][:, None] * doi
     return dt, dv
+
+
+# ----------------------------------------------------------------------------- GATv2
+
+def gatv2_row_scores(i, indptr, indices, xd, xs, attn, scale=1.0, neg_slope=0.2):
+    """e [deg, H] of row i: scale * sum_c a[h,c] LeakyReLU(xd[i,h,c] + xs[j,h,c])."""
+    J = _neighbours(indptr, indices, i)
+    z = widen(xd[i])[None] + widen(xs[J])                     # [deg, H, d]
+    return float(scale) * np.einsum("hc,khc->kh", widen(attn), leaky_relu(z, float(neg_slope)))
+
+
+def forward_gatv2_rows(indptr, indices, xd, xs, attn, rows, scale=1.0, neg_slope=0.2):
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = xs.shape[1], xs.shape[2]
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    for r, i in enumerate(rows):
+        J = _neighbours(indptr, indices, i)
+        if J.size == 0:
+            continue
+        alpha, lse[r] = row_softmax(gatv2_row_scores(i, indptr, indices, xd, xs, attn, scale,
+                                                      neg_slope))
+        out[r] = np.einsum("kh,khc->hc", alpha, widen(xs[J]))
+    return out, lse
+
+
+def forward_gatv2(indptr, indices, xd, xs, attn, scale=1.0, neg_slope=0.2):
+    return forward_gatv2_rows(indptr, indices, xd, xs, attn, np.arange(indptr.size - 1), scale,
+                              neg_slope)
+
+
+def _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, scale, neg_slope):
+    """Per-row pieces: (J, alpha [deg,H], dS [deg,H], g [deg,H,d], lrelu(z) [deg,H,d])."""
+    J = _neighbours(indptr, indices, i)
+    z = widen(xd[i])[None] + widen(xs[J])
+    lz = leaky_relu(z, float(neg_slope))
+    e = float(scale) * np.einsum("hc,khc->kh", widen(attn), lz)
+    alpha, _ = row_softmax(e)
+    dp = np.einsum("hc,khc->kh", widen(dout[i]), widen(xs[J]))
+    D = (alpha * dp).sum(axis=0)
+    return J, alpha, alpha * (dp - D[None, :]), leaky_relu_grad(z, float(neg_slope)), lz
+
+
+def backward_gatv2(indptr, indices, xd, xs, attn, dout, scale=1.0, neg_slope=0.2):
+    """dxd, dxs [N,H,d] and dattn [H,d] (fp64), by rows with a sequential scatter."""
+    sc = float(scale)
+    a = widen(attn)
+    n = indptr.size - 1
+    dxd = np.zeros(xd.shape)
+    dxs = np.zeros(xs.shape)
+    da = np.zeros(attn.shape)
+    for i in range(n):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        J, alpha, dS, g, lz = _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, sc,
+                                                  neg_slope)
+        w = sc * dS[:, :, None] * g * a[None]                   # [deg, H, d]
+        dxd[i] = w.sum(axis=0)
+        np.add.at(dxs, J, w + alpha[:, :, None] * widen(dout[i])[None])
+        da += sc * np.einsum("kh,khc->hc", dS, lz)
+    return dxd, dxs, da
+
+
+def grad_gatv2_rows(indptr, indices, xd, xs, attn, dout, rows, scale=1.0, neg_slope=0.2):
+    """dxd [R,H,d] for the listed rows and those rows' contribution to dattn."""
+    sc = float(scale)
+    a = widen(attn)
+    rows = np.asarray(rows, dtype=np.int64)
+    dxd = np.zeros((rows.size,) + tuple(xd.shape[1:]))
+    da = np.zeros(attn.shape)
+    for r, i in enumerate(rows):
+        if indptr[i + 1] == indptr[i]:
+            continue
+        _, _, dS, g, lz = _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, sc,
+                                              neg_slope)
+        dxd[r] = (sc * dS[:, :, None] * g * a[None]).sum(axis=0)
+        da += sc * np.einsum("kh,khc->hc", dS, lz)
+    return dxd, da
+
+
+def grad_gatv2_cols(indptr, indices, xd, xs, attn, dout, cols, scale=1.0, neg_slope=0.2):
+    """dxs [C,H,d] for the listed source columns only."""
+    sc = float(scale)
+    a = widen(attn)
+    cols = np.asarray(cols, dtype=np.int64)
+    slot = {int(j): c for c, j in enumerate(cols)}
+    dxs = np.zeros((cols.size,) + tuple(xs.shape[1:]))
+    pos = np.flatnonzero(np.isin(indices, cols))
+    rows = np.searchsorted(indptr, pos, side="right") - 1
+    for i in np.unique(rows):
+        J, alpha, dS, g, _ = _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, sc,
+                                                 neg_slope)
+        doi = widen(dout[i])
+        for kk in np.flatnonzero(np.isin(J, cols)):
+            dxs[slot[int(J[kk])]] += sc * dS[kk][:, None] * g[kk] * a + alpha[kk][:, None] * doi
+    return dxs
