@@ -159,6 +159,18 @@ ga_status graph_attn_fwd(const ga_plan* plan, ga_score score, ga_dtype dtype, in
                          const void* k_or_t, const void* v, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* GATv2 forward (the GATv2 layer the Methodology names; the textbook score, not printed on
+ * the pages): per head h,
+ *     e_ij = scale * sum_c attn[h,c] * LeakyReLU_{neg_slope}(xd[i,h,c] + xs[j,h,c])
+ *     out[i,h,:] = sum_j softmax_j(e_ij) xs[j,h,:],   lse[i,h] = ln sum_j exp(e_ij)
+ * xd (destination projection) and xs (source projection, also the message) are [N,H,d] of
+ * `dtype`; attn is fp32 [H,d] (16-byte aligned); out, lse and the workspace as for
+ * graph_attn_fwd (same workspace size). Each edge gathers one source row. */
+ga_status graph_attn_fwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t heads, int32_t dim,
+                               float scale, float neg_slope, const void* xd, const void* xs,
+                               const float* attn, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Workspace the backward needs (either score): per-node (lse*log2 e, D) records N*H*8
  * bytes, fp32 row-chunk partials n_row_chunks*(2*H*d + 4*ceil(2H/4))*4 bytes and fp32
  * column-chunk partials n_col_chunks*2*H*d*4 bytes, each section 256-byte aligned. */

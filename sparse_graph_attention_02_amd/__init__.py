@@ -26,7 +26,8 @@ import numpy as np
 from . import capi
 from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,  # noqa: F401
                    graph_attn_bwd, graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
-                   graph_attn_fwd, graph_attn_fwd_workspace_bytes, graph_attn_gather_probe,
+                   graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_workspace_bytes,
+                   graph_attn_gather_probe,
                    graph_attn_plan_array,
                    graph_attn_plan_array_count, graph_attn_plan_array_name,
                    graph_attn_plan_create, graph_attn_plan_destroy,
@@ -35,7 +36,7 @@ from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError, 
                    graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
-__all__ = ["Plan", "fwd", "bwd", "graph_attention", "copy_probe", "timers", "default_opts",
+__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "graph_attention", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
 
@@ -196,6 +197,30 @@ def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2
         graph_attn_fwd(plan.handle, sc, _dtype_code(v), H, d, float(scale), float(neg_slope),
                        _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                        wsb, _stream(stream))
+    return out, lse
+
+
+def fwd_gatv2(plan: Plan, xd, xs, attn, *, scale=1.0, neg_slope=0.2, out=None, lse=None,
+              workspace=None, stream=None):
+    """GATv2 forward: e = scale * attn . LeakyReLU(xd_i + xs_j), message xs_j.
+    xd, xs [N,H,d] (fp32 or bf16), attn fp32 [H,d]; returns (out [N,H,d], lse [N,H])."""
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    N, H, d = xs.shape
+    dev = xs.device
+    _need(xd, "xd", (N, H, d), xs.dtype, dev)
+    _need(xs, "xs", (N, H, d), xs.dtype, dev)
+    _need(attn, "attn", (H, d), torch.float32, dev)
+    out = torch.empty_like(xs) if out is None else out
+    lse = torch.empty((N, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", (N, H, d), xs.dtype, dev)
+    _need(lse, "lse", (N, H), torch.float32, dev)
+    ws, wsb = _workspace(plan.fwd_workspace_bytes(H, d), dev, workspace)
+    with torch.cuda.device(dev):
+        graph_attn_fwd_gatv2(plan.handle, _dtype_code(xs), H, d, float(scale), float(neg_slope),
+                             _ptr(xd), _ptr(xs), _ptr(attn), _ptr(out), _ptr(lse), _ptr(ws), wsb,
+                             _stream(stream))
     return out, lse
 
 

@@ -61,6 +61,9 @@ _SIGS = {
     "graph_attn_fwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
+    "graph_attn_fwd_gatv2": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_float, c_float,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
     "graph_attn_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_size_t)]),
     "graph_attn_bwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
                                  c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -132,6 +135,7 @@ graph_attn_plan_array_name = _wrap("graph_attn_plan_array_name")
 graph_attn_plan_destroy = _wrap("graph_attn_plan_destroy")
 graph_attn_fwd_workspace_bytes = _wrap("graph_attn_fwd_workspace_bytes")
 graph_attn_fwd = _wrap("graph_attn_fwd")
+graph_attn_fwd_gatv2 = _wrap("graph_attn_fwd_gatv2")
 graph_attn_bwd_workspace_bytes = _wrap("graph_attn_bwd_workspace_bytes")
 graph_attn_bwd = _wrap("graph_attn_bwd")
 graph_attn_timer_enable = _wrap("graph_attn_timer_enable")

@@ -360,7 +360,49 @@ ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
                    : nullptr;
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
-  const int rc = ga::launch_fwd(dtype, score, g, args, p->n, stream, active_hook());
+  const int rc = ga::launch_fwd(dtype, score == GA_SCORE_DOT ? ga::kModeDot : ga::kModeGat, g,
+                                args, p->n, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, int32_t dim,
+                               float scale, float neg_slope, const void* xd, const void* xs,
+                               const float* attn, void* out, float* lse, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (!ga::fwd_supported(dtype, GA_SCORE_DOT, g)) return GA_ERR_UNSUPPORTED;
+  if ((s = check_ptr(attn, 16)) != GA_OK) return s;
+  if (p->n > 0) {
+    if ((s = check_ptr(xd, 16)) != GA_OK || (s = check_ptr(xs, 16)) != GA_OK ||
+        (s = check_ptr(out, 16)) != GA_OK || (s = check_ptr(lse, 4)) != GA_OK)
+      return s;
+  }
+  const size_t need = fwd_ws_bytes(p, g);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+  ga::FwdArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.bins = p->d_rows;
+  args.a = xd;
+  args.b = xs;
+  args.v = xs;
+  args.attn = attn;
+  args.out = out;
+  args.lse = lse;
+  const size_t nc = p->rows.chunk_row.size();
+  args.ws_ml = static_cast<float*>(ws);
+  args.ws_acc = nc ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align_up(nc * heads * 2 * sizeof(float)))
+                   : nullptr;
+  args.sc2 = scale * 1.4426950408889634f;
+  args.neg_slope = neg_slope;
+  const int rc = ga::launch_fwd(dtype, ga::kModeGatV2, g, args, p->n, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
 

@@ -15,6 +15,10 @@
 // Bins are sorted by degree descending, so the longest items start first. A second
 // launch (fwd_hub_merge) folds each hub row's chunk partials in ascending chunk order.
 //
+// Score modes: dot (q_i . k_j), GAT-style (LeakyReLU(s_i + t_j)) and GATv2
+// (a . LeakyReLU(xd_i + xs_j), where the gathered source row xs_j is also the value, so a
+// GATv2 edge gathers one row instead of two).
+//
 // Per edge a lane group gathers the neighbour's K and V rows with 16-byte loads per lane
 // (coalesced across the group), reduces the per-head dot product with DPP adds, and folds
 // U edges at a time into the running (m, l, acc) state: one rescale per U edges. Scores
@@ -26,8 +30,10 @@
 namespace ga {
 namespace {
 
-template <typename T, int G, int LH, bool GAT, int U>
+template <typename T, int G, int LH, int MODE, int U>
 struct Fwd {
+  static constexpr bool GAT = MODE == kModeGat;
+  static constexpr bool GATV2 = MODE == kModeGatV2;
   using L16 = Lane16<T>;
   using raw_t = typename L16::raw_t;
   static constexpr int VEC = L16::VEC;
@@ -47,10 +53,13 @@ struct Fwd {
     for (int c = 0; c < VEC; ++c) s.acc[c] = 0.f;
   }
 
-  // Row-side operand of the score: the query row slice (dot) or s[i, h] (gat).
+  // Row-side operand of the score: the query row slice (dot), s[i, h] (gat), or the
+  // destination projection xd_i plus the lane's slice of the attention vector (gatv2).
   struct RowOp {
     raw_t q;
     float si;
+    float xd[GATV2 ? VEC : 1];
+    float av[GATV2 ? VEC : 1];
   };
 
   __device__ __forceinline__ static void load_row(const FwdArgs& a, int row, int r, int h,
@@ -59,6 +68,18 @@ struct Fwd {
       q.si = ld_stream(static_cast<const float*>(a.a) + static_cast<size_t>(row) * H + h);
     } else {
       q.q = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * G + r);
+    }
+    if constexpr (GATV2) {
+      L16::unpack(q.q, q.xd);
+      const f32x4* ap = reinterpret_cast<const f32x4*>(a.attn + r * VEC);
+#pragma unroll
+      for (int k = 0; k < VEC / 4; ++k) {
+        const f32x4 x = ap[k];
+        q.av[4 * k] = x.x;
+        q.av[4 * k + 1] = x.y;
+        q.av[4 * k + 2] = x.z;
+        q.av[4 * k + 3] = x.w;
+      }
     }
   }
 
@@ -95,7 +116,10 @@ struct Fwd {
             tv[u] = Tt[static_cast<size_t>(jj[u]) * H + h];
           else
             kr[u] = Kr[static_cast<size_t>(jj[u]) * G + r];
-          vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
+          if constexpr (GATV2)
+            vr[u] = kr[u];  // the message is the gathered source projection
+          else
+            vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
         }
         float s[U];
 #pragma unroll
@@ -104,6 +128,16 @@ struct Fwd {
           if constexpr (GAT) {
             x = q.si + tv[u];
             x = (x >= 0.f ? x : x * a.neg_slope) * a.sc2;
+          } else if constexpr (GATV2) {
+            float xs[VEC];
+            L16::unpack(kr[u], xs);
+            float e = 0.f;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+              const float z = q.xd[c] + xs[c];
+              e = fmaf(q.av[c], z >= 0.f ? z : z * a.neg_slope, e);
+            }
+            x = head_sum<LH>(e) * a.sc2;
           } else {
             x = head_sum<LH>(L16::dot(q.q, kr[u])) * a.sc2;
           }
@@ -177,9 +211,9 @@ struct Fwd {
   }
 };
 
-template <typename T, int G, int LH, bool GAT, int U>
+template <typename T, int G, int LH, int MODE, int U>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a) {
-  using K = Fwd<T, G, LH, GAT, U>;
+  using K = Fwd<T, G, LH, MODE, U>;
   constexpr int NG = K::NG;
   const int lane = threadIdx.x & (kWave - 1);
   const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -223,7 +257,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a) {
 // order, then the NG group states are combined by the fixed butterfly (deterministic).
 template <typename T, int G, int LH>
 __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
-  using K = Fwd<T, G, LH, false, 1>;
+  using K = Fwd<T, G, LH, kModeDot, 1>;
   constexpr int H = K::H, F = K::F, VEC = K::VEC, NG = K::NG;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int lane = threadIdx.x & (kWave - 1);
@@ -258,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   if (g == 0) K::write_row(a, row, r, h, st);
 }
 
-template <typename T, int G, int LH, bool GAT>
+template <typename T, int G, int LH, int MODE>
 int launch(const FwdArgs& a, void* stream, TimerHook hook) {
   constexpr int U = GA_UNROLL_FWD;
   constexpr int NG = kWave / G;
@@ -268,7 +302,7 @@ int launch(const FwdArgs& a, void* stream, TimerHook hook) {
   if (items > 0) {
     const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     if (hook) hook("fwd_main", stream, 1);
-    hipLaunchKernelGGL((fwd_main<T, G, LH, GAT, U>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kBlock), 0, s, a);
     if (hook) hook("fwd_main", stream, 0);
     hipError_t e = hipGetLastError();
@@ -291,10 +325,10 @@ int launch(const FwdArgs& a, void* stream, TimerHook hook) {
   X(32, 4) X(32, 8) X(32, 16) X(32, 32) X(64, 2) X(64, 4) X(64, 8) X(64, 16) X(64, 32) \
   X(64, 64)
 
-template <typename T, bool GAT>
+template <typename T, int MODE>
 int dispatch(const Geometry& g, const FwdArgs& a, void* stream, TimerHook hook) {
 #define GA_CASE(GG, LL) \
-  if (g.G == GG && g.LH == LL) return launch<T, GG, LL, GAT>(a, stream, hook);
+  if (g.G == GG && g.LH == LL) return launch<T, GG, LL, MODE>(a, stream, hook);
   GA_GEOMS(GA_CASE)
 #undef GA_CASE
   return -1;
@@ -315,13 +349,20 @@ bool fwd_supported(ga_dtype dt, ga_score sc, const Geometry& g) {
          geom_ok(g);
 }
 
-int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, int64_t,
+template <typename T>
+int dispatch_mode(int mode, const Geometry& g, const FwdArgs& a, void* stream, TimerHook hook) {
+  switch (mode) {
+    case kModeDot: return dispatch<T, kModeDot>(g, a, stream, hook);
+    case kModeGat: return dispatch<T, kModeGat>(g, a, stream, hook);
+    case kModeGatV2: return dispatch<T, kModeGatV2>(g, a, stream, hook);
+  }
+  return -1;
+}
+
+int launch_fwd(ga_dtype dt, int mode, const Geometry& g, const FwdArgs& a, int64_t,
                void* stream, TimerHook hook) {
-  if (dt == GA_F32)
-    return sc == GA_SCORE_DOT ? dispatch<float, false>(g, a, stream, hook)
-                              : dispatch<float, true>(g, a, stream, hook);
-  return sc == GA_SCORE_DOT ? dispatch<bf16_t, false>(g, a, stream, hook)
-                            : dispatch<bf16_t, true>(g, a, stream, hook);
+  return dt == GA_F32 ? dispatch_mode<float>(mode, g, a, stream, hook)
+                      : dispatch_mode<bf16_t>(mode, g, a, stream, hook);
 }
 
 }  // namespace ga

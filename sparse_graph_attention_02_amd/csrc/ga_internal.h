@@ -74,6 +74,7 @@ struct FwdArgs {
   const void* a;  // q (dot) or s (gat)
   const void* b;  // k (dot) or t (gat)
   const void* v;
+  const float* attn;  // GATv2 attention vector [H*d] (null otherwise)
   void* out;
   float* lse;
   float* ws_ml;   // [n_chunks][H][2]  (m in log2 units, l)
@@ -111,6 +112,10 @@ inline int64_t dq_partial_floats(int64_t heads, int64_t dim) {
   return 2 * heads * dim + (2 * heads + 3) / 4 * 4;
 }
 
+// Forward score modes of the kernels (ga_score values, plus GATv2 which has its own entry
+// point because it takes the attention vector).
+enum FwdMode { kModeDot = 0, kModeGat = 1, kModeGatV2 = 2 };
+
 // Returns false when the geometry/dtype/score combination has no compiled kernels.
 bool fwd_supported(ga_dtype dt, ga_score sc, const Geometry& g);
 bool bwd_supported(ga_dtype dt, const Geometry& g);
@@ -119,7 +124,7 @@ bool bwd_supported(ga_dtype dt, const Geometry& g);
 // and after (begin = 0) each launch with the kernel's name (the library's event timers).
 // Both return hipSuccess or the first launch error (as int to keep HIP headers out).
 typedef void (*TimerHook)(const char* name, void* stream, int begin);
-int launch_fwd(ga_dtype dt, ga_score sc, const Geometry& g, const FwdArgs& a, int64_t n,
+int launch_fwd(ga_dtype dt, int mode, const Geometry& g, const FwdArgs& a, int64_t n,
                void* stream, TimerHook hook);
 int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t n, void* stream,
                TimerHook hook);

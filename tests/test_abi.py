@@ -210,6 +210,20 @@ def test_gather_probe_argument_checks():
     assert call(p) == capi.GA_ERR_NOT_READY
 
 
+def test_fwd_gatv2_argument_checks():
+    p, _, _ = _hub_plan()
+    call = lambda H=8, d=32, xd=FAKE, xs=FAKE, attn=FAKE, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30: \
+        capi.raw_status("graph_attn_fwd_gatv2", p.handle, capi.GA_BF16, H, d, ctypes.c_float(1.0),
+                        ctypes.c_float(0.2), c_void_p(xd), c_void_p(xs), c_void_p(attn),
+                        c_void_p(out), c_void_p(lse), c_void_p(ws), wsb, None)
+    assert call(d=12) == capi.GA_ERR_UNSUPPORTED
+    assert call(attn=0) == capi.GA_ERR_INVALID_ARG
+    assert call(attn=FAKE + 4) == capi.GA_ERR_INVALID_ARG
+    assert call(xs=FAKE + 8) == capi.GA_ERR_INVALID_ARG
+    assert call(ws=0) == capi.GA_ERR_WORKSPACE
+    assert call() == capi.GA_ERR_NOT_READY
+
+
 def test_default_opts():
     o = default_opts()
     assert o["light_max_deg"] <= o["hub_min_deg_exclusive"] and o["hub_chunk"] >= 1

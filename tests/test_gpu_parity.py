@@ -461,3 +461,45 @@ def test_full_chunglu100k_gat_backward_sampled():
     cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3], rng.choice(w.n, 200, replace=False)])
     gat_bwd_case("full chunglu100k gat bwd (sampled)", ip, ix, s, t, v, do, "f32", rows=rows,
                  cols=cols)
+
+
+# ------------------------------------------------------------------ GATv2
+
+def gatv2_fwd_case(tag, ip, ix, xd, xs, a, dtype, scale=1.0, slope=0.2, rows=None, **plan_kw):
+    from sparse_graph_attention_02_amd import fwd_gatv2
+    say(tag, "N", ip.size - 1, "E", ix.size, "H", xs.shape[1], "d", xs.shape[2], dtype, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    out, lse = fwd_gatv2(plan, dev(xd), dev(xs), dev(a), scale=scale, neg_slope=slope)
+    torch.cuda.synchronize()
+    rows = np.arange(ip.size - 1) if rows is None else np.asarray(rows)
+    ro, rl = A.forward_gatv2_rows(ip, ix, xd, xs, a, rows, scale, f32(slope))
+    rt = torch.from_numpy(rows).cuda()
+    check(f"{tag} out", host64(out[rt]), ro, dtype)
+    check_lse(f"{tag} lse", host64(lse[rt]), rl)
+    return plan, out, lse
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G,LH", [(8, 8), (16, 4), (32, 4), (64, 16), (4, 2), (64, 64)])
+def test_gatv2_forward_geometries(dtype, G, LH):
+    eb = 4 if dtype == "f32" else 2
+    H, d = G // LH, LH * 16 // eb
+    rng = np.random.default_rng(G * 13 + LH)
+    n = 500
+    ip, ix = gg.random_multigraph(n, 5000, rng, hub_rows=(2,), hub_deg=900)
+    xd, xs = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    if dtype == "bf16":
+        xd, xs = gg.f32_to_bf16_bits(xd), gg.f32_to_bf16_bits(xs)
+    gatv2_fwd_case(f"gatv2 fwd G{G} LH{LH} {dtype}", ip, ix, xd, xs, a, dtype, scale=1.2,
+                   slope=0.2, light_max_deg=6, hub_min_deg_exclusive=24, hub_chunk=16)
+
+
+def test_gatv2_forward_chunglu100k_every_row():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w)
+    rng = np.random.default_rng(17)
+    xd, xs = (rng.standard_normal((w.n, 4, 64)).astype(np.float32) for _ in range(2))
+    a = (rng.standard_normal((4, 64)) / 8).astype(np.float32)
+    plan, out, lse = gatv2_fwd_case("gatv2 chunglu100k f32", ip, ix, xd, xs, a, "f32")
+    assert plan.info()["n_row_hub"] > 0
