@@ -201,6 +201,30 @@ ga_status graph_attn_bwd(const ga_plan* plan, ga_score score, ga_dtype dtype, in
                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Workspace of graph_attn_bwd_gatv2: per-node records N*H*8 bytes, row-chunk partials
+ * n_row_chunks*(4*H*d + 4*ceil(2H/4))*4, column-chunk partials n_col_chunks*2*H*d*4, the
+ * attention-gradient partials (one per 16 row-pass work items and per hub row, H*d*4 each)
+ * and a 256-row fp64 reduction stage 256*H*d*8 bytes, each section 256-byte aligned. The
+ * number of row-pass work items depends on the lanes per feature row, hence `dtype`. */
+ga_status graph_attn_bwd_gatv2_workspace_bytes(const ga_plan* plan, ga_dtype dtype,
+                                               int32_t heads, int32_t dim, size_t* bytes);
+
+/* GATv2 backward by recomputation. With z_ij = xd_i + xs_j, g = LeakyReLU'(z) (1 where
+ * z >= 0, else neg_slope, elementwise), P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, xs_j>,
+ * D_i = sum_j P_ij dp_ij and dS_ij = P_ij (dp_ij - D_i):
+ *     dxd_i = scale * attn (.) sum_j dS_ij g_ij
+ *     dxs_j = scale * attn (.) sum_i dS_ij g_ij + sum_i P_ij dout_i
+ *     dattn = scale * sum_(i,j) dS_ij LeakyReLU(z_ij)     (fp32 [H,d])
+ * Rows are renormalised as in graph_attn_bwd. xd, xs, dout, dxd, dxs are [N,H,d] of
+ * `dtype` (16-byte aligned); attn and dattn fp32 [H,d] (16-byte aligned). dattn is reduced
+ * in a fixed order (fp64 final stages), so results are bitwise reproducible. Needs a plan
+ * with the transpose, uploaded. */
+ga_status graph_attn_bwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t heads, int32_t dim,
+                               float scale, float neg_slope, const void* xd, const void* xs,
+                               const float* attn, const void* dout, const float* lse, void* dxd,
+                               void* dxs, float* dattn, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Kernel timers (tracing). When enabled, every kernel the library launches is bracketed
  * by two hipEvents recorded on its stream; graph_attn_timer_read synchronises those
  * events and reports, per kernel name, the number of launches and their summed duration

@@ -25,7 +25,8 @@ import numpy as np
 
 from . import capi
 from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,  # noqa: F401
-                   graph_attn_bwd, graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
+                   graph_attn_bwd, graph_attn_bwd_gatv2, graph_attn_bwd_gatv2_workspace_bytes,
+                   graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
                    graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_workspace_bytes,
                    graph_attn_gather_probe,
                    graph_attn_plan_array,
@@ -36,7 +37,7 @@ from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError, 
                    graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
-__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "graph_attention", "copy_probe", "timers", "default_opts",
+__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
 
@@ -262,6 +263,31 @@ def bwd(plan: Plan, q_or_s, k_or_t, v, dout, lse, *, score="dot", scale=None, ne
                        _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq),
                        _ptr(dk), _ptr(dv), _ptr(ws), wsb, _stream(stream))
     return dq, dk, dv
+
+
+def bwd_gatv2(plan: Plan, xd, xs, attn, dout, lse, *, scale=1.0, neg_slope=0.2, dxd=None,
+              dxs=None, dattn=None, workspace=None, stream=None):
+    """GATv2 backward from the forward's lse; returns (dxd, dxs [N,H,d], dattn fp32 [H,d])."""
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    N, H, d = xs.shape
+    dev = xs.device
+    for name, t in (("xd", xd), ("xs", xs), ("dout", dout)):
+        _need(t, name, (N, H, d), xs.dtype, dev)
+    _need(attn, "attn", (H, d), torch.float32, dev)
+    _need(lse, "lse", (N, H), torch.float32, dev)
+    dxd = torch.empty_like(xd) if dxd is None else dxd
+    dxs = torch.empty_like(xs) if dxs is None else dxs
+    dattn = torch.empty((H, d), dtype=torch.float32, device=dev) if dattn is None else dattn
+    b = c_size_t()
+    graph_attn_bwd_gatv2_workspace_bytes(plan.handle, _dtype_code(xs), H, d, byref(b))
+    ws, wsb = _workspace(int(b.value), dev, workspace)
+    with torch.cuda.device(dev):
+        graph_attn_bwd_gatv2(plan.handle, _dtype_code(xs), H, d, float(scale), float(neg_slope),
+                             _ptr(xd), _ptr(xs), _ptr(attn), _ptr(dout), _ptr(lse), _ptr(dxd),
+                             _ptr(dxs), _ptr(dattn), _ptr(ws), wsb, _stream(stream))
+    return dxd, dxs, dattn
 
 
 def _autograd_fn():

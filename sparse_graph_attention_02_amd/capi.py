@@ -68,6 +68,12 @@ _SIGS = {
     "graph_attn_bwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
                                  c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "graph_attn_bwd_gatv2_workspace_bytes": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
+                                                       POINTER(c_size_t)]),
+    "graph_attn_bwd_gatv2": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_float, c_float,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                       c_void_p]),
     "graph_attn_timer_enable": (c_int32, [c_int32]),
     "graph_attn_timer_reset": (c_int32, []),
     "graph_attn_timer_count": (c_int32, []),
@@ -138,6 +144,8 @@ graph_attn_fwd = _wrap("graph_attn_fwd")
 graph_attn_fwd_gatv2 = _wrap("graph_attn_fwd_gatv2")
 graph_attn_bwd_workspace_bytes = _wrap("graph_attn_bwd_workspace_bytes")
 graph_attn_bwd = _wrap("graph_attn_bwd")
+graph_attn_bwd_gatv2_workspace_bytes = _wrap("graph_attn_bwd_gatv2_workspace_bytes")
+graph_attn_bwd_gatv2 = _wrap("graph_attn_bwd_gatv2")
 graph_attn_timer_enable = _wrap("graph_attn_timer_enable")
 graph_attn_timer_reset = _wrap("graph_attn_timer_reset")
 graph_attn_timer_count = _wrap("graph_attn_timer_count")

@@ -147,6 +147,25 @@ size_t bwd_ws_bytes(const ga_plan* p, const ga::Geometry& g) {
          align_up(p->cols.chunk_row.size() * 2 * F * sizeof(float));
 }
 
+// GATv2 backward workspace sections (bytes, each 256-aligned): record, row-chunk partials,
+// column-chunk partials, da partial slots, first-stage da reduction (fp64).
+struct Gv2Layout {
+  size_t ld, rows, cols, da, da64, total;
+};
+
+Gv2Layout gatv2_layout(const ga_plan* p, const ga::Geometry& g) {
+  const size_t F = size_t(g.heads) * g.dim;
+  Gv2Layout L;
+  L.ld = align_up(size_t(p->n) * g.heads * 2 * sizeof(float));
+  L.rows = align_up(p->rows.chunk_row.size() * (4 * F + (2 * g.heads + 3) / 4 * 4) *
+                    sizeof(float));
+  L.cols = align_up(p->cols.chunk_row.size() * 2 * F * sizeof(float));
+  L.da = align_up(size_t(ga::gatv2_da_slots(p, g)) * F * sizeof(float));
+  L.da64 = align_up(size_t(ga::gatv2_reduce_rows()) * F * sizeof(double));
+  L.total = L.ld + L.rows + L.cols + L.da + L.da64;
+  return L;
+}
+
 ga_status check_device(const ga_plan* p) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
@@ -461,6 +480,69 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.neg_slope = neg_slope;
   const int rc = score == GA_SCORE_DOT ? ga::launch_bwd(dtype, g, args, p->n, stream, active_hook())
                                        : ga::launch_bwd_gat(dtype, g, args, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_bwd_gatv2_workspace_bytes(const ga_plan* p, ga_dtype dtype, int32_t heads,
+                                               int32_t dim, size_t* bytes) {
+  if (!p || !bytes) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  const ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  *bytes = gatv2_layout(p, g).total;
+  return GA_OK;
+}
+
+ga_status graph_attn_bwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, int32_t dim,
+                               float scale, float neg_slope, const void* xd, const void* xs,
+                               const float* attn, const void* dout, const float* lse, void* dxd,
+                               void* dxs, float* dattn, void* ws, size_t ws_bytes,
+                               void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (!ga::bwd_supported(dtype, g)) return GA_ERR_UNSUPPORTED;
+  if ((s = check_ptr(attn, 16)) != GA_OK || (s = check_ptr(dattn, 16)) != GA_OK) return s;
+  if (p->n > 0) {
+    const void* f16[] = {xd, xs, dout, dxd, dxs};
+    for (const void* x : f16)
+      if ((s = check_ptr(x, 16)) != GA_OK) return s;
+    if ((s = check_ptr(lse, 4)) != GA_OK) return s;
+  }
+  if (!p->has_csc) return GA_ERR_NOT_READY;
+  const Gv2Layout L = gatv2_layout(p, g);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 16)) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if ((s = check_device(p)) != GA_OK) return s;
+  // an empty graph still launches the final reduction stage, which writes dattn = 0
+  ga::BwdArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.colptr = p->d_colptr;
+  args.rowidx = p->d_rowidx;
+  args.rows = p->d_rows;
+  args.cols = p->d_cols;
+  args.q = xd;
+  args.k = xs;
+  args.v = xs;
+  args.dout = dout;
+  args.lse = lse;
+  args.dq = dxd;
+  args.dk = dxs;
+  args.dv = nullptr;
+  char* w = static_cast<char*>(ws);
+  args.ws_ld = reinterpret_cast<float*>(w);
+  args.ws_dq = reinterpret_cast<float*>(w + L.ld);
+  args.ws_dkv = reinterpret_cast<float*>(w + L.ld + L.rows);
+  args.ws_da = reinterpret_cast<float*>(w + L.ld + L.rows + L.cols);
+  args.ws_da64 = reinterpret_cast<double*>(w + L.ld + L.rows + L.cols + L.da);
+  args.attn = attn;
+  args.dattn = dattn;
+  args.scale = scale;
+  args.sc2 = scale * 1.4426950408889634f;
+  args.neg_slope = neg_slope;
+  const int rc = ga::launch_bwd_gatv2(dtype, g, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
 

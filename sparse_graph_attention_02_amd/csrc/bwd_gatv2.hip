@@ -1,0 +1,541 @@
+// Backward kernels of the GATv2 score for gfx950:
+//   e_ij = scale * sum_c a[c] LeakyReLU(z_ij[c]),  z_ij = xd_i + xs_j,  message xs_j.
+//
+// Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
+// Summary > Methodology, attention-based layers, backward pass (weights recomputed from the
+// per-node log-sum-exp; cached transposed adjacency for the backward). GATv2 is the layer
+// the pages name; its score is the textbook one.
+//
+// With g = LeakyReLU'(z), lz = LeakyReLU(z) (elementwise), P_ij = exp(e_ij - lse_i),
+// dp_ij = <dout_i, xs_j>, L_i = sum_j P_ij (1 up to the stored lse's rounding; the weights
+// are renormalised by it), D^_i = sum_j P_ij dp_ij / L_i, dS_ij = P_ij / L_i (dp_ij - D^_i):
+//   bwd_gatv2_rows_main   over CSR rows: per lane element
+//                           A1 = sum P dp g,  B1 = sum P g,  A2 = sum P dp lz,  B2 = sum P lz
+//                         dxd_i = scale a (A1 - D^ B1) / L,  da_i = scale (A2 - D^ B2) / L
+//                         and the record (lse_i log2 e + log2 L_i, D^_i) for the column pass.
+//                         Each of the W wavefronts runs kItemsPerWave work items dealt in
+//                         snake order (pass k takes item k W + w, or k W + W-1-w on odd
+//                         passes; items are sorted by size, so every wave gets a mix) and
+//                         writes one fp32 partial of da (hub rows: chunk partials, see merge)
+//   bwd_gatv2_rows_merge  hub rows: ordered sums of the chunk partials, then as above (one
+//                         da partial per hub row)
+//   bwd_gatv2_da_reduce   two fixed-order fp64 stages over the da partials -> dattn [H*d]
+//   bwd_gatv2_cols_main   over transpose columns: dxs_j = scale a sum_i dS_ij g_ij
+//                                                          + sum_i P_ij dout_i
+//   bwd_gatv2_cols_merge  hub columns: ordered sums of partials
+// No atomics; every sum has a fixed order, so results are bitwise reproducible.
+#include "ga_device.h"
+#include "ga_internal.h"
+
+namespace ga {
+namespace {
+
+constexpr int kItemsPerWave = 16;   // row-pass work items per wavefront (bounds da partials)
+constexpr int kReduceBlocks = 256;  // stage-1 blocks of the da reduction
+
+template <typename T, int G, int LH, int U>
+struct BwdV2 : RowIO<T, G, LH> {
+  using IO = RowIO<T, G, LH>;
+  using typename IO::L16;
+  using typename IO::raw_t;
+  using IO::F;
+  using IO::H;
+  using IO::NG;
+  using IO::R;
+  using IO::VEC;
+  using typename IO::acc_t;
+  static constexpr int kRowStride = 4 * F + (2 * H + 3) / 4 * 4;  // A1 B1 A2 B2 [F], D L [H]
+  static constexpr int kColStride = 2 * F;                        // C1 C2 [F]
+
+  // A1, B1 (for dxd) are row-normalised fp32 sums. A2, B2, D, L feed dattn, a sum over
+  // every edge of the graph whose per-row terms cancel; for fp32 features they are kept in
+  // fp64 (acc_t) so the graph-wide sum keeps fp32-level accuracy.
+  struct RowAcc {
+    float A1[VEC], B1[VEC];
+    acc_t A2[VEC], B2[VEC];
+    acc_t D, L;
+  };
+
+  __device__ __forceinline__ static void zero(RowAcc& s) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      s.A1[c] = s.B1[c] = 0.f;
+      s.A2[c] = s.B2[c] = 0;
+    }
+    s.D = s.L = 0;
+  }
+
+  __device__ __forceinline__ static void load_attn(const BwdArgs& a, int r, float* av) {
+    const f32x4* ap = reinterpret_cast<const f32x4*>(a.attn + r * VEC);
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k) {
+      const f32x4 x = ap[k];
+      av[4 * k] = x.x;
+      av[4 * k + 1] = x.y;
+      av[4 * k + 2] = x.z;
+      av[4 * k + 3] = x.w;
+    }
+  }
+
+  // e in log2 units of edge (xd, xs): head-summed a . LeakyReLU(xd + xs) * sc2.
+  __device__ __forceinline__ static float score2(const BwdArgs& a, const float* xd,
+                                                 const float* xs, const float* av) {
+    float e = 0.f;
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      const float z = xd[c] + xs[c];
+      e = fmaf(av[c], z >= 0.f ? z : z * a.neg_slope, e);
+    }
+    return head_sum<LH>(e) * a.sc2;
+  }
+
+  // Row pass over edges [e0, e1) of a row (xd, dout held by the lane).
+  template <int NGS>
+  __device__ __forceinline__ static void run_rows(const BwdArgs& a, int e0, int e1, int seg0,
+                                                  int gs, int r, const float* xd,
+                                                  const raw_t& dor, const float* av,
+                                                  float lse2, RowAcc& s) {
+    constexpr int L = NGS * G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const raw_t* __restrict__ Xs = R(a.k);
+    for (int base = e0; base < e1; base += L) {
+      const int nb = min(L, e1 - base);
+      const int li = lane - seg0;
+      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
+      for (int t = 0; t < nb; t += NGS * U) {
+        int jj[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pos = t + u * NGS + gs;
+          ok[u] = pos < nb;
+          jj[u] = __shfl(my_j, seg0 + (ok[u] ? pos : t));
+        }
+        raw_t xr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xr[u] = Xs[static_cast<size_t>(jj[u]) * G + r];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float xs[VEC];
+          L16::unpack(xr[u], xs);
+          const float s2 = score2(a, xd, xs, av);
+          const float dp = head_sum<LH>(L16::dot(dor, xr[u]));
+          const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
+          const float pdp = p * dp;
+          s.D += static_cast<acc_t>(pdp);
+          s.L += static_cast<acc_t>(p);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            const float z = xd[c] + xs[c];
+            const bool pos = z >= 0.f;
+            const float g = pos ? 1.f : a.neg_slope;
+            const float lz = pos ? z : z * a.neg_slope;
+            s.A1[c] = fmaf(pdp, g, s.A1[c]);
+            s.B1[c] = fmaf(p, g, s.B1[c]);
+            s.A2[c] += static_cast<acc_t>(pdp * lz);
+            s.B2[c] += static_cast<acc_t>(p * lz);
+          }
+        }
+      }
+    }
+  }
+
+  template <int NGS>
+  __device__ __forceinline__ static void combine(RowAcc& s) {
+    IO::template group_sum<NGS>(s.A1);
+    IO::template group_sum<NGS>(s.B1);
+    IO::template group_sum<NGS>(s.A2);
+    IO::template group_sum<NGS>(s.B2);
+    IO::template group_sum1<NGS>(s.D);
+    IO::template group_sum1<NGS>(s.L);
+  }
+
+  // Row epilogue: dxd, the record, and this row's da contribution added into `da`.
+  __device__ __forceinline__ static void finish_row(const BwdArgs& a, int row, int r, int h,
+                                                    float lse2, const float* av,
+                                                    const RowAcc& s, acc_t* da) {
+    const acc_t inv = s.L > 0 ? acc_t(1) / s.L : acc_t(0);
+    const acc_t Dn = s.D * inv;
+    const acc_t f = static_cast<acc_t>(a.scale) * inv;
+    const float Dn32 = static_cast<float>(Dn);
+    float x[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+      x[c] = av[c] * fmaf(-Dn32, s.B1[c], s.A1[c]);
+      da[c] += f * (s.A2[c] - Dn * s.B2[c]);
+    }
+    IO::store(a.dq, row, r, x, static_cast<float>(f));
+    if (r % LH == 0) {
+      const float L32 = static_cast<float>(s.L);
+      st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h,
+                f32x2{L32 > 0.f ? lse2 + __log2f(L32) : lse2, Dn32});
+    }
+  }
+
+  __device__ __forceinline__ static void store_partial(float* p, int r, int h, const RowAcc& s) {
+    IO::store_f32(p, r, s.A1);
+    IO::store_f32(p + F, r, s.B1);
+    IO::store_f32(p + 2 * F, r, s.A2);
+    IO::store_f32(p + 3 * F, r, s.B2);
+    if (r % LH == 0) {
+      st_stream(p + 4 * F + h, static_cast<float>(s.D));
+      st_stream(p + 4 * F + H + h, static_cast<float>(s.L));
+    }
+  }
+
+  __device__ __forceinline__ static void add_partial(const float* p, int r, int h, RowAcc& s) {
+    IO::add_f32(p, r, s.A1);
+    IO::add_f32(p + F, r, s.B1);
+    IO::add_f32(p + 2 * F, r, s.A2);
+    IO::add_f32(p + 3 * F, r, s.B2);
+    s.D += static_cast<acc_t>(ld_stream(p + 4 * F + h));
+    s.L += static_cast<acc_t>(ld_stream(p + 4 * F + H + h));
+  }
+
+  // Column pass over transpose edges [e0, e1) of column j (xs_j held by the lane).
+  template <int NGS>
+  __device__ __forceinline__ static void run_cols(const BwdArgs& a, int e0, int e1, int seg0,
+                                                  int gs, int r, int h, const raw_t& xsr,
+                                                  const float* xs, const float* av, acc_t* C1,
+                                                  acc_t* C2) {
+    constexpr int L = NGS * G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const raw_t* __restrict__ Xd = R(a.q);
+    const raw_t* __restrict__ Or = R(a.dout);
+    const f32x2* __restrict__ LD = reinterpret_cast<const f32x2*>(a.ws_ld);
+    for (int base = e0; base < e1; base += L) {
+      const int nb = min(L, e1 - base);
+      const int li = lane - seg0;
+      const int my_i = (li < nb) ? ld_stream(a.rowidx + base + li) : 0;
+      for (int t = 0; t < nb; t += NGS * U) {
+        int ii[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pos = t + u * NGS + gs;
+          ok[u] = pos < nb;
+          ii[u] = __shfl(my_i, seg0 + (ok[u] ? pos : t));
+        }
+        raw_t xdr[U], dr[U];
+        f32x2 ld[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          xdr[u] = Xd[static_cast<size_t>(ii[u]) * G + r];
+          dr[u] = Or[static_cast<size_t>(ii[u]) * G + r];
+          ld[u] = LD[static_cast<size_t>(ii[u]) * H + h];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float xd[VEC], df[VEC];
+          L16::unpack(xdr[u], xd);
+          L16::unpack(dr[u], df);
+          const float s2 = score2(a, xd, xs, av);
+          const float dp = head_sum<LH>(L16::dot(dr[u], xsr));
+          const float p = ok[u] ? fast_exp2(s2 - ld[u].x) : 0.f;
+          const float ds = p * (dp - ld[u].y);
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            const float g = xd[c] + xs[c] >= 0.f ? 1.f : a.neg_slope;
+            C1[c] += static_cast<acc_t>(ds * g);
+            C2[c] = fma(static_cast<acc_t>(p), static_cast<acc_t>(df[c]), C2[c]);
+          }
+        }
+      }
+    }
+  }
+
+  // dxs_j = scale a C1 + C2.
+  __device__ __forceinline__ static void store_col(const BwdArgs& a, int col, int r,
+                                                   const float* av, const acc_t* C1,
+                                                   const acc_t* C2) {
+    acc_t x[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c)
+      x[c] = static_cast<acc_t>(a.scale * av[c]) * C1[c] + C2[c];
+    IO::store(a.dk, col, r, x, 1.f);
+  }
+};
+
+template <typename T, int G, int LH, int U>
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdArgs a) {
+  using K = BwdV2<T, G, LH, U>;
+  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int slot = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int g = lane / G, r = lane % G, h = r / LH;
+  const DevBins& B = a.rows;
+  const int64_t n_items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  const int64_t W = (n_items + kItemsPerWave - 1) / kItemsPerWave;  // waves = da slots
+  // waves of the last block past the last slot own no partial: leave before writing one
+  if (slot >= W) return;
+  float av[VEC];
+  typename K::acc_t da[VEC];
+  K::load_attn(a, r, av);
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) da[c] = 0;
+  for (int k = 0; k < kItemsPerWave; ++k) {
+    const int64_t item = int64_t(k) * W + ((k & 1) ? W - 1 - slot : slot);
+    if (item >= n_items) continue;
+    typename K::RowAcc s;
+    K::zero(s);
+    float xd[VEC], lse2;
+    typename K::raw_t dor;
+    if (item < B.n_chunks + B.n_medium) {
+      int row, e0, e1;
+      const bool chunk = item < B.n_chunks;
+      if (chunk) {
+        row = B.chunk_row[item];
+        e0 = B.chunk_begin[item];
+        e1 = B.chunk_end[item];
+      } else {
+        row = B.medium[item - B.n_chunks];
+        e0 = a.indptr[row];
+        e1 = a.indptr[row + 1];
+      }
+      const size_t off = static_cast<size_t>(row) * G + r;
+      K::L16::unpack(ld_stream(K::R(a.q) + off), xd);
+      dor = ld_stream(K::R(a.dout) + off);
+      lse2 = ld_stream(a.lse + static_cast<size_t>(row) * K::H + h) * kLog2e;
+      K::template run_rows<NG>(a, e0, e1, 0, g, r, xd, dor, av, lse2, s);
+      K::template combine<NG>(s);
+      if (g == 0) {
+        if (chunk)
+          K::store_partial(a.ws_dq + static_cast<size_t>(item) * K::kRowStride, r, h, s);
+        else
+          K::finish_row(a, row, r, h, lse2, av, s, da);
+      }
+    } else {
+      const int64_t li = (item - B.n_chunks - B.n_medium) * NG + g;
+      if (li < B.n_light) {
+        const int row = B.light[li];
+        const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
+        const size_t off = static_cast<size_t>(row) * G + r;
+        K::L16::unpack(ld_stream(K::R(a.q) + off), xd);
+        dor = ld_stream(K::R(a.dout) + off);
+        lse2 = ld_stream(a.lse + static_cast<size_t>(row) * K::H + h) * kLog2e;
+        K::template run_rows<1>(a, e0, e1, g * G, 0, r, xd, dor, av, lse2, s);
+        K::finish_row(a, row, r, h, lse2, av, s, da);
+      }
+    }
+  }
+  K::template group_sum<NG>(da);
+  if (g == 0) K::store_f32(a.ws_da + static_cast<size_t>(slot) * F, r, da);
+}
+
+// One wavefront per hub row; its da contribution goes to partial slot n_row_slots + hub.
+template <typename T, int G, int LH>
+__global__ __launch_bounds__(kBlock) void bwd_gatv2_rows_merge(BwdArgs a, int n_row_slots) {
+  using K = BwdV2<T, G, LH, 1>;
+  constexpr int NG = K::NG, VEC = K::VEC, F = K::F, H = K::H;
+  const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G, r = lane % G, h = r / LH;
+  if (hub >= a.rows.n_hub) return;
+  const int row = a.rows.hub[hub];
+  const int c0 = a.rows.hub_chunk_ptr[hub], c1 = a.rows.hub_chunk_ptr[hub + 1];
+  typename K::RowAcc s;
+  K::zero(s);
+#pragma unroll 2
+  for (int c = c0 + g; c < c1; c += NG)
+    K::add_partial(a.ws_dq + static_cast<size_t>(c) * K::kRowStride, r, h, s);
+  K::template combine<NG>(s);
+  if (g != 0) return;
+  float av[VEC];
+  typename K::acc_t da[VEC];
+  K::load_attn(a, r, av);
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) da[c] = 0;
+  const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
+  K::finish_row(a, row, r, h, lse2, av, s, da);
+  K::store_f32(a.ws_da + static_cast<size_t>(n_row_slots + hub) * F, r, da);
+}
+
+// Stage 1: block b sums partial slots [b*per, min((b+1)*per, n)) in fp64, in slot order.
+// Stage 2 (a single block, src = stage-1 output): sums the stage-1 rows in order.
+template <typename S>
+__global__ __launch_bounds__(kBlock) void bwd_gatv2_da_reduce(const S* __restrict__ src, int64_t n,
+                                                              int64_t per, int F,
+                                                              double* __restrict__ dst64,
+                                                              float* __restrict__ dst32) {
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t s1 = min(n, s0 + per);
+  for (int c = threadIdx.x; c < F; c += kBlock) {
+    double acc = 0.0;
+    for (int64_t sl = s0; sl < s1; ++sl) acc += static_cast<double>(src[sl * F + c]);
+    if (dst32)
+      dst32[c] = static_cast<float>(acc);
+    else
+      dst64[static_cast<size_t>(blockIdx.x) * F + c] = acc;
+  }
+}
+
+template <typename T, int G, int LH, int U>
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdArgs a) {
+  using K = BwdV2<T, G, LH, U>;
+  constexpr int NG = K::NG, VEC = K::VEC;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int g = lane / G, r = lane % G, h = r / LH;
+  const DevBins& B = a.cols;
+  float av[VEC], xs[VEC];
+  typename K::acc_t C1[VEC], C2[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) C1[c] = C2[c] = 0;
+  K::load_attn(a, r, av);
+  if (item < B.n_chunks + B.n_medium) {
+    int col, e0, e1;
+    const bool chunk = item < B.n_chunks;
+    if (chunk) {
+      col = B.chunk_row[item];
+      e0 = B.chunk_begin[item];
+      e1 = B.chunk_end[item];
+    } else {
+      col = B.medium[item - B.n_chunks];
+      e0 = a.colptr[col];
+      e1 = a.colptr[col + 1];
+    }
+    const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
+    K::L16::unpack(xsr, xs);
+    K::template run_cols<NG>(a, e0, e1, 0, g, r, h, xsr, xs, av, C1, C2);
+    K::template group_sum<NG>(C1);
+    K::template group_sum<NG>(C2);
+    if (g != 0) return;
+    if (chunk) {
+      float* p = a.ws_dkv + static_cast<size_t>(item) * K::kColStride;
+      K::store_f32(p, r, C1);
+      K::store_f32(p + K::F, r, C2);
+    } else {
+      K::store_col(a, col, r, av, C1, C2);
+    }
+    return;
+  }
+  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  if (li >= B.n_light) return;
+  const int col = B.light[li];
+  const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
+  const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
+  K::L16::unpack(xsr, xs);
+  K::template run_cols<1>(a, e0, e1, g * G, 0, r, h, xsr, xs, av, C1, C2);
+  K::store_col(a, col, r, av, C1, C2);
+}
+
+template <typename T, int G, int LH>
+__global__ __launch_bounds__(kBlock) void bwd_gatv2_cols_merge(BwdArgs a) {
+  using K = BwdV2<T, G, LH, 1>;
+  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
+  const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G, r = lane % G;
+  if (hub >= a.cols.n_hub) return;
+  const int col = a.cols.hub[hub];
+  const int c0 = a.cols.hub_chunk_ptr[hub], c1 = a.cols.hub_chunk_ptr[hub + 1];
+  typename K::acc_t C1[VEC], C2[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) C1[c] = C2[c] = 0;
+#pragma unroll 4
+  for (int c = c0 + g; c < c1; c += NG) {
+    const float* p = a.ws_dkv + static_cast<size_t>(c) * K::kColStride;
+    K::add_f32(p, r, C1);
+    K::add_f32(p + F, r, C2);
+  }
+  K::template group_sum<NG>(C1);
+  K::template group_sum<NG>(C2);
+  if (g != 0) return;
+  float av[VEC];
+  K::load_attn(a, r, av);
+  K::store_col(a, col, r, av, C1, C2);
+}
+
+template <typename T, int G, int LH>
+int launch(const BwdArgs& a, void* stream, TimerHook hook) {
+  constexpr int NG = kWave / G;
+  constexpr int F = G * Lane16<T>::VEC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto items_of = [](const DevBins& B) {
+    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  };
+  const int64_t row_slots = (items_of(a.rows) + kItemsPerWave - 1) / kItemsPerWave;
+  const int64_t n_slots = row_slots + a.rows.n_hub;
+  int e;
+  auto done = [&](const char* name) -> int {
+    if (hook) hook(name, stream, 0);
+    return static_cast<int>(hipGetLastError());
+  };
+  if (row_slots > 0) {
+    if (hook) hook("bwd_gatv2_rows_main", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, GA_UNROLL_DQ>),
+                       dim3(static_cast<unsigned>((row_slots + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kBlock), 0, s, a);
+    if ((e = done("bwd_gatv2_rows_main"))) return e;
+  }
+  if (a.rows.n_hub > 0) {
+    if (hook) hook("bwd_gatv2_rows_merge", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_rows_merge<T, G, LH>),
+                       dim3((a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
+                       s, a, static_cast<int>(row_slots));
+    if ((e = done("bwd_gatv2_rows_merge"))) return e;
+  }
+  {
+    // stage 1 over the partial slots (skipped when there are none), then stage 2, which
+    // always runs so that dattn is written (zeros for a graph without rows)
+    const int64_t per = n_slots > 0 ? (n_slots + kReduceBlocks - 1) / kReduceBlocks : 1;
+    const int64_t nb = (n_slots + per - 1) / per;
+    if (hook) hook("bwd_gatv2_da_reduce", stream, 1);
+    if (nb > 0)
+      hipLaunchKernelGGL((bwd_gatv2_da_reduce<float>), dim3(static_cast<unsigned>(nb)),
+                         dim3(kBlock), 0, s, a.ws_da, n_slots, per, F, a.ws_da64,
+                         static_cast<float*>(nullptr));
+    hipLaunchKernelGGL((bwd_gatv2_da_reduce<double>), dim3(1), dim3(kBlock), 0, s,
+                       static_cast<const double*>(a.ws_da64), nb, nb > 0 ? nb : 1, F,
+                       static_cast<double*>(nullptr), a.dattn);
+    if ((e = done("bwd_gatv2_da_reduce"))) return e;
+  }
+  const int64_t col_items = items_of(a.cols);
+  if (col_items > 0) {
+    if (hook) hook("bwd_gatv2_cols_main", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_cols_main<T, G, LH, GA_UNROLL_DKDV>),
+                       dim3(static_cast<unsigned>((col_items + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kBlock), 0, s, a);
+    if ((e = done("bwd_gatv2_cols_main"))) return e;
+  }
+  if (a.cols.n_hub > 0) {
+    if (hook) hook("bwd_gatv2_cols_merge", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_cols_merge<T, G, LH>),
+                       dim3((a.cols.n_hub + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
+                       s, a);
+    if ((e = done("bwd_gatv2_cols_merge"))) return e;
+  }
+  return 0;
+}
+
+#define GA_GEOMS(X)                                                                       \
+  X(4, 2) X(4, 4) X(8, 2) X(8, 4) X(8, 8) X(16, 2) X(16, 4) X(16, 8) X(16, 16) X(32, 2) \
+  X(32, 4) X(32, 8) X(32, 16) X(32, 32) X(64, 2) X(64, 4) X(64, 8) X(64, 16) X(64, 32) \
+  X(64, 64)
+
+template <typename T>
+int dispatch(const Geometry& g, const BwdArgs& a, void* stream, TimerHook hook) {
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return launch<T, GG, LL>(a, stream, hook);
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  return -1;
+}
+
+}  // namespace
+
+int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g) {
+  const int64_t NG = kWave / g.G;
+  const int64_t items = int64_t(p->rows.chunk_row.size()) + int64_t(p->rows.medium.size()) +
+                        (int64_t(p->rows.light.size()) + NG - 1) / NG;
+  return (items + kItemsPerWave - 1) / kItemsPerWave + int64_t(p->rows.hub.size());
+}
+
+int64_t gatv2_reduce_rows() { return kReduceBlocks; }
+
+int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
+                     TimerHook hook) {
+  return dt == GA_F32 ? dispatch<float>(g, a, stream, hook) : dispatch<bf16_t>(g, a, stream, hook);
+}
+
+}  // namespace ga

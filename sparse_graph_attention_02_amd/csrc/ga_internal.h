@@ -103,7 +103,12 @@ struct BwdArgs {
   float* ws_dkv;   // [n_col_chunks][2][H*d]
   float scale;
   float sc2;       // scale * log2(e)
-  float neg_slope; // LeakyReLU slope (GAT score only)
+  float neg_slope; // LeakyReLU slope (GAT and GATv2 scores)
+  // GATv2 only
+  const float* attn;  // attention vector [H*d]
+  float* dattn;       // its gradient [H*d]
+  float* ws_da;       // da partials [n_slots][H*d]
+  double* ws_da64;    // first-stage da reduction [kReduceBlocks][H*d]
 };
 
 // fp32 floats per hub-row chunk partial of the row pass: A [H*d], B [H*d], D [H], L [H]
@@ -131,6 +136,12 @@ int launch_bwd(ga_dtype dt, const Geometry& g, const BwdArgs& a, int64_t n, void
 // GAT-style score: q/k/dq/dk carry s/t/ds/dt (fp32 [N, H]).
 int launch_bwd_gat(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
                    TimerHook hook);
+// GATv2: q/k/dq/dk carry xd/xs/dxd/dxs ([N, H, d]); attn/dattn/ws_da/ws_da64 set.
+int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
+                     TimerHook hook);
+// da partial slots of the GATv2 row pass and the rows of its first reduction stage.
+int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g);
+int64_t gatv2_reduce_rows();
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
 int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
                         void* sink, void* stream, TimerHook hook);

@@ -224,6 +224,35 @@ def test_fwd_gatv2_argument_checks():
     assert call() == capi.GA_ERR_NOT_READY
 
 
+def test_bwd_gatv2_argument_checks():
+    p, ip, ix = _hub_plan()
+    need = c_size_t()
+    capi.graph_attn_bwd_gatv2_workspace_bytes(p.handle, capi.GA_BF16, 8, 32, byref(need))
+    info = p.info()
+    al = lambda x: (x + 255) // 256 * 256
+    items = info["n_row_chunks"] + info["n_row_medium"] + -(-info["n_row_light"] // 2)
+    slots = -(-items // 16) + info["n_row_hub"]
+    assert need.value == al(64 * 8 * 8) + al(info["n_row_chunks"] * (4 * 256 + 16) * 4) + \
+        al(info["n_col_chunks"] * 2 * 256 * 4) + al(slots * 256 * 4) + al(256 * 256 * 8)
+
+    def call(ptrs=None, attn=FAKE, dattn=FAKE, ws=FAKE, wsb=1 << 30, plan=p):
+        ptrs = ptrs or [FAKE] * 6
+        return capi.raw_status("graph_attn_bwd_gatv2", plan.handle, capi.GA_BF16, 8, 32,
+                               ctypes.c_float(1.0), ctypes.c_float(0.2), c_void_p(ptrs[0]),
+                               c_void_p(ptrs[1]), c_void_p(attn), c_void_p(ptrs[2]),
+                               c_void_p(ptrs[3]), c_void_p(ptrs[4]), c_void_p(ptrs[5]),
+                               c_void_p(dattn), c_void_p(ws), wsb, None)
+    assert call(attn=0) == capi.GA_ERR_INVALID_ARG
+    assert call(dattn=FAKE + 4) == capi.GA_ERR_INVALID_ARG
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = 0
+        assert call(ptrs) == capi.GA_ERR_INVALID_ARG
+    assert call(wsb=need.value - 1) == capi.GA_ERR_WORKSPACE
+    assert call(wsb=need.value) == capi.GA_ERR_NOT_READY
+    assert call(plan=Plan(ip, ix, build_csc=False)) == capi.GA_ERR_NOT_READY
+
+
 def test_default_opts():
     o = default_opts()
     assert o["light_max_deg"] <= o["hub_min_deg_exclusive"] and o["hub_chunk"] >= 1

@@ -503,3 +503,92 @@ def test_gatv2_forward_chunglu100k_every_row():
     a = (rng.standard_normal((4, 64)) / 8).astype(np.float32)
     plan, out, lse = gatv2_fwd_case("gatv2 chunglu100k f32", ip, ix, xd, xs, a, "f32")
     assert plan.info()["n_row_hub"] > 0
+
+
+def gatv2_bwd_case(tag, ip, ix, xd, xs, a, do, dtype, scale=1.0, slope=0.2, rows=None, cols=None,
+                   **plan_kw):
+    from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2
+    say(tag, "N", ip.size - 1, "E", ix.size, "H", xs.shape[1], "d", xs.shape[2], dtype, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    txd, txs, ta, td = dev(xd), dev(xs), dev(a), dev(do)
+    out, lse = fwd_gatv2(plan, txd, txs, ta, scale=scale, neg_slope=slope)
+    dxd, dxs, da = bwd_gatv2(plan, txd, txs, ta, td, lse, scale=scale, neg_slope=slope)
+    torch.cuda.synchronize()
+    sl = f32(slope)
+    if rows is None:
+        rxd, rxs, rda = A.backward_gatv2(ip, ix, xd, xs, a, do, scale, sl)
+        errs = [check(f"{tag} dxd", host64(dxd), rxd, dtype), check(f"{tag} dxs", host64(dxs), rxs, dtype)]
+    else:
+        rxd, _ = A.grad_gatv2_rows(ip, ix, xd, xs, a, do, rows, scale, sl)
+        rxs = A.grad_gatv2_cols(ip, ix, xd, xs, a, do, cols, scale, sl)
+        r_t, c_t = torch.from_numpy(np.asarray(rows)).cuda(), torch.from_numpy(np.asarray(cols)).cuda()
+        errs = [check(f"{tag} dxd", host64(dxd[r_t]), rxd, dtype),
+                check(f"{tag} dxs", host64(dxs[c_t]), rxs, dtype)]
+        _, rda = A.grad_gatv2_rows(ip, ix, xd, xs, a, do, np.arange(ip.size - 1), scale, sl)
+    errs.append(check(f"{tag} dattn", host64(da), rda, dtype))
+    say(tag, "max abs / norm-rel errors", errs)
+    return plan, (dxd, dxs, da)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G,LH", [(8, 8), (32, 4), (64, 16), (4, 2), (16, 16)])
+def test_gatv2_backward_every_element(dtype, G, LH):
+    eb = 4 if dtype == "f32" else 2
+    H, d = G // LH, LH * 16 // eb
+    rng = np.random.default_rng(G * 31 + LH)
+    n = 600
+    src = np.r_[rng.integers(0, n, 6000), np.full(900, 13)]       # column hub 13
+    dst = np.r_[rng.integers(0, n, 6000), rng.integers(0, n, 900)]
+    dst[:800] = 5                                                 # row hub 5
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    xd, xs, do = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(3))
+    a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    if dtype == "bf16":
+        xd, xs, do = (gg.f32_to_bf16_bits(x) for x in (xd, xs, do))
+    plan, _ = gatv2_bwd_case(f"gatv2 bwd G{G} LH{LH} {dtype}", ip, ix, xd, xs, a, do, dtype,
+                             scale=1.1, slope=0.2, light_max_deg=6, hub_min_deg_exclusive=40,
+                             hub_chunk=32)
+    info = plan.info()
+    assert info["n_row_chunks"] > info["n_row_hub"] > 0 and info["n_col_chunks"] > info["n_col_hub"] > 0
+
+
+def test_gatv2_backward_deterministic_and_empty_graph():
+    from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    rng = np.random.default_rng(5)
+    xd, xs, do = (gg.f32_to_bf16_bits(rng.standard_normal((20_000, 4, 64)).astype(np.float32))
+                  for _ in range(3))
+    a = (rng.standard_normal((4, 64)) / 8).astype(np.float32)
+    say("gatv2 determinism")
+    plan = Plan(ip, ix, light_max_deg=8, hub_min_deg_exclusive=128, hub_chunk=64).upload()
+    t = [dev(x) for x in (xd, xs, a, do)]
+    res = []
+    for _ in range(2):
+        out, lse = fwd_gatv2(plan, t[0], t[1], t[2])
+        res.append((out, lse) + bwd_gatv2(plan, t[0], t[1], t[2], t[3], lse))
+    torch.cuda.synchronize()
+    for x, y in zip(*res):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+    # a graph with no nodes: dattn comes back as zeros
+    empty = Plan(np.zeros(1, np.int32), np.zeros(0, np.int32)).upload()
+    z = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    dattn = torch.full((4, 64), 7.0, device="cuda")
+    bwd_gatv2(empty, z, z, t[2], z, torch.zeros((0, 4), device="cuda"), dattn=dattn)
+    torch.cuda.synchronize()
+    assert torch.all(dattn == 0)
+
+
+@pytest.mark.slow
+def test_full_chunglu100k_gatv2_backward_sampled():
+    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    ip, ix = gg.make_graph(w)
+    rng = np.random.default_rng(9)
+    xd, xs, do = (rng.standard_normal((w.n, 4, 64)).astype(np.float32) for _ in range(3))
+    a = (rng.standard_normal((4, 64)) / 8).astype(np.float32)
+    rows = _sample_rows(ip, rng, k=300)
+    odeg = np.bincount(ix, minlength=w.n)
+    cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:2], rng.choice(w.n, 100, replace=False)])
+    gatv2_bwd_case("full chunglu100k gatv2 bwd (sampled)", ip, ix, xd, xs, a, do, "f32", rows=rows,
+                   cols=cols)
