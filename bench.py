@@ -37,25 +37,36 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 # ---------------------------------------------------------------- algorithmic bytes
 
-def algorithmic_bytes(kernel, N, E, H, d, b):
+def algorithmic_bytes(kernel, N, E, H, d, b, score="dot"):
     """Bytes a launch must move at minimum: the CSR (or transpose) once, one read of each
     gathered row per edge, each per-node operand once and each output once."""
     F = H * d
-    if kernel == "fwd_main":       # indptr, indices, K_j + V_j per edge, Q, out, lse
-        return 4 * (N + 1) + 4 * E + 2 * E * F * b + N * F * b + N * F * b + 4 * N * H
-    if kernel == "bwd_dq_main":    # indptr, indices, K_j + V_j per edge, Q, dOut, lse, dQ,
-        return (4 * (N + 1) + 4 * E + 2 * E * F * b + 2 * N * F * b + 4 * N * H
-                + N * F * b + 8 * N * H)  # + (lse, D) record written
-    if kernel == "bwd_dkdv_main":  # colptr, rowidx, Q_i + dOut_i + (lse, D)_i per edge, K, V, dK, dV
-        return 4 * (N + 1) + 4 * E + E * (2 * F * b + 8 * H) + 2 * N * F * b + 2 * N * F * b
+    csr = 4 * (N + 1) + 4 * E
+    if kernel == "fwd_main":
+        if score == "gat":      # V_j + t_j per edge; s, out, lse per node
+            return csr + E * (F * b + 4 * H) + 4 * N * H + N * F * b + 4 * N * H
+        if score == "gatv2":    # xs_j per edge (score operand and message); xd, out, lse; attn
+            return csr + E * F * b + 2 * N * F * b + 4 * N * H + 4 * F
+        return csr + 2 * E * F * b + 2 * N * F * b + 4 * N * H   # K_j + V_j; Q, out, lse
+    if kernel == "bwd_dq_main":    # K_j + V_j per edge; Q, dOut, lse; dQ, (lse, D) record
+        return csr + 2 * E * F * b + 2 * N * F * b + 4 * N * H + N * F * b + 8 * N * H
+    if kernel == "bwd_dkdv_main":  # Q_i + dOut_i + record_i per edge; K, V; dK, dV
+        return csr + E * (2 * F * b + 8 * H) + 2 * N * F * b + 2 * N * F * b
+    if kernel == "bwd_gatv2_rows_main":  # xs_j per edge; xd, dOut, lse; dxd, record; attn
+        return csr + E * F * b + 2 * N * F * b + 4 * N * H + N * F * b + 8 * N * H + 4 * F
+    if kernel == "bwd_gatv2_cols_main":  # xd_i + dOut_i + record_i per edge; xs; dxs; attn
+        return csr + E * (2 * F * b + 8 * H) + N * F * b + N * F * b + 4 * F
     return None
 
 
-def step_bytes(N, E, H, d, b, backward):
-    tot = algorithmic_bytes("fwd_main", N, E, H, d, b)
-    if backward:
-        tot += algorithmic_bytes("bwd_dq_main", N, E, H, d, b)
-        tot += algorithmic_bytes("bwd_dkdv_main", N, E, H, d, b)
+def step_bytes(N, E, H, d, b, backward, score="dot"):
+    tot = algorithmic_bytes("fwd_main", N, E, H, d, b, score)
+    if backward and score == "gatv2":
+        tot += algorithmic_bytes("bwd_gatv2_rows_main", N, E, H, d, b, score)
+        tot += algorithmic_bytes("bwd_gatv2_cols_main", N, E, H, d, b, score)
+    elif backward:
+        tot += algorithmic_bytes("bwd_dq_main", N, E, H, d, b, score)
+        tot += algorithmic_bytes("bwd_dkdv_main", N, E, H, d, b, score)
     return tot
 
 
@@ -202,6 +213,8 @@ def main():
     N, E, H, d = ip.size - 1, ix.size, w.heads, w.dim
     b = 2 if w.dtype == "bf16" else 4
     scale = float(np.float32(1 / math.sqrt(d))) if w.score == "dot" else 1.0
+    if w.score == "gatv2" and args.cpu_budget > 0:
+        args.cpu_budget = 0  # the oracle baseline leg covers the dot and GAT-style steps
     print(f"[bench] {w.name}: N={N} E={E} H={H} d={d} {w.dtype} {w.score} "
           f"backward={w.backward} (inputs {gen_s:.1f}s)", file=sys.stderr, flush=True)
 
@@ -242,14 +255,26 @@ def main():
     copy_gbps = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    out = torch.empty_like(tens[2])
+    vt = tens[1] if w.score == "gatv2" else tens[2]
+    out = torch.empty_like(vt)
     lse = torch.empty((N, H), dtype=torch.float32, device="cuda")
     fws = torch.empty(max(plan.fwd_workspace_bytes(H, d), 1), dtype=torch.uint8, device="cuda")
-    if w.backward:
+    if w.backward and w.score == "gatv2":
+        dq, dk = torch.empty_like(vt), torch.empty_like(vt)
+        dv = torch.empty((H, d), dtype=torch.float32, device="cuda")
+        bws = torch.empty(ga.bwd_gatv2_workspace_bytes(plan, vt.dtype, H, d), dtype=torch.uint8,
+                          device="cuda")
+    elif w.backward:
         dq, dk, dv = (torch.empty_like(tens[0]) for _ in range(3))
         bws = torch.empty(plan.bwd_workspace_bytes(H, d), dtype=torch.uint8, device="cuda")
 
     def step(backward=w.backward):
+        if w.score == "gatv2":
+            ga.fwd_gatv2(plan, *tens, scale=scale, out=out, lse=lse, workspace=fws)
+            if backward:
+                ga.bwd_gatv2(plan, *tens, tdo, lse, scale=scale, dxd=dq, dxs=dk, dattn=dv,
+                             workspace=bws)
+            return
         ga.fwd(plan, *tens, score=w.score, scale=scale, out=out, lse=lse, workspace=fws)
         if backward:
             ga.bwd(plan, *tens, tdo, lse, scale=scale, dq=dq, dk=dk, dv=dv, workspace=bws)
@@ -275,15 +300,16 @@ def main():
     ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
     # gather floor: the forward's neighbour gathers alone (same graph, same lane pattern)
     sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
-    kv = (tens[1], tens[2]) if w.score == "dot" else (tens[2], tens[2])
+    kv = {"dot": (tens[1], tens[2]), "gat": (tens[2], tens[2]),
+          "gatv2": (tens[1], tens[1])}[w.score]
     ga.gather_probe(plan, *kv, sink=sink)
     ms_gather, _ = timed(lambda: ga.gather_probe(plan, *kv, sink=sink), args.steps)
-    gather_bytes = 2 * E * H * d * b + 4 * E
+    gather_bytes = 2 * E * H * d * b + 4 * E    # the probe gathers two rows per edge
 
     kernels = {}
     for name, (launches, tot) in kt.items():
         per = tot / launches
-        ab = algorithmic_bytes(name, N, E, H, d, b)
+        ab = algorithmic_bytes(name, N, E, H, d, b, w.score)
         kernels[name] = {"launches_per_step": launches / args.steps, "avg_ms": per,
                          "share": tot / (ms_step * args.steps)}
         if ab is not None:
@@ -293,8 +319,8 @@ def main():
     dk_ = kernels[dom]
     ach = dk_["GBps"]
     traffic = measured_traffic(w.name, dom)
-    fwd_bytes = step_bytes(N, E, H, d, b, False)
-    tot_bytes = step_bytes(N, E, H, d, b, w.backward)
+    fwd_bytes = step_bytes(N, E, H, d, b, False, w.score)
+    tot_bytes = step_bytes(N, E, H, d, b, w.backward, w.score)
     fwd_main_ms = kt_fwd["fwd_main"][1] / kt_fwd["fwd_main"][0]
     rec = {
         "metric": "fused graph-attn fwd/bwd edges/sec + achieved HBM GB/s (% of MI355X peak)",
@@ -339,7 +365,7 @@ def main():
         "copy_probe_GBps": copy_gbps,
         "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,
         "workspace_bytes": {"fwd": plan.fwd_workspace_bytes(H, d),
-                            "bwd": plan.bwd_workspace_bytes(H, d) if w.backward else 0,
+                            "bwd": (bws.numel() if w.backward else 0),
                             "edge_score_tensor_would_be": E * H * 4},
     }
     print(json.dumps(rec), flush=True)

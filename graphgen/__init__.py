@@ -207,7 +207,7 @@ class Workload:
     heads: int
     dim: int
     dtype: str                 # "f32" | "bf16"
-    score: str                 # "dot" | "gat"
+    score: str                 # "dot" | "gat" | "gatv2"
     backward: bool
     graph_args: dict = field(default_factory=dict)
     graph_wid: int = 0         # wid whose graph/feature streams this workload reuses (0 = own)
@@ -229,6 +229,8 @@ WORKLOADS = {
                  {"scale": 21, "avg_deg": 30, "a": 0.57, "b": 0.19, "c": 0.19}),
         Workload(5, "chunglu1m_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "dot", True,
                  {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
+        Workload(6, "chunglu1m_gatv2_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "gatv2",
+                 True, {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
     ]
 }
 
@@ -279,10 +281,12 @@ def _make_graph(w: Workload, n: int):
 def make_features(w: Workload, n: int | None = None):
     """Inputs of the forward pass, drawn in a fixed order from the feature stream.
 
-    dot: (q, k, v) each [n, H, d];  gat: (s [n, H] f32, t [n, H] f32, v [n, H, d]).
+    dot: (q, k, v) each [n, H, d];  gat: (s [n, H] f32, t [n, H] f32, v [n, H, d]);
+    gatv2: (xd [n, H, d], xs [n, H, d], attn [H, d] f32 ~ N(0, 1/d)).
     """
     n = w.n if n is None else int(n)
-    return _cached(f"feat_{w.seed_id}_{n}", lambda: _make_features(w, n))
+    tag = "" if w.score != "gatv2" else "_gatv2"
+    return _cached(f"feat{tag}_{w.seed_id}_{n}", lambda: _make_features(w, n))
 
 
 def _make_features(w: Workload, n: int):
@@ -293,6 +297,11 @@ def _make_features(w: Workload, n: int):
         k = normal_features(rng, (n, H, d), w.dtype)
         v = normal_features(rng, (n, H, d), w.dtype)
         return q, k, v
+    if w.score == "gatv2":
+        xd = normal_features(rng, (n, H, d), w.dtype)
+        xs = normal_features(rng, (n, H, d), w.dtype)
+        attn = (rng.standard_normal(size=(H, d), dtype=np.float32) / np.float32(np.sqrt(d)))
+        return xd, xs, attn.astype(np.float32)
     s = rng.standard_normal(size=(n, H), dtype=np.float32)
     t = rng.standard_normal(size=(n, H), dtype=np.float32)
     v = normal_features(rng, (n, H, d), w.dtype)

@@ -265,6 +265,17 @@ def bwd(plan: Plan, q_or_s, k_or_t, v, dout, lse, *, score="dot", scale=None, ne
     return dq, dk, dv
 
 
+def bwd_gatv2_workspace_bytes(plan: Plan, dtype, heads: int, dim: int) -> int:
+    b = c_size_t()
+    graph_attn_bwd_gatv2_workspace_bytes(plan.handle, _dtype_code_of(dtype), heads, dim, byref(b))
+    return int(b.value)
+
+
+def _dtype_code_of(dtype) -> int:
+    import torch
+    return GA_F32 if dtype == torch.float32 else GA_BF16 if dtype == torch.bfloat16 else -1
+
+
 def bwd_gatv2(plan: Plan, xd, xs, attn, dout, lse, *, scale=1.0, neg_slope=0.2, dxd=None,
               dxs=None, dattn=None, workspace=None, stream=None):
     """GATv2 backward from the forward's lse; returns (dxd, dxs [N,H,d], dattn fp32 [H,d])."""

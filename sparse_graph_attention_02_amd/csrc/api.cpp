@@ -160,8 +160,9 @@ Gv2Layout gatv2_layout(const ga_plan* p, const ga::Geometry& g) {
   L.rows = align_up(p->rows.chunk_row.size() * (4 * F + (2 * g.heads + 3) / 4 * 4) *
                     sizeof(float));
   L.cols = align_up(p->cols.chunk_row.size() * 2 * F * sizeof(float));
-  L.da = align_up(size_t(ga::gatv2_da_slots(p, g)) * F * sizeof(float));
-  L.da64 = align_up(size_t(ga::gatv2_reduce_rows()) * F * sizeof(double));
+  const int64_t slots = ga::gatv2_da_slots(p, g);
+  L.da = align_up(size_t(slots) * F * sizeof(float));
+  L.da64 = align_up(size_t(ga::gatv2_reduce_rows(slots)) * F * sizeof(double));
   L.total = L.ld + L.rows + L.cols + L.da + L.da64;
   return L;
 }
@@ -512,7 +513,7 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   }
   if (!p->has_csc) return GA_ERR_NOT_READY;
   const Gv2Layout L = gatv2_layout(p, g);
-  if (!ws || ws_bytes < L.total || !aligned(ws, 16)) return GA_ERR_WORKSPACE;
+  if (L.total > 0 && (!ws || ws_bytes < L.total || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
   if (!p->uploaded) return GA_ERR_NOT_READY;
   if ((s = check_device(p)) != GA_OK) return s;
   // an empty graph still launches the final reduction stage, which writes dattn = 0

@@ -19,7 +19,8 @@
 //                         writes one fp32 partial of da (hub rows: chunk partials, see merge)
 //   bwd_gatv2_rows_merge  hub rows: ordered sums of the chunk partials, then as above (one
 //                         da partial per hub row)
-//   bwd_gatv2_da_reduce   two fixed-order fp64 stages over the da partials -> dattn [H*d]
+//   bwd_gatv2_da_reduce   fixed-order fp64 tree over the da partials (32 rows per block per
+//                         stage, ping-pong buffers) -> dattn [H*d]
 //   bwd_gatv2_cols_main   over transpose columns: dxs_j = scale a sum_i dS_ij g_ij
 //                                                          + sum_i P_ij dout_i
 //   bwd_gatv2_cols_merge  hub columns: ordered sums of partials
@@ -30,8 +31,9 @@
 namespace ga {
 namespace {
 
-constexpr int kItemsPerWave = 16;   // row-pass work items per wavefront (bounds da partials)
-constexpr int kReduceBlocks = 256;  // stage-1 blocks of the da reduction
+constexpr int kItemsPerWave = 16;  // row-pass work items per wavefront (bounds da partials)
+constexpr int kReduceFan = 32;     // rows summed per block in each da reduction stage
+constexpr int kRowsUnroll = 3;     // edges in flight per lane group in the row pass (4 waves/SIMD)
 
 template <typename T, int G, int LH, int U>
 struct BwdV2 : RowIO<T, G, LH> {
@@ -350,17 +352,18 @@ __global__ __launch_bounds__(kBlock) void bwd_gatv2_rows_merge(BwdArgs a, int n_
   K::store_f32(a.ws_da + static_cast<size_t>(n_row_slots + hub) * F, r, da);
 }
 
-// Stage 1: block b sums partial slots [b*per, min((b+1)*per, n)) in fp64, in slot order.
-// Stage 2 (a single block, src = stage-1 output): sums the stage-1 rows in order.
+// One reduction stage: block b sums rows [b*kReduceFan, min((b+1)*kReduceFan, n)) of src
+// (row length F) in row order, in fp64, into row b of dst64 (or into dst32 for the last
+// stage, which has a single block).
 template <typename S>
 __global__ __launch_bounds__(kBlock) void bwd_gatv2_da_reduce(const S* __restrict__ src, int64_t n,
-                                                              int64_t per, int F,
-                                                              double* __restrict__ dst64,
+                                                              int F, double* __restrict__ dst64,
                                                               float* __restrict__ dst32) {
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * per;
-  const int64_t s1 = min(n, s0 + per);
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kReduceFan;
+  const int64_t s1 = min(n, s0 + kReduceFan);
   for (int c = threadIdx.x; c < F; c += kBlock) {
     double acc = 0.0;
+#pragma unroll 8
     for (int64_t sl = s0; sl < s1; ++sl) acc += static_cast<double>(src[sl * F + c]);
     if (dst32)
       dst32[c] = static_cast<float>(acc);
@@ -463,7 +466,7 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   };
   if (row_slots > 0) {
     if (hook) hook("bwd_gatv2_rows_main", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, GA_UNROLL_DQ>),
+    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, kRowsUnroll>),
                        dim3(static_cast<unsigned>((row_slots + kWavesPerBlock - 1) / kWavesPerBlock)),
                        dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_rows_main"))) return e;
@@ -476,18 +479,36 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
     if ((e = done("bwd_gatv2_rows_merge"))) return e;
   }
   {
-    // stage 1 over the partial slots (skipped when there are none), then stage 2, which
-    // always runs so that dattn is written (zeros for a graph without rows)
-    const int64_t per = n_slots > 0 ? (n_slots + kReduceBlocks - 1) / kReduceBlocks : 1;
-    const int64_t nb = (n_slots + per - 1) / per;
+    // fp32 slots -> fp64 rows, then fp64 stages until one block remains; that last stage
+    // always runs, so dattn is written even when there are no slots (zeros)
     if (hook) hook("bwd_gatv2_da_reduce", stream, 1);
-    if (nb > 0)
-      hipLaunchKernelGGL((bwd_gatv2_da_reduce<float>), dim3(static_cast<unsigned>(nb)),
-                         dim3(kBlock), 0, s, a.ws_da, n_slots, per, F, a.ws_da64,
-                         static_cast<float*>(nullptr));
-    hipLaunchKernelGGL((bwd_gatv2_da_reduce<double>), dim3(1), dim3(kBlock), 0, s,
-                       static_cast<const double*>(a.ws_da64), nb, nb > 0 ? nb : 1, F,
-                       static_cast<double*>(nullptr), a.dattn);
+    double* bufA = a.ws_da64;
+    double* bufB = a.ws_da64 + gatv2_reduce_rows_a(n_slots) * F;
+    int64_t n = n_slots;
+    const double* src64 = nullptr;
+    bool first = true;
+    while (true) {
+      const int64_t nb = (n + kReduceFan - 1) / kReduceFan;
+      if (nb <= 1) {
+        if (first)
+          hipLaunchKernelGGL((bwd_gatv2_da_reduce<float>), dim3(1), dim3(kBlock), 0, s, a.ws_da,
+                             n, F, static_cast<double*>(nullptr), a.dattn);
+        else
+          hipLaunchKernelGGL((bwd_gatv2_da_reduce<double>), dim3(1), dim3(kBlock), 0, s, src64, n,
+                             F, static_cast<double*>(nullptr), a.dattn);
+        break;
+      }
+      double* dst = (src64 == bufA) ? bufB : bufA;
+      if (first)
+        hipLaunchKernelGGL((bwd_gatv2_da_reduce<float>), dim3(static_cast<unsigned>(nb)),
+                           dim3(kBlock), 0, s, a.ws_da, n, F, dst, static_cast<float*>(nullptr));
+      else
+        hipLaunchKernelGGL((bwd_gatv2_da_reduce<double>), dim3(static_cast<unsigned>(nb)),
+                           dim3(kBlock), 0, s, src64, n, F, dst, static_cast<float*>(nullptr));
+      src64 = dst;
+      n = nb;
+      first = false;
+    }
     if ((e = done("bwd_gatv2_da_reduce"))) return e;
   }
   const int64_t col_items = items_of(a.cols);
@@ -531,7 +552,14 @@ int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g) {
   return (items + kItemsPerWave - 1) / kItemsPerWave + int64_t(p->rows.hub.size());
 }
 
-int64_t gatv2_reduce_rows() { return kReduceBlocks; }
+// fp64 rows of the two ping-pong buffers of the da reduction: the first stage writes
+// ceil(n / fan) rows into buffer A, the second ceil(n / fan^2) into buffer B, and later
+// stages alternate within those sizes.
+int64_t gatv2_reduce_rows_a(int64_t n_slots) { return (n_slots + kReduceFan - 1) / kReduceFan; }
+int64_t gatv2_reduce_rows(int64_t n_slots) {
+  const int64_t a = gatv2_reduce_rows_a(n_slots);
+  return a + (a + kReduceFan - 1) / kReduceFan;
+}
 
 int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
                      TimerHook hook) {

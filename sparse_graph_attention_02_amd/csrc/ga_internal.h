@@ -139,9 +139,11 @@ int launch_bwd_gat(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* strea
 // GATv2: q/k/dq/dk carry xd/xs/dxd/dxs ([N, H, d]); attn/dattn/ws_da/ws_da64 set.
 int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
                      TimerHook hook);
-// da partial slots of the GATv2 row pass and the rows of its first reduction stage.
+// da partial slots of the GATv2 row pass, and the fp64 rows of its reduction buffers
+// (total, and the first buffer's share).
 int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g);
-int64_t gatv2_reduce_rows();
+int64_t gatv2_reduce_rows(int64_t n_slots);
+int64_t gatv2_reduce_rows_a(int64_t n_slots);
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
 int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
                         void* sink, void* stream, TimerHook hook);
