@@ -207,7 +207,7 @@ class Workload:
     heads: int
     dim: int
     dtype: str                 # "f32" | "bf16"
-    score: str                 # "dot" | "gat" | "gatv2"
+    score: str                 # "dot" | "gat" | "gatv2" | "max" | "min" (reductions)
     backward: bool
     graph_args: dict = field(default_factory=dict)
     graph_wid: int = 0         # wid whose graph/feature streams this workload reuses (0 = own)
@@ -230,6 +230,8 @@ WORKLOADS = {
         Workload(5, "chunglu1m_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "dot", True,
                  {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
         Workload(6, "chunglu1m_gatv2_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "gatv2",
+                 True, {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
+        Workload(7, "chunglu1m_max_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "max",
                  True, {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
     ]
 }
@@ -282,10 +284,11 @@ def make_features(w: Workload, n: int | None = None):
     """Inputs of the forward pass, drawn in a fixed order from the feature stream.
 
     dot: (q, k, v) each [n, H, d];  gat: (s [n, H] f32, t [n, H] f32, v [n, H, d]);
-    gatv2: (xd [n, H, d], xs [n, H, d], attn [H, d] f32 ~ N(0, 1/d)).
+    gatv2: (xd [n, H, d], xs [n, H, d], attn [H, d] f32 ~ N(0, 1/d));
+    max / min: (x [n, H, d],) (the first draw of the stream, like q).
     """
     n = w.n if n is None else int(n)
-    tag = "" if w.score != "gatv2" else "_gatv2"
+    tag = {"gatv2": "_gatv2", "max": "_red", "min": "_red"}.get(w.score, "")
     return _cached(f"feat{tag}_{w.seed_id}_{n}", lambda: _make_features(w, n))
 
 
@@ -297,6 +300,8 @@ def _make_features(w: Workload, n: int):
         k = normal_features(rng, (n, H, d), w.dtype)
         v = normal_features(rng, (n, H, d), w.dtype)
         return q, k, v
+    if w.score in ("max", "min"):
+        return (normal_features(rng, (n, H, d), w.dtype),)
     if w.score == "gatv2":
         xd = normal_features(rng, (n, H, d), w.dtype)
         xs = normal_features(rng, (n, H, d), w.dtype)

@@ -1,5 +1,6 @@
 /*
- * graph_attn.h -- C ABI of the fused CSR graph-attention library for AMD MI355X (gfx950).
+ * graph_attn.h -- C ABI of the fused CSR graph-attention library for AMD MI355X (gfx950),
+ * with the degree-aware min / max neighbourhood reduction beside it (end of this file).
  *
  * What the library computes is the attention-based layer family of "On Efficient Scaling
  * of GNNs via IO-Aware Layers Implementations" (gist.science explainer of arXiv
@@ -226,6 +227,50 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t head
                                const float* attn, const void* dout, const float* lse, void* dxd,
                                void* dxs, float* dattn, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* ---- Neighbourhood reduction (min / max pooling) -------------------------------------
+ * The reduction-based layer family of the same pages (Technical Summary > Methodology,
+ * reduction-based layers: a per-edge message reduced over each node's neighbourhood by
+ * min or max, rows split by degree into light rows handled feature-parallel and heavy
+ * rows reduced as parallel edge chunks whose partial results combine as (value, index)
+ * pairs). The message of edge (i <- j) is the source row x[j] itself; every one of the
+ * F feature elements is reduced separately:
+ *     out[i,c] = max_j x[j,c]  (or min)     arg[i,c] = the source id j attaining it
+ * Equal values go to the smallest source id, so arg does not depend on the order of a
+ * row's neighbours. out[i,c] is x[arg[i,c],c] bit for bit (values compare as numbers:
+ * -0 equals +0). A row with no neighbours gives out = 0 and arg = -1. NaN never wins a
+ * comparison (a row whose candidates are all NaN reads as empty); inputs are meant to be
+ * free of NaN. x, out, dout, dx: [N, F] of `dtype`, F*sizeof(dtype) one of 64, 128, 256,
+ * 512 or 1024 bytes; arg int32 [N, F]; every pointer 16-byte aligned. Results are
+ * bitwise reproducible (no atomics; the backward's sums run in a fixed order). */
+typedef enum { GA_REDUCE_MAX = 0, GA_REDUCE_MIN = 1 } ga_reduce;
+
+/* Workspace of graph_attn_reduce_fwd: per hub-row chunk, fp32 values and int32 ids of its
+ * partial result, two sections of n_row_chunks*F*4 bytes, each 256-byte aligned (0 when
+ * the plan has no hub rows; the workspace may then be NULL). */
+ga_status graph_attn_reduce_fwd_workspace_bytes(const ga_plan* plan, int32_t features,
+                                                size_t* bytes);
+
+/* Forward: out and arg for every row (see above). The plan must be uploaded. */
+ga_status graph_attn_reduce_fwd(const ga_plan* plan, ga_reduce op, ga_dtype dtype,
+                                int32_t features, const void* x, void* out, int32_t* arg,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of graph_attn_reduce_bwd: fp32 partial sums of the hub-column chunks,
+ * n_col_chunks*F*4 bytes (0 when the transpose has no hub columns; NULL allowed then). */
+ga_status graph_attn_reduce_bwd_workspace_bytes(const ga_plan* plan, int32_t features,
+                                                size_t* bytes);
+
+/* Backward: dx[j,c] = sum of dout[i,c] over the destinations i with arg[i,c] = j (each
+ * distinct i once; a parallel edge does not count twice), the gradient of the forward
+ * routed to the element that won. arg is the forward's output (entries -1 or a node id;
+ * arg is only compared with column ids, never used as an address, so an entry that is
+ * neither simply matches nothing). Computed over
+ * the plan's cached transpose, one pass per source column, sums in fp32 (fp64 when dtype
+ * is fp32) in a fixed order. Needs a plan with the transpose, uploaded. */
+ga_status graph_attn_reduce_bwd(const ga_plan* plan, ga_dtype dtype, int32_t features,
+                                const int32_t* arg, const void* dout, void* dx,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Kernel timers (tracing). When enabled, every kernel the library launches is bracketed
  * by two hipEvents recorded on its stream; graph_attn_timer_read synchronises those

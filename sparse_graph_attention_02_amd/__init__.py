@@ -10,10 +10,14 @@ current HIP stream.  ``capi`` holds the raw C entry points under their C names.
     out, lse = fwd(plan, q, k, v)         # dot score, scale 1/sqrt(d)
     dq, dk, dv = bwd(plan, q, k, v, dout, lse)
     out, lse = fwd(plan, s, t, v, score="gat")
+    out, arg = reduce_fwd(plan, x, op="max")  # neighbourhood max pooling and its arg
+    dx = reduce_bwd(plan, arg, dout)
 
 Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
 Summary > Methodology, attention-based layers (fused score -> online softmax ->
-aggregation; backward recomputes weights from the per-node log-sum-exp).
+aggregation; backward recomputes weights from the per-node log-sum-exp) and
+reduction-based layers (degree-aware min / max pooling, heavy rows as edge chunks whose
+partials combine as (value, index) pairs).
 """
 from __future__ import annotations
 
@@ -24,7 +28,10 @@ from ctypes import POINTER, byref, c_int32, c_int64, c_size_t, c_void_p
 import numpy as np
 
 from . import capi
-from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,  # noqa: F401
+from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
+                   GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,
+                   graph_attn_reduce_bwd, graph_attn_reduce_bwd_workspace_bytes,
+                   graph_attn_reduce_fwd, graph_attn_reduce_fwd_workspace_bytes,
                    graph_attn_bwd, graph_attn_bwd_gatv2, graph_attn_bwd_gatv2_workspace_bytes,
                    graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
                    graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_workspace_bytes,
@@ -37,7 +44,8 @@ from .capi import (GA_BF16, GA_F32, GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError, 
                    graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
-__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention", "copy_probe", "timers", "default_opts",
+__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention", "reduce_fwd",
+           "reduce_bwd", "graph_reduce", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
 
@@ -332,6 +340,95 @@ def graph_attention(plan: Plan, q, k, v, scale=None):
     if _FN is None:
         _FN = _autograd_fn()
     return _FN.apply(q, k, v, plan, scale)
+
+
+def _features_view(t, name, device=None):
+    """[N, ...] contiguous tensor -> (N, F)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError(f"{name} must live on {device or 'a GPU'}")
+    if not t.is_contiguous() or t.dim() < 1:
+        raise ValueError(f"{name} must be a contiguous [N, ...] tensor")
+    return t.shape[0], (t.numel() // t.shape[0] if t.shape[0] else int(np.prod(t.shape[1:])))
+
+
+def reduce_fwd(plan: Plan, x, *, op="max", out=None, arg=None, workspace=None, stream=None):
+    """Neighbourhood max (or min) of the source rows, elementwise, and the winning source
+    id per element (smallest id on ties; empty rows give 0 and -1).  x: [N, ...] fp32 or
+    bf16; returns (out like x, arg int32 of x's shape)."""
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    code = {"max": GA_REDUCE_MAX, "min": GA_REDUCE_MIN}.get(op)
+    if code is None:
+        raise ValueError(op)
+    N, F = _features_view(x, "x")
+    if N != plan.n_nodes:
+        raise ValueError(f"x has {N} rows, the graph {plan.n_nodes} nodes")
+    out = torch.empty_like(x) if out is None else out
+    arg = torch.empty(x.shape, dtype=torch.int32, device=x.device) if arg is None else arg
+    _need(out, "out", x.shape, x.dtype, x.device)
+    _need(arg, "arg", x.shape, torch.int32, x.device)
+    b = c_size_t()
+    graph_attn_reduce_fwd_workspace_bytes(plan.handle, F, byref(b))
+    ws, wsb = _workspace(int(b.value), x.device, workspace)
+    with torch.cuda.device(x.device):
+        graph_attn_reduce_fwd(plan.handle, code, _dtype_code(x), F, _ptr(x), _ptr(out),
+                              _ptr(arg), _ptr(ws), wsb, _stream(stream))
+    return out, arg
+
+
+def reduce_bwd(plan: Plan, arg, dout, *, dx=None, workspace=None, stream=None):
+    """Gradient of reduce_fwd: dx[j] collects dout[i] where arg[i] == j (each destination
+    once).  The plan needs the transpose (build_csc=True)."""
+    import torch
+    if plan.device_buffer is None:
+        raise RuntimeError("plan is not uploaded")
+    N, F = _features_view(dout, "dout")
+    if N != plan.n_nodes:
+        raise ValueError(f"dout has {N} rows, the graph {plan.n_nodes} nodes")
+    _need(arg, "arg", dout.shape, torch.int32, dout.device)
+    dx = torch.empty_like(dout) if dx is None else dx
+    _need(dx, "dx", dout.shape, dout.dtype, dout.device)
+    b = c_size_t()
+    graph_attn_reduce_bwd_workspace_bytes(plan.handle, F, byref(b))
+    ws, wsb = _workspace(int(b.value), dout.device, workspace)
+    with torch.cuda.device(dout.device):
+        graph_attn_reduce_bwd(plan.handle, _dtype_code(dout), F, _ptr(arg), _ptr(dout),
+                              _ptr(dx), _ptr(ws), wsb, _stream(stream))
+    return dx
+
+
+def _reduce_fn():
+    import torch
+
+    class _GraphReduce(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, plan, op):
+            out, arg = reduce_fwd(plan, x.contiguous(), op=op)
+            ctx.save_for_backward(arg)
+            ctx.plan = plan
+            ctx.mark_non_differentiable(arg)
+            return out, arg
+
+        @staticmethod
+        def backward(ctx, g, _garg):
+            (arg,) = ctx.saved_tensors
+            return reduce_bwd(ctx.plan, arg, g.contiguous()), None, None
+
+    return _GraphReduce
+
+
+_RFN = None
+
+
+def graph_reduce(plan: Plan, x, op="max"):
+    """Neighbourhood max / min pooling as a differentiable torch op; returns (out, arg)."""
+    global _RFN
+    if _RFN is None:
+        _RFN = _reduce_fn()
+    return _RFN.apply(x, plan, op)
 
 
 def copy_probe(dst, src, stream=None):

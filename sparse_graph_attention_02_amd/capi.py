@@ -19,6 +19,7 @@ GA_OK, GA_ERR_INVALID_ARG, GA_ERR_BAD_GRAPH, GA_ERR_UNSUPPORTED = 0, 1, 2, 3
 GA_ERR_WORKSPACE, GA_ERR_NOT_READY, GA_ERR_HIP, GA_ERR_HOST_ALLOC = 4, 5, 6, 7
 GA_F32, GA_BF16 = 0, 1
 GA_SCORE_DOT, GA_SCORE_GAT = 0, 1
+GA_REDUCE_MAX, GA_REDUCE_MIN = 0, 1
 
 
 class ga_plan_opts(Structure):
@@ -74,6 +75,12 @@ _SIGS = {
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
+    "graph_attn_reduce_fwd_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
+    "graph_attn_reduce_fwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+    "graph_attn_reduce_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
+    "graph_attn_reduce_bwd": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]),
     "graph_attn_timer_enable": (c_int32, [c_int32]),
     "graph_attn_timer_reset": (c_int32, []),
     "graph_attn_timer_count": (c_int32, []),
@@ -146,6 +153,10 @@ graph_attn_bwd_workspace_bytes = _wrap("graph_attn_bwd_workspace_bytes")
 graph_attn_bwd = _wrap("graph_attn_bwd")
 graph_attn_bwd_gatv2_workspace_bytes = _wrap("graph_attn_bwd_gatv2_workspace_bytes")
 graph_attn_bwd_gatv2 = _wrap("graph_attn_bwd_gatv2")
+graph_attn_reduce_fwd_workspace_bytes = _wrap("graph_attn_reduce_fwd_workspace_bytes")
+graph_attn_reduce_fwd = _wrap("graph_attn_reduce_fwd")
+graph_attn_reduce_bwd_workspace_bytes = _wrap("graph_attn_reduce_bwd_workspace_bytes")
+graph_attn_reduce_bwd = _wrap("graph_attn_reduce_bwd")
 graph_attn_timer_enable = _wrap("graph_attn_timer_enable")
 graph_attn_timer_reset = _wrap("graph_attn_timer_reset")
 graph_attn_timer_count = _wrap("graph_attn_timer_count")

@@ -167,6 +167,24 @@ Gv2Layout gatv2_layout(const ga_plan* p, const ga::Geometry& g) {
   return L;
 }
 
+// Reduction geometry: F elements of `dt` are G = F*size/16 lanes (4..64, a power of two).
+ga_status reduce_geometry(ga_dtype dt, int32_t features, int* G) {
+  if (dt != GA_F32 && dt != GA_BF16) return GA_ERR_INVALID_ARG;
+  if (features < 1) return GA_ERR_INVALID_ARG;
+  const int64_t row_bytes = int64_t(features) * (dt == GA_F32 ? 4 : 2);
+  if (row_bytes % 16 || row_bytes > 1024) return GA_ERR_UNSUPPORTED;
+  *G = static_cast<int>(row_bytes / 16);
+  return ga::reduce_supported(dt, *G) ? GA_OK : GA_ERR_UNSUPPORTED;
+}
+
+size_t reduce_fwd_ws_bytes(const ga_plan* p, int32_t features) {
+  return 2 * align_up(p->rows.chunk_row.size() * size_t(features) * 4);
+}
+
+size_t reduce_bwd_ws_bytes(const ga_plan* p, int32_t features) {
+  return align_up(p->cols.chunk_row.size() * size_t(features) * 4);
+}
+
 ga_status check_device(const ga_plan* p) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
@@ -544,6 +562,85 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
   const int rc = ga::launch_bwd_gatv2(dtype, g, args, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_reduce_fwd_workspace_bytes(const ga_plan* p, int32_t features,
+                                                size_t* bytes) {
+  if (!p || !bytes || features < 1) return GA_ERR_INVALID_ARG;
+  *bytes = reduce_fwd_ws_bytes(p, features);
+  return GA_OK;
+}
+
+ga_status graph_attn_reduce_bwd_workspace_bytes(const ga_plan* p, int32_t features,
+                                                size_t* bytes) {
+  if (!p || !bytes || features < 1) return GA_ERR_INVALID_ARG;
+  *bytes = reduce_bwd_ws_bytes(p, features);
+  return GA_OK;
+}
+
+ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
+                                int32_t features, const void* x, void* out, int32_t* arg,
+                                void* ws, size_t ws_bytes, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  if (op != GA_REDUCE_MAX && op != GA_REDUCE_MIN) return GA_ERR_INVALID_ARG;
+  int G = 0;
+  ga_status s = reduce_geometry(dtype, features, &G);
+  if (s != GA_OK) return s;
+  if (p->n > 0) {
+    if ((s = check_ptr(x, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
+        (s = check_ptr(arg, 16)) != GA_OK)
+      return s;
+  }
+  const size_t need = reduce_fwd_ws_bytes(p, features);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+  ga::RedArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.rows = p->d_rows;
+  args.x = x;
+  args.out = out;
+  args.arg = arg;
+  if (need > 0) {
+    args.ws_val = static_cast<float*>(ws);
+    args.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
+  }
+  const int rc = ga::launch_reduce(dtype, false, op == GA_REDUCE_MAX ? ga::kReduceMax
+                                                                     : ga::kReduceMin,
+                                   G, args, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t features,
+                                const int32_t* arg, const void* dout, void* dx, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  int G = 0;
+  ga_status s = reduce_geometry(dtype, features, &G);
+  if (s != GA_OK) return s;
+  if (p->n > 0) {
+    if ((s = check_ptr(arg, 16)) != GA_OK || (s = check_ptr(dout, 16)) != GA_OK ||
+        (s = check_ptr(dx, 16)) != GA_OK)
+      return s;
+  }
+  if (!p->has_csc) return GA_ERR_NOT_READY;
+  const size_t need = reduce_bwd_ws_bytes(p, features);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+  ga::RedArgs args{};
+  args.colptr = p->d_colptr;
+  args.rowidx = p->d_rowidx;
+  args.cols = p->d_cols;
+  args.arg_in = arg;
+  args.dout = dout;
+  args.dx = dx;
+  args.ws_sum = need > 0 ? static_cast<float*>(ws) : nullptr;
+  const int rc = ga::launch_reduce(dtype, true, ga::kReduceMax, G, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
 

@@ -144,6 +144,29 @@ int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* str
 int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g);
 int64_t gatv2_reduce_rows(int64_t n_slots);
 int64_t gatv2_reduce_rows_a(int64_t n_slots);
+// Neighbourhood min / max reduction (reduce.hip). Rows of F elements are G lanes x 16 B.
+enum ReduceOp { kReduceMax = 0, kReduceMin = 1 };
+struct RedArgs {
+  const int32_t* indptr;
+  const int32_t* indices;
+  const int32_t* colptr;
+  const int32_t* rowidx;
+  DevBins rows, cols;
+  // forward
+  const void* x;     // [N, F]
+  void* out;         // [N, F]
+  int32_t* arg;      // [N, F]
+  float* ws_val;     // hub chunk partials [n_row_chunks][F]: values
+  int32_t* ws_idx;   //                                      and ids
+  // backward
+  const int32_t* arg_in;  // [N, F] (the forward's arg)
+  const void* dout;       // [N, F]
+  void* dx;               // [N, F]
+  float* ws_sum;          // hub column partial sums [n_col_chunks][F]
+};
+bool reduce_supported(ga_dtype dt, int G);
+int launch_reduce(ga_dtype dt, bool backward, int op, int G, const RedArgs& a, void* stream,
+                  TimerHook hook);
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
 int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
                         void* sink, void* stream, TimerHook hook);

@@ -258,3 +258,74 @@ def test_default_opts():
     o = default_opts()
     assert o["light_max_deg"] <= o["hub_min_deg_exclusive"] and o["hub_chunk"] >= 1
     assert o["build_csc"] == 1
+
+
+def _rfwd(p, op=capi.GA_REDUCE_MAX, dtype=capi.GA_BF16, F=256, ptrs=None, ws=FAKE, wsb=1 << 30):
+    ptrs = ptrs or [FAKE] * 3
+    return capi.raw_status("graph_attn_reduce_fwd", p.handle if p else None, op, dtype, F,
+                           *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb, None)
+
+
+def _rbwd(p, dtype=capi.GA_BF16, F=256, ptrs=None, ws=FAKE, wsb=1 << 30):
+    ptrs = ptrs or [FAKE] * 3
+    return capi.raw_status("graph_attn_reduce_bwd", p.handle if p else None, dtype, F,
+                           *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb, None)
+
+
+def _rws(p, fn, F):
+    b = c_size_t()
+    assert capi.raw_status(fn, p.handle, F, byref(b)) == capi.GA_OK
+    return b.value
+
+
+def test_reduce_argument_checks_before_any_hip_call():
+    rng = np.random.default_rng(1)
+    src = np.concatenate([rng.integers(0, 64, 200), np.full(300, 9), rng.integers(0, 64, 300)])
+    dst = np.concatenate([rng.integers(0, 64, 200), rng.integers(0, 64, 300), np.full(300, 5)])
+    ip, ix = gg.csr_from_edges(64, src, dst)     # node 5: hub row, node 9: hub column
+    p = Plan(ip, ix, light_max_deg=4, hub_min_deg_exclusive=64, hub_chunk=32)
+    info = p.info()
+    al = lambda x: (x + 255) // 256 * 256
+    assert info["n_row_chunks"] > 0 and info["n_col_chunks"] > 0
+    # declared workspace formulas
+    for F in (16, 64, 256, 512):
+        assert _rws(p, "graph_attn_reduce_fwd_workspace_bytes", F) == \
+            2 * al(info["n_row_chunks"] * F * 4)
+        assert _rws(p, "graph_attn_reduce_bwd_workspace_bytes", F) == \
+            al(info["n_col_chunks"] * F * 4)
+    nfw = _rws(p, "graph_attn_reduce_fwd_workspace_bytes", 256)
+    nbw = _rws(p, "graph_attn_reduce_bwd_workspace_bytes", 256)
+    assert _rfwd(None) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, op=2) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, dtype=5) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, F=0) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, F=12) == capi.GA_ERR_UNSUPPORTED               # 24-byte rows
+    assert _rfwd(p, F=1024) == capi.GA_ERR_UNSUPPORTED             # 2 KB rows
+    assert _rfwd(p, F=24) == capi.GA_ERR_UNSUPPORTED               # 48 B: 3 lanes
+    assert _rfwd(p, dtype=capi.GA_F32, F=8) == capi.GA_ERR_UNSUPPORTED  # 32 B: 2 lanes
+    for i in range(3):
+        ptrs = [FAKE] * 3
+        ptrs[i] = 0
+        assert _rfwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
+        ptrs[i] = FAKE + 8
+        assert _rfwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, ws=0) == capi.GA_ERR_WORKSPACE
+    assert _rfwd(p, wsb=nfw - 1) == capi.GA_ERR_WORKSPACE
+    assert _rfwd(p, wsb=nfw) == capi.GA_ERR_NOT_READY               # valid, not uploaded
+    assert _rfwd(p, op=capi.GA_REDUCE_MIN, dtype=capi.GA_F32, F=64) == capi.GA_ERR_NOT_READY
+    # backward
+    assert _rbwd(None) == capi.GA_ERR_INVALID_ARG
+    assert _rbwd(p, F=12) == capi.GA_ERR_UNSUPPORTED
+    for i in range(3):
+        ptrs = [FAKE] * 3
+        ptrs[i] = 0
+        assert _rbwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
+    assert _rbwd(p, wsb=nbw - 1) == capi.GA_ERR_WORKSPACE
+    assert _rbwd(p, wsb=nbw) == capi.GA_ERR_NOT_READY
+    assert _rbwd(Plan(ip, ix, build_csc=False)) == capi.GA_ERR_NOT_READY
+    # a graph without hub rows needs no workspace, and NULL is accepted for it
+    q = Plan(*gg.csr_from_edges(4, [0, 1], [1, 2]))
+    assert _rws(q, "graph_attn_reduce_fwd_workspace_bytes", 256) == 0
+    assert _rws(q, "graph_attn_reduce_bwd_workspace_bytes", 256) == 0
+    assert _rfwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY
+    assert _rbwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY

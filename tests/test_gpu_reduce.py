@@ -1,0 +1,220 @@
+"""GPU parity of the min / max neighbourhood reduction: the HIP path (through the C ABI)
+against the fp64 oracle on the same seeded inputs.
+
+The forward is index and selection work, so out and arg must be bit-exact (out bit
+patterns included, which covers the sign of zero and infinities).  The backward sums
+gradients, so dx is held to the float criteria of tests/gpu_util.py.  Every test prints
+the case it is about to run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import graphgen as gg
+from oracle import planner as P
+from oracle import reduction as R
+from sparse_graph_attention_02_amd import Plan, graph_reduce, reduce_bwd, reduce_fwd
+from tests.gpu_util import check, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X")
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def bits(t):
+    """Raw bit patterns of a GPU tensor (bf16 -> int16, fp32 -> int32)."""
+    t = t.detach().cpu()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).numpy()
+
+
+def oracle_bits(vals, dtype):
+    v32 = np.asarray(vals, np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return gg.f32_to_bf16_bits(v32).view(np.int16)   # exact: values are bf16 already
+    return v32.view(np.int32)
+
+
+def fwd_exact(tag, ip, ix, x, dtype, op, rows=None, **plan_kw):
+    say(tag, op, "N", ip.size - 1, "E", ix.size, "shape", x.shape, dtype, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    out, arg = reduce_fwd(plan, dev(x), op=op)
+    torch.cuda.synchronize()
+    rows = np.arange(ip.size - 1) if rows is None else np.asarray(rows)
+    ro, ra = R.reduce_rows(ip, ix, x, rows, op)
+    rt = torch.from_numpy(rows).cuda()
+    F = ra.shape[1]
+    ga = arg[rt].reshape(len(rows), F).cpu().numpy()
+    bad = ga != ra
+    assert not bad.any(), f"{tag}: {bad.sum()} args differ; first at " \
+                          f"{np.argwhere(bad)[0]}: got {ga[bad][0]} ref {ra[bad][0]}"
+    gb = bits(out[rt].reshape(len(rows), F))
+    assert np.array_equal(gb, oracle_bits(ro, dtype)), f"{tag}: out bits differ"
+    return plan, out, arg, ra
+
+
+def bwd_parity(tag, plan, ip, ix, arg, ref_arg, dout, dtype):
+    """The GPU backward on the GPU forward's arg; the oracle backward on its own arg (the
+    two args were just shown to be identical)."""
+    say(tag, "backward", "N", ip.size - 1, "E", ix.size, dtype)
+    dx = reduce_bwd(plan, arg, dev(dout))
+    torch.cuda.synchronize()
+    ref = R.reduce_backward(ref_arg, dout, ip.size - 1)
+    return dx, check(f"{tag} dx", host64(dx).reshape(ref.shape), ref, dtype)
+
+
+SMALL_BINS = dict(light_max_deg=4, hub_min_deg_exclusive=9, hub_chunk=3)
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("bins", [{}, SMALL_BINS])
+def test_er2k_f32_every_row(op, bins):
+    w = gg.WORKLOADS["er2k_dot_f32"]
+    ip, ix = gg.make_graph(w)
+    x = gg.make_features(w)[0]                     # [2000, 1, 32] fp32: 128-byte rows
+    plan, out, arg, ra = fwd_exact("er2k f32", ip, ix, x, "f32", op, **bins)
+    dout = gg.make_features(w)[2]
+    bwd_parity("er2k f32", plan, ip, ix, arg, ra, dout, "f32")
+
+
+@pytest.mark.parametrize("tl,th,c", [(8, 64, 32), (16, 1024, 512), (0, 0, 5)])
+def test_chunglu20k_bf16_every_row_and_backward(tl, th, c):
+    w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    (x,) = gg.make_features(w, n=20_000)
+    dout = gg.make_dout(w, n=20_000)
+    for op in ("max", "min"):
+        plan, out, arg, ra = fwd_exact("chunglu20k bf16", ip, ix, x, "bf16", op,
+                                       light_max_deg=tl, hub_min_deg_exclusive=th, hub_chunk=c)
+        info = plan.info()
+        assert info["n_row_hub"] > 0 and info["n_col_hub"] > 0
+        bwd_parity(f"chunglu20k bf16 {op}", plan, ip, ix, arg, ra, dout, "bf16")
+
+
+@pytest.mark.parametrize("dtype,F", [("f32", 16), ("f32", 32), ("f32", 64), ("f32", 128),
+                                     ("f32", 256), ("bf16", 32), ("bf16", 64), ("bf16", 128),
+                                     ("bf16", 256), ("bf16", 512)])
+def test_every_row_width(dtype, F):
+    rng = np.random.default_rng(F)
+    ip, ix = gg.random_multigraph(600, 4000, rng, hub_rows=(3, 77), hub_deg=700)
+    x = gg.normal_features(rng, (600, F), dtype)
+    dout = gg.normal_features(rng, (600, F), dtype)
+    for op in ("max", "min"):
+        plan, out, arg, ra = fwd_exact(f"width {F}", ip, ix, x, dtype, op, light_max_deg=4,
+                                       hub_min_deg_exclusive=64, hub_chunk=40)
+        bwd_parity(f"width {F} {op}", plan, ip, ix, arg, ra, dout, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ties_signed_zeros_and_infinities(dtype):
+    # values on a coarse grid (ties everywhere), with -0.0, +0.0, -inf and +inf mixed in,
+    # on a multigraph with many parallel edges and neighbour lists in random order
+    rng = np.random.default_rng(11)
+    n, F = 300, 64
+    ip, ix = gg.random_multigraph(n, 6000, rng, hub_rows=(7,), hub_deg=900)
+    ix = ix.copy()
+    for i in range(n):
+        rng.shuffle(ix[ip[i]:ip[i + 1]])
+    xv = rng.integers(-2, 3, size=(n, F)).astype(np.float32)
+    special = np.array([-0.0, 0.0, -np.inf, np.inf], np.float32)
+    pick = rng.random((n, F)) < 0.15
+    xv[pick] = special[rng.integers(0, 4, pick.sum())]
+    x = gg.f32_to_bf16_bits(xv) if dtype == "bf16" else xv
+    for op in ("max", "min"):
+        for bins in ({}, dict(light_max_deg=2, hub_min_deg_exclusive=20, hub_chunk=7)):
+            plan, out, arg, ra = fwd_exact(f"ties {dtype}", ip, ix, x, dtype, op, **bins)
+            # backward: each parallel edge is one variable; gradient finite everywhere
+            dout = gg.normal_features(rng, (n, F), dtype)
+            bwd_parity(f"ties {dtype} {op}", plan, ip, ix, arg, ra, dout, dtype)
+
+
+def test_empty_rows_and_graphs():
+    rng = np.random.default_rng(5)
+    ip, ix = gg.random_multigraph(500, 300, rng, self_loops=False)   # many empty rows
+    assert (np.diff(ip) == 0).sum() > 100
+    x = gg.normal_features(rng, (500, 128), "bf16")
+    dout = gg.normal_features(rng, (500, 128), "bf16")
+    for op in ("max", "min"):
+        plan, out, arg, ra = fwd_exact("empty rows", ip, ix, x, "bf16", op)
+        empty = torch.from_numpy(np.diff(ip) == 0).cuda()
+        assert (arg[empty] == -1).all() and (out[empty] == 0).all()
+        dx, _ = bwd_parity("empty rows", plan, ip, ix, arg, ra, dout, "bf16")
+        nosrc = torch.from_numpy(np.bincount(ix, minlength=500) == 0).cuda()
+        assert (dx[nosrc] == 0).all()
+    # nodes but no edges: every row empty, every column empty
+    say("no edges")
+    plan = Plan(np.zeros(9, np.int32), np.zeros(0, np.int32)).upload()
+    xt = torch.randn(8, 64, device="cuda")
+    out, arg = reduce_fwd(plan, xt, op="max")
+    dx = reduce_bwd(plan, arg, torch.randn(8, 64, device="cuda"))
+    assert (out == 0).all() and (arg == -1).all() and (dx == 0).all()
+    # no nodes at all
+    say("no nodes")
+    plan = Plan(np.zeros(1, np.int32), np.zeros(0, np.int32)).upload()
+    z = torch.zeros((0, 64), device="cuda")
+    out, arg = reduce_fwd(plan, z)
+    assert out.shape == (0, 64) and reduce_bwd(plan, arg, z).shape == (0, 64)
+
+
+def test_deterministic_and_autograd():
+    w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    (x,) = gg.make_features(w, n=20_000)
+    say("determinism and autograd, chunglu20k bf16")
+    plan = Plan(ip, ix, light_max_deg=8, hub_min_deg_exclusive=64, hub_chunk=32).upload()
+    xt = dev(x).float().requires_grad_(True)
+    g = torch.randn_like(xt)
+    out, arg = graph_reduce(plan, xt, "max")
+    out.backward(g)
+    dx1 = reduce_bwd(plan, arg, g)
+    assert torch.equal(xt.grad, dx1)
+    out2, arg2 = reduce_fwd(plan, xt.detach(), op="max")
+    dx2 = reduce_bwd(plan, arg2, g)
+    assert torch.equal(out, out2) and torch.equal(arg, arg2) and torch.equal(dx1, dx2)
+
+
+@pytest.mark.slow
+def test_full_chunglu1m_sampled():
+    """Full workload size: the forward on sampled rows (hub, medium and light), the
+    backward on sampled columns (one of them a hub column), against the oracle computed
+    row by row; and the gradient-mass identity over the whole graph."""
+    w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
+    ip, ix = gg.make_graph(w)
+    (x,) = gg.make_features(w)
+    dout = gg.make_dout(w)
+    N = ip.size - 1
+    deg = np.diff(ip)
+    rng = np.random.default_rng(0)
+    hub_rows = np.argsort(-deg)[:3]
+    med = rng.choice(np.nonzero((deg > 16) & (deg <= 1024))[0], 40, replace=False)
+    light = rng.choice(np.nonzero(deg <= 16)[0], 40, replace=False)
+    rows = np.concatenate([hub_rows, med, light])
+    plan, out, arg, _ = fwd_exact("chunglu1m bf16 sampled", ip, ix, x, "bf16", "max",
+                                  rows=rows)
+    say("chunglu1m backward sampled columns")
+    dx = reduce_bwd(plan, arg, dev(dout))
+    torch.cuda.synchronize()
+    colptr, rowidx = P.transpose(ip, ix)
+    odeg = np.diff(colptr)
+    hubc = np.nonzero((odeg > 1024) & (odeg < 3000))[0][:1]
+    cols = np.concatenate([hubc, rng.choice(np.nonzero((odeg > 16) & (odeg <= 200))[0], 5,
+                                            replace=False),
+                           rng.choice(np.nonzero(odeg <= 16)[0], 10, replace=False)])
+    ref, rrows, rarg = R.grad_cols_sampled(ip, ix, colptr, rowidx, x, dout, cols, "max")
+    # the GPU's args of every row that feeds these columns equal the oracle's
+    assert np.array_equal(arg[torch.from_numpy(rrows).cuda()].reshape(len(rrows), -1)
+                          .cpu().numpy(), rarg)
+    ct = torch.from_numpy(cols).cuda()
+    check("chunglu1m dx sampled", host64(dx[ct]).reshape(ref.shape), ref, "bf16")
+    # every (row, element) with a neighbour routes its gradient to exactly one source
+    tot = host64(dx).reshape(N, -1).sum(0)
+    dref = gg.bf16_bits_to_f32(dout).reshape(N, -1).astype(np.float64)[deg > 0].sum(0)
+    scale = np.abs(host64(dx)).reshape(N, -1).sum(0)
+    assert np.all(np.abs(tot - dref) <= 2 ** -8 * scale)
