@@ -56,10 +56,23 @@ def algorithmic_bytes(kernel, N, E, H, d, b, score="dot"):
         return csr + E * F * b + 2 * N * F * b + 4 * N * H + N * F * b + 8 * N * H + 4 * F
     if kernel == "bwd_gatv2_cols_main":  # xd_i + dOut_i + record_i per edge; xs; dxs; attn
         return csr + E * (2 * F * b + 8 * H) + N * F * b + N * F * b + 4 * F
+    if kernel == "reduce_fwd_main":      # x_j per edge; out, int32 arg and 16-bit slot
+        return csr + E * F * b + N * F * b + 4 * N * F + 2 * N * F
+    if kernel == "reduce_bwd_main":      # per transpose edge its row position and the row's
+        # 16-bit slots; each dout element once (it matches once); dx
+        return csr + 4 * E + 2 * E * F + N * F * b + N * F * b
     return None
 
 
+REDUCTIONS = ("max", "min")
+
+
 def step_bytes(N, E, H, d, b, backward, score="dot"):
+    if score in REDUCTIONS:
+        tot = algorithmic_bytes("reduce_fwd_main", N, E, H, d, b, score)
+        if backward:
+            tot += algorithmic_bytes("reduce_bwd_main", N, E, H, d, b, score)
+        return tot
     tot = algorithmic_bytes("fwd_main", N, E, H, d, b, score)
     if backward and score == "gatv2":
         tot += algorithmic_bytes("bwd_gatv2_rows_main", N, E, H, d, b, score)
@@ -85,7 +98,13 @@ def _cpu_worker(args):
     with threadpool_limits(1):
         for s in range(0, rows.size, 128):
             batch = rows[s:s + 128]
-            if backward:
+            if g["score"] in REDUCTIONS:
+                from oracle import reduction as R
+                if backward:
+                    R.train_step_rows(g["ip"], g["ix"], g["q"], g["dout"], batch, g["score"])
+                else:
+                    R.reduce_rows(g["ip"], g["ix"], g["q"], batch, g["score"])
+            elif backward:
                 A.train_step_rows(g["ip"], g["ix"], g["q"], g["k"], g["v"], g["dout"], batch,
                                   g["scale"])
             else:
@@ -101,11 +120,13 @@ def _cpu_worker(args):
 def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     import multiprocessing as mp
     cores = min(16, len(os.sched_getaffinity(0)))
-    _SHARED.update(ip=ip, ix=ix, q=feats[0], k=feats[1], v=feats[2], dout=dout, scale=scale,
-                   score=w.score, slope=0.2)
+    red = w.score in REDUCTIONS
+    _SHARED.update(ip=ip, ix=ix, q=feats[0], k=None if red else feats[1],
+                   v=None if red else feats[2], dout=dout, scale=scale, score=w.score, slope=0.2)
     rng = np.random.default_rng(12345)
     n = ip.size - 1
-    rows = rng.permutation(n)[: min(n, 400_000)]
+    # a bounded row sample; the reduction oracle is fast enough to take every row
+    rows = rng.permutation(n)[: n if red else min(n, 400_000)]
     parts = np.array_split(rows, cores)
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
@@ -124,6 +145,8 @@ def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     except OSError:
         pass
     what = "forward+backward" if w.backward else "forward"
+    if red:
+        what = f"{w.score}-pooling {what} (backward: the rows' routed gradient)"
     return {
         "value": e / longest, "unit": "edges/s", "cores": cores, "kind": "oracle",
         "sample": f"{what} of {r} uniformly sampled rows ({e} edges) of the same graph, "
@@ -150,6 +173,14 @@ def relabel_by_out_degree(ip, ix, feats, dout):
 
 
 # ---------------------------------------------------------------- GPU
+
+def capi_ws(fn, plan, features):
+    from ctypes import byref, c_size_t
+    from sparse_graph_attention_02_amd import capi
+    v = c_size_t()
+    getattr(capi, fn)(plan.handle, features, byref(v))
+    return v.value
+
 
 def to_dev(x):
     import torch
@@ -255,11 +286,21 @@ def main():
     copy_gbps = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    vt = tens[1] if w.score == "gatv2" else tens[2]
+    red = w.score in REDUCTIONS
+    vt = tens[1] if w.score == "gatv2" else tens[0] if red else tens[2]
     out = torch.empty_like(vt)
     lse = torch.empty((N, H), dtype=torch.float32, device="cuda")
     fws = torch.empty(max(plan.fwd_workspace_bytes(H, d), 1), dtype=torch.uint8, device="cuda")
-    if w.backward and w.score == "gatv2":
+    if red:
+        arg = torch.empty(vt.shape, dtype=torch.int32, device="cuda")
+        slot = torch.empty(vt.shape, dtype=ga.reduce_slot_dtype(plan), device="cuda")
+        fws = torch.empty(max(int(capi_ws("graph_attn_reduce_fwd_workspace_bytes", plan,
+                                          H * d)), 1), dtype=torch.uint8, device="cuda")
+        if w.backward:
+            dq = torch.empty_like(vt)
+            bws = torch.empty(max(int(capi_ws("graph_attn_reduce_bwd_workspace_bytes", plan,
+                                              H * d)), 1), dtype=torch.uint8, device="cuda")
+    elif w.backward and w.score == "gatv2":
         dq, dk = torch.empty_like(vt), torch.empty_like(vt)
         dv = torch.empty((H, d), dtype=torch.float32, device="cuda")
         bws = torch.empty(ga.bwd_gatv2_workspace_bytes(plan, vt.dtype, H, d), dtype=torch.uint8,
@@ -269,6 +310,11 @@ def main():
         bws = torch.empty(plan.bwd_workspace_bytes(H, d), dtype=torch.uint8, device="cuda")
 
     def step(backward=w.backward):
+        if red:
+            ga.reduce_fwd(plan, tens[0], op=w.score, out=out, arg=arg, slot=slot, workspace=fws)
+            if backward:
+                ga.reduce_bwd(plan, None, tdo, slot=slot, dx=dq, workspace=bws)
+            return
         if w.score == "gatv2":
             ga.fwd_gatv2(plan, *tens, scale=scale, out=out, lse=lse, workspace=fws)
             if backward:
@@ -300,11 +346,14 @@ def main():
     ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
     # gather floor: the forward's neighbour gathers alone (same graph, same lane pattern)
     sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
-    kv = {"dot": (tens[1], tens[2]), "gat": (tens[2], tens[2]),
-          "gatv2": (tens[1], tens[1])}[w.score]
+    # dot gathers two rows per edge (K_j, V_j); the other forms one (the probe then loads
+    # the same row twice and the second load hits in cache)
+    kv = (tens[1], tens[2]) if w.score == "dot" else (vt, vt)
     ga.gather_probe(plan, *kv, sink=sink)
     ms_gather, _ = timed(lambda: ga.gather_probe(plan, *kv, sink=sink), args.steps)
-    gather_bytes = 2 * E * H * d * b + 4 * E    # the probe gathers two rows per edge
+    rows_per_edge = 2 if w.score == "dot" else 1
+    gather_bytes = rows_per_edge * E * H * d * b + 4 * E
+    main_fwd = "reduce_fwd_main" if red else "fwd_main"
 
     kernels = {}
     for name, (launches, tot) in kt.items():
@@ -321,7 +370,7 @@ def main():
     traffic = measured_traffic(w.name, dom)
     fwd_bytes = step_bytes(N, E, H, d, b, False, w.score)
     tot_bytes = step_bytes(N, E, H, d, b, w.backward, w.score)
-    fwd_main_ms = kt_fwd["fwd_main"][1] / kt_fwd["fwd_main"][0]
+    fwd_main_ms = kt_fwd[main_fwd][1] / kt_fwd[main_fwd][0]
     rec = {
         "metric": "fused graph-attn fwd/bwd edges/sec + achieved HBM GB/s (% of MI355X peak)",
         "value": E / (ms_step * 1e-3),
@@ -358,9 +407,10 @@ def main():
         "gather_floor": {
             "ms": ms_gather, "GBps_algorithmic": gather_bytes / (ms_gather * 1e-3) / 1e9,
             "fwd_main_frac_of_floor": ms_gather / fwd_main_ms,
-            "note": "K and V rows of every edge gathered with the forward's lane pattern and "
-                    "no arithmetic (graph_attn_gather_probe); the memory system's floor for "
-                    "the forward's gathers on this graph"},
+            "rows_per_edge": rows_per_edge,
+            "note": "the source rows of every edge gathered with the forward's lane pattern "
+                    "and no arithmetic (graph_attn_gather_probe); the memory system's floor "
+                    "for the forward's gathers on this graph"},
         "kernels": kernels,
         "copy_probe_GBps": copy_gbps,
         "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,

@@ -86,6 +86,7 @@ typedef struct {
   int64_t light_max_deg, hub_min_deg_exclusive, hub_chunk;
   int64_t device_bytes;
   int64_t uploaded;
+  int64_t rows_sorted;  /* 1 when every row's neighbour ids are non-decreasing */
 } ga_plan_info;
 
 typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */
@@ -104,8 +105,9 @@ ga_status graph_attn_plan_opts_default(ga_plan_opts* opts);
  * Bins: each bin lists its rows by degree descending, ties by ascending row id. Hub row
  * chunks: [indptr[i] + k*C, min(indptr[i] + (k+1)*C, indptr[i+1])), listed hub by hub.
  * Transpose (build_csc): colptr [N+1] and rowidx [E], destinations ascending within each
- * column (the order a stable scatter over rows produces); column bins/chunks follow the
- * same rules on out-degree. indptr_host/indices_host are only read during the call
+ * column (the order a stable scatter over rows produces), and csc_rel [E], for each
+ * transpose entry the position of that edge within its CSR row (k - indptr[i] for CSR
+ * edge k of row i); column bins/chunks follow the same rules on out-degree. indptr_host/indices_host are only read during the call
  * (indices_host may be NULL when n_edges == 0). opts NULL = defaults. On success *out
  * receives a plan to be released with graph_attn_plan_destroy. */
 ga_status graph_attn_plan_create(const int32_t* indptr_host, const int32_t* indices_host,
@@ -129,7 +131,7 @@ ga_status graph_attn_plan_upload(ga_plan* plan, void* dev_buf, size_t bytes, voi
  * "row_light", "row_medium", "row_hub", "row_chunk_row", "row_chunk_begin",
  * "row_chunk_end", "row_hub_chunk_ptr", and with the transpose "colptr", "rowidx",
  * "col_light", "col_medium", "col_hub", "col_chunk_row", "col_chunk_begin",
- * "col_chunk_end", "col_hub_chunk_ptr". *data stays valid until the plan is destroyed
+ * "col_chunk_end", "col_hub_chunk_ptr", "csc_rel". *data stays valid until the plan is destroyed
  * (it may be NULL when *count == 0). GA_ERR_INVALID_ARG for an unknown name,
  * GA_ERR_NOT_READY for a transpose array of a plan built without it. */
 ga_status graph_attn_plan_array(const ga_plan* plan, const char* name, const int32_t** data,
@@ -238,23 +240,35 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t head
  *     out[i,c] = max_j x[j,c]  (or min)     arg[i,c] = the source id j attaining it
  * Equal values go to the smallest source id, so arg does not depend on the order of a
  * row's neighbours. out[i,c] is x[arg[i,c],c] bit for bit (values compare as numbers:
- * -0 equals +0). A row with no neighbours gives out = 0 and arg = -1. NaN never wins a
+ * -0 equals +0). A row with no neighbours gives out = 0 and arg = -1. Optionally the
+ * forward also writes slot[i,c] = the position within row i (k - indptr[i]) of the first
+ * edge of that row from arg[i,c], as unsigned 16-bit values when no row has more than
+ * 65536 edges, else 32-bit (graph_attn_reduce_slot_bytes); empty rows get all ones. The
+ * backward reads slot (2 bytes per element per transpose edge) in place of arg (4), so a
+ * training step should keep slot. NaN never wins a
  * comparison (a row whose candidates are all NaN reads as empty); inputs are meant to be
  * free of NaN. x, out, dout, dx: [N, F] of `dtype`, F*sizeof(dtype) one of 64, 128, 256,
  * 512 or 1024 bytes; arg int32 [N, F]; every pointer 16-byte aligned. Results are
  * bitwise reproducible (no atomics; the backward's sums run in a fixed order). */
 typedef enum { GA_REDUCE_MAX = 0, GA_REDUCE_MIN = 1 } ga_reduce;
 
-/* Workspace of graph_attn_reduce_fwd: per hub-row chunk, fp32 values and int32 ids of its
- * partial result, two sections of n_row_chunks*F*4 bytes, each 256-byte aligned (0 when
- * the plan has no hub rows; the workspace may then be NULL). */
+/* Workspace of graph_attn_reduce_fwd: per hub-row chunk, the fp32 values, int32 ids and
+ * int32 edge indices of its partial result, three sections of n_row_chunks*F*4 bytes,
+ * each 256-byte aligned (0 when the plan has no hub rows; the workspace may then be
+ * NULL). */
 ga_status graph_attn_reduce_fwd_workspace_bytes(const ga_plan* plan, int32_t features,
                                                 size_t* bytes);
 
-/* Forward: out and arg for every row (see above). The plan must be uploaded. */
+/* Bytes per element of the plan's slot array: 2 when no row has more than 65536 edges,
+ * else 4. */
+ga_status graph_attn_reduce_slot_bytes(const ga_plan* plan, size_t* bytes);
+
+/* Forward: out and arg for every row, and slot when `slot` is not NULL ([N, F] of
+ * graph_attn_reduce_slot_bytes each, 16-byte aligned). The plan must be uploaded. */
 ga_status graph_attn_reduce_fwd(const ga_plan* plan, ga_reduce op, ga_dtype dtype,
                                 int32_t features, const void* x, void* out, int32_t* arg,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                void* slot, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Workspace of graph_attn_reduce_bwd: fp32 partial sums of the hub-column chunks,
  * n_col_chunks*F*4 bytes (0 when the transpose has no hub columns; NULL allowed then). */
@@ -263,14 +277,15 @@ ga_status graph_attn_reduce_bwd_workspace_bytes(const ga_plan* plan, int32_t fea
 
 /* Backward: dx[j,c] = sum of dout[i,c] over the destinations i with arg[i,c] = j (each
  * distinct i once; a parallel edge does not count twice), the gradient of the forward
- * routed to the element that won. arg is the forward's output (entries -1 or a node id;
- * arg is only compared with column ids, never used as an address, so an entry that is
- * neither simply matches nothing). Computed over
- * the plan's cached transpose, one pass per source column, sums in fp32 (fp64 when dtype
- * is fp32) in a fixed order. Needs a plan with the transpose, uploaded. */
+ * routed to the element that won. Pass the forward's slot (then arg may be NULL and is not
+ * read) or, without slot, its arg. Both are only compared with column ids or transpose
+ * positions, never used as addresses, so an entry that is neither matches nothing.
+ * Computed over the plan's cached transpose, one pass per source column, sums in fp32
+ * (fp64 when dtype is fp32) in a fixed order. Needs a plan with the transpose, uploaded. */
 ga_status graph_attn_reduce_bwd(const ga_plan* plan, ga_dtype dtype, int32_t features,
-                                const int32_t* arg, const void* dout, void* dx,
-                                void* workspace, size_t workspace_bytes, void* stream);
+                                const int32_t* arg, const void* slot, const void* dout,
+                                void* dx, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Kernel timers (tracing). When enabled, every kernel the library launches is bracketed
  * by two hipEvents recorded on its stream; graph_attn_timer_read synchronises those

@@ -73,6 +73,17 @@ def transpose(indptr, indices):
     return colptr.astype(np.int32), edge_row[order].astype(np.int32)
 
 
+def transpose_positions(indptr, indices):
+    """For each transpose entry (in transpose order), the position of that edge within its
+    CSR row: the CSR edges listed column by column, then k - indptr[row(k)]."""
+    indptr = np.asarray(indptr, dtype=np.int64)
+    indices = np.asarray(indices, dtype=np.int64)
+    k = np.arange(indices.size, dtype=np.int64)
+    row = np.repeat(np.arange(indptr.size - 1, dtype=np.int64), np.diff(indptr))
+    order = np.argsort(indices, kind="stable")
+    return (k - indptr[row])[order].astype(np.int32)
+
+
 def plan(indptr, indices, light_max_deg=16, hub_min_deg_exclusive=1024, hub_chunk=1024,
          build_csc=True):
     """All plan arrays as a dict of int32 arrays (names match the library's export)."""
@@ -86,6 +97,7 @@ def plan(indptr, indices, light_max_deg=16, hub_min_deg_exclusive=1024, hub_chun
     if build_csc:
         colptr, rowidx = transpose(indptr, indices)
         out["colptr"], out["rowidx"] = colptr, rowidx
+        out["csc_rel"] = transpose_positions(indptr, indices)
         odeg = np.diff(colptr.astype(np.int64))
         out["col_light"], out["col_medium"], out["col_hub"] = bin_rows(
             odeg, light_max_deg, hub_min_deg_exclusive)

@@ -18,6 +18,9 @@ the order of a row's neighbours, so the index result is unique.  Values compare 
 numbers (-0 equals +0); out[i, c] is x[arg[i, c], c] as stored.  A row with no
 neighbours gives out = 0 and arg = -1.  Inputs are finite or infinite, never NaN.
 
+The compact form of arg used by the backward, slot[i, c], is the position within row i
+(k - indptr[i]) of the first edge of that row coming from arg[i, c]; -1 for an empty row.
+
 Backward (the gradient of a max/min is routed to the element that attained it):
     dx[arg[i, c], c] += dout[i, c]    for every row i with arg[i, c] >= 0
 A parallel edge (j listed twice in a row) is one variable x_j, so it receives the
@@ -34,7 +37,7 @@ from .attention import widen
 
 __all__ = ["EMPTY_ARG", "reduce_rows", "reduce_forward", "merge_pairs",
            "reduce_forward_chunked", "reduce_backward", "reduce_backward_by_columns",
-           "reduce_backward_cols", "grad_cols_sampled"]
+           "reduce_backward_cols", "grad_cols_sampled", "train_step_rows", "slots_of"]
 
 EMPTY_ARG = -1
 
@@ -168,3 +171,32 @@ def grad_cols_sampled(indptr, indices, colptr, rowidx, x, dout, cols, op="max"):
             hit = arg_rows[pos[int(i)]] == j
             out[n][hit] += widen(dout[i]).reshape(-1)[hit]
     return out, rows, arg_rows
+
+
+def train_step_rows(indptr, indices, x, dout, rows, op="max"):
+    """Forward of the listed rows and their share of the backward: the gradient they
+    route, returned compressed as (ids, dx_ids) with dx_ids[k] the contribution to
+    dx[ids[k]] (so a sample of rows needs no [N, F] array)."""
+    out, arg = reduce_rows(indptr, indices, x, rows, op)
+    dof = np.stack([widen(dout[i]).reshape(-1) for i in rows]) if len(rows) else \
+        np.zeros((0, arg.shape[1]))
+    ids, local = np.unique(arg[arg >= 0], return_inverse=True)
+    dx_ids = np.zeros((ids.size, arg.shape[1]))
+    r, c = np.nonzero(arg >= 0)
+    np.add.at(dx_ids, (local, c), dof[r, c])
+    return out, arg, ids, dx_ids
+
+
+def slots_of(indptr, indices, rows, arg_rows):
+    """slot of the listed rows given their arg: the position within the row of the first
+    edge from the winning id (-1 where arg is -1)."""
+    arg_rows = np.asarray(arg_rows, dtype=np.int64)
+    out = np.full(arg_rows.shape, -1, dtype=np.int64)
+    for n, i in enumerate(np.asarray(rows, dtype=np.int64)):
+        J = np.asarray(indices[indptr[i]:indptr[i + 1]], dtype=np.int64)
+        a = arg_rows[n]
+        if J.size == 0:
+            continue
+        first = (J[:, None] == a[None, :]).argmax(axis=0)
+        out[n] = np.where(a >= 0, first, -1)
+    return out

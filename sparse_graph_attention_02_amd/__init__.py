@@ -10,8 +10,8 @@ current HIP stream.  ``capi`` holds the raw C entry points under their C names.
     out, lse = fwd(plan, q, k, v)         # dot score, scale 1/sqrt(d)
     dq, dk, dv = bwd(plan, q, k, v, dout, lse)
     out, lse = fwd(plan, s, t, v, score="gat")
-    out, arg = reduce_fwd(plan, x, op="max")  # neighbourhood max pooling and its arg
-    dx = reduce_bwd(plan, arg, dout)
+    out, arg, slot = reduce_fwd(plan, x, op="max")  # neighbourhood max pooling, its arg
+    dx = reduce_bwd(plan, arg, dout, slot=slot)
 
 Method: "On Efficient Scaling of GNNs via IO-Aware Layers Implementations", Technical
 Summary > Methodology, attention-based layers (fused score -> online softmax ->
@@ -32,6 +32,7 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    GA_SCORE_DOT, GA_SCORE_GAT, GraphAttnError,
                    graph_attn_reduce_bwd, graph_attn_reduce_bwd_workspace_bytes,
                    graph_attn_reduce_fwd, graph_attn_reduce_fwd_workspace_bytes,
+                   graph_attn_reduce_slot_bytes,
                    graph_attn_bwd, graph_attn_bwd_gatv2, graph_attn_bwd_gatv2_workspace_bytes,
                    graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
                    graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_workspace_bytes,
@@ -45,7 +46,7 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
 __all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention", "reduce_fwd",
-           "reduce_bwd", "graph_reduce", "copy_probe", "timers", "default_opts",
+           "reduce_bwd", "reduce_slot_dtype", "graph_reduce", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
 
@@ -353,10 +354,22 @@ def _features_view(t, name, device=None):
     return t.shape[0], (t.numel() // t.shape[0] if t.shape[0] else int(np.prod(t.shape[1:])))
 
 
-def reduce_fwd(plan: Plan, x, *, op="max", out=None, arg=None, workspace=None, stream=None):
+def reduce_slot_dtype(plan: Plan):
+    """torch dtype holding the plan's slot values (int16 storage of unsigned 16-bit
+    positions, or int32)."""
+    import torch
+    b = c_size_t()
+    graph_attn_reduce_slot_bytes(plan.handle, byref(b))
+    return torch.int16 if b.value == 2 else torch.int32
+
+
+def reduce_fwd(plan: Plan, x, *, op="max", out=None, arg=None, slot=None, with_slot=True,
+               workspace=None, stream=None):
     """Neighbourhood max (or min) of the source rows, elementwise, and the winning source
     id per element (smallest id on ties; empty rows give 0 and -1).  x: [N, ...] fp32 or
-    bf16; returns (out like x, arg int32 of x's shape)."""
+    bf16.  Returns (out like x, arg int32 of x's shape, slot): slot holds each winner's
+    position within its row (reduce_slot_dtype; the backward's compact input), None when
+    ``with_slot`` is false."""
     import torch
     if plan.device_buffer is None:
         raise RuntimeError("plan is not uploaded")
@@ -370,32 +383,43 @@ def reduce_fwd(plan: Plan, x, *, op="max", out=None, arg=None, workspace=None, s
     arg = torch.empty(x.shape, dtype=torch.int32, device=x.device) if arg is None else arg
     _need(out, "out", x.shape, x.dtype, x.device)
     _need(arg, "arg", x.shape, torch.int32, x.device)
+    if with_slot:
+        sdt = reduce_slot_dtype(plan)
+        slot = torch.empty(x.shape, dtype=sdt, device=x.device) if slot is None else slot
+        _need(slot, "slot", x.shape, sdt, x.device)
+    else:
+        slot = None
     b = c_size_t()
     graph_attn_reduce_fwd_workspace_bytes(plan.handle, F, byref(b))
     ws, wsb = _workspace(int(b.value), x.device, workspace)
     with torch.cuda.device(x.device):
         graph_attn_reduce_fwd(plan.handle, code, _dtype_code(x), F, _ptr(x), _ptr(out),
-                              _ptr(arg), _ptr(ws), wsb, _stream(stream))
-    return out, arg
+                              _ptr(arg), _ptr(slot), _ptr(ws), wsb, _stream(stream))
+    return out, arg, slot
 
 
-def reduce_bwd(plan: Plan, arg, dout, *, dx=None, workspace=None, stream=None):
+def reduce_bwd(plan: Plan, arg, dout, *, slot=None, dx=None, workspace=None, stream=None):
     """Gradient of reduce_fwd: dx[j] collects dout[i] where arg[i] == j (each destination
-    once).  The plan needs the transpose (build_csc=True)."""
+    once).  With the forward's ``slot`` the kernels read it instead of arg (half the
+    bytes; arg may then be None).  The plan needs the transpose (build_csc=True)."""
     import torch
     if plan.device_buffer is None:
         raise RuntimeError("plan is not uploaded")
     N, F = _features_view(dout, "dout")
     if N != plan.n_nodes:
         raise ValueError(f"dout has {N} rows, the graph {plan.n_nodes} nodes")
-    _need(arg, "arg", dout.shape, torch.int32, dout.device)
+    if slot is not None:
+        _need(slot, "slot", dout.shape, reduce_slot_dtype(plan), dout.device)
+    else:
+        _need(arg, "arg", dout.shape, torch.int32, dout.device)
     dx = torch.empty_like(dout) if dx is None else dx
     _need(dx, "dx", dout.shape, dout.dtype, dout.device)
     b = c_size_t()
     graph_attn_reduce_bwd_workspace_bytes(plan.handle, F, byref(b))
     ws, wsb = _workspace(int(b.value), dout.device, workspace)
     with torch.cuda.device(dout.device):
-        graph_attn_reduce_bwd(plan.handle, _dtype_code(dout), F, _ptr(arg), _ptr(dout),
+        graph_attn_reduce_bwd(plan.handle, _dtype_code(dout), F,
+                              _ptr(arg) if slot is None else None, _ptr(slot), _ptr(dout),
                               _ptr(dx), _ptr(ws), wsb, _stream(stream))
     return dx
 
@@ -406,16 +430,16 @@ def _reduce_fn():
     class _GraphReduce(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, plan, op):
-            out, arg = reduce_fwd(plan, x.contiguous(), op=op)
-            ctx.save_for_backward(arg)
+            out, arg, slot = reduce_fwd(plan, x.contiguous(), op=op)
+            ctx.save_for_backward(slot)
             ctx.plan = plan
             ctx.mark_non_differentiable(arg)
             return out, arg
 
         @staticmethod
         def backward(ctx, g, _garg):
-            (arg,) = ctx.saved_tensors
-            return reduce_bwd(ctx.plan, arg, g.contiguous()), None, None
+            (slot,) = ctx.saved_tensors
+            return reduce_bwd(ctx.plan, None, g.contiguous(), slot=slot), None, None
 
     return _GraphReduce
 
@@ -424,7 +448,8 @@ _RFN = None
 
 
 def graph_reduce(plan: Plan, x, op="max"):
-    """Neighbourhood max / min pooling as a differentiable torch op; returns (out, arg)."""
+    """Neighbourhood max / min pooling as a differentiable torch op; returns (out, arg)
+    (the backward uses the forward's slot array, kept for it)."""
     global _RFN
     if _RFN is None:
         _RFN = _reduce_fn()

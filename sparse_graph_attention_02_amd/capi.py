@@ -32,7 +32,7 @@ class ga_plan_info(Structure):
         "n_nodes", "n_edges", "n_row_light", "n_row_medium", "n_row_hub", "n_row_chunks",
         "has_csc", "n_col_light", "n_col_medium", "n_col_hub", "n_col_chunks",
         "max_in_degree", "max_out_degree", "light_max_deg", "hub_min_deg_exclusive",
-        "hub_chunk", "device_bytes", "uploaded")]
+        "hub_chunk", "device_bytes", "uploaded", "rows_sorted")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -76,11 +76,12 @@ _SIGS = {
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                        c_void_p]),
     "graph_attn_reduce_fwd_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
+    "graph_attn_reduce_slot_bytes": (c_int32, [c_void_p, POINTER(c_size_t)]),
     "graph_attn_reduce_fwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
-                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "graph_attn_reduce_bwd_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
     "graph_attn_reduce_bwd": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p,
-                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "graph_attn_timer_enable": (c_int32, [c_int32]),
     "graph_attn_timer_reset": (c_int32, []),
     "graph_attn_timer_count": (c_int32, []),
@@ -154,6 +155,7 @@ graph_attn_bwd = _wrap("graph_attn_bwd")
 graph_attn_bwd_gatv2_workspace_bytes = _wrap("graph_attn_bwd_gatv2_workspace_bytes")
 graph_attn_bwd_gatv2 = _wrap("graph_attn_bwd_gatv2")
 graph_attn_reduce_fwd_workspace_bytes = _wrap("graph_attn_reduce_fwd_workspace_bytes")
+graph_attn_reduce_slot_bytes = _wrap("graph_attn_reduce_slot_bytes")
 graph_attn_reduce_fwd = _wrap("graph_attn_reduce_fwd")
 graph_attn_reduce_bwd_workspace_bytes = _wrap("graph_attn_reduce_bwd_workspace_bytes")
 graph_attn_reduce_bwd = _wrap("graph_attn_reduce_bwd")

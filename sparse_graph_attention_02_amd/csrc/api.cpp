@@ -97,6 +97,7 @@ const ArrayRef kArrays[] = {
     GA_REF("col_chunk_begin", p->cols.chunk_begin, true),
     GA_REF("col_chunk_end", p->cols.chunk_end, true),
     GA_REF("col_hub_chunk_ptr", p->cols.hub_chunk_ptr, true),
+    GA_REF("csc_rel", p->csc_rel, true),
 };
 #undef GA_REF
 constexpr int kNumArrays = sizeof(kArrays) / sizeof(kArrays[0]);
@@ -178,7 +179,7 @@ ga_status reduce_geometry(ga_dtype dt, int32_t features, int* G) {
 }
 
 size_t reduce_fwd_ws_bytes(const ga_plan* p, int32_t features) {
-  return 2 * align_up(p->rows.chunk_row.size() * size_t(features) * 4);
+  return 3 * align_up(p->rows.chunk_row.size() * size_t(features) * 4);
 }
 
 size_t reduce_bwd_ws_bytes(const ga_plan* p, int32_t features) {
@@ -259,6 +260,7 @@ ga_status graph_attn_plan_get_info(const ga_plan* p, ga_plan_info* info) {
   info->hub_min_deg_exclusive = p->opts.hub_min_deg_exclusive;
   info->hub_chunk = p->opts.hub_chunk;
   info->device_bytes = static_cast<int64_t>(device_layout(p, nullptr));
+  info->rows_sorted = p->rows_sorted ? 1 : 0;
   info->uploaded = p->uploaded;
   return GA_OK;
 }
@@ -312,6 +314,7 @@ ga_status graph_attn_plan_upload(ga_plan* p, void* dev_buf, size_t bytes, void* 
   p->d_colptr = ptrs[9];
   p->d_rowidx = ptrs[10];
   p->d_cols = p->has_csc ? bins(11, p->cols) : ga::DevBins{};
+  p->d_csc_rel = ptrs[18];
   p->device = dev;
   p->uploaded = true;
   return GA_OK;
@@ -579,9 +582,15 @@ ga_status graph_attn_reduce_bwd_workspace_bytes(const ga_plan* p, int32_t featur
   return GA_OK;
 }
 
+ga_status graph_attn_reduce_slot_bytes(const ga_plan* p, size_t* bytes) {
+  if (!p || !bytes) return GA_ERR_INVALID_ARG;
+  *bytes = static_cast<size_t>(ga::reduce_slot_bytes(p->max_in));
+  return GA_OK;
+}
+
 ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
                                 int32_t features, const void* x, void* out, int32_t* arg,
-                                void* ws, size_t ws_bytes, void* stream) {
+                                void* slot, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return GA_ERR_INVALID_ARG;
   if (op != GA_REDUCE_MAX && op != GA_REDUCE_MIN) return GA_ERR_INVALID_ARG;
   int G = 0;
@@ -591,6 +600,7 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
     if ((s = check_ptr(x, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
         (s = check_ptr(arg, 16)) != GA_OK)
       return s;
+    if (slot && !aligned(slot, 16)) return GA_ERR_INVALID_ARG;
   }
   const size_t need = reduce_fwd_ws_bytes(p, features);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
@@ -604,9 +614,13 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   args.x = x;
   args.out = out;
   args.arg = arg;
+  args.slot = slot;
+  args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
+  args.rows_sorted = p->rows_sorted;
   if (need > 0) {
     args.ws_val = static_cast<float*>(ws);
-    args.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
+    args.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 3);
+    args.ws_pos = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + 2 * (need / 3));
   }
   const int rc = ga::launch_reduce(dtype, false, op == GA_REDUCE_MAX ? ga::kReduceMax
                                                                      : ga::kReduceMin,
@@ -615,15 +629,15 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
 }
 
 ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t features,
-                                const int32_t* arg, const void* dout, void* dx, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                const int32_t* arg, const void* slot, const void* dout,
+                                void* dx, void* ws, size_t ws_bytes, void* stream) {
   if (!p) return GA_ERR_INVALID_ARG;
   int G = 0;
   ga_status s = reduce_geometry(dtype, features, &G);
   if (s != GA_OK) return s;
   if (p->n > 0) {
-    if ((s = check_ptr(arg, 16)) != GA_OK || (s = check_ptr(dout, 16)) != GA_OK ||
-        (s = check_ptr(dx, 16)) != GA_OK)
+    if ((s = check_ptr(slot ? slot : static_cast<const void*>(arg), 16)) != GA_OK ||
+        (s = check_ptr(dout, 16)) != GA_OK || (s = check_ptr(dx, 16)) != GA_OK)
       return s;
   }
   if (!p->has_csc) return GA_ERR_NOT_READY;
@@ -636,7 +650,10 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   args.colptr = p->d_colptr;
   args.rowidx = p->d_rowidx;
   args.cols = p->d_cols;
-  args.arg_in = arg;
+  args.arg_in = slot ? nullptr : arg;
+  args.slot_in = slot;
+  args.csc_rel = p->d_csc_rel;
+  args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.dout = dout;
   args.dx = dx;
   args.ws_sum = need > 0 ? static_cast<float*>(ws) : nullptr;

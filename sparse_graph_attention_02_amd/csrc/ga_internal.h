@@ -39,8 +39,10 @@ struct ga_plan {
   ga::Bins rows;
   bool has_csc = false;
   std::vector<int32_t> colptr, rowidx;
+  std::vector<int32_t> csc_rel;  // per transpose entry: the edge's position in its CSR row
   ga::Bins cols;
   int64_t max_in = 0, max_out = 0;
+  bool rows_sorted = true;  // every row's neighbour ids are non-decreasing
 
   // device copy (caller-owned memory)
   bool uploaded = false;
@@ -49,6 +51,7 @@ struct ga_plan {
   const int32_t* d_indices = nullptr;
   const int32_t* d_colptr = nullptr;
   const int32_t* d_rowidx = nullptr;
+  const int32_t* d_csc_rel = nullptr;
   ga::DevBins d_rows, d_cols;
 };
 
@@ -152,18 +155,26 @@ struct RedArgs {
   const int32_t* colptr;
   const int32_t* rowidx;
   DevBins rows, cols;
+  const int32_t* csc_rel;  // per transpose entry: the edge's position in its CSR row
+  int slot_bytes;          // 2 or 4: width of the slot array
+  bool rows_sorted;        // host-side: every row's neighbour ids non-decreasing
   // forward
   const void* x;     // [N, F]
   void* out;         // [N, F]
   int32_t* arg;      // [N, F]
-  float* ws_val;     // hub chunk partials [n_row_chunks][F]: values
-  int32_t* ws_idx;   //                                      and ids
-  // backward
+  void* slot;        // [N, F] row positions of the winners (optional)
+  float* ws_val;     // hub chunk partials [n_row_chunks][F]: values,
+  int32_t* ws_idx;   //                                      ids
+  int32_t* ws_pos;   //                                      and edge indices
+  // backward: match on slot_in when it is set, else on arg_in
   const int32_t* arg_in;  // [N, F] (the forward's arg)
+  const void* slot_in;    // [N, F] (the forward's slot)
   const void* dout;       // [N, F]
   void* dx;               // [N, F]
   float* ws_sum;          // hub column partial sums [n_col_chunks][F]
 };
+// Width of the slot array of a plan (2 bytes when no row has more than 65536 edges).
+inline int reduce_slot_bytes(int64_t max_in_degree) { return max_in_degree <= 65536 ? 2 : 4; }
 bool reduce_supported(ga_dtype dt, int G);
 int launch_reduce(ga_dtype dt, bool backward, int op, int G, const RedArgs& a, void* stream,
                   TimerHook hook);

@@ -78,6 +78,13 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
     p->indptr.assign(indptr, indptr + n + 1);
     p->indices.assign(indices, indices + e);
     bin_by_degree(p->indptr, o, &p->rows, &p->max_in);
+    p->rows_sorted = true;
+    for (int64_t i = 0; i < n && p->rows_sorted; ++i)
+      for (int32_t k = indptr[i] + 1; k < indptr[i + 1]; ++k)
+        if (indices[k] < indices[k - 1]) {
+          p->rows_sorted = false;
+          break;
+        }
     p->has_csc = o.build_csc != 0;
     p->max_out = 0;
     if (p->has_csc) {
@@ -88,13 +95,18 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
       for (int64_t j = 0; j < n; ++j) p->colptr[j + 1] += p->colptr[j];
       std::vector<int32_t> cursor(p->colptr.begin(), p->colptr.end() - 1);
       p->rowidx.assign(static_cast<size_t>(e), 0);
+      p->csc_rel.assign(static_cast<size_t>(e), 0);
       for (int64_t i = 0; i < n; ++i)
-        for (int32_t k = indptr[i]; k < indptr[i + 1]; ++k)
-          p->rowidx[cursor[indices[k]]++] = static_cast<int32_t>(i);
+        for (int32_t k = indptr[i]; k < indptr[i + 1]; ++k) {
+          const int32_t at = cursor[indices[k]]++;
+          p->rowidx[at] = static_cast<int32_t>(i);
+          p->csc_rel[at] = k - indptr[i];  // the edge's position within its CSR row
+        }
       bin_by_degree(p->colptr, o, &p->cols, &p->max_out);
     } else {
       p->colptr.clear();
       p->rowidx.clear();
+      p->csc_rel.clear();
       p->cols = Bins{};
     }
   } catch (const std::bad_alloc&) {

@@ -9,7 +9,9 @@
 //   out[i, c] = max_j x[j, c] (or min) over the neighbours j of row i,
 //   arg[i, c] = the source id attaining it; equal values go to the smallest id, so the
 //               result does not depend on neighbour order or on how a row is split.
-//   Empty rows: out = 0, arg = -1.
+//   slot[i, c] (optional) = the position within row i of the first edge from that id,
+//               16-bit when every row has at most 65536 edges, else 32-bit.
+//   Empty rows: out = 0, arg = -1 (slot all ones).
 //
 // Forward (one launch over every row, the plan's row bins, like the attention forward):
 //   reduce_fwd_main   hub chunks -> (value, index) partials; medium rows one wavefront each;
@@ -19,13 +21,17 @@
 //                     order does not matter; it is fixed anyway)
 // Backward, dx[arg[i, c], c] += dout[i, c], over the cached transpose (column bins by
 // out-degree), so each source row is written once and no atomics are needed:
-//   reduce_bwd_main   column j walks its destinations i (ascending; a parallel edge lists i
-//                     twice in a row and is counted once), gathers arg[i] and, in the
-//                     lanes where some element's arg is j, dout[i]
+//   reduce_bwd_main   column j walks its destinations i (ascending) and gathers either
+//                     arg[i] (4 bytes per element; a parallel edge lists i twice in a row
+//                     and is counted once) or, cheaper, slot[i] (2 bytes per element),
+//                     matched against the transpose entry's position in row i (csc_rel;
+//                     only the first of parallel edges can match); where an element
+//                     matches, dout[i] is gathered and added
 //   reduce_bwd_merge  hub columns: ordered sums of chunk partials
 // The message is the gathered row itself, so values are compared as stored (bf16 widens
 // exactly to fp32) and out is written back bit-exact.
 #include <climits>
+#include <type_traits>
 
 #include "ga_device.h"
 #include "ga_internal.h"
@@ -34,8 +40,15 @@ namespace ga {
 namespace {
 
 constexpr int kNoArg = INT_MAX;  // id of an empty state: any real neighbour id is smaller
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <typename T, int G, int OP, int U>
+// Backward modes: match on arg (source ids) or on 16- / 32-bit slots (row positions).
+enum { kMatchArg = 0, kMatchSlot16 = 2, kMatchSlot32 = 4 };
+
+// SORTED: every row lists its neighbours by ascending id, so among equal values the
+// smallest id is also the earliest edge; the state then orders by (value, edge index)
+// alone and the id is read from the row at the end (fewer operations per element).
+template <typename T, int G, int OP, int U, bool SORTED = false>
 struct Red : RowIO<T, G, G> {
   using IO = RowIO<T, G, G>;
   using typename IO::L16;
@@ -47,7 +60,8 @@ struct Red : RowIO<T, G, G> {
 
   struct State {
     float v[VEC];
-    int id[VEC];
+    int id[VEC];   // winner's id (unused while SORTED: read from indices at the end)
+    int pos[VEC];  // CSR edge index of the winner (first edge from that id); INT_MAX = none
   };
 
   __device__ __forceinline__ static void init(State& s) {
@@ -55,21 +69,41 @@ struct Red : RowIO<T, G, G> {
     for (int c = 0; c < VEC; ++c) {
       s.v[c] = OP == kReduceMax ? -INFINITY : INFINITY;
       s.id[c] = kNoArg;
+      s.pos[c] = INT_MAX;
     }
   }
 
   // (v, j) beats (b, i): a strictly better value, or an equal value from a smaller id.
+  // Non-short-circuit operators keep the rule branch-free (lane masks and selects).
   __device__ __forceinline__ static bool better(float v, int j, float b, int i) {
     const bool w = OP == kReduceMax ? v > b : v < b;
-    return w || (v == b && j < i);
+    return w | ((v == b) & (j < i));
+  }
+  // ... and between two edges from the same id (equal values), the earlier edge. With
+  // sorted rows the edge index alone orders equal values.
+  __device__ __forceinline__ static bool better3(float v, int j, int p, float b, int i, int q) {
+    const bool w = OP == kReduceMax ? v > b : v < b;
+    if constexpr (SORTED) return w | ((v == b) & (p < q));
+    return better(v, j, b, i) | ((j == i) & (p < q));
   }
 
-  __device__ __forceinline__ static void fold(State& s, const float* x, int j) {
+  // Edge k from source j (ok = the edge slot is in range); a lane group visits a row's
+  // edges in increasing k, so an edge from an id already held is never earlier and the
+  // two-way rule suffices here.
+  __device__ __forceinline__ static void fold(State& s, const float* x, int j, int k, bool ok) {
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
-      const bool t = better(x[c], j, s.v[c], s.id[c]);
-      s.v[c] = t ? x[c] : s.v[c];
-      s.id[c] = t ? j : s.id[c];
+      if constexpr (SORTED) {
+        // edges arrive in increasing k, so an equal value never displaces the winner
+        const bool t = ok & (OP == kReduceMax ? x[c] > s.v[c] : x[c] < s.v[c]);
+        s.v[c] = t ? x[c] : s.v[c];
+        s.pos[c] = t ? k : s.pos[c];
+      } else {
+        const bool t = ok & better(x[c], j, s.v[c], s.id[c]);
+        s.v[c] = t ? x[c] : s.v[c];
+        s.id[c] = t ? j : s.id[c];
+        s.pos[c] = t ? k : s.pos[c];
+      }
     }
   }
 
@@ -99,10 +133,9 @@ struct Red : RowIO<T, G, G> {
         for (int u = 0; u < U; ++u) xr[u] = X[static_cast<size_t>(jj[u]) * G + r];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (!ok[u]) continue;
           float xf[VEC];
           L16::unpack(xr[u], xf);
-          fold(s, xf, jj[u]);
+          fold(s, xf, jj[u], base + t + u * NGS + gs, ok[u]);
         }
       }
     }
@@ -117,23 +150,50 @@ struct Red : RowIO<T, G, G> {
 #pragma unroll
       for (int c = 0; c < VEC; ++c) {
         const float ov = __shfl_xor(s.v[c], off);
-        const int oi = __shfl_xor(s.id[c], off);
-        const bool t = better(ov, oi, s.v[c], s.id[c]);
+        const int oi = SORTED ? 0 : __shfl_xor(s.id[c], off);
+        const int op = __shfl_xor(s.pos[c], off);
+        const bool t = better3(ov, oi, op, s.v[c], s.id[c], s.pos[c]);
         s.v[c] = t ? ov : s.v[c];
-        s.id[c] = t ? oi : s.id[c];
+        if constexpr (!SORTED) s.id[c] = t ? oi : s.id[c];
+        s.pos[c] = t ? op : s.pos[c];
       }
     }
   }
 
-  __device__ __forceinline__ static void write_row(const RedArgs& a, int row, int r,
-                                                   const State& s) {
+  // Store the row's result; row_start = indptr[row] (slot positions are row-relative).
+  __device__ __forceinline__ static void write_row(const RedArgs& a, int row, int row_start,
+                                                   int r, const State& s) {
     float o[VEC];
     int ar[VEC];
+    unsigned sl[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
-      const bool empty = s.id[c] == kNoArg;
+      const bool empty = s.pos[c] == INT_MAX;
       o[c] = empty ? 0.f : s.v[c];
-      ar[c] = empty ? -1 : s.id[c];
+      if constexpr (SORTED)
+        ar[c] = empty ? -1 : a.indices[s.pos[c]];
+      else
+        ar[c] = empty ? -1 : s.id[c];
+      sl[c] = empty ? 0xffffffffu : static_cast<unsigned>(s.pos[c] - row_start);
+    }
+    if (a.slot) {
+      const size_t e0 = static_cast<size_t>(row) * F + r * VEC;
+      if (a.slot_bytes == 2) {
+        unsigned w[VEC / 2];
+#pragma unroll
+        for (int k = 0; k < VEC / 2; ++k) w[k] = (sl[2 * k] & 0xffffu) | (sl[2 * k + 1] << 16);
+        if constexpr (VEC == 8)
+          st_stream(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.slot) + e0),
+                    u32x4{w[0], w[1], w[2], w[3]});
+        else
+          st_stream(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.slot) + e0),
+                    u32x2{w[0], w[1]});
+      } else {
+        u32x4* sp = reinterpret_cast<u32x4*>(static_cast<uint32_t*>(a.slot) + e0);
+#pragma unroll
+        for (int k = 0; k < VEC / 4; ++k)
+          st_stream(sp + k, u32x4{sl[4 * k], sl[4 * k + 1], sl[4 * k + 2], sl[4 * k + 3]});
+      }
     }
     st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * G + r, L16::pack(o));
     u32x4* ap = reinterpret_cast<u32x4*>(a.arg + static_cast<size_t>(row) * F + r * VEC);
@@ -144,16 +204,20 @@ struct Red : RowIO<T, G, G> {
                               static_cast<unsigned>(ar[4 * k + 3])});
   }
 
+  __device__ __forceinline__ static void st_int(int32_t* base, int r, const int* x) {
+    u32x4* p = reinterpret_cast<u32x4*>(base + r * VEC);
+#pragma unroll
+    for (int k = 0; k < VEC / 4; ++k)
+      st_stream(p + k, u32x4{static_cast<unsigned>(x[4 * k]), static_cast<unsigned>(x[4 * k + 1]),
+                             static_cast<unsigned>(x[4 * k + 2]),
+                             static_cast<unsigned>(x[4 * k + 3])});
+  }
+
   __device__ __forceinline__ static void write_partial(const RedArgs& a, int chunk, int r,
                                                        const State& s) {
     IO::store_f32(a.ws_val + static_cast<size_t>(chunk) * F, r, s.v);
-    u32x4* ip = reinterpret_cast<u32x4*>(a.ws_idx + static_cast<size_t>(chunk) * F + r * VEC);
-#pragma unroll
-    for (int k = 0; k < VEC / 4; ++k)
-      st_stream(ip + k, u32x4{static_cast<unsigned>(s.id[4 * k]),
-                              static_cast<unsigned>(s.id[4 * k + 1]),
-                              static_cast<unsigned>(s.id[4 * k + 2]),
-                              static_cast<unsigned>(s.id[4 * k + 3])});
+    if constexpr (!SORTED) st_int(a.ws_idx + static_cast<size_t>(chunk) * F, r, s.id);
+    st_int(a.ws_pos + static_cast<size_t>(chunk) * F, r, s.pos);
   }
 
   __device__ __forceinline__ static void fold_partial(const RedArgs& a, int chunk, int r,
@@ -162,27 +226,73 @@ struct Red : RowIO<T, G, G> {
         reinterpret_cast<const f32x4*>(a.ws_val + static_cast<size_t>(chunk) * F + r * VEC);
     const u32x4* ip =
         reinterpret_cast<const u32x4*>(a.ws_idx + static_cast<size_t>(chunk) * F + r * VEC);
+    const u32x4* pp =
+        reinterpret_cast<const u32x4*>(a.ws_pos + static_cast<size_t>(chunk) * F + r * VEC);
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k) {
       const f32x4 v = ld_stream(vp + k);
-      const u32x4 i = ld_stream(ip + k);
+      const u32x4 i = SORTED ? u32x4{} : ld_stream(ip + k);
+      const u32x4 q4 = ld_stream(pp + k);
       const float vv[4] = {v.x, v.y, v.z, v.w};
       const int ii[4] = {static_cast<int>(i.x), static_cast<int>(i.y), static_cast<int>(i.z),
                          static_cast<int>(i.w)};
+      const int qq[4] = {static_cast<int>(q4.x), static_cast<int>(q4.y), static_cast<int>(q4.z),
+                         static_cast<int>(q4.w)};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = 4 * k + q;
-        const bool t = better(vv[q], ii[q], s.v[c], s.id[c]);
+        const bool t = better3(vv[q], ii[q], qq[q], s.v[c], s.id[c], s.pos[c]);
         s.v[c] = t ? vv[q] : s.v[c];
-        s.id[c] = t ? ii[q] : s.id[c];
+        if constexpr (!SORTED) s.id[c] = t ? ii[q] : s.id[c];
+        s.pos[c] = t ? qq[q] : s.pos[c];
       }
     }
   }
 
   // ---- backward over transpose columns ---------------------------------------------
-  // Destinations [e0, e1) of column j (cs = the column's first position, for the
-  // duplicate test across a chunk boundary).
-  template <int NGS>
+  // The lane's VEC match keys of destination row i: arg ids, or slots (row positions).
+  template <int MODE>
+  __device__ __forceinline__ static void load_keys(const RedArgs& a, int i, int r,
+                                                   unsigned* key) {
+    const size_t e0 = static_cast<size_t>(i) * F + r * VEC;
+    if constexpr (MODE == kMatchSlot16) {
+      const uint16_t* sp = static_cast<const uint16_t*>(a.slot_in) + e0;
+      unsigned w[VEC / 2];
+      if constexpr (VEC == 8) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(sp);
+        w[0] = x.x;
+        w[1] = x.y;
+        w[2] = x.z;
+        w[3] = x.w;
+      } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(sp);
+        w[0] = x.x;
+        w[1] = x.y;
+      }
+#pragma unroll
+      for (int k = 0; k < VEC / 2; ++k) {
+        key[2 * k] = w[k] & 0xffffu;
+        key[2 * k + 1] = w[k] >> 16;
+      }
+    } else {
+      const u32x4* kp = reinterpret_cast<const u32x4*>(
+          MODE == kMatchArg ? static_cast<const void*>(a.arg_in + e0)
+                            : static_cast<const void*>(static_cast<const uint32_t*>(a.slot_in) + e0));
+#pragma unroll
+      for (int k = 0; k < VEC / 4; ++k) {
+        const u32x4 x = kp[k];
+        key[4 * k] = x.x;
+        key[4 * k + 1] = x.y;
+        key[4 * k + 2] = x.z;
+        key[4 * k + 3] = x.w;
+      }
+    }
+  }
+
+  // Destinations [e0, e1) of column j (cs = the column's first position). An element of
+  // destination i matches when its arg is j (arg mode; a repeated i, a parallel edge, is
+  // skipped) or when its slot is this transpose entry's position in row i (slot modes).
+  template <int NGS, int MODE>
   __device__ __forceinline__ static void run_cols(const RedArgs& a, int j, int e0, int e1,
                                                   int cs, int seg0, int gs, int r, acc_t* s) {
     constexpr int L = NGS * G;
@@ -193,40 +303,43 @@ struct Red : RowIO<T, G, G> {
       const int li = lane - seg0;
       const int p = base + li;
       const int my_i = (li < nb) ? ld_stream(a.rowidx + p) : 0;
-      // previous destination of the column (-1 at its start): equal ids are adjacent
-      const int my_prev = (li < nb && p > cs) ? ld_stream(a.rowidx + p - 1) : -1;
+      // arg mode: the previous destination of the column (-1 at its start; equal ids are
+      // adjacent); slot modes: this entry's position within its CSR row
+      int my_k;
+      if constexpr (MODE == kMatchArg)
+        my_k = (li < nb && p > cs) ? ld_stream(a.rowidx + p - 1) : -1;
+      else
+        my_k = (li < nb) ? ld_stream(a.csc_rel + p) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int ii[U];
+        unsigned want[U];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int pos = t + u * NGS + gs;
           const int src = seg0 + (pos < nb ? pos : t);
           ii[u] = __shfl(my_i, src);
-          const int prev = __shfl(my_prev, src);  // every lane takes part in the shuffle
-          ok[u] = pos < nb && prev != ii[u];
+          const int k = __shfl(my_k, src);  // every lane takes part in the shuffles
+          if constexpr (MODE == kMatchArg) {
+            ok[u] = pos < nb && k != ii[u];
+            want[u] = static_cast<unsigned>(j);
+          } else {
+            ok[u] = pos < nb;
+            want[u] = static_cast<unsigned>(k);
+          }
         }
-        u32x4 ar[U][VEC / 4];
+        unsigned key[U][VEC];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const u32x4* ap =
-              reinterpret_cast<const u32x4*>(a.arg_in + static_cast<size_t>(ii[u]) * F + r * VEC);
-#pragma unroll
-          for (int k = 0; k < VEC / 4; ++k) ar[u][k] = ap[k];
-        }
+        for (int u = 0; u < U; ++u) load_keys<MODE>(a, ii[u], r, key[u]);
         bool hit[U][VEC];
         bool any[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           any[u] = false;
 #pragma unroll
-          for (int k = 0; k < VEC / 4; ++k) {
-            const unsigned w[4] = {ar[u][k].x, ar[u][k].y, ar[u][k].z, ar[u][k].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              hit[u][4 * k + q] = ok[u] && static_cast<int>(w[q]) == j;
-              any[u] |= hit[u][4 * k + q];
-            }
+          for (int c = 0; c < VEC; ++c) {
+            hit[u][c] = ok[u] && key[u][c] == want[u];
+            any[u] |= hit[u][c];
           }
         }
         raw_t dr[U];
@@ -249,9 +362,9 @@ struct Red : RowIO<T, G, G> {
   }
 };
 
-template <typename T, int G, int OP, int U>
+template <typename T, int G, int OP, int U, bool SORTED>
 __global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a) {
-  using K = Red<T, G, OP, U>;
+  using K = Red<T, G, OP, U, SORTED>;
   constexpr int NG = K::NG;
   const int lane = threadIdx.x & (kWave - 1);
   const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -277,20 +390,21 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a) {
     if (chunk)
       K::write_partial(a, item, r, s);
     else
-      K::write_row(a, row, r, s);
+      K::write_row(a, row, e0, r, s);
     return;
   }
   const int li = (item - B.n_chunks - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int row = B.light[li];
-  K::template run<1>(a, a.indptr[row], a.indptr[row + 1], g * G, 0, r, s);
-  K::write_row(a, row, r, s);
+  const int e0 = a.indptr[row];
+  K::template run<1>(a, e0, a.indptr[row + 1], g * G, 0, r, s);
+  K::write_row(a, row, e0, r, s);
 }
 
 // One wavefront per hub row: group g folds chunks c0+g, c0+g+NG, ..., then the butterfly.
-template <typename T, int G, int OP>
+template <typename T, int G, int OP, bool SORTED>
 __global__ __launch_bounds__(kBlock) void reduce_fwd_merge(RedArgs a) {
-  using K = Red<T, G, OP, 1>;
+  using K = Red<T, G, OP, 1, SORTED>;
   constexpr int NG = K::NG;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int lane = threadIdx.x & (kWave - 1);
@@ -303,10 +417,10 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_merge(RedArgs a) {
 #pragma unroll 4
   for (int c = c0 + g; c < c1; c += NG) K::fold_partial(a, c, r, s);
   K::template combine<NG>(s);
-  if (g == 0) K::write_row(a, row, r, s);
+  if (g == 0) K::write_row(a, row, a.indptr[row], r, s);
 }
 
-template <typename T, int G, int U>
+template <typename T, int G, int U, int MODE>
 __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
   using K = Red<T, G, kReduceMax, U>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
@@ -329,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
       e0 = a.colptr[col];
       e1 = a.colptr[col + 1];
     }
-    K::template run_cols<NG>(a, col, e0, e1, a.colptr[col], 0, g, r, s);
+    K::template run_cols<NG, MODE>(a, col, e0, e1, a.colptr[col], 0, g, r, s);
     K::template group_sum<NG>(s);
     if (g != 0) return;
     if (chunk)
@@ -342,7 +456,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
   if (li >= B.n_light) return;
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
-  K::template run_cols<1>(a, col, e0, e1, e0, g * G, 0, r, s);
+  K::template run_cols<1, MODE>(a, col, e0, e1, e0, g * G, 0, r, s);
   K::store(a.dx, col, r, s, 1.f);
 }
 
@@ -385,20 +499,30 @@ int launch_g(bool backward, int op, const RedArgs& a, void* stream, TimerHook ho
   };
   int e;
   if (backward) {
-    if ((e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd>, items_of(a.cols))))
-      return e;
+    const int64_t w = items_of(a.cols);
+    if (!a.slot_in)
+      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchArg>, w);
+    else if (a.slot_bytes == 2)
+      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot16>, w);
+    else
+      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot32>, w);
+    if (e) return e;
     return go("reduce_bwd_merge", reduce_bwd_merge<T, G>, a.cols.n_hub);
   }
-  if (op == kReduceMax) {
-    if ((e = go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMax, kUnrollRed>,
+  auto fwd = [&](auto op_tag, auto sorted_tag) -> int {
+    constexpr int OPV = decltype(op_tag)::value;
+    constexpr bool SRT = decltype(sorted_tag)::value;
+    int r;
+    if ((r = go("reduce_fwd_main", reduce_fwd_main<T, G, OPV, kUnrollRed, SRT>,
                 items_of(a.rows))))
-      return e;
-    return go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax>, a.rows.n_hub);
-  }
-  if ((e = go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMin, kUnrollRed>,
-              items_of(a.rows))))
-    return e;
-  return go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin>, a.rows.n_hub);
+      return r;
+    return go("reduce_fwd_merge", reduce_fwd_merge<T, G, OPV, SRT>, a.rows.n_hub);
+  };
+  using Max = std::integral_constant<int, kReduceMax>;
+  using Min = std::integral_constant<int, kReduceMin>;
+  if (op == kReduceMax)
+    return a.rows_sorted ? fwd(Max{}, std::true_type{}) : fwd(Max{}, std::false_type{});
+  return a.rows_sorted ? fwd(Min{}, std::true_type{}) : fwd(Min{}, std::false_type{});
 }
 
 template <typename T>

@@ -260,14 +260,16 @@ def test_default_opts():
     assert o["build_csc"] == 1
 
 
-def _rfwd(p, op=capi.GA_REDUCE_MAX, dtype=capi.GA_BF16, F=256, ptrs=None, ws=FAKE, wsb=1 << 30):
+def _rfwd(p, op=capi.GA_REDUCE_MAX, dtype=capi.GA_BF16, F=256, ptrs=None, slot=FAKE, ws=FAKE,
+          wsb=1 << 30):
     ptrs = ptrs or [FAKE] * 3
     return capi.raw_status("graph_attn_reduce_fwd", p.handle if p else None, op, dtype, F,
-                           *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb, None)
+                           *[c_void_p(x) for x in ptrs], c_void_p(slot), c_void_p(ws), wsb,
+                           None)
 
 
 def _rbwd(p, dtype=capi.GA_BF16, F=256, ptrs=None, ws=FAKE, wsb=1 << 30):
-    ptrs = ptrs or [FAKE] * 3
+    ptrs = ptrs or [FAKE] * 4           # arg, slot, dout, dx
     return capi.raw_status("graph_attn_reduce_bwd", p.handle if p else None, dtype, F,
                            *[c_void_p(x) for x in ptrs], c_void_p(ws), wsb, None)
 
@@ -290,7 +292,7 @@ def test_reduce_argument_checks_before_any_hip_call():
     # declared workspace formulas
     for F in (16, 64, 256, 512):
         assert _rws(p, "graph_attn_reduce_fwd_workspace_bytes", F) == \
-            2 * al(info["n_row_chunks"] * F * 4)
+            3 * al(info["n_row_chunks"] * F * 4)
         assert _rws(p, "graph_attn_reduce_bwd_workspace_bytes", F) == \
             al(info["n_col_chunks"] * F * 4)
     nfw = _rws(p, "graph_attn_reduce_fwd_workspace_bytes", 256)
@@ -309,6 +311,8 @@ def test_reduce_argument_checks_before_any_hip_call():
         assert _rfwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
         ptrs[i] = FAKE + 8
         assert _rfwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
+    assert _rfwd(p, slot=0) == capi.GA_ERR_NOT_READY               # slot is optional
+    assert _rfwd(p, slot=FAKE + 8) == capi.GA_ERR_INVALID_ARG       # but aligned if given
     assert _rfwd(p, ws=0) == capi.GA_ERR_WORKSPACE
     assert _rfwd(p, wsb=nfw - 1) == capi.GA_ERR_WORKSPACE
     assert _rfwd(p, wsb=nfw) == capi.GA_ERR_NOT_READY               # valid, not uploaded
@@ -316,8 +320,12 @@ def test_reduce_argument_checks_before_any_hip_call():
     # backward
     assert _rbwd(None) == capi.GA_ERR_INVALID_ARG
     assert _rbwd(p, F=12) == capi.GA_ERR_UNSUPPORTED
-    for i in range(3):
-        ptrs = [FAKE] * 3
+    assert _rbwd(p, ptrs=[0, FAKE, FAKE, FAKE]) == capi.GA_ERR_NOT_READY   # slot replaces arg
+    assert _rbwd(p, ptrs=[FAKE, 0, FAKE, FAKE]) == capi.GA_ERR_NOT_READY   # arg without slot
+    assert _rbwd(p, ptrs=[0, 0, FAKE, FAKE]) == capi.GA_ERR_INVALID_ARG    # neither
+    assert _rbwd(p, ptrs=[FAKE, FAKE + 4, FAKE, FAKE]) == capi.GA_ERR_INVALID_ARG
+    for i in (2, 3):
+        ptrs = [FAKE] * 4
         ptrs[i] = 0
         assert _rbwd(p, ptrs=ptrs) == capi.GA_ERR_INVALID_ARG
     assert _rbwd(p, wsb=nbw - 1) == capi.GA_ERR_WORKSPACE
@@ -329,3 +337,13 @@ def test_reduce_argument_checks_before_any_hip_call():
     assert _rws(q, "graph_attn_reduce_bwd_workspace_bytes", 256) == 0
     assert _rfwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY
     assert _rbwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY
+    # slot width: 2 bytes unless some row has more than 65536 edges
+    b = c_size_t()
+    capi.graph_attn_reduce_slot_bytes(p.handle, byref(b))
+    assert b.value == 2
+    big = Plan(*gg.csr_from_edges(3, np.zeros(65537, np.int64), np.full(65537, 1)))
+    capi.graph_attn_reduce_slot_bytes(big.handle, byref(b))
+    assert b.value == 4
+    ok = Plan(*gg.csr_from_edges(3, np.zeros(65536, np.int64), np.full(65536, 1)))
+    capi.graph_attn_reduce_slot_bytes(ok.handle, byref(b))
+    assert b.value == 2

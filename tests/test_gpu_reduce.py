@@ -13,7 +13,8 @@ import torch
 import graphgen as gg
 from oracle import planner as P
 from oracle import reduction as R
-from sparse_graph_attention_02_amd import Plan, graph_reduce, reduce_bwd, reduce_fwd
+from sparse_graph_attention_02_amd import (Plan, graph_reduce, reduce_bwd, reduce_fwd,
+                                           reduce_slot_dtype)
 from tests.gpu_util import check, dev, host64
 
 pytestmark = pytest.mark.gpu
@@ -42,10 +43,20 @@ def oracle_bits(vals, dtype):
     return v32.view(np.int32)
 
 
+def slot_values(slot):
+    """GPU slot tensor -> int64 row positions (all-ones -> -1)."""
+    s = slot.cpu().numpy()
+    if s.dtype == np.int16:
+        v = s.view(np.uint16).astype(np.int64)
+        return np.where(v == 0xFFFF, -1, v)
+    v = s.view(np.uint32).astype(np.int64)
+    return np.where(v == 0xFFFFFFFF, -1, v)
+
+
 def fwd_exact(tag, ip, ix, x, dtype, op, rows=None, **plan_kw):
     say(tag, op, "N", ip.size - 1, "E", ix.size, "shape", x.shape, dtype, plan_kw)
     plan = Plan(ip, ix, **plan_kw).upload()
-    out, arg = reduce_fwd(plan, dev(x), op=op)
+    out, arg, slot = reduce_fwd(plan, dev(x), op=op)
     torch.cuda.synchronize()
     rows = np.arange(ip.size - 1) if rows is None else np.asarray(rows)
     ro, ra = R.reduce_rows(ip, ix, x, rows, op)
@@ -57,16 +68,23 @@ def fwd_exact(tag, ip, ix, x, dtype, op, rows=None, **plan_kw):
                           f"{np.argwhere(bad)[0]}: got {ga[bad][0]} ref {ra[bad][0]}"
     gb = bits(out[rt].reshape(len(rows), F))
     assert np.array_equal(gb, oracle_bits(ro, dtype)), f"{tag}: out bits differ"
-    return plan, out, arg, ra
+    gs = slot_values(slot[rt].reshape(len(rows), F))
+    assert np.array_equal(gs, R.slots_of(ip, ix, rows, ra)), f"{tag}: slots differ"
+    return plan, out, (arg, slot), ra
 
 
-def bwd_parity(tag, plan, ip, ix, arg, ref_arg, dout, dtype):
-    """The GPU backward on the GPU forward's arg; the oracle backward on its own arg (the
-    two args were just shown to be identical)."""
+def bwd_parity(tag, plan, ip, ix, arg_slot, ref_arg, dout, dtype):
+    """The GPU backward on the GPU forward's slot, and on its arg; the oracle backward on
+    its own arg (the forward outputs were just shown to be identical).  Both GPU modes
+    must agree bit for bit (same terms, same order)."""
+    arg, slot = arg_slot
     say(tag, "backward", "N", ip.size - 1, "E", ix.size, dtype)
-    dx = reduce_bwd(plan, arg, dev(dout))
+    td = dev(dout)
+    dx = reduce_bwd(plan, None, td, slot=slot)
+    dx_arg = reduce_bwd(plan, arg, td)
     torch.cuda.synchronize()
     ref = R.reduce_backward(ref_arg, dout, ip.size - 1)
+    assert torch.equal(dx, dx_arg), f"{tag}: slot and arg backward differ"
     return dx, check(f"{tag} dx", host64(dx).reshape(ref.shape), ref, dtype)
 
 
@@ -106,10 +124,16 @@ def test_every_row_width(dtype, F):
     ip, ix = gg.random_multigraph(600, 4000, rng, hub_rows=(3, 77), hub_deg=700)
     x = gg.normal_features(rng, (600, F), dtype)
     dout = gg.normal_features(rng, (600, F), dtype)
+    shuffled = ix.copy()                      # the same graph with rows in random order
+    for i in range(600):
+        rng.shuffle(shuffled[ip[i]:ip[i + 1]])
     for op in ("max", "min"):
-        plan, out, arg, ra = fwd_exact(f"width {F}", ip, ix, x, dtype, op, light_max_deg=4,
-                                       hub_min_deg_exclusive=64, hub_chunk=40)
-        bwd_parity(f"width {F} {op}", plan, ip, ix, arg, ra, dout, dtype)
+        for tag, idx in (("sorted", ix), ("unsorted", shuffled)):
+            plan, out, arg, ra = fwd_exact(f"width {F} {tag}", ip, idx, x, dtype, op,
+                                           light_max_deg=4, hub_min_deg_exclusive=64,
+                                           hub_chunk=40)
+            assert plan.info()["rows_sorted"] == (tag == "sorted")
+            bwd_parity(f"width {F} {op} {tag}", plan, ip, idx, arg, ra, dout, dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -144,7 +168,7 @@ def test_empty_rows_and_graphs():
     for op in ("max", "min"):
         plan, out, arg, ra = fwd_exact("empty rows", ip, ix, x, "bf16", op)
         empty = torch.from_numpy(np.diff(ip) == 0).cuda()
-        assert (arg[empty] == -1).all() and (out[empty] == 0).all()
+        assert (arg[0][empty] == -1).all() and (out[empty] == 0).all()
         dx, _ = bwd_parity("empty rows", plan, ip, ix, arg, ra, dout, "bf16")
         nosrc = torch.from_numpy(np.bincount(ix, minlength=500) == 0).cuda()
         assert (dx[nosrc] == 0).all()
@@ -152,15 +176,15 @@ def test_empty_rows_and_graphs():
     say("no edges")
     plan = Plan(np.zeros(9, np.int32), np.zeros(0, np.int32)).upload()
     xt = torch.randn(8, 64, device="cuda")
-    out, arg = reduce_fwd(plan, xt, op="max")
-    dx = reduce_bwd(plan, arg, torch.randn(8, 64, device="cuda"))
-    assert (out == 0).all() and (arg == -1).all() and (dx == 0).all()
+    out, arg, slot = reduce_fwd(plan, xt, op="max")
+    dx = reduce_bwd(plan, None, torch.randn(8, 64, device="cuda"), slot=slot)
+    assert (out == 0).all() and (arg == -1).all() and (dx == 0).all() and (slot == -1).all()
     # no nodes at all
     say("no nodes")
     plan = Plan(np.zeros(1, np.int32), np.zeros(0, np.int32)).upload()
     z = torch.zeros((0, 64), device="cuda")
-    out, arg = reduce_fwd(plan, z)
-    assert out.shape == (0, 64) and reduce_bwd(plan, arg, z).shape == (0, 64)
+    out, arg, slot = reduce_fwd(plan, z)
+    assert out.shape == (0, 64) and reduce_bwd(plan, arg, z, slot=slot).shape == (0, 64)
 
 
 def test_deterministic_and_autograd():
@@ -175,8 +199,8 @@ def test_deterministic_and_autograd():
     out.backward(g)
     dx1 = reduce_bwd(plan, arg, g)
     assert torch.equal(xt.grad, dx1)
-    out2, arg2 = reduce_fwd(plan, xt.detach(), op="max")
-    dx2 = reduce_bwd(plan, arg2, g)
+    out2, arg2, slot2 = reduce_fwd(plan, xt.detach(), op="max")
+    dx2 = reduce_bwd(plan, None, g, slot=slot2)
     assert torch.equal(out, out2) and torch.equal(arg, arg2) and torch.equal(dx1, dx2)
 
 
@@ -196,10 +220,11 @@ def test_full_chunglu1m_sampled():
     med = rng.choice(np.nonzero((deg > 16) & (deg <= 1024))[0], 40, replace=False)
     light = rng.choice(np.nonzero(deg <= 16)[0], 40, replace=False)
     rows = np.concatenate([hub_rows, med, light])
-    plan, out, arg, _ = fwd_exact("chunglu1m bf16 sampled", ip, ix, x, "bf16", "max",
-                                  rows=rows)
+    plan, out, (arg, slot), _ = fwd_exact("chunglu1m bf16 sampled", ip, ix, x, "bf16", "max",
+                                          rows=rows)
+    assert slot.dtype == torch.int16
     say("chunglu1m backward sampled columns")
-    dx = reduce_bwd(plan, arg, dev(dout))
+    dx = reduce_bwd(plan, None, dev(dout), slot=slot)
     torch.cuda.synchronize()
     colptr, rowidx = P.transpose(ip, ix)
     odeg = np.diff(colptr)
@@ -218,3 +243,19 @@ def test_full_chunglu1m_sampled():
     dref = gg.bf16_bits_to_f32(dout).reshape(N, -1).astype(np.float64)[deg > 0].sum(0)
     scale = np.abs(host64(dx)).reshape(N, -1).sum(0)
     assert np.all(np.abs(tot - dref) <= 2 ** -8 * scale)
+
+
+def test_wide_slots_for_rows_beyond_65536_edges():
+    """A row with more than 65536 edges makes the slots 32-bit; forward and backward in
+    both match modes, with parallel edges in the long row."""
+    rng = np.random.default_rng(21)
+    n = 4000
+    src = np.concatenate([rng.integers(0, n, 70_000), rng.integers(0, n, 20_000)])
+    dst = np.concatenate([np.full(70_000, 11), rng.integers(0, n, 20_000)])
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    x = gg.normal_features(rng, (n, 32), "bf16")
+    dout = gg.normal_features(rng, (n, 32), "bf16")
+    for op in ("max", "min"):
+        plan, out, arg_slot, ra = fwd_exact("wide slots", ip, ix, x, "bf16", op)
+        assert reduce_slot_dtype(plan) == torch.int32 and arg_slot[1].dtype == torch.int32
+        bwd_parity("wide slots", plan, ip, ix, arg_slot, ra, dout, "bf16")

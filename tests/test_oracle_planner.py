@@ -34,6 +34,11 @@ def test_transpose_matches_scipy(name, g):
     same_col = col_of_slot[1:] == col_of_slot[:-1]
     assert np.all(np.diff(m.data)[same_col] > 0)
     assert np.all(np.diff(rowidx)[same_col] >= 0)
+    # and its position within the CSR row it came from
+    rel = P.transpose_positions(ip, ix)
+    assert np.array_equal(rel, m.data - np.asarray(ip, np.int64)[rowidx])
+    assert np.array_equal(np.asarray(ix)[np.asarray(ip, np.int64)[rowidx] + rel],
+                          col_of_slot)
 
 
 @pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")

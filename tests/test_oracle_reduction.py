@@ -207,3 +207,35 @@ def test_backward_invariants_and_parallel_edges():
 def test_nan_is_rejected():
     with pytest.raises(ValueError):
         R.reduce_forward(np.array([0, 1]), np.array([0]), np.array([[math.nan]]))
+
+
+def test_train_step_rows_is_the_row_share_of_the_backward():
+    rng, ip, ix = _graph(9, n=30, m=200)
+    x = rng.standard_normal((30, 4))
+    dout = rng.standard_normal((30, 4))
+    rows = np.array([1, 4, 5, 17, 29])
+    out, arg, ids, dxi = R.train_step_rows(ip, ix, x, dout, rows, "max")
+    full_out, full_arg = R.reduce_forward(ip, ix, x, "max")
+    assert np.array_equal(out, full_out[rows]) and np.array_equal(arg, full_arg[rows])
+    masked = np.full_like(full_arg, -1)
+    masked[rows] = full_arg[rows]
+    dx = R.reduce_backward(masked, dout, 30)
+    assert np.array_equal(dx[ids], dxi) and not np.delete(dx, ids, axis=0).any()
+
+
+def test_slots_point_at_the_first_edge_of_the_winner():
+    rng, ip, ix = _graph(10, n=40, m=900)        # many parallel edges
+    ix = ix.copy()
+    for i in range(40):
+        rng.shuffle(ix[ip[i]:ip[i + 1]])
+    x = rng.integers(-2, 3, size=(40, 6)).astype(float)
+    _, arg = R.reduce_forward(ip, ix, x, "min")
+    sl = R.slots_of(ip, ix, np.arange(40), arg)
+    for i in range(40):
+        J = ix[ip[i]:ip[i + 1]]
+        for c in range(6):
+            k = sl[i, c]
+            assert J[k] == arg[i, c] and not (J[:k] == arg[i, c]).any()
+    e_ip = np.array([0, 0, 2]); e_ix = np.array([0, 0])
+    _, a2 = R.reduce_forward(e_ip, e_ix, np.ones((2, 3)), "max")
+    assert np.array_equal(R.slots_of(e_ip, e_ix, [0, 1], a2), [[-1] * 3, [0] * 3])

@@ -44,6 +44,10 @@ def test_cpp_planner_equals_reference(name, g, tl, th, c):
     info = p.info()
     n = ip.size - 1
     assert info["n_row_hub"] == ref["row_hub"].size
+    ixs = np.asarray(ix, np.int64)
+    same_row = np.repeat(np.arange(n), np.diff(ip))
+    srt = not np.any((np.diff(ixs) < 0) & (same_row[1:] == same_row[:-1])) if ixs.size else True
+    assert info["rows_sorted"] == int(srt)
     assert info["max_in_degree"] == (int(np.diff(ip).max()) if n else 0)
 
 
@@ -69,3 +73,11 @@ def test_threshold_edges_and_chunk_multiples():
     hub = p.array("row_hub")
     expect = {i: -(-degs[i] // c) for i in hub}
     assert [expect[i] for i in hub] == chunks.tolist()
+
+
+def test_rows_sorted_flag():
+    ip = np.array([0, 2, 4, 5])
+    assert Plan(ip, np.array([0, 1, 2, 2, 1])).info()["rows_sorted"] == 1
+    assert Plan(ip, np.array([1, 0, 2, 2, 1])).info()["rows_sorted"] == 0
+    assert Plan(ip, np.array([0, 1, 2, 0, 1])).info()["rows_sorted"] == 0
+    assert Plan(np.array([0, 2, 3]), np.array([1, 1, 0])).info()["rows_sorted"] == 1
