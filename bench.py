@@ -224,6 +224,8 @@ def main():
     ap.add_argument("--light", type=int, default=None)
     ap.add_argument("--hub", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--slices", type=int, default=None,
+                    help="feature slices per XCD group (0 = automatic, 1 = off, 2, 4, 8)")
     ap.add_argument("--order", choices=["as-generated", "out-degree"], default="as-generated",
                     help="node order ablation: relabel nodes by descending out-degree (hot "
                          "source rows contiguous) before the run")
@@ -261,7 +263,7 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     plan = ga.Plan(ip, ix, light_max_deg=args.light, hub_min_deg_exclusive=args.hub,
-                   hub_chunk=args.chunk, build_csc=w.backward)
+                   hub_chunk=args.chunk, build_csc=w.backward, feature_slices=args.slices)
     plan_host_s = time.perf_counter() - t0
     plan.upload("cuda")
     torch.cuda.synchronize()
@@ -392,7 +394,8 @@ def main():
             "plan": {k: info[k] for k in ("light_max_deg", "hub_min_deg_exclusive", "hub_chunk",
                                           "n_row_light", "n_row_medium", "n_row_hub",
                                           "n_row_chunks", "n_col_hub", "n_col_chunks",
-                                          "max_in_degree", "max_out_degree")},
+                                          "max_in_degree", "max_out_degree", "rows_sorted",
+                                          "feature_slices")},
             "parallelism": "single GPU",
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,

@@ -67,13 +67,23 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * (light_max_deg, hub_min_deg_exclusive] is "medium" (one wavefront per row); larger
  * rows are "hubs", cut into chunks of hub_chunk edges that separate wavefronts reduce,
  * merged in ascending chunk order. build_csc != 0 also builds the transpose needed by
- * graph_attn_bwd. Constraints: 0 <= light_max_deg <= hub_min_deg_exclusive,
- * hub_chunk >= 1. */
+ * graph_attn_bwd. feature_slices: the kernels that gather whole feature rows per edge
+ * (the dot and GATv2 forwards, the dot backward's row pass, both reduction passes) split
+ * each row into S slices of whole heads and deal the slices to the GPU's 8 L2 partitions
+ * (XCDs), so each partition caches a slice of every hot row instead of whole rows. Each
+ * slice repeats the per-edge fixed work, so it pays only where rows are wide: 0 =
+ * automatic (the dot forward and the dot backward's row pass, which gather two rows per
+ * edge, take the largest S dividing 8 whose slices are at least 256 bytes; the other
+ * kernels 1), 1 = off, 2, 4 or 8 = that many slices for every kernel named above,
+ * lowered until they hold whole heads of at least 64 bytes. Results agree to rounding
+ * (bit for bit for the reduction, whose selection is exact). Constraints: 0 <= light_max_deg <= hub_min_deg_exclusive,
+ * hub_chunk >= 1, feature_slices in {0, 1, 2, 4, 8}. */
 typedef struct {
   int32_t light_max_deg;
   int32_t hub_min_deg_exclusive;
   int32_t hub_chunk;
   int32_t build_csc;
+  int32_t feature_slices;
 } ga_plan_opts;
 
 /* Counts describing a built plan (all int64 so the struct has no padding). */
@@ -87,6 +97,7 @@ typedef struct {
   int64_t device_bytes;
   int64_t uploaded;
   int64_t rows_sorted;  /* 1 when every row's neighbour ids are non-decreasing */
+  int64_t feature_slices;  /* the option as given (0 = automatic) */
 } ga_plan_info;
 
 typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */

@@ -61,14 +61,14 @@ class Plan:
     built on the host by the library's planner; ``upload`` copies it to the GPU."""
 
     def __init__(self, indptr, indices, *, light_max_deg=None, hub_min_deg_exclusive=None,
-                 hub_chunk=None, build_csc=True):
+                 hub_chunk=None, build_csc=True, feature_slices=None):
         ip = np.ascontiguousarray(indptr, dtype=np.int32)
         ix = np.ascontiguousarray(indices, dtype=np.int32)
         opts = capi.ga_plan_opts()
         graph_attn_plan_opts_default(byref(opts))
         for k, v in (("light_max_deg", light_max_deg),
                      ("hub_min_deg_exclusive", hub_min_deg_exclusive),
-                     ("hub_chunk", hub_chunk)):
+                     ("hub_chunk", hub_chunk), ("feature_slices", feature_slices)):
             if v is not None:
                 setattr(opts, k, int(v))
         opts.build_csc = 1 if build_csc else 0

@@ -218,6 +218,7 @@ ga_status graph_attn_plan_opts_default(ga_plan_opts* o) {
   o->hub_min_deg_exclusive = 1024;
   o->hub_chunk = 512;
   o->build_csc = 1;
+  o->feature_slices = 0;
   return GA_OK;
 }
 
@@ -261,6 +262,7 @@ ga_status graph_attn_plan_get_info(const ga_plan* p, ga_plan_info* info) {
   info->hub_chunk = p->opts.hub_chunk;
   info->device_bytes = static_cast<int64_t>(device_layout(p, nullptr));
   info->rows_sorted = p->rows_sorted ? 1 : 0;
+  info->feature_slices = p->opts.feature_slices;
   info->uploaded = p->uploaded;
   return GA_OK;
 }
@@ -401,6 +403,12 @@ ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
                    : nullptr;
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
+  args.ld = g.G;
+  args.hf = g.heads;
+  // GAT-style scores gather t_j per head, a partial line per slice: not sliced
+  args.slices = score == GA_SCORE_DOT ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
+                                                           ga::kAutoSliceLanesTwoRows)
+                                      : 1;
   const int rc = ga::launch_fwd(dtype, score == GA_SCORE_DOT ? ga::kModeDot : ga::kModeGat, g,
                                 args, p->n, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
@@ -443,6 +451,9 @@ ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
                    : nullptr;
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
+  args.ld = g.G;
+  args.hf = g.heads;
+  args.slices = ga::feature_slices(g.G, g.LH, p->opts.feature_slices, 0);
   const int rc = ga::launch_fwd(dtype, ga::kModeGatV2, g, args, p->n, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
@@ -500,6 +511,10 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.scale = scale;
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
+  args.ld = g.G;
+  args.hf = g.heads;
+  args.slices = ga::feature_slices(g.G, g.LH, p->opts.feature_slices, ga::kAutoSliceLanesTwoRows);
+  args.dq_stride = static_cast<int>(ga::dq_partial_floats(heads, dim));
   const int rc = score == GA_SCORE_DOT ? ga::launch_bwd(dtype, g, args, p->n, stream, active_hook())
                                        : ga::launch_bwd_gat(dtype, g, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
@@ -617,6 +632,8 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   args.slot = slot;
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.rows_sorted = p->rows_sorted;
+  args.ld = G;
+  args.slices = ga::feature_slices(G, 1, p->opts.feature_slices, 0);
   if (need > 0) {
     args.ws_val = static_cast<float*>(ws);
     args.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 3);
@@ -654,6 +671,8 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   args.slot_in = slot;
   args.csc_rel = p->d_csc_rel;
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
+  args.ld = G;
+  args.slices = ga::feature_slices(G, 1, p->opts.feature_slices, 0);
   args.dout = dout;
   args.dx = dx;
   args.ws_sum = need > 0 ? static_cast<float*>(ws) : nullptr;

@@ -71,8 +71,8 @@ struct Bwd : RowIO<T, G, LH> {
         raw_t kr[U], vr[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          kr[u] = Kr[static_cast<size_t>(jj[u]) * G + r];
-          vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
+          kr[u] = Kr[static_cast<size_t>(jj[u]) * a.ld + r];
+          vr[u] = Vr[static_cast<size_t>(jj[u]) * a.ld + r];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -147,10 +147,10 @@ struct Bwd : RowIO<T, G, LH> {
   // Row prologue of the dQ pass: q and dout slices, lse in log2 units.
   __device__ __forceinline__ static void row_prologue(const BwdArgs& a, int row, int r, int h,
                                                       raw_t& qr, raw_t& dor, float& lse2) {
-    const size_t off = static_cast<size_t>(row) * G + r;
+    const size_t off = static_cast<size_t>(row) * a.ld + r;
     qr = ld_stream(R(a.q) + off);
     dor = ld_stream(R(a.dout) + off);
-    lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
+    lse2 = ld_stream(a.lse + static_cast<size_t>(row) * a.hf + h) * kLog2e;
   }
 
   // Row-pass epilogue: dq = scale (A - D^ B) / L in the feature dtype, and the record
@@ -163,22 +163,36 @@ struct Bwd : RowIO<T, G, LH> {
     float x[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) x[c] = fmaf(-Dn, Bk[c], A[c]);
-    store(a.dq, row, r, x, a.scale * inv);
+    store(a.dq, row, r, x, a.scale * inv, a.ld);
     if (r % LH == 0)
-      st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * H + h,
+      st_stream(reinterpret_cast<f32x2*>(a.ws_ld) + static_cast<size_t>(row) * a.hf + h,
                 f32x2{Lp > 0.f ? lse2 + __log2f(Lp) : lse2, Dn});
   }
 
 };
 
-// dQ pass. Hub-row chunk partial layout in ws_dq: [chunk][A: F | B: F | D: H, padded to 4]
-// fp32 (kDqStride floats per chunk, a multiple of 4 so the 16-byte stores stay aligned).
+// dQ pass. Hub-row chunk partial layout in ws_dq (full row of F_full elements and H_full
+// heads): [chunk][A: F_full | B: F_full | D: H_full | L: H_full, padded to 4] fp32
+// (a.dq_stride floats per chunk, a multiple of 4 so the 16-byte stores stay aligned). The
+// main kernel works on a feature slice of G lanes (whole heads; see fwd_main); each slice
+// writes its part of A, B, D and L.
 template <typename T, int G, int LH, int U>
-__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
   using K = Bwd<T, G, LH, U>;
-  constexpr int NG = K::NG, VEC = K::VEC, H = K::H, F = K::F;
+  using raw_t = typename K::raw_t;
+  constexpr int NG = K::NG, VEC = K::VEC, H = K::H;
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const SliceItem si = slice_of(a0.slices);
+  const int item = si.item;
+  const int so = si.slice * G, ho = si.slice * H;  // lanes / heads before this slice
+  BwdArgs a = a0;
+  a.q = static_cast<const raw_t*>(a0.q) + so;
+  a.k = static_cast<const raw_t*>(a0.k) + so;
+  a.v = static_cast<const raw_t*>(a0.v) + so;
+  a.dout = static_cast<const raw_t*>(a0.dout) + so;
+  a.dq = static_cast<raw_t*>(a0.dq) + so;
+  a.lse = a0.lse + ho;
+  a.ws_ld = a0.ws_ld + 2 * ho;
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.rows;
   typename K::raw_t qr, dor;
@@ -205,12 +219,13 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a) {
     K::template group_sum1<NG>(Lp);
     if (g != 0) return;
     if (chunk) {
-      float* p = a.ws_dq + static_cast<size_t>(item) * K::kDqStride;
-      K::store_f32(p, r, A);
-      K::store_f32(p + F, r, Bk);
+      const int Ff = a.ld * VEC;  // elements of the full row
+      float* p = a.ws_dq + static_cast<size_t>(item) * a.dq_stride;
+      K::store_f32(p + so * VEC, r, A);
+      K::store_f32(p + Ff + so * VEC, r, Bk);
       if (r % LH == 0) {
-        st_stream(p + 2 * F + h, D);
-        st_stream(p + 2 * F + H + h, Lp);
+        st_stream(p + 2 * Ff + ho + h, D);
+        st_stream(p + 2 * Ff + a.hf + ho + h, Lp);
       }
     } else {
       K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
@@ -243,7 +258,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
 #pragma unroll 4
   for (int c = c0 + g; c < c1; c += NG) {
-    const float* p = a.ws_dq + static_cast<size_t>(c) * K::kDqStride;
+    const float* p = a.ws_dq + static_cast<size_t>(c) * a.dq_stride;
     K::add_f32(p, r, A);
     K::add_f32(p + F, r, Bk);
     D += ld_stream(p + 2 * F + h);
@@ -254,7 +269,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
   K::template group_sum1<NG>(D);
   K::template group_sum1<NG>(Lp);
   if (g != 0) return;
-  const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
+  const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * a.hf + h) * kLog2e;
   K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
 }
 
@@ -338,34 +353,42 @@ __global__ __launch_bounds__(kBlock) void bwd_dkdv_merge(BwdArgs a) {
 }
 
 template <typename T, int G, int LH>
-int launch(const BwdArgs& a, void* stream, TimerHook hook) {
-  constexpr int NG = kWave / G;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  auto items_of = [](const DevBins& B) {
+struct Launcher {
+  static constexpr int NG = kWave / G;
+  static int64_t items_of(const DevBins& B) {
     return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
-  };
-  auto go = [&](const char* name, auto kernel, int64_t blocks) -> int {
+  }
+  template <typename Kern>
+  static int go(const char* name, Kern kernel, int64_t blocks, const BwdArgs& a, void* stream,
+                TimerHook hook) {
     if (blocks <= 0) return 0;
     if (hook) hook(name, stream, 1);
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
     if (hook) hook(name, stream, 0);
     return static_cast<int>(hipGetLastError());
-  };
-  int e;
-  if ((e = go("bwd_dq_main", bwd_dq_main<T, G, LH, GA_UNROLL_DQ>,
-              (items_of(a.rows) + kWavesPerBlock - 1) / kWavesPerBlock)))
-    return e;
-  if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>,
-              (a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock)))
-    return e;
-  if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, GA_UNROLL_DKDV>,
-              (items_of(a.cols) + kWavesPerBlock - 1) / kWavesPerBlock)))
-    return e;
-  if ((e = go("bwd_dkdv_merge", bwd_dkdv_merge<T, G, LH>,
-              (a.cols.n_hub + kWavesPerBlock - 1) / kWavesPerBlock)))
-    return e;
-  return 0;
-}
+  }
+  // dQ main pass on the slice geometry (G lanes per slice, a.slices slices)
+  static int dq_main(const BwdArgs& a, void* stream, TimerHook hook) {
+    const int64_t items = items_of(a.rows);
+    if (items <= 0) return 0;
+    return go("bwd_dq_main", bwd_dq_main<T, G, LH, GA_UNROLL_DQ>,
+              slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices), a, stream,
+              hook);
+  }
+  // the rest on the full row geometry
+  static int rest(const BwdArgs& a, void* stream, TimerHook hook) {
+    int e;
+    if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>,
+                (a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock, a, stream, hook)))
+      return e;
+    if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, GA_UNROLL_DKDV>,
+                (items_of(a.cols) + kWavesPerBlock - 1) / kWavesPerBlock, a, stream, hook)))
+      return e;
+    return go("bwd_dkdv_merge", bwd_dkdv_merge<T, G, LH>,
+              (a.cols.n_hub + kWavesPerBlock - 1) / kWavesPerBlock, a, stream, hook);
+  }
+};
 
 #define GA_GEOMS(X)                                                                       \
   X(4, 2) X(4, 4) X(8, 2) X(8, 4) X(8, 8) X(16, 2) X(16, 4) X(16, 8) X(16, 16) X(32, 2) \
@@ -374,8 +397,15 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
 
 template <typename T>
 int dispatch(const Geometry& g, const BwdArgs& a, void* stream, TimerHook hook) {
+  const int GS = g.G / a.slices;
+  int e = -1;
 #define GA_CASE(GG, LL) \
-  if (g.G == GG && g.LH == LL) return launch<T, GG, LL>(a, stream, hook);
+  if (GS == GG && g.LH == LL) e = Launcher<T, GG, LL>::dq_main(a, stream, hook);
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  if (e) return e;
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return Launcher<T, GG, LL>::rest(a, stream, hook);
   GA_GEOMS(GA_CASE)
 #undef GA_CASE
   return -1;

@@ -65,9 +65,9 @@ struct Fwd {
   __device__ __forceinline__ static void load_row(const FwdArgs& a, int row, int r, int h,
                                                   RowOp& q) {
     if constexpr (GAT) {
-      q.si = ld_stream(static_cast<const float*>(a.a) + static_cast<size_t>(row) * H + h);
+      q.si = ld_stream(static_cast<const float*>(a.a) + static_cast<size_t>(row) * a.hf + h);
     } else {
-      q.q = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * G + r);
+      q.q = ld_stream(static_cast<const raw_t*>(a.a) + static_cast<size_t>(row) * a.ld + r);
     }
     if constexpr (GATV2) {
       L16::unpack(q.q, q.xd);
@@ -113,13 +113,13 @@ struct Fwd {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if constexpr (GAT)
-            tv[u] = Tt[static_cast<size_t>(jj[u]) * H + h];
+            tv[u] = Tt[static_cast<size_t>(jj[u]) * a.hf + h];
           else
-            kr[u] = Kr[static_cast<size_t>(jj[u]) * G + r];
+            kr[u] = Kr[static_cast<size_t>(jj[u]) * a.ld + r];
           if constexpr (GATV2)
             vr[u] = kr[u];  // the message is the gathered source projection
           else
-            vr[u] = Vr[static_cast<size_t>(jj[u]) * G + r];
+            vr[u] = Vr[static_cast<size_t>(jj[u]) * a.ld + r];
         }
         float s[U];
 #pragma unroll
@@ -191,9 +191,9 @@ struct Fwd {
     float o[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) o[c] = st.acc[c] * inv;
-    st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * G + r, L16::pack(o));
+    st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * a.ld + r, L16::pack(o));
     if (r % LH == 0)
-      st_stream(a.lse + static_cast<size_t>(row) * H + h,
+      st_stream(a.lse + static_cast<size_t>(row) * a.hf + h,
                 st.l > 0.f ? (st.m + __log2f(st.l)) * kLn2 : -INFINITY);
   }
 
@@ -201,9 +201,10 @@ struct Fwd {
                                                        const State& st) {
     if (r % LH == 0) {
       f32x2* ml = reinterpret_cast<f32x2*>(a.ws_ml);
-      st_stream(ml + static_cast<size_t>(chunk) * H + h, f32x2{st.m, st.l});
+      st_stream(ml + static_cast<size_t>(chunk) * a.hf + h, f32x2{st.m, st.l});
     }
-    f32x4* acc = reinterpret_cast<f32x4*>(a.ws_acc + static_cast<size_t>(chunk) * F + r * VEC);
+    f32x4* acc = reinterpret_cast<f32x4*>(a.ws_acc + static_cast<size_t>(chunk) * a.ld * VEC +
+                                          r * VEC);
 #pragma unroll
     for (int c = 0; c < VEC / 4; ++c)
       st_stream(acc + c, f32x4{st.acc[4 * c], st.acc[4 * c + 1], st.acc[4 * c + 2],
@@ -211,12 +212,35 @@ struct Fwd {
   }
 };
 
+// A "slice" is G lanes (whole heads) of a feature row of a.ld lanes; the kernel's template
+// geometry is the slice's. slice_of() deals slices to XCDs (see ga_device.h); each wave
+// moves its operand pointers to its slice, after which row strides (a.ld lanes, a.hf
+// heads) address the full rows.
 template <typename T, int G, int LH, int MODE, int U>
-__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   using K = Fwd<T, G, LH, MODE, U>;
-  constexpr int NG = K::NG;
+  using raw_t = typename K::raw_t;
+  constexpr int NG = K::NG, H = K::H, VEC = K::VEC;
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const SliceItem si = slice_of(a0.slices);
+  const int item = si.item;
+  FwdArgs a = a0;
+  {
+    const int so = si.slice * G, ho = si.slice * H;  // lanes / heads before this slice
+    if constexpr (MODE == kModeGat) {
+      a.a = static_cast<const float*>(a0.a) + ho;
+      a.b = static_cast<const float*>(a0.b) + ho;
+    } else {
+      a.a = static_cast<const raw_t*>(a0.a) + so;
+      a.b = static_cast<const raw_t*>(a0.b) + so;
+    }
+    a.v = static_cast<const raw_t*>(a0.v) + so;
+    a.out = static_cast<raw_t*>(a0.out) + so;
+    a.lse = a0.lse + ho;
+    if (a0.attn) a.attn = a0.attn + so * VEC;
+    a.ws_ml = a0.ws_ml + 2 * ho;
+    a.ws_acc = a0.ws_acc + so * VEC;
+  }
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.bins;
   typename K::State st;
@@ -270,8 +294,9 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   K::init(st);
 #pragma unroll 4
   for (int c = c0 + g; c < c1; c += NG) {
-    const f32x2 p = ld_stream(ml + static_cast<size_t>(c) * H + h);
-    const f32x4* acc = reinterpret_cast<const f32x4*>(a.ws_acc + static_cast<size_t>(c) * F + r * VEC);
+    const f32x2 p = ld_stream(ml + static_cast<size_t>(c) * a.hf + h);
+    const f32x4* acc =
+        reinterpret_cast<const f32x4*>(a.ws_acc + static_cast<size_t>(c) * a.ld * VEC + r * VEC);
     f32x4 x[VEC / 4];
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k) x[k] = ld_stream(acc + k);
@@ -292,31 +317,33 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   if (g == 0) K::write_row(a, row, r, h, st);
 }
 
+// Main kernel on the slice geometry (G lanes per slice), a.slices slices.
 template <typename T, int G, int LH, int MODE>
-int launch(const FwdArgs& a, void* stream, TimerHook hook) {
+int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
   constexpr int U = GA_UNROLL_FWD;
   constexpr int NG = kWave / G;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const DevBins& B = a.bins;
   const int64_t items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
-  if (items > 0) {
-    const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (hook) hook("fwd_main", stream, 1);
-    hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kBlock), 0, s, a);
-    if (hook) hook("fwd_main", stream, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return static_cast<int>(e);
-  }
-  if (B.n_hub > 0) {
-    const int blocks = (B.n_hub + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (hook) hook("fwd_hub_merge", stream, 1);
-    hipLaunchKernelGGL((fwd_hub_merge<T, G, LH>), dim3(blocks), dim3(kBlock), 0, s, a);
-    if (hook) hook("fwd_hub_merge", stream, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return static_cast<int>(e);
-  }
-  return 0;
+  if (items <= 0) return 0;
+  const int64_t blocks = slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices);
+  if (hook) hook("fwd_main", stream, 1);
+  hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+  if (hook) hook("fwd_main", stream, 0);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Hub merge on the full row geometry.
+template <typename T, int G, int LH>
+int launch_merge(const FwdArgs& a, void* stream, TimerHook hook) {
+  const DevBins& B = a.bins;
+  if (B.n_hub <= 0) return 0;
+  const int blocks = (B.n_hub + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (hook) hook("fwd_hub_merge", stream, 1);
+  hipLaunchKernelGGL((fwd_hub_merge<T, G, LH>), dim3(blocks), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), a);
+  if (hook) hook("fwd_hub_merge", stream, 0);
+  return static_cast<int>(hipGetLastError());
 }
 
 // (G, LH) pairs with compiled kernels: rows of 64..1024 bytes, heads of 32..1024 bytes.
@@ -327,8 +354,15 @@ int launch(const FwdArgs& a, void* stream, TimerHook hook) {
 
 template <typename T, int MODE>
 int dispatch(const Geometry& g, const FwdArgs& a, void* stream, TimerHook hook) {
+  const int GS = g.G / a.slices;
+  int e = -1;
 #define GA_CASE(GG, LL) \
-  if (g.G == GG && g.LH == LL) return launch<T, GG, LL, MODE>(a, stream, hook);
+  if (GS == GG && g.LH == LL) e = launch_main<T, GG, LL, MODE>(a, stream, hook);
+  GA_GEOMS(GA_CASE)
+#undef GA_CASE
+  if (e) return e;
+#define GA_CASE(GG, LL) \
+  if (g.G == GG && g.LH == LL) return launch_merge<T, GG, LL>(a, stream, hook);
   GA_GEOMS(GA_CASE)
 #undef GA_CASE
   return -1;

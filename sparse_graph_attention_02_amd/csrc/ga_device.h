@@ -166,14 +166,15 @@ struct RowIO {
   __device__ __forceinline__ static const raw_t* R(const void* p) {
     return static_cast<const raw_t*>(p);
   }
-  // x * mul, converted to T, into row `row` of a [N, H*d] array (streamed store).
+  // x * mul, converted to T, into row `row` of a [N, H*d] array (streamed store); ld = the
+  // row stride in 16-byte lanes (G unless the kernel works on a slice of a wider row).
   template <typename X>
   __device__ __forceinline__ static void store(void* base, int row, int r, const X* x,
-                                               float mul) {
+                                               float mul, int ld = G) {
     float o[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) o[c] = static_cast<float>(x[c] * static_cast<X>(mul));
-    st_stream(static_cast<raw_t*>(base) + static_cast<size_t>(row) * G + r, L16::pack(o));
+    st_stream(static_cast<raw_t*>(base) + static_cast<size_t>(row) * ld + r, L16::pack(o));
   }
   // fp32 row-slice store / accumulate (chunk partials are fp32; X is the accumulator).
   template <typename X>
@@ -212,5 +213,29 @@ struct RowIO {
 };
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Feature slices dealt to XCDs. The hardware hands workgroups to the 8 XCDs round-robin by
+// block id, and each XCD has its own L2. A launch whose work items are split into S feature
+// slices (S dividing 8) maps block b to slice (b mod 8) / (8 / S): every XCD then caches
+// only its slice of the gathered rows, so hot source rows take S times less of its L2 and
+// are re-read S times as often there. Returns the wave's slice and its work item within
+// the slice; the grid is slice_blocks(blocks per slice, S) blocks, and items past the
+// slice's end are the caller's to skip. S = 1 is the plain mapping.
+struct SliceItem {
+  int slice, item;
+};
+__device__ __forceinline__ SliceItem slice_of(int S) {
+  const int wave = threadIdx.x >> 6;
+  if (S == 1) return {0, wave_uniform(blockIdx.x * kWavesPerBlock + wave)};
+  const int q = 8 / S;  // XCDs per slice
+  const int x = blockIdx.x & 7;
+  const int blk = (blockIdx.x >> 3) * q + x % q;
+  return {wave_uniform(x / q), wave_uniform(blk * kWavesPerBlock + wave)};
+}
+inline int64_t slice_blocks(int64_t blocks_per_slice, int S) {
+  if (S == 1) return blocks_per_slice;
+  const int q = 8 / S;
+  return 8 * ((blocks_per_slice + q - 1) / q);
+}
 
 }  // namespace ga

@@ -69,6 +69,31 @@ struct Geometry {
   int LH = 0;  // lanes per head (head bytes / 16)
 };
 
+// Feature slices for a row of G lanes with heads of LH lanes (LH = 1 when the kernel has
+// no heads): S divides 8 and G and a slice holds whole heads. A requested S (2, 4 or 8)
+// is lowered until it fits with slices of at least 4 lanes. requested = 0 (auto) picks the
+// largest S whose slices are at least auto_lanes lanes, or 1 when auto_lanes is 0: each
+// slice repeats the per-edge fixed work (index broadcast, head sums, exponentials), which
+// measured slower than the L2 gain for kernels that gather one row per edge and faster
+// with 256-byte slices (16 lanes) for the two-row gathers of the dot forward and dQ pass.
+inline int feature_slices(int G, int LH, int requested, int auto_lanes) {
+  auto fits = [&](int S, int min_lanes) {
+    return G % S == 0 && (G / S) % LH == 0 && G / S >= min_lanes;
+  };
+  if (requested == 1) return 1;
+  if (requested > 1) {
+    for (int S = requested; S > 1; S /= 2)
+      if (fits(S, 4)) return S;
+    return 1;
+  }
+  int best = 1;
+  if (auto_lanes > 0)
+    for (int S = 2; S <= 8; S *= 2)
+      if (fits(S, auto_lanes)) best = S;
+  return best;
+}
+constexpr int kAutoSliceLanesTwoRows = 16;  // auto slices of the dot forward / dQ pass
+
 // Forward kernels (fwd.hip).
 struct FwdArgs {
   const int32_t* indptr;
@@ -84,6 +109,9 @@ struct FwdArgs {
   float* ws_acc;  // [n_chunks][H*d]
   float sc2;      // scale * log2(e)
   float neg_slope;
+  int ld;         // feature row stride in 16-byte lanes (the full row)
+  int hf;         // heads per node (stride of lse / s / t / partial (m, l))
+  int slices;     // feature slices of the main kernel (1, 2, 4 or 8)
 };
 
 // Backward kernels (bwd.hip).
@@ -107,6 +135,10 @@ struct BwdArgs {
   float scale;
   float sc2;       // scale * log2(e)
   float neg_slope; // LeakyReLU slope (GAT and GATv2 scores)
+  int ld;            // feature row stride in 16-byte lanes (the full row)
+  int hf;            // heads per node (stride of lse and of the records)
+  int slices;        // feature slices of the dQ pass (1, 2, 4 or 8)
+  int dq_stride;     // floats per dQ chunk partial of the full row (dq_partial_floats)
   // GATv2 only
   const float* attn;  // attention vector [H*d]
   float* dattn;       // its gradient [H*d]
@@ -158,6 +190,8 @@ struct RedArgs {
   const int32_t* csc_rel;  // per transpose entry: the edge's position in its CSR row
   int slot_bytes;          // 2 or 4: width of the slot array
   bool rows_sorted;        // host-side: every row's neighbour ids non-decreasing
+  int ld;                  // feature row stride in 16-byte lanes (the full row)
+  int slices;              // feature slices of the main kernels (1, 2, 4 or 8)
   // forward
   const void* x;     // [N, F]
   void* out;         // [N, F]

@@ -64,6 +64,9 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
   if (!indptr || (e > 0 && !indices)) return GA_ERR_INVALID_ARG;
   if (o.light_max_deg < 0 || o.hub_min_deg_exclusive < o.light_max_deg || o.hub_chunk < 1)
     return GA_ERR_INVALID_ARG;
+  if (o.feature_slices != 0 && o.feature_slices != 1 && o.feature_slices != 2 &&
+      o.feature_slices != 4 && o.feature_slices != 8)
+    return GA_ERR_INVALID_ARG;
   // validation
   if (indptr[0] != 0 || indptr[n] != e) return GA_ERR_BAD_GRAPH;
   for (int64_t i = 0; i < n; ++i)

@@ -130,7 +130,7 @@ struct Red : RowIO<T, G, G> {
         }
         raw_t xr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[u] = X[static_cast<size_t>(jj[u]) * G + r];
+        for (int u = 0; u < U; ++u) xr[u] = X[static_cast<size_t>(jj[u]) * a.ld + r];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float xf[VEC];
@@ -176,8 +176,8 @@ struct Red : RowIO<T, G, G> {
         ar[c] = empty ? -1 : s.id[c];
       sl[c] = empty ? 0xffffffffu : static_cast<unsigned>(s.pos[c] - row_start);
     }
+    const size_t e0 = static_cast<size_t>(row) * a.ld * VEC + r * VEC;  // element offset
     if (a.slot) {
-      const size_t e0 = static_cast<size_t>(row) * F + r * VEC;
       if (a.slot_bytes == 2) {
         unsigned w[VEC / 2];
 #pragma unroll
@@ -195,8 +195,8 @@ struct Red : RowIO<T, G, G> {
           st_stream(sp + k, u32x4{sl[4 * k], sl[4 * k + 1], sl[4 * k + 2], sl[4 * k + 3]});
       }
     }
-    st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * G + r, L16::pack(o));
-    u32x4* ap = reinterpret_cast<u32x4*>(a.arg + static_cast<size_t>(row) * F + r * VEC);
+    st_stream(static_cast<raw_t*>(a.out) + static_cast<size_t>(row) * a.ld + r, L16::pack(o));
+    u32x4* ap = reinterpret_cast<u32x4*>(a.arg + e0);
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k)
       st_stream(ap + k, u32x4{static_cast<unsigned>(ar[4 * k]), static_cast<unsigned>(ar[4 * k + 1]),
@@ -215,19 +215,18 @@ struct Red : RowIO<T, G, G> {
 
   __device__ __forceinline__ static void write_partial(const RedArgs& a, int chunk, int r,
                                                        const State& s) {
-    IO::store_f32(a.ws_val + static_cast<size_t>(chunk) * F, r, s.v);
-    if constexpr (!SORTED) st_int(a.ws_idx + static_cast<size_t>(chunk) * F, r, s.id);
-    st_int(a.ws_pos + static_cast<size_t>(chunk) * F, r, s.pos);
+    const size_t c0 = static_cast<size_t>(chunk) * a.ld * VEC;  // partials span full rows
+    IO::store_f32(a.ws_val + c0, r, s.v);
+    if constexpr (!SORTED) st_int(a.ws_idx + c0, r, s.id);
+    st_int(a.ws_pos + c0, r, s.pos);
   }
 
   __device__ __forceinline__ static void fold_partial(const RedArgs& a, int chunk, int r,
                                                       State& s) {
-    const f32x4* vp =
-        reinterpret_cast<const f32x4*>(a.ws_val + static_cast<size_t>(chunk) * F + r * VEC);
-    const u32x4* ip =
-        reinterpret_cast<const u32x4*>(a.ws_idx + static_cast<size_t>(chunk) * F + r * VEC);
-    const u32x4* pp =
-        reinterpret_cast<const u32x4*>(a.ws_pos + static_cast<size_t>(chunk) * F + r * VEC);
+    const size_t c0 = static_cast<size_t>(chunk) * a.ld * VEC + r * VEC;
+    const f32x4* vp = reinterpret_cast<const f32x4*>(a.ws_val + c0);
+    const u32x4* ip = reinterpret_cast<const u32x4*>(a.ws_idx + c0);
+    const u32x4* pp = reinterpret_cast<const u32x4*>(a.ws_pos + c0);
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k) {
       const f32x4 v = ld_stream(vp + k);
@@ -254,7 +253,7 @@ struct Red : RowIO<T, G, G> {
   template <int MODE>
   __device__ __forceinline__ static void load_keys(const RedArgs& a, int i, int r,
                                                    unsigned* key) {
-    const size_t e0 = static_cast<size_t>(i) * F + r * VEC;
+    const size_t e0 = static_cast<size_t>(i) * a.ld * VEC + r * VEC;
     if constexpr (MODE == kMatchSlot16) {
       const uint16_t* sp = static_cast<const uint16_t*>(a.slot_in) + e0;
       unsigned w[VEC / 2];
@@ -346,7 +345,7 @@ struct Red : RowIO<T, G, G> {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           dr[u] = raw_t{};
-          if (any[u]) dr[u] = Do[static_cast<size_t>(ii[u]) * G + r];
+          if (any[u]) dr[u] = Do[static_cast<size_t>(ii[u]) * a.ld + r];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -362,12 +361,27 @@ struct Red : RowIO<T, G, G> {
   }
 };
 
+// The main kernels work on a feature slice of G lanes of a row of a.ld lanes, slices dealt
+// to XCDs by slice_of (ga_device.h); each wave moves its pointers to its slice.
 template <typename T, int G, int OP, int U, bool SORTED>
-__global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a) {
+__global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a0) {
   using K = Red<T, G, OP, U, SORTED>;
-  constexpr int NG = K::NG;
+  using raw_t = typename K::raw_t;
+  constexpr int NG = K::NG, VEC = K::VEC;
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const SliceItem si = slice_of(a0.slices);
+  const int item = si.item;
+  const int so = si.slice * G;  // lanes before this slice
+  RedArgs a = a0;
+  a.x = static_cast<const raw_t*>(a0.x) + so;
+  a.out = static_cast<raw_t*>(a0.out) + so;
+  a.arg = a0.arg + so * VEC;
+  if (a0.slot) a.slot = static_cast<char*>(a0.slot) + static_cast<size_t>(so) * VEC * a0.slot_bytes;
+  if (a0.ws_val) {
+    a.ws_val = a0.ws_val + so * VEC;
+    a.ws_idx = a0.ws_idx + so * VEC;
+    a.ws_pos = a0.ws_pos + so * VEC;
+  }
   const int g = lane / G, r = lane % G;
   const DevBins& B = a.rows;
   typename K::State s;
@@ -421,11 +435,21 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_merge(RedArgs a) {
 }
 
 template <typename T, int G, int U, int MODE>
-__global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
+__global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a0) {
   using K = Red<T, G, kReduceMax, U>;
-  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
+  using raw_t = typename K::raw_t;
+  constexpr int NG = K::NG, VEC = K::VEC;
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const SliceItem si = slice_of(a0.slices);
+  const int item = si.item;
+  const int so = si.slice * G;  // lanes before this slice
+  RedArgs a = a0;
+  if (a0.arg_in) a.arg_in = a0.arg_in + so * VEC;
+  if (a0.slot_in)
+    a.slot_in = static_cast<const char*>(a0.slot_in) + static_cast<size_t>(so) * VEC * a0.slot_bytes;
+  a.dout = static_cast<const raw_t*>(a0.dout) + so;
+  a.dx = static_cast<raw_t*>(a0.dx) + so;
+  if (a0.ws_sum) a.ws_sum = a0.ws_sum + so * VEC;
   const int g = lane / G, r = lane % G;
   const DevBins& B = a.cols;
   typename K::acc_t s[VEC];
@@ -447,9 +471,9 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
     K::template group_sum<NG>(s);
     if (g != 0) return;
     if (chunk)
-      K::store_f32(a.ws_sum + static_cast<size_t>(item) * F, r, s);
+      K::store_f32(a.ws_sum + static_cast<size_t>(item) * a.ld * VEC, r, s);
     else
-      K::store(a.dx, col, r, s, 1.f);
+      K::store(a.dx, col, r, s, 1.f, a.ld);
     return;
   }
   const int li = (item - B.n_chunks - B.n_medium) * NG + g;
@@ -457,7 +481,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a) {
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
   K::template run_cols<1, MODE>(a, col, e0, e1, e0, g * G, 0, r, s);
-  K::store(a.dx, col, r, s, 1.f);
+  K::store(a.dx, col, r, s, 1.f, a.ld);
 }
 
 template <typename T, int G>
@@ -474,7 +498,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
 #pragma unroll
   for (int c = 0; c < VEC; ++c) s[c] = 0;
 #pragma unroll 4
-  for (int c = c0 + g; c < c1; c += NG) K::add_f32(a.ws_sum + static_cast<size_t>(c) * F, r, s);
+  for (int c = c0 + g; c < c1; c += NG) K::add_f32(a.ws_sum + static_cast<size_t>(c) * a.ld * VEC, r, s);
   K::template group_sum<NG>(s);
   if (g == 0) K::store(a.dx, col, r, s, 1.f);
 }
@@ -482,57 +506,88 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
 constexpr int kUnrollRed = 8;
 constexpr int kUnrollRedBwd = 4;
 
+template <typename Kern>
+int go(const char* name, Kern kernel, int64_t blocks, const RedArgs& a, void* stream,
+       TimerHook hook) {
+  if (blocks <= 0) return 0;
+  if (hook) hook(name, stream, 1);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), a);
+  if (hook) hook(name, stream, 0);
+  return static_cast<int>(hipGetLastError());
+}
+
+inline int64_t blocks_of(int64_t waves) { return (waves + kWavesPerBlock - 1) / kWavesPerBlock; }
+
+// Main kernel on the slice geometry (G lanes per slice, a.slices slices).
 template <typename T, int G>
-int launch_g(bool backward, int op, const RedArgs& a, void* stream, TimerHook hook) {
+int launch_main(bool backward, int op, const RedArgs& a, void* stream, TimerHook hook) {
   constexpr int NG = kWave / G;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   auto items_of = [](const DevBins& B) {
     return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   };
-  auto go = [&](const char* name, auto kernel, int64_t waves) -> int {
-    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    if (blocks <= 0) return 0;
-    if (hook) hook(name, stream, 1);
-    hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);
-    if (hook) hook(name, stream, 0);
-    return static_cast<int>(hipGetLastError());
-  };
-  int e;
   if (backward) {
-    const int64_t w = items_of(a.cols);
+    const int64_t b = slice_blocks(blocks_of(items_of(a.cols)), a.slices);
+    if (items_of(a.cols) <= 0) return 0;
     if (!a.slot_in)
-      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchArg>, w);
-    else if (a.slot_bytes == 2)
-      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot16>, w);
-    else
-      e = go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot32>, w);
-    if (e) return e;
-    return go("reduce_bwd_merge", reduce_bwd_merge<T, G>, a.cols.n_hub);
+      return go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchArg>, b, a, stream,
+                hook);
+    if (a.slot_bytes == 2)
+      return go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot16>, b, a,
+                stream, hook);
+    return go("reduce_bwd_main", reduce_bwd_main<T, G, kUnrollRedBwd, kMatchSlot32>, b, a,
+              stream, hook);
   }
-  auto fwd = [&](auto op_tag, auto sorted_tag) -> int {
-    constexpr int OPV = decltype(op_tag)::value;
-    constexpr bool SRT = decltype(sorted_tag)::value;
-    int r;
-    if ((r = go("reduce_fwd_main", reduce_fwd_main<T, G, OPV, kUnrollRed, SRT>,
-                items_of(a.rows))))
-      return r;
-    return go("reduce_fwd_merge", reduce_fwd_merge<T, G, OPV, SRT>, a.rows.n_hub);
-  };
-  using Max = std::integral_constant<int, kReduceMax>;
-  using Min = std::integral_constant<int, kReduceMin>;
+  if (items_of(a.rows) <= 0) return 0;
+  const int64_t b = slice_blocks(blocks_of(items_of(a.rows)), a.slices);
   if (op == kReduceMax)
-    return a.rows_sorted ? fwd(Max{}, std::true_type{}) : fwd(Max{}, std::false_type{});
-  return a.rows_sorted ? fwd(Min{}, std::true_type{}) : fwd(Min{}, std::false_type{});
+    return a.rows_sorted
+               ? go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMax, kUnrollRed, true>, b, a,
+                    stream, hook)
+               : go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMax, kUnrollRed, false>, b,
+                    a, stream, hook);
+  return a.rows_sorted
+             ? go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMin, kUnrollRed, true>, b, a,
+                  stream, hook)
+             : go("reduce_fwd_main", reduce_fwd_main<T, G, kReduceMin, kUnrollRed, false>, b, a,
+                  stream, hook);
+}
+
+// Hub merges on the full row geometry.
+template <typename T, int G>
+int launch_merge(bool backward, int op, const RedArgs& a, void* stream, TimerHook hook) {
+  if (backward)
+    return go("reduce_bwd_merge", reduce_bwd_merge<T, G>, blocks_of(a.cols.n_hub), a, stream,
+              hook);
+  const int64_t b = blocks_of(a.rows.n_hub);
+  if (op == kReduceMax)
+    return a.rows_sorted
+               ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, true>, b, a, stream, hook)
+               : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, false>, b, a, stream,
+                    hook);
+  return a.rows_sorted
+             ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin, true>, b, a, stream, hook)
+             : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin, false>, b, a, stream,
+                  hook);
 }
 
 template <typename T>
 int launch_t(bool backward, int op, int G, const RedArgs& a, void* stream, TimerHook hook) {
+  int e = -1;
+  switch (G / a.slices) {
+    case 4: e = launch_main<T, 4>(backward, op, a, stream, hook); break;
+    case 8: e = launch_main<T, 8>(backward, op, a, stream, hook); break;
+    case 16: e = launch_main<T, 16>(backward, op, a, stream, hook); break;
+    case 32: e = launch_main<T, 32>(backward, op, a, stream, hook); break;
+    case 64: e = launch_main<T, 64>(backward, op, a, stream, hook); break;
+  }
+  if (e) return e;
   switch (G) {
-    case 4: return launch_g<T, 4>(backward, op, a, stream, hook);
-    case 8: return launch_g<T, 8>(backward, op, a, stream, hook);
-    case 16: return launch_g<T, 16>(backward, op, a, stream, hook);
-    case 32: return launch_g<T, 32>(backward, op, a, stream, hook);
-    case 64: return launch_g<T, 64>(backward, op, a, stream, hook);
+    case 4: return launch_merge<T, 4>(backward, op, a, stream, hook);
+    case 8: return launch_merge<T, 8>(backward, op, a, stream, hook);
+    case 16: return launch_merge<T, 16>(backward, op, a, stream, hook);
+    case 32: return launch_merge<T, 32>(backward, op, a, stream, hook);
+    case 64: return launch_merge<T, 64>(backward, op, a, stream, hook);
   }
   return -1;
 }

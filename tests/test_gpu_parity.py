@@ -190,6 +190,33 @@ def bwd_case(tag, ip, ix, q, k, v, dout, dtype, rows=None, cols=None, **plan_kw)
     return plan, (out, lse, dq, dk, dv)
 
 
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 8, 32), ("f32", 4, 32), ("bf16", 2, 128)])
+def test_feature_slices_every_element(S, dtype, H, d):
+    """Feature slices dealt to XCDs (forward and the dQ pass): every element against the
+    oracle for each slice count, including forced counts that fall back for wide heads, and
+    the same result twice in a row."""
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    n = 3000
+    ip, ix = gg.make_graph(w, n=n)
+    rng = np.random.default_rng(31 + S)
+    feats = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(4)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    plan, res = bwd_case(f"slices {S} {dtype} H{H} d{d}", ip, ix, *feats, dtype, light_max_deg=8,
+                         hub_min_deg_exclusive=64, hub_chunk=32, feature_slices=S)
+    assert plan.info()["feature_slices"] == S
+    q, k, v, do = (dev(x) for x in feats)
+    scale = f32(1 / math.sqrt(d))
+    out, lse = fwd(plan, q, k, v, scale=scale)
+    dq, dk, dv = bwd(plan, q, k, v, do, lse, scale=scale)
+    for a, b in zip(res, (out, lse, dq, dk, dv)):
+        assert torch.equal(a, b)
+    ro, rl = A.forward(ip, ix, *feats[:3], "dot", scale)
+    check(f"slices {S} out", host64(out), ro, dtype)
+    check_lse(f"slices {S} lse", host64(lse), rl)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_backward_chunglu5k_every_element(dtype):
     w = gg.WORKLOADS["chunglu1m_train_bf16"]

@@ -259,3 +259,23 @@ def test_wide_slots_for_rows_beyond_65536_edges():
         plan, out, arg_slot, ra = fwd_exact("wide slots", ip, ix, x, "bf16", op)
         assert reduce_slot_dtype(plan) == torch.int32 and arg_slot[1].dtype == torch.int32
         bwd_parity("wide slots", plan, ip, ix, arg_slot, ra, dout, "bf16")
+
+
+@pytest.mark.parametrize("dtype,F", [("bf16", 256), ("f32", 128), ("bf16", 64)])
+def test_feature_slices(dtype, F):
+    """Every slice count gives the same out, arg and slot bit for bit (selection is exact)
+    and the oracle's dx."""
+    rng = np.random.default_rng(41)
+    ip, ix = gg.random_multigraph(800, 6000, rng, hub_rows=(5, 9), hub_deg=900)
+    x = gg.normal_features(rng, (800, F), dtype)
+    dout = gg.normal_features(rng, (800, F), dtype)
+    first = None
+    for S in (1, 2, 4, 8):
+        plan, out, (arg, slot), ra = fwd_exact(f"slices {S} F{F}", ip, ix, x, dtype, "max",
+                                               light_max_deg=4, hub_min_deg_exclusive=64,
+                                               hub_chunk=40, feature_slices=S)
+        bwd_parity(f"slices {S} F{F}", plan, ip, ix, (arg, slot), ra, dout, dtype)
+        if first is None:
+            first = (out, arg, slot)
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(first, (out, arg, slot)))
