@@ -120,22 +120,27 @@ struct BwdV2 : RowIO<T, G, LH> {
         for (int u = 0; u < U; ++u) {
           float xs[VEC];
           L16::unpack(xr[u], xs);
-          const float s2 = score2(a, xd, xs, av);
-          const float dp = head_sum<LH>(L16::dot(dor, xr[u]));
+          // g = LeakyReLU'(z) by one select, LeakyReLU(z) = z g exactly (g is 1 or the slope)
+          float g[VEC], lz[VEC], e = 0.f;
+#pragma unroll
+          for (int c = 0; c < VEC; ++c) {
+            const float z = xd[c] + xs[c];
+            g[c] = z >= 0.f ? 1.f : a.neg_slope;
+            lz[c] = z * g[c];
+            e = fmaf(av[c], lz[c], e);
+          }
+          const float s2 = head_sum<LH>(e) * a.sc2;
+          const float dp = head_sum<LH>(L16::dot_packed(dor, xr[u]));
           const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
           const float pdp = p * dp;
           s.D += static_cast<acc_t>(pdp);
           s.L += static_cast<acc_t>(p);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
-            const float z = xd[c] + xs[c];
-            const bool pos = z >= 0.f;
-            const float g = pos ? 1.f : a.neg_slope;
-            const float lz = pos ? z : z * a.neg_slope;
-            s.A1[c] = fmaf(pdp, g, s.A1[c]);
-            s.B1[c] = fmaf(p, g, s.B1[c]);
-            s.A2[c] += static_cast<acc_t>(pdp * lz);
-            s.B2[c] += static_cast<acc_t>(p * lz);
+            s.A1[c] = fmaf(pdp, g[c], s.A1[c]);
+            s.B1[c] = fmaf(p, g[c], s.B1[c]);
+            s.A2[c] += static_cast<acc_t>(pdp * lz[c]);
+            s.B2[c] += static_cast<acc_t>(p * lz[c]);
           }
         }
       }

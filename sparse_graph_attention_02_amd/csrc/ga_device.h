@@ -82,6 +82,9 @@ struct Lane16<float> {
   __device__ __forceinline__ static float dot(const raw_t& x, const raw_t& y) {
     return fmaf(x.w, y.w, fmaf(x.z, y.z, fmaf(x.y, y.y, x.x * y.x)));
   }
+  __device__ __forceinline__ static float dot_packed(const raw_t& x, const raw_t& y) {
+    return dot(x, y);
+  }
 };
 
 // fp32 -> bf16 by round-to-nearest-even (NaN stays a quiet NaN).
@@ -119,6 +122,21 @@ struct Lane16<bf16_t> {
     float d = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) d = fmaf(a[c], b[c], d);
+    return d;
+  }
+  // The same sum by four v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32
+  // accumulation): half the instructions, for passes bound by VALU issue.
+  __device__ __forceinline__ static float dot_packed(const raw_t& x, const raw_t& y) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t wx[4] = {x.x, x.y, x.z, x.w}, wy[4] = {y.x, y.y, y.z, y.w};
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bf16x2_t p, q;
+      __builtin_memcpy(&p, &wx[k], 4);
+      __builtin_memcpy(&q, &wy[k], 4);
+      d = __builtin_amdgcn_fdot2_f32_bf16(p, q, d, false);
+    }
     return d;
   }
 };
