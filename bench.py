@@ -224,6 +224,8 @@ def main():
     ap.add_argument("--light", type=int, default=None)
     ap.add_argument("--hub", type=int, default=None)
     ap.add_argument("--chunk", type=int, default=None)
+    ap.add_argument("--col-hub", type=int, default=None)
+    ap.add_argument("--col-chunk", type=int, default=None)
     ap.add_argument("--slices", type=int, default=None,
                     help="feature slices per XCD group (0 = automatic, 1 = off, 2, 4, 8)")
     ap.add_argument("--order", choices=["as-generated", "out-degree"], default="as-generated",
@@ -263,7 +265,8 @@ def main():
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     plan = ga.Plan(ip, ix, light_max_deg=args.light, hub_min_deg_exclusive=args.hub,
-                   hub_chunk=args.chunk, build_csc=w.backward, feature_slices=args.slices)
+                   hub_chunk=args.chunk, build_csc=w.backward, feature_slices=args.slices,
+                   col_hub_min_deg_exclusive=args.col_hub, col_hub_chunk=args.col_chunk)
     plan_host_s = time.perf_counter() - t0
     plan.upload("cuda")
     torch.cuda.synchronize()
@@ -346,6 +349,32 @@ def main():
 
     ms_step, kt = timed(step, args.steps)
     ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
+
+    def per_step(fn, k):
+        """Each of k launches bracketed by its own pair of events on the launch stream:
+        median, p10 and p90 in ms."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(k)]
+        torch.cuda.synchronize()
+        for a, z in ev:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(z) for a, z in ev])
+        return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+                "p90": float(np.percentile(t, 90))}
+
+    dist_step = per_step(step, args.steps)
+    dist_fwd = per_step(lambda: step(False), args.steps)
+    # peak memory of one step above what is already allocated (inputs, outputs, plan and
+    # workspaces are allocated before the timed region; a step allocates nothing)
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    step()
+    torch.cuda.synchronize()
+    step_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
     # gather floor: the forward's neighbour gathers alone (same graph, same lane pattern)
     sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
     # dot gathers two rows per edge (K_j, V_j); the other forms one (the probe then loads
@@ -381,6 +410,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "step_ms_distribution": dist_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -395,7 +425,8 @@ def main():
                                           "n_row_light", "n_row_medium", "n_row_hub",
                                           "n_row_chunks", "n_col_hub", "n_col_chunks",
                                           "max_in_degree", "max_out_degree", "rows_sorted",
-                                          "feature_slices")},
+                                          "feature_slices", "col_hub_min_deg_exclusive",
+                                          "col_hub_chunk")},
             "parallelism": "single GPU",
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
@@ -403,7 +434,7 @@ def main():
         "cpu_baseline": cpu,
         "step_GBps_algorithmic": tot_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": tot_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "fwd": {"ms": ms_fwd, "edges_per_s": E / (ms_fwd * 1e-3),
+        "fwd": {"ms": ms_fwd, "ms_distribution": dist_fwd, "edges_per_s": E / (ms_fwd * 1e-3),
                 "GBps_algorithmic": fwd_bytes / (ms_fwd * 1e-3) / 1e9,
                 "frac_of_peak": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "fwd_main_ms": fwd_main_ms},
@@ -417,9 +448,12 @@ def main():
         "kernels": kernels,
         "copy_probe_GBps": copy_gbps,
         "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,
-        "workspace_bytes": {"fwd": plan.fwd_workspace_bytes(H, d),
+        "workspace_bytes": {"fwd": fws.numel(),
                             "bwd": (bws.numel() if w.backward else 0),
                             "edge_score_tensor_would_be": E * H * 4},
+        "memory_bytes": {"plan_device": plan.device_bytes(),
+                         "allocated_before_step": base_alloc,
+                         "extra_peak_during_step": step_peak_extra},
     }
     print(json.dumps(rec), flush=True)
 

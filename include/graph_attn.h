@@ -76,14 +76,25 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * edge, take the largest S dividing 8 whose slices are at least 256 bytes; the other
  * kernels 1), 1 = off, 2, 4 or 8 = that many slices for every kernel named above,
  * lowered until they hold whole heads of at least 64 bytes. Results agree to rounding
- * (bit for bit for the reduction, whose selection is exact). Constraints: 0 <= light_max_deg <= hub_min_deg_exclusive,
- * hub_chunk >= 1, feature_slices in {0, 1, 2, 4, 8}. */
+ * (bit for bit for the reduction, whose selection is exact).
+ * col_hub_min_deg_exclusive and col_hub_chunk are the hub threshold and chunk of the
+ * transpose's column bins (light columns use light_max_deg).
+ * A hub threshold or chunk of -1 (the defaults) is chosen from the graph: the row hub
+ * threshold is the power of two nearest E / 8192 kept within [256, 8192] (about one
+ * wavefront's share of the edges when ~8192 are in flight, so no single row item becomes
+ * the tail), at least light_max_deg; the row chunk max(256, threshold / 4); the column
+ * threshold min(1024, row threshold) and column chunk min(512, row chunk), as the column
+ * passes do more work per edge. graph_attn_plan_get_info reports the values used.
+ * Constraints: light_max_deg >= 0; an explicit threshold >= light_max_deg; an explicit
+ * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}. */
 typedef struct {
   int32_t light_max_deg;
   int32_t hub_min_deg_exclusive;
   int32_t hub_chunk;
   int32_t build_csc;
   int32_t feature_slices;
+  int32_t col_hub_min_deg_exclusive;
+  int32_t col_hub_chunk;
 } ga_plan_opts;
 
 /* Counts describing a built plan (all int64 so the struct has no padding). */
@@ -98,6 +109,7 @@ typedef struct {
   int64_t uploaded;
   int64_t rows_sorted;  /* 1 when every row's neighbour ids are non-decreasing */
   int64_t feature_slices;  /* the option as given (0 = automatic) */
+  int64_t col_hub_min_deg_exclusive, col_hub_chunk;
 } ga_plan_info;
 
 typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */

@@ -85,7 +85,7 @@ def transpose_positions(indptr, indices):
 
 
 def plan(indptr, indices, light_max_deg=16, hub_min_deg_exclusive=1024, hub_chunk=1024,
-         build_csc=True):
+         build_csc=True, col_hub_min_deg_exclusive=None, col_hub_chunk=None):
     """All plan arrays as a dict of int32 arrays (names match the library's export)."""
     indptr = np.asarray(indptr, dtype=np.int64)
     out = {}
@@ -99,8 +99,10 @@ def plan(indptr, indices, light_max_deg=16, hub_min_deg_exclusive=1024, hub_chun
         out["colptr"], out["rowidx"] = colptr, rowidx
         out["csc_rel"] = transpose_positions(indptr, indices)
         odeg = np.diff(colptr.astype(np.int64))
-        out["col_light"], out["col_medium"], out["col_hub"] = bin_rows(
-            odeg, light_max_deg, hub_min_deg_exclusive)
+        cth = hub_min_deg_exclusive if col_hub_min_deg_exclusive is None \
+            else col_hub_min_deg_exclusive
+        cch = hub_chunk if col_hub_chunk is None else col_hub_chunk
+        out["col_light"], out["col_medium"], out["col_hub"] = bin_rows(odeg, light_max_deg, cth)
         (out["col_chunk_row"], out["col_chunk_begin"], out["col_chunk_end"],
-         out["col_hub_chunk_ptr"]) = chunk_hubs(colptr, out["col_hub"], hub_chunk)
+         out["col_hub_chunk_ptr"]) = chunk_hubs(colptr, out["col_hub"], cch)
     return out

@@ -58,17 +58,27 @@ def default_opts() -> dict:
 
 class Plan:
     """A graph's cached metadata: degree bins, hub chunks and (optionally) the transpose,
-    built on the host by the library's planner; ``upload`` copies it to the GPU."""
+    built on the host by the library's planner; ``upload`` copies it to the GPU.
+
+    Thresholds left as None take the library defaults, except that the column hub
+    threshold and chunk follow explicitly given row values unless given themselves."""
 
     def __init__(self, indptr, indices, *, light_max_deg=None, hub_min_deg_exclusive=None,
-                 hub_chunk=None, build_csc=True, feature_slices=None):
+                 hub_chunk=None, build_csc=True, feature_slices=None,
+                 col_hub_min_deg_exclusive=None, col_hub_chunk=None):
         ip = np.ascontiguousarray(indptr, dtype=np.int32)
         ix = np.ascontiguousarray(indices, dtype=np.int32)
         opts = capi.ga_plan_opts()
         graph_attn_plan_opts_default(byref(opts))
+        if col_hub_min_deg_exclusive is None:
+            col_hub_min_deg_exclusive = hub_min_deg_exclusive
+        if col_hub_chunk is None:
+            col_hub_chunk = hub_chunk
         for k, v in (("light_max_deg", light_max_deg),
                      ("hub_min_deg_exclusive", hub_min_deg_exclusive),
-                     ("hub_chunk", hub_chunk), ("feature_slices", feature_slices)):
+                     ("hub_chunk", hub_chunk), ("feature_slices", feature_slices),
+                     ("col_hub_min_deg_exclusive", col_hub_min_deg_exclusive),
+                     ("col_hub_chunk", col_hub_chunk)):
             if v is not None:
                 setattr(opts, k, int(v))
         opts.build_csc = 1 if build_csc else 0

@@ -24,7 +24,8 @@ GA_REDUCE_MAX, GA_REDUCE_MIN = 0, 1
 
 class ga_plan_opts(Structure):
     _fields_ = [("light_max_deg", c_int32), ("hub_min_deg_exclusive", c_int32),
-                ("hub_chunk", c_int32), ("build_csc", c_int32), ("feature_slices", c_int32)]
+                ("hub_chunk", c_int32), ("build_csc", c_int32), ("feature_slices", c_int32),
+                ("col_hub_min_deg_exclusive", c_int32), ("col_hub_chunk", c_int32)]
 
 
 class ga_plan_info(Structure):
@@ -32,7 +33,8 @@ class ga_plan_info(Structure):
         "n_nodes", "n_edges", "n_row_light", "n_row_medium", "n_row_hub", "n_row_chunks",
         "has_csc", "n_col_light", "n_col_medium", "n_col_hub", "n_col_chunks",
         "max_in_degree", "max_out_degree", "light_max_deg", "hub_min_deg_exclusive",
-        "hub_chunk", "device_bytes", "uploaded", "rows_sorted", "feature_slices")]
+        "hub_chunk", "device_bytes", "uploaded", "rows_sorted", "feature_slices",
+        "col_hub_min_deg_exclusive", "col_hub_chunk")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -215,10 +215,12 @@ const char* graph_attn_status_string(ga_status s) {
 ga_status graph_attn_plan_opts_default(ga_plan_opts* o) {
   if (!o) return GA_ERR_INVALID_ARG;
   o->light_max_deg = 16;
-  o->hub_min_deg_exclusive = 1024;
-  o->hub_chunk = 512;
+  o->hub_min_deg_exclusive = -1;  // automatic, from the graph's size
+  o->hub_chunk = -1;
   o->build_csc = 1;
   o->feature_slices = 0;
+  o->col_hub_min_deg_exclusive = -1;
+  o->col_hub_chunk = -1;
   return GA_OK;
 }
 
@@ -263,6 +265,8 @@ ga_status graph_attn_plan_get_info(const ga_plan* p, ga_plan_info* info) {
   info->device_bytes = static_cast<int64_t>(device_layout(p, nullptr));
   info->rows_sorted = p->rows_sorted ? 1 : 0;
   info->feature_slices = p->opts.feature_slices;
+  info->col_hub_min_deg_exclusive = p->opts.col_hub_min_deg_exclusive;
+  info->col_hub_chunk = p->opts.col_hub_chunk;
   info->uploaded = p->uploaded;
   return GA_OK;
 }

@@ -57,12 +57,39 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins*
 
 }  // namespace
 
+// Hub thresholds and chunks left at -1 are chosen from the graph's size. A hub row is
+// split so that no single wavefront holds much more than its share of the edges: with
+// about 8192 wavefronts in flight on the GPU, rows longer than E / 8192 edges (rounded to
+// the nearest power of two, kept within [256, 8192]) become chunked hubs, in chunks of a
+// quarter of that (at least 256). Column passes do more work per edge and keep smaller
+// hubs (at most 1024, chunks at most 512).
+ga_plan_opts resolve_opts(const ga_plan_opts& in, int64_t e) {
+  ga_plan_opts o = in;
+  if (o.hub_min_deg_exclusive == -1) {
+    const double share = static_cast<double>(e) / 8192.0;
+    int64_t t = 256;
+    while (t < 8192 && static_cast<double>(t) * 1.4142135623730951 < share) t *= 2;
+    o.hub_min_deg_exclusive = static_cast<int32_t>(std::max<int64_t>(t, o.light_max_deg));
+  }
+  if (o.hub_chunk == -1) o.hub_chunk = std::max(256, o.hub_min_deg_exclusive / 4);
+  if (o.col_hub_min_deg_exclusive == -1)
+    o.col_hub_min_deg_exclusive = std::max(std::min(1024, o.hub_min_deg_exclusive),
+                                           o.light_max_deg);
+  if (o.col_hub_chunk == -1) o.col_hub_chunk = std::min(512, o.hub_chunk);
+  return o;
+}
+
 ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, int64_t e,
-                     const ga_plan_opts& o, ga_plan* p) {
+                     const ga_plan_opts& given, ga_plan* p) {
   if (n < 0 || e < 0 || n >= (int64_t(1) << 31) || e >= (int64_t(1) << 31))
     return GA_ERR_INVALID_ARG;
   if (!indptr || (e > 0 && !indices)) return GA_ERR_INVALID_ARG;
-  if (o.light_max_deg < 0 || o.hub_min_deg_exclusive < o.light_max_deg || o.hub_chunk < 1)
+  if (given.light_max_deg < 0 || given.hub_min_deg_exclusive < -1 || given.hub_chunk < -1 ||
+      given.hub_chunk == 0 || given.col_hub_min_deg_exclusive < -1 ||
+      given.col_hub_chunk < -1 || given.col_hub_chunk == 0)
+    return GA_ERR_INVALID_ARG;
+  const ga_plan_opts o = resolve_opts(given, e);
+  if (o.hub_min_deg_exclusive < o.light_max_deg || o.col_hub_min_deg_exclusive < o.light_max_deg)
     return GA_ERR_INVALID_ARG;
   if (o.feature_slices != 0 && o.feature_slices != 1 && o.feature_slices != 2 &&
       o.feature_slices != 4 && o.feature_slices != 8)
@@ -105,7 +132,10 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
           p->rowidx[at] = static_cast<int32_t>(i);
           p->csc_rel[at] = k - indptr[i];  // the edge's position within its CSR row
         }
-      bin_by_degree(p->colptr, o, &p->cols, &p->max_out);
+      ga_plan_opts oc = o;  // the transpose's columns use their own hub threshold / chunk
+      oc.hub_min_deg_exclusive = o.col_hub_min_deg_exclusive;
+      oc.hub_chunk = o.col_hub_chunk;
+      bin_by_degree(p->colptr, oc, &p->cols, &p->max_out);
     } else {
       p->colptr.clear();
       p->rowidx.clear();

@@ -62,12 +62,20 @@ def test_bad_graphs_are_rejected(ip, ix):
 
 
 def test_bad_opts_are_rejected():
-    o = capi.ga_plan_opts(5, 4, 16, 1)          # light > hub threshold
-    assert _create([0, 1], [0], o)[0] == capi.GA_ERR_INVALID_ARG
-    o = capi.ga_plan_opts(1, 4, 0, 1)           # chunk 0
-    assert _create([0, 1], [0], o)[0] == capi.GA_ERR_INVALID_ARG
-    o = capi.ga_plan_opts(-1, 4, 8, 1)
-    assert _create([0, 1], [0], o)[0] == capi.GA_ERR_INVALID_ARG
+    # fields: light, hub threshold, hub chunk, build_csc, feature_slices, column hub
+    # threshold, column hub chunk
+    assert _create([0, 1], [0], capi.ga_plan_opts(1, 4, 8, 1, 0, 4, 8))[0] == capi.GA_OK
+    assert _create([0, 1], [0], capi.ga_plan_opts(1, -1, -1, 1, 0, -1, -1))[0] == capi.GA_OK
+    for bad in [(5, 4, 16, 1, 0, 8, 8),       # light > hub threshold
+                (1, 4, 0, 1, 0, 4, 8),        # chunk 0
+                (1, 4, -2, 1, 0, 4, 8),       # chunk below -1
+                (-1, 4, 8, 1, 0, 4, 8),       # negative light
+                (5, 8, 8, 1, 0, 4, 8),        # light > column hub threshold
+                (1, 4, 8, 1, 0, 4, 0),        # column chunk 0
+                (1, -4, 8, 1, 0, 4, 8),       # hub threshold below -1
+                (1, 4, 8, 1, 3, 4, 8),        # feature slices not a power of two
+                (1, 4, 8, 1, 16, 4, 8)]:      # too many feature slices
+        assert _create([0, 1], [0], capi.ga_plan_opts(*bad))[0] == capi.GA_ERR_INVALID_ARG, bad
     assert capi.raw_status("graph_attn_plan_create", None, None, 0, 0, None, None) == \
         capi.GA_ERR_INVALID_ARG
 
@@ -256,8 +264,58 @@ def test_bwd_gatv2_argument_checks():
 
 def test_default_opts():
     o = default_opts()
-    assert o["light_max_deg"] <= o["hub_min_deg_exclusive"] and o["hub_chunk"] >= 1
     assert o["build_csc"] == 1
+    # -1 = chosen from the graph's size
+    assert (o["light_max_deg"], o["hub_min_deg_exclusive"], o["hub_chunk"]) == (16, -1, -1)
+    assert (o["col_hub_min_deg_exclusive"], o["col_hub_chunk"]) == (-1, -1)
+    assert o["feature_slices"] == 0
+    # the binding: explicit row thresholds also set the columns unless given
+    rng = np.random.default_rng(3)
+    ip, ix = gg.random_multigraph(64, 200, rng, hub_rows=(5,), hub_deg=300)
+    i = Plan(ip, ix, hub_min_deg_exclusive=64, hub_chunk=32).info()
+    assert (i["col_hub_min_deg_exclusive"], i["col_hub_chunk"]) == (64, 32)
+    i = Plan(ip, ix, hub_min_deg_exclusive=64, col_hub_chunk=7).info()
+    assert (i["hub_chunk"], i["col_hub_min_deg_exclusive"], i["col_hub_chunk"]) == (256, 64, 7)
+    i = Plan(ip, ix).info()        # 264 edges: the smallest automatic values
+    assert (i["hub_min_deg_exclusive"], i["hub_chunk"], i["col_hub_min_deg_exclusive"],
+            i["col_hub_chunk"]) == (256, 256, 256, 256)
+
+
+def _auto(e, light=16):
+    """The documented automatic thresholds, restated: the power of two nearest E/8192 in
+    [256, 8192] (nearest on a log scale), chunk max(256, t/4), columns min(1024, t) and
+    min(512, chunk)."""
+    import math
+    share = e / 8192
+    t = 256
+    while t < 8192 and t * math.sqrt(2) < share:
+        t *= 2
+    t = max(t, light)
+    c = max(256, t // 4)
+    return t, c, max(min(1024, t), light), min(512, c)
+
+
+@pytest.mark.parametrize("e", [0, 100, 2_100_000, 2_966_000, 2_967_000, 16_000_000,
+                               51_000_000, 65_000_000, 500_000_000])
+def test_automatic_thresholds(e):
+    # a star-free CSR with e edges spread over rows; only the edge count matters
+    n = 1000
+    ip = (np.arange(n + 1, dtype=np.int64) * e // n).astype(np.int32)
+    ix = np.zeros(e, np.int32)
+    st, h = _create(ip, ix, None) if e <= 2_000_000 else (None, None)
+    if st is None:                     # build the big ones through the binding (same call)
+        p = Plan(ip, ix, build_csc=False)
+        i = p.info()
+    else:
+        assert st == capi.GA_OK
+        info = capi.ga_plan_info()
+        capi.graph_attn_plan_get_info(h, byref(info))
+        i = info.as_dict()
+        capi.graph_attn_plan_destroy(h)
+    got = (i["hub_min_deg_exclusive"], i["hub_chunk"], i["col_hub_min_deg_exclusive"],
+           i["col_hub_chunk"])
+    assert got == _auto(e), (e, got)
+    assert _auto(51_000_000)[:2] == (8192, 2048) and _auto(2_100_000)[:2] == (256, 256)
 
 
 def _rfwd(p, op=capi.GA_REDUCE_MAX, dtype=capi.GA_BF16, F=256, ptrs=None, slot=FAKE, ws=FAKE,

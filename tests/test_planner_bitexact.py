@@ -81,3 +81,18 @@ def test_rows_sorted_flag():
     assert Plan(ip, np.array([1, 0, 2, 2, 1])).info()["rows_sorted"] == 0
     assert Plan(ip, np.array([0, 1, 2, 0, 1])).info()["rows_sorted"] == 0
     assert Plan(np.array([0, 2, 3]), np.array([1, 1, 0])).info()["rows_sorted"] == 1
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("tl,th,c,cth,cc", [(16, 8192, 2048, 1024, 512), (4, 64, 16, 8, 3),
+                                            (2, 3, 2, 100, 50)])
+def test_cpp_planner_column_thresholds(name, g, tl, th, c, cth, cc):
+    """Rows and columns binned with their own hub threshold and chunk."""
+    ip, ix = g
+    ref = P.plan(ip, ix, tl, th, c, build_csc=True, col_hub_min_deg_exclusive=cth,
+                 col_hub_chunk=cc)
+    p = Plan(ip, ix, light_max_deg=tl, hub_min_deg_exclusive=th, hub_chunk=c,
+             col_hub_min_deg_exclusive=cth, col_hub_chunk=cc)
+    for nm in _names():
+        want = {"indptr": ip, "indices": ix}.get(nm, ref.get(nm))
+        assert np.array_equal(p.array(nm), np.asarray(want, np.int32)), nm
