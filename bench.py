@@ -98,7 +98,14 @@ def _cpu_worker(args):
     with threadpool_limits(1):
         for s in range(0, rows.size, 128):
             batch = rows[s:s + 128]
-            if g["score"] in REDUCTIONS:
+            if g["score"] == "gatv2":
+                if backward:
+                    A.train_step_rows_gatv2(g["ip"], g["ix"], g["q"], g["k"], g["v"], g["dout"],
+                                            batch, g["scale"], g["slope"])
+                else:
+                    A.forward_gatv2_rows(g["ip"], g["ix"], g["q"], g["k"], g["v"], batch,
+                                         g["scale"], g["slope"])
+            elif g["score"] in REDUCTIONS:
                 from oracle import reduction as R
                 if backward:
                     R.train_step_rows(g["ip"], g["ix"], g["q"], g["dout"], batch, g["score"])
@@ -248,8 +255,6 @@ def main():
     N, E, H, d = ip.size - 1, ix.size, w.heads, w.dim
     b = 2 if w.dtype == "bf16" else 4
     scale = float(np.float32(1 / math.sqrt(d))) if w.score == "dot" else 1.0
-    if w.score == "gatv2" and args.cpu_budget > 0:
-        args.cpu_budget = 0  # the oracle baseline leg covers the dot and GAT-style steps
     print(f"[bench] {w.name}: N={N} E={E} H={H} d={d} {w.dtype} {w.score} "
           f"backward={w.backward} (inputs {gen_s:.1f}s)", file=sys.stderr, flush=True)
 

@@ -47,6 +47,7 @@ __all__ = [
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
     "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
     "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
+    "train_step_rows_gatv2",
 ]
 
 
@@ -351,6 +352,41 @@ def _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, scale, neg_slope
     dp = np.einsum("hc,khc->kh", widen(dout[i]), widen(xs[J]))
     D = (alpha * dp).sum(axis=0)
     return J, alpha, alpha * (dp - D[None, :]), leaky_relu_grad(z, float(neg_slope)), lz
+
+
+def train_step_rows_gatv2(indptr, indices, xd, xs, attn, dout, rows, scale=1.0, neg_slope=0.2):
+    """GATv2 forward and backward of the listed rows, each row's work done once.
+
+    Returns (out [R,H,d], lse [R,H], dxd [R,H,d], cols, dxs_part [C,H,d], dattn_part [H,d]):
+    ``cols`` are the source columns the rows touch (ascending), dxs_part and dattn_part
+    those rows' contributions.  With rows = all rows this is exactly ``forward_gatv2``
+    plus ``backward_gatv2``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = xs.shape[1], xs.shape[2]
+    segs = [np.asarray(indices[int(indptr[i]):int(indptr[i + 1])], dtype=np.int64) for i in rows]
+    cols = np.unique(np.concatenate(segs)) if segs else np.zeros(0, np.int64)
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    dxd = np.zeros((rows.size, H, d))
+    dxs = np.zeros((cols.size, H, d))
+    da = np.zeros((H, d))
+    a = widen(attn)
+    for r, i in enumerate(rows):
+        if segs[r].size == 0:
+            continue
+        e = gatv2_row_scores(i, indptr, indices, xd, xs, attn, scale, neg_slope)
+        _, lse[r] = row_softmax(e)
+        J, alpha, dS, g, lz = _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout,
+                                                   scale, neg_slope)
+        xsj = widen(xs[J])
+        out[r] = np.einsum("kh,khc->hc", alpha, xsj)
+        t = float(scale) * dS[:, :, None] * g * a[None]
+        dxd[r] = t.sum(axis=0)
+        slot = np.searchsorted(cols, J)
+        np.add.at(dxs, slot, t + alpha[:, :, None] * widen(dout[i])[None])
+        da += float(scale) * np.einsum("kh,khc->hc", dS, lz)
+    return out, lse, dxd, cols, dxs, da
 
 
 def backward_gatv2(indptr, indices, xd, xs, attn, dout, scale=1.0, neg_slope=0.2):

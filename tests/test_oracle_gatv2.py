@@ -102,3 +102,23 @@ def test_gatv2_sampled_forms_agree():
     np.testing.assert_allclose(da_all, ga, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(A.grad_gatv2_cols(ip, ix, xd, xs, a, do, sel), gxs[sel],
                                rtol=1e-12, atol=1e-13)
+
+
+def test_train_step_rows_gatv2_is_the_plain_step():
+    ip, ix, xd, xs, a, do = _inputs(11, 30, 250, H=2, d=4)
+    out, lse = A.forward_gatv2(ip, ix, xd, xs, a, 0.8, 0.15)
+    dxd, dxs, da = A.backward_gatv2(ip, ix, xd, xs, a, do, 0.8, 0.15)
+    o2, l2, dxd2, cols, dxs2, da2 = A.train_step_rows_gatv2(ip, ix, xd, xs, a, do,
+                                                           np.arange(30), 0.8, 0.15)
+    np.testing.assert_allclose(o2, out, atol=1e-13)
+    np.testing.assert_allclose(l2, lse, atol=1e-13)
+    np.testing.assert_allclose(dxd2, dxd, atol=1e-12)
+    full = np.zeros_like(dxs)
+    full[cols] = dxs2
+    np.testing.assert_allclose(full, dxs, atol=1e-12)
+    np.testing.assert_allclose(da2, da, atol=1e-12)
+    # a subset of rows gives those rows' shares
+    rows = np.array([2, 7, 19])
+    o3, _, dxd3, _, _, _ = A.train_step_rows_gatv2(ip, ix, xd, xs, a, do, rows, 0.8, 0.15)
+    np.testing.assert_allclose(o3, out[rows], atol=1e-13)
+    np.testing.assert_allclose(dxd3, dxd[rows], atol=1e-12)
