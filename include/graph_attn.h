@@ -18,7 +18,8 @@
  *     dot:  e_ij = scale * sum_c q[i,h,c] k[j,h,c]
  *     gat:  e_ij = scale * LeakyReLU_{neg_slope}(s[i,h] + t[j,h])
  *     out[i,h,:] = sum_j softmax_j(e_ij) v[j,h,:],   lse[i,h] = ln sum_j exp(e_ij)
- * A row with no neighbours gives out = 0 and lse = -inf.
+ * A row with no neighbours gives out = 0 and lse = -inf. The GATv2 score has entry points
+ * of its own (graph_attn_fwd_gatv2, graph_attn_bwd_gatv2), as it takes an attention vector.
  *
  * Conventions shared by every call
  *   Graph: CSR with int32 indptr [N+1] and indices [E], row i = destination, indices =
@@ -104,12 +105,12 @@ typedef struct {
   int64_t has_csc;
   int64_t n_col_light, n_col_medium, n_col_hub, n_col_chunks;
   int64_t max_in_degree, max_out_degree;
-  int64_t light_max_deg, hub_min_deg_exclusive, hub_chunk;
+  int64_t light_max_deg, hub_min_deg_exclusive, hub_chunk;  /* as used (automatic resolved) */
   int64_t device_bytes;
   int64_t uploaded;
   int64_t rows_sorted;  /* 1 when every row's neighbour ids are non-decreasing */
   int64_t feature_slices;  /* the option as given (0 = automatic) */
-  int64_t col_hub_min_deg_exclusive, col_hub_chunk;
+  int64_t col_hub_min_deg_exclusive, col_hub_chunk;      /* as used */
 } ga_plan_info;
 
 typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */
@@ -120,7 +121,8 @@ const char* graph_attn_version(void);
 /* Human-readable name of a status code. Never NULL. */
 const char* graph_attn_status_string(ga_status status);
 
-/* Fill *opts with the default thresholds. */
+/* Fill *opts with the defaults: light_max_deg 16, hub thresholds and chunks -1 (chosen
+ * from the graph), build_csc 1, feature_slices 0 (automatic). */
 ga_status graph_attn_plan_opts_default(ga_plan_opts* opts);
 
 /* Build a plan from a host CSR graph (the planner of the degree-aware tiling; runs on the
@@ -130,9 +132,10 @@ ga_status graph_attn_plan_opts_default(ga_plan_opts* opts);
  * Transpose (build_csc): colptr [N+1] and rowidx [E], destinations ascending within each
  * column (the order a stable scatter over rows produces), and csc_rel [E], for each
  * transpose entry the position of that edge within its CSR row (k - indptr[i] for CSR
- * edge k of row i); column bins/chunks follow the same rules on out-degree. indptr_host/indices_host are only read during the call
- * (indices_host may be NULL when n_edges == 0). opts NULL = defaults. On success *out
- * receives a plan to be released with graph_attn_plan_destroy. */
+ * edge k of row i); column bins/chunks follow the same rules on out-degree.
+ * indptr_host/indices_host are only read during the call (indices_host may be NULL when
+ * n_edges == 0). opts NULL = defaults. On success *out receives a plan to be released
+ * with graph_attn_plan_destroy. */
 ga_status graph_attn_plan_create(const int32_t* indptr_host, const int32_t* indices_host,
                                  int64_t n_nodes, int64_t n_edges, const ga_plan_opts* opts,
                                  ga_plan** out);
@@ -154,8 +157,8 @@ ga_status graph_attn_plan_upload(ga_plan* plan, void* dev_buf, size_t bytes, voi
  * "row_light", "row_medium", "row_hub", "row_chunk_row", "row_chunk_begin",
  * "row_chunk_end", "row_hub_chunk_ptr", and with the transpose "colptr", "rowidx",
  * "col_light", "col_medium", "col_hub", "col_chunk_row", "col_chunk_begin",
- * "col_chunk_end", "col_hub_chunk_ptr", "csc_rel". *data stays valid until the plan is destroyed
- * (it may be NULL when *count == 0). GA_ERR_INVALID_ARG for an unknown name,
+ * "col_chunk_end", "col_hub_chunk_ptr", "csc_rel". *data stays valid until the plan is
+ * destroyed (it may be NULL when *count == 0). GA_ERR_INVALID_ARG for an unknown name,
  * GA_ERR_NOT_READY for a transpose array of a plan built without it. */
 ga_status graph_attn_plan_array(const ga_plan* plan, const char* name, const int32_t** data,
                                 int64_t* count);

@@ -149,7 +149,7 @@ size_t bwd_ws_bytes(const ga_plan* p, const ga::Geometry& g) {
 }
 
 // GATv2 backward workspace sections (bytes, each 256-aligned): record, row-chunk partials,
-// column-chunk partials, da partial slots, first-stage da reduction (fp64).
+// column-chunk partials, da partial slots, the two fp64 buffers of the da reduction tree.
 struct Gv2Layout {
   size_t ld, rows, cols, da, da64, total;
 };
@@ -746,7 +746,8 @@ ga_status graph_attn_gather_probe(const ga_plan* p, ga_dtype dtype, int32_t head
   if (!p->uploaded) return GA_ERR_NOT_READY;
   if (p->e == 0) return GA_OK;
   if ((s = check_device(p)) != GA_OK) return s;
-  const int rc = ga::launch_gather_probe(p->d_indices, p->e, g.G, k, v, sink, stream, active_hook());
+  const int rc =
+      ga::launch_gather_probe(p->d_indices, p->e, g.G, k, v, sink, stream, active_hook());
   return rc == 0 ? GA_OK : GA_ERR_HIP;
 }
 

@@ -472,7 +472,8 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   if (row_slots > 0) {
     if (hook) hook("bwd_gatv2_rows_main", stream, 1);
     hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, kRowsUnroll>),
-                       dim3(static_cast<unsigned>((row_slots + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(static_cast<unsigned>((row_slots + kWavesPerBlock - 1) /
+                                                  kWavesPerBlock)),
                        dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_rows_main"))) return e;
   }
@@ -520,7 +521,8 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   if (col_items > 0) {
     if (hook) hook("bwd_gatv2_cols_main", stream, 1);
     hipLaunchKernelGGL((bwd_gatv2_cols_main<T, G, LH, GA_UNROLL_DKDV>),
-                       dim3(static_cast<unsigned>((col_items + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(static_cast<unsigned>((col_items + kWavesPerBlock - 1) /
+                                                  kWavesPerBlock)),
                        dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_cols_main"))) return e;
   }

@@ -143,7 +143,7 @@ struct BwdArgs {
   const float* attn;  // attention vector [H*d]
   float* dattn;       // its gradient [H*d]
   float* ws_da;       // da partials [n_slots][H*d]
-  double* ws_da64;    // first-stage da reduction [kReduceBlocks][H*d]
+  double* ws_da64;    // da reduction tree: two fp64 buffers of gatv2_reduce_rows() rows of H*d
 };
 
 // fp32 floats per hub-row chunk partial of the row pass: A [H*d], B [H*d], D [H], L [H]

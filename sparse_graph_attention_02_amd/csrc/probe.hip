@@ -21,7 +21,8 @@ __global__ __launch_bounds__(kBlock) void copy_probe(u32x4* __restrict__ dst,
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(x[u], dst + i + u * stride);
   }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  for (; i < n16; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // Gather-only pass over a CSR: for every edge, the G lanes of a group load the 16-byte
@@ -29,7 +30,8 @@ __global__ __launch_bounds__(kBlock) void copy_probe(u32x4* __restrict__ dst,
 // step, U = 8 steps in flight), with no arithmetic beyond an XOR that keeps the loads live.
 // Its time is the memory system's floor for the forward's neighbour gathers on that graph.
 template <int G>
-__global__ __launch_bounds__(kBlock) void gather_probe(const int32_t* __restrict__ indices, int64_t e,
+__global__ __launch_bounds__(kBlock) void gather_probe(const int32_t* __restrict__ indices,
+                                                      int64_t e,
                                                        const u32x4* __restrict__ K,
                                                        const u32x4* __restrict__ V, u32x4* sink) {
   constexpr int NG = kWave / G, U = 8;

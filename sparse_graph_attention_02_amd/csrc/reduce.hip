@@ -199,7 +199,8 @@ struct Red : RowIO<T, G, G> {
     u32x4* ap = reinterpret_cast<u32x4*>(a.arg + e0);
 #pragma unroll
     for (int k = 0; k < VEC / 4; ++k)
-      st_stream(ap + k, u32x4{static_cast<unsigned>(ar[4 * k]), static_cast<unsigned>(ar[4 * k + 1]),
+      st_stream(ap + k, u32x4{static_cast<unsigned>(ar[4 * k]),
+                              static_cast<unsigned>(ar[4 * k + 1]),
                               static_cast<unsigned>(ar[4 * k + 2]),
                               static_cast<unsigned>(ar[4 * k + 3])});
   }
@@ -276,7 +277,8 @@ struct Red : RowIO<T, G, G> {
     } else {
       const u32x4* kp = reinterpret_cast<const u32x4*>(
           MODE == kMatchArg ? static_cast<const void*>(a.arg_in + e0)
-                            : static_cast<const void*>(static_cast<const uint32_t*>(a.slot_in) + e0));
+                            : static_cast<const void*>(
+                                  static_cast<const uint32_t*>(a.slot_in) + e0));
 #pragma unroll
       for (int k = 0; k < VEC / 4; ++k) {
         const u32x4 x = kp[k];
@@ -446,7 +448,8 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a0) {
   RedArgs a = a0;
   if (a0.arg_in) a.arg_in = a0.arg_in + so * VEC;
   if (a0.slot_in)
-    a.slot_in = static_cast<const char*>(a0.slot_in) + static_cast<size_t>(so) * VEC * a0.slot_bytes;
+    a.slot_in =
+        static_cast<const char*>(a0.slot_in) + static_cast<size_t>(so) * VEC * a0.slot_bytes;
   a.dout = static_cast<const raw_t*>(a0.dout) + so;
   a.dx = static_cast<raw_t*>(a0.dx) + so;
   if (a0.ws_sum) a.ws_sum = a0.ws_sum + so * VEC;
@@ -498,7 +501,8 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
 #pragma unroll
   for (int c = 0; c < VEC; ++c) s[c] = 0;
 #pragma unroll 4
-  for (int c = c0 + g; c < c1; c += NG) K::add_f32(a.ws_sum + static_cast<size_t>(c) * a.ld * VEC, r, s);
+  for (int c = c0 + g; c < c1; c += NG)
+    K::add_f32(a.ws_sum + static_cast<size_t>(c) * a.ld * VEC, r, s);
   K::template group_sum<NG>(s);
   if (g == 0) K::store(a.dx, col, r, s, 1.f);
 }
@@ -562,7 +566,8 @@ int launch_merge(bool backward, int op, const RedArgs& a, void* stream, TimerHoo
   const int64_t b = blocks_of(a.rows.n_hub);
   if (op == kReduceMax)
     return a.rows_sorted
-               ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, true>, b, a, stream, hook)
+               ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, true>, b, a, stream,
+                    hook)
                : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, false>, b, a, stream,
                     hook);
   return a.rows_sorted
