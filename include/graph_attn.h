@@ -27,7 +27,9 @@
  *   Features: node-major, contiguous [N, H, d] in the call's dtype (fp32 or bf16), each
  *     pointer 16-byte aligned, H*d*sizeof(dtype) a multiple of 16 bytes and at most 1024
  *     bytes, d*sizeof(dtype) a power of two between 32 and 1024 bytes dividing the row.
- *     lse is fp32 [N, H].  GAT mode: s and t are fp32 [N, H] (4-byte aligned).
+ *     lse is fp32 [N, H].  GAT mode: s and t are fp32 [N, H] (4-byte aligned). N is the
+ *     plan's node count: calls receive pointers only and cannot check buffer sizes, so
+ *     every per-node array must hold N rows (kernels index them by node id).
  *   Ownership: the caller allocates and frees every device buffer (features, outputs,
  *     the plan's device copy, workspaces). The library never calls hipMalloc/hipFree;
  *     it owns only the host-side plan metadata.

@@ -173,6 +173,12 @@ def _need(t, name, shape, dtype, device):
                          f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()}")
 
 
+def _rows_match(plan, n_rows):
+    """Feature tensors must have one row per node: the kernels index them by node id."""
+    if n_rows != plan.n_nodes:
+        raise ValueError(f"tensors have {n_rows} rows, the plan's graph {plan.n_nodes} nodes")
+
+
 def _workspace(nbytes, device, ws):
     import torch
     if nbytes == 0:
@@ -194,8 +200,7 @@ def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2
         raise RuntimeError("plan is not uploaded")
     N, H, d = v.shape
     dev = v.device
-    if N != plan.n_nodes:
-        raise ValueError("feature rows != plan nodes")
+    _rows_match(plan, N)
     sc = GA_SCORE_DOT if score == "dot" else GA_SCORE_GAT if score == "gat" else None
     if sc is None:
         raise ValueError(score)
@@ -229,6 +234,7 @@ def fwd_gatv2(plan: Plan, xd, xs, attn, *, scale=1.0, neg_slope=0.2, out=None, l
         raise RuntimeError("plan is not uploaded")
     N, H, d = xs.shape
     dev = xs.device
+    _rows_match(plan, N)
     _need(xd, "xd", (N, H, d), xs.dtype, dev)
     _need(xs, "xs", (N, H, d), xs.dtype, dev)
     _need(attn, "attn", (H, d), torch.float32, dev)
@@ -257,6 +263,7 @@ def bwd(plan: Plan, q_or_s, k_or_t, v, dout, lse, *, score="dot", scale=None, ne
         raise RuntimeError("plan is not uploaded")
     N, H, d = v.shape
     dev = v.device
+    _rows_match(plan, N)
     sc = GA_SCORE_DOT if score == "dot" else GA_SCORE_GAT if score == "gat" else None
     if sc is None:
         raise ValueError(score)
@@ -303,6 +310,7 @@ def bwd_gatv2(plan: Plan, xd, xs, attn, dout, lse, *, scale=1.0, neg_slope=0.2, 
         raise RuntimeError("plan is not uploaded")
     N, H, d = xs.shape
     dev = xs.device
+    _rows_match(plan, N)
     for name, t in (("xd", xd), ("xs", xs), ("dout", dout)):
         _need(t, name, (N, H, d), xs.dtype, dev)
     _need(attn, "attn", (H, d), torch.float32, dev)
@@ -480,6 +488,7 @@ def gather_probe(plan: Plan, k, v, sink=None, stream=None):
     if sink is None:
         sink = torch.empty(1024, dtype=torch.uint8, device=k.device)
     N, H, d = k.shape
+    _rows_match(plan, N)
     with torch.cuda.device(k.device):
         graph_attn_gather_probe(plan.handle, _dtype_code(k), H, d, _ptr(k), _ptr(v), _ptr(sink),
                                 _stream(stream))

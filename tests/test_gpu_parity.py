@@ -619,3 +619,21 @@ def test_full_chunglu100k_gatv2_backward_sampled():
     cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:2], rng.choice(w.n, 100, replace=False)])
     gatv2_bwd_case("full chunglu100k gatv2 bwd (sampled)", ip, ix, xd, xs, a, do, "f32", rows=rows,
                    cols=cols)
+
+
+def test_binding_rejects_mismatched_rows():
+    """The C calls take pointers only; the binding refuses tensors whose row count is not
+    the plan's node count (the kernels would index past them)."""
+    from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2, gather_probe
+    say("binding row checks")
+    ip, ix = gg.csr_from_edges(10, np.arange(10), (np.arange(10) + 1) % 10)
+    plan = Plan(ip, ix).upload()
+    x = torch.zeros((9, 2, 32), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((9, 2), device="cuda")
+    attn = torch.zeros((2, 32), device="cuda")
+    for call in (lambda: fwd(plan, x, x, x), lambda: bwd(plan, x, x, x, x, lse),
+                 lambda: fwd_gatv2(plan, x, x, attn),
+                 lambda: bwd_gatv2(plan, x, x, attn, x, lse),
+                 lambda: gather_probe(plan, x, x)):
+        with pytest.raises(ValueError):
+            call()
