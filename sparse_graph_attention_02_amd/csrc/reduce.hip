@@ -47,7 +47,10 @@ enum { kMatchArg = 0, kMatchSlot16 = 2, kMatchSlot32 = 4 };
 
 // SORTED: every row lists its neighbours by ascending id, so among equal values the
 // smallest id is also the earliest edge; the state then orders by (value, edge index)
-// alone and the id is read from the row at the end (fewer operations per element).
+// alone and the id is read from the row at the end (fewer operations per element). Lane
+// groups then visit a row's edges from last to first and take values at least as good:
+// the last such take among equal values is the earliest edge, an initial -inf (max) or
+// +inf (min) is taken like any value, and NaN (never >= or <=) never is.
 template <typename T, int G, int OP, int U, bool SORTED = false>
 struct Red : RowIO<T, G, G> {
   using IO = RowIO<T, G, G>;
@@ -87,15 +90,15 @@ struct Red : RowIO<T, G, G> {
     return better(v, j, b, i) | ((j == i) & (p < q));
   }
 
-  // Edge k from source j (ok = the edge slot is in range); a lane group visits a row's
-  // edges in increasing k, so an edge from an id already held is never earlier and the
-  // two-way rule suffices here.
+  // Edge k from source j (ok = the edge slot is in range). Unsorted rows: a lane group
+  // visits a row's edges in increasing k, so an edge from an id already held is never
+  // earlier and the two-way rule suffices. Sorted rows: edges arrive in decreasing k and
+  // an equal value replaces the winner (see SORTED above).
   __device__ __forceinline__ static void fold(State& s, const float* x, int j, int k, bool ok) {
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
       if constexpr (SORTED) {
-        // edges arrive in increasing k, so an equal value never displaces the winner
-        const bool t = ok & (OP == kReduceMax ? x[c] > s.v[c] : x[c] < s.v[c]);
+        const bool t = ok & (OP == kReduceMax ? x[c] >= s.v[c] : x[c] <= s.v[c]);
         s.v[c] = t ? x[c] : s.v[c];
         s.pos[c] = t ? k : s.pos[c];
       } else {
@@ -107,7 +110,11 @@ struct Red : RowIO<T, G, G> {
     }
   }
 
-  // Edges [e0, e1) of a row through the state; NGS lane groups share the edges.
+  // Edges [e0, e1) of a row through the state; NGS lane groups share the edges. The loop
+  // counter runs forward; with SORTED it maps to the edges in reverse (k = e0 + e1 - 1 - n).
+  __device__ __forceinline__ static int edge_of(int e0, int e1, int n) {
+    return SORTED ? e0 + e1 - 1 - n : n;
+  }
   template <int NGS>
   __device__ __forceinline__ static void run(const RedArgs& a, int e0, int e1, int seg0, int gs,
                                              int r, State& s) {
@@ -117,7 +124,7 @@ struct Red : RowIO<T, G, G> {
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
+      const int my_j = (li < nb) ? ld_stream(a.indices + edge_of(e0, e1, base + li)) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
@@ -135,7 +142,7 @@ struct Red : RowIO<T, G, G> {
         for (int u = 0; u < U; ++u) {
           float xf[VEC];
           L16::unpack(xr[u], xf);
-          fold(s, xf, jj[u], base + t + u * NGS + gs, ok[u]);
+          fold(s, xf, jj[u], edge_of(e0, e1, base + t + u * NGS + gs), ok[u]);
         }
       }
     }

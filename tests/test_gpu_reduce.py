@@ -136,16 +136,19 @@ def test_every_row_width(dtype, F):
             bwd_parity(f"width {F} {op} {tag}", plan, ip, idx, arg, ra, dout, dtype)
 
 
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_ties_signed_zeros_and_infinities(dtype):
+def test_ties_signed_zeros_and_infinities(dtype, order):
     # values on a coarse grid (ties everywhere), with -0.0, +0.0, -inf and +inf mixed in,
-    # on a multigraph with many parallel edges and neighbour lists in random order
+    # on a multigraph with many parallel edges; neighbour lists sorted (the kernels' sorted
+    # path) or in random order
     rng = np.random.default_rng(11)
     n, F = 300, 64
     ip, ix = gg.random_multigraph(n, 6000, rng, hub_rows=(7,), hub_deg=900)
     ix = ix.copy()
-    for i in range(n):
-        rng.shuffle(ix[ip[i]:ip[i + 1]])
+    if order == "shuffled":
+        for i in range(n):
+            rng.shuffle(ix[ip[i]:ip[i + 1]])
     xv = rng.integers(-2, 3, size=(n, F)).astype(np.float32)
     special = np.array([-0.0, 0.0, -np.inf, np.inf], np.float32)
     pick = rng.random((n, F)) < 0.15
@@ -279,3 +282,31 @@ def test_feature_slices(dtype, F):
             first = (out, arg, slot)
         else:
             assert all(torch.equal(a, b) for a, b in zip(first, (out, arg, slot)))
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+@pytest.mark.parametrize("op", ["max", "min"])
+def test_rows_of_only_infinities_and_nan(op, order):
+    """A row whose values are all -inf (max) or +inf (min) returns that infinity and the
+    smallest id; NaN never wins, and a row of NaN only reads as empty."""
+    inf = -np.inf if op == "max" else np.inf
+    # node values: 0, 1, 3 = inf; 2 = NaN.  Rows: 0 <- {1, 2, 3} (inf, NaN, inf);
+    # 1 <- {0, 2} (inf, NaN); 2 <- {2, 2} (NaN only, a parallel edge); 3 <- {} (empty)
+    ip, ix = gg.csr_from_edges(4, np.array([1, 2, 3, 0, 2, 2, 2]),
+                               np.array([0, 0, 0, 1, 1, 2, 2]))
+    assert np.array_equal(ix, [1, 2, 3, 0, 2, 2, 2])
+    if order == "shuffled":
+        ix = np.array([3, 1, 2, 2, 0, 2, 2], dtype=ix.dtype)   # rows out of id order
+    x = np.zeros((4, 16), np.float32)
+    x[1] = x[3] = inf
+    x[0] = inf
+    x[2] = np.nan
+    say("infinities and NaN", op, order)
+    plan = Plan(ip, ix).upload()
+    assert plan.info()["rows_sorted"] == (order == "sorted")
+    out, arg, _ = reduce_fwd(plan, dev(x), op=op)
+    o, a = out.cpu().numpy(), arg.cpu().numpy()
+    assert np.all(o[0] == inf) and np.all(a[0] == 1)
+    assert np.all(o[1] == inf) and np.all(a[1] == 0)
+    assert np.all(o[2] == 0) and np.all(a[2] == -1)
+    assert np.all(o[3] == 0) and np.all(a[3] == -1)
