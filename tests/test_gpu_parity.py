@@ -621,6 +621,45 @@ def test_full_chunglu100k_gatv2_backward_sampled():
                    cols=cols)
 
 
+@pytest.mark.slow
+def test_full_chunglu1m_gatv2_training_step_sampled():
+    """The GATv2 training step at full size in the bench's launch configuration (default
+    plan): forward and dxd on sampled rows (top hubs, single-neighbour rows, random rows),
+    dxs on sampled columns, against the oracle; dattn, a sum over all 51M edges that the
+    oracle cannot form here, by linearity: doubling dout doubles every gradient exactly."""
+    from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2
+    w = gg.WORKLOADS["chunglu1m_gatv2_train_bf16"]
+    ip, ix = gg.make_graph(w)
+    xd, xs, a = gg.make_features(w)
+    do = gg.make_dout(w)
+    say("full chunglu1m gatv2 training step (sampled)", "E", ix.size)
+    plan = Plan(ip, ix).upload()
+    txd, txs, ta, td = dev(xd), dev(xs), dev(a), dev(do)
+    out, lse = fwd_gatv2(plan, txd, txs, ta)
+    dxd, dxs, da = bwd_gatv2(plan, txd, txs, ta, td, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = _sample_rows(ip, rng, k=48)
+    odeg = np.bincount(ix, minlength=w.n)
+    mid = np.flatnonzero((odeg > 100) & (odeg <= 400))
+    cols = np.unique(np.r_[rng.choice(mid, 3, replace=False),
+                           rng.choice(np.flatnonzero(odeg <= 16), 12, replace=False)])
+    sl = f32(0.2)
+    ro, rl = A.forward_gatv2_rows(ip, ix, xd, xs, a, rows, 1.0, sl)
+    rt, ct = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    check("gatv2 1M out", host64(out[rt]), ro, "bf16")
+    check_lse("gatv2 1M lse", host64(lse[rt]), rl)
+    rxd, _ = A.grad_gatv2_rows(ip, ix, xd, xs, a, do, rows, 1.0, sl)
+    check("gatv2 1M dxd", host64(dxd[rt]), rxd, "bf16")
+    rxs = A.grad_gatv2_cols(ip, ix, xd, xs, a, do, cols, 1.0, sl)
+    check("gatv2 1M dxs", host64(dxs[ct]), rxs, "bf16")
+    assert torch.isfinite(da).all() and da.abs().sum() > 0
+    dxd2, dxs2, da2 = bwd_gatv2(plan, txd, txs, ta, (td.float() * 2).to(td.dtype), lse)
+    torch.cuda.synchronize()
+    assert torch.equal(da2, da * 2)
+    assert torch.equal(dxd2, dxd * 2) and torch.equal(dxs2, dxs * 2)
+
+
 def test_binding_rejects_mismatched_rows():
     """The C calls take pointers only; the binding refuses tensors whose row count is not
     the plan's node count (the kernels would index past them)."""
