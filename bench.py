@@ -163,20 +163,38 @@ def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     }
 
 
-def relabel_by_out_degree(ip, ix, feats, dout):
-    """Node order ablation: new id = rank by out-degree (descending, ties by old id). The
-    graph is the same up to relabelling; features move with their nodes."""
+def relabel(ip, ix, feats, dout, old_of_new):
+    """The same graph with node old_of_new[k] renamed k; per-node arrays move with their
+    nodes (per-graph arrays such as the GATv2 attention vector stay)."""
     n = ip.size - 1
-    odeg = np.bincount(ix, minlength=n)
-    old_of_new = np.lexsort((np.arange(n), -odeg))
     new_of_old = np.empty(n, np.int64)
     new_of_old[old_of_new] = np.arange(n)
     dst = new_of_old[np.repeat(np.arange(n), np.diff(ip))]
     src = new_of_old[ix]
     ip2, ix2 = gg.csr_from_edges(n, src, dst)
-    feats = tuple(np.ascontiguousarray(f[old_of_new]) for f in feats)
+    feats = tuple(np.ascontiguousarray(f[old_of_new]) if f.shape[0] == n else f for f in feats)
     dout = None if dout is None else np.ascontiguousarray(dout[old_of_new])
     return ip2, ix2, feats, dout
+
+
+def order_by_out_degree(ip, ix):
+    """Node order ablation: rank by out-degree (descending, ties by old id), so the hot
+    source rows are contiguous."""
+    n = ip.size - 1
+    odeg = np.bincount(ix, minlength=n)
+    return np.lexsort((np.arange(n), -odeg))
+
+
+def order_rcm(ip, ix):
+    """Node order ablation: reverse Cuthill-McKee on the symmetrised pattern (scipy), a
+    bandwidth-reducing locality order: neighbours get nearby ids."""
+    import scipy.sparse as sp
+    from scipy.sparse.csgraph import reverse_cuthill_mckee
+    n = ip.size - 1
+    a = sp.csr_matrix((np.ones(ix.size, np.int8), ix, ip), shape=(n, n))
+    sym = (a + a.T).tocsr()
+    sym.sum_duplicates()
+    return np.asarray(reverse_cuthill_mckee(sym, symmetric_mode=True), dtype=np.int64)
 
 
 # ---------------------------------------------------------------- GPU
@@ -235,9 +253,11 @@ def main():
     ap.add_argument("--col-chunk", type=int, default=None)
     ap.add_argument("--slices", type=int, default=None,
                     help="feature slices per XCD group (0 = automatic, 1 = off, 2, 4, 8)")
-    ap.add_argument("--order", choices=["as-generated", "out-degree"], default="as-generated",
+    ap.add_argument("--order", choices=["as-generated", "out-degree", "rcm"],
+                    default="as-generated",
                     help="node order ablation: relabel nodes by descending out-degree (hot "
-                         "source rows contiguous) before the run")
+                         "source rows contiguous) or by reverse Cuthill-McKee (locality) "
+                         "before the run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -249,8 +269,9 @@ def main():
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)
     dout = gg.make_dout(w) if w.backward else None
-    if args.order == "out-degree":
-        ip, ix, feats, dout = relabel_by_out_degree(ip, ix, feats, dout)
+    if args.order != "as-generated":
+        order = order_by_out_degree(ip, ix) if args.order == "out-degree" else order_rcm(ip, ix)
+        ip, ix, feats, dout = relabel(ip, ix, feats, dout, order)
     gen_s = time.perf_counter() - t0
     N, E, H, d = ip.size - 1, ix.size, w.heads, w.dim
     b = 2 if w.dtype == "bf16" else 4
