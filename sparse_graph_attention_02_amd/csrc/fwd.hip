@@ -14,6 +14,8 @@
 //   [.., + ceil(n_light / NG))   light rows: one G-lane group per row, NG rows per wave
 // Bins are sorted by degree descending, so the longest items start first. A second
 // launch (fwd_hub_merge) folds each hub row's chunk partials in ascending chunk order.
+// With feature slices (see fwd_main) every item is run once per slice of whole heads, the
+// slices dealt to XCD groups; the merge works on full rows.
 //
 // Score modes: dot (q_i . k_j), GAT-style (LeakyReLU(s_i + t_j)) and GATv2
 // (a . LeakyReLU(xd_i + xs_j), where the gathered source row xs_j is also the value, so a
