@@ -34,7 +34,9 @@
  *     the plan's device copy, workspaces). The library never calls hipMalloc/hipFree;
  *     it owns only the host-side plan metadata.
  *   Streams: `stream` is a hipStream_t (NULL = the default stream). fwd/bwd only enqueue
- *     work and return; results are ready when the stream reaches them.
+ *     work and return; results are ready when the stream reaches them. They neither
+ *     allocate nor synchronise nor memset, so they can be captured into a HIP graph
+ *     (with the kernel timers off) and replayed.
  *   Errors: every call returns a ga_status; nothing throws or aborts across the ABI.
  *     Argument checks run before any HIP call, so an invalid call enqueues nothing.
  *   Determinism: no atomics anywhere; partial states merge in a fixed order, so two runs
