@@ -235,12 +235,13 @@ ga_status graph_attn_bwd(const ga_plan* plan, ga_score score, ga_dtype dtype, in
                          void* stream);
 
 /* Workspace of graph_attn_bwd_gatv2: per-node records N*H*8 bytes, row-chunk partials
- * n_row_chunks*(4*H*d + 4*ceil(2H/4))*4, column-chunk partials n_col_chunks*2*H*d*4, the
- * attention-gradient partials (S = one per 16 row-pass work items plus one per hub row,
- * H*d*4 bytes each) and fp64 reduction buffers of (ceil(S/32) + ceil(S/1024))*H*d*8
+ * n_row_chunks*(2*H*d + 4*ceil(2H/4))*4, column-chunk partials n_col_chunks*2*H*d*4, the
+ * attention-gradient partials (S = one per 16 work items of the row pass, one per 16 of the
+ * column pass, plus one per hub row and hub column, H*d*4 bytes each) and fp64 reduction buffers
+ * of (ceil(S/32) + ceil(S/1024))*H*d*8
  * bytes, each section 256-byte aligned (0 bytes for a graph with no nodes: then the
- * workspace may be NULL). The number of row-pass work items depends on the lanes per
- * feature row, hence `dtype`. */
+ * workspace may be NULL). The number of work items depends on the lanes per feature row,
+ * hence `dtype`. */
 ga_status graph_attn_bwd_gatv2_workspace_bytes(const ga_plan* plan, ga_dtype dtype,
                                                int32_t heads, int32_t dim, size_t* bytes);
 

@@ -158,8 +158,8 @@ Gv2Layout gatv2_layout(const ga_plan* p, const ga::Geometry& g) {
   const size_t F = size_t(g.heads) * g.dim;
   Gv2Layout L;
   L.ld = align_up(size_t(p->n) * g.heads * 2 * sizeof(float));
-  L.rows = align_up(p->rows.chunk_row.size() * (4 * F + (2 * g.heads + 3) / 4 * 4) *
-                    sizeof(float));
+  L.rows = align_up(p->rows.chunk_row.size() *
+                    size_t(ga::gatv2_row_partial_floats(g.heads, g.dim)) * sizeof(float));
   L.cols = align_up(p->cols.chunk_row.size() * 2 * F * sizeof(float));
   const int64_t slots = ga::gatv2_da_slots(p, g);
   L.da = align_up(size_t(slots) * F * sizeof(float));

@@ -6,24 +6,29 @@
 // per-node log-sum-exp; cached transposed adjacency for the backward). GATv2 is the layer
 // the pages name; its score is the textbook one.
 //
-// With g = LeakyReLU'(z), lz = LeakyReLU(z) (elementwise), P_ij = exp(e_ij - lse_i),
-// dp_ij = <dout_i, xs_j>, L_i = sum_j P_ij (1 up to the stored lse's rounding; the weights
-// are renormalised by it), D^_i = sum_j P_ij dp_ij / L_i, dS_ij = P_ij / L_i (dp_ij - D^_i):
-//   bwd_gatv2_rows_main   over CSR rows: per lane element
-//                           A1 = sum P dp g,  B1 = sum P g,  A2 = sum P dp lz,  B2 = sum P lz
-//                         dxd_i = scale a (A1 - D^ B1) / L,  da_i = scale (A2 - D^ B2) / L
-//                         and the record (lse_i log2 e + log2 L_i, D^_i) for the column pass.
-//                         Each of the W wavefronts runs kItemsPerWave work items dealt in
-//                         snake order (pass k takes item k W + w, or k W + W-1-w on odd
-//                         passes; items are sorted by size, so every wave gets a mix) and
-//                         writes one fp32 partial of da (hub rows: chunk partials, see merge)
+// With g = LeakyReLU'(z) (elementwise), P_ij = exp(e_ij - lse_i), dp_ij = <dout_i, xs_j>,
+// L_i = sum_j P_ij (1 up to the stored lse's rounding; the weights are renormalised by it),
+// D^_i = sum_j P_ij dp_ij / L_i, dS_ij = P_ij / L_i (dp_ij - D^_i),
+//   R_i = sum_j dS_ij g_ij  and  C_j = sum_i dS_ij g_ij  (elementwise):
+//   dxd_i = scale a R_i,   dxs_j = scale a C_j + sum_i P_ij dout_i,
+//   dattn = scale sum_ij dS_ij LeakyReLU(z_ij) = scale (sum_i xd_i R_i + sum_j xs_j C_j),
+// the last because LeakyReLU(z) = g z and z_ij = xd_i + xs_j: the attention gradient costs
+// one product per node instead of two per edge.
+//   bwd_gatv2_rows_main   over CSR rows: per lane element A1 = sum P dp g, B1 = sum P g,
+//                         R_i = (A1 - D^ B1) / L; writes dxd, the record
+//                         (lse_i log2 e + log2 L_i, D^_i) for the column pass, and
+//                         scale xd_i R_i into the wave's dattn partial. Each of the W
+//                         wavefronts runs kItemsPerWave work items dealt in snake order (pass
+//                         k takes item k W + w, or k W + W-1-w on odd passes; items are sorted
+//                         by size, so every wave gets a mix) and writes one fp32 partial
 //   bwd_gatv2_rows_merge  hub rows: ordered sums of the chunk partials, then as above (one
-//                         da partial per hub row)
-//   bwd_gatv2_da_reduce   fixed-order fp64 tree over the da partials (32 rows per block per
-//                         stage, ping-pong buffers) -> dattn [H*d]
-//   bwd_gatv2_cols_main   over transpose columns: dxs_j = scale a sum_i dS_ij g_ij
-//                                                          + sum_i P_ij dout_i
-//   bwd_gatv2_cols_merge  hub columns: ordered sums of partials
+//                         partial per hub row)
+//   bwd_gatv2_cols_main   over transpose columns, dealt to waves the same way (fewer items
+//                         per wave): dxs_j, and scale xs_j C_j into the wave's LDS tile; the
+//                         block's four tiles are summed into one partial per block
+//   bwd_gatv2_cols_merge  hub columns: ordered sums of partials, then as above
+//   bwd_gatv2_da_reduce   fixed-order fp64 tree over all dattn partials (32 rows per block
+//                         per stage, ping-pong buffers) -> dattn [H*d]
 // No atomics; every sum has a fixed order, so results are bitwise reproducible.
 #include "ga_device.h"
 #include "ga_internal.h"
@@ -32,6 +37,12 @@ namespace ga {
 namespace {
 
 constexpr int kItemsPerWave = 16;  // row-pass work items per wavefront (bounds da partials)
+// Column-pass work items per wavefront. Fewer than the row pass: the column pass is
+// memory-bound and balances best with fine-grained waves; its partials are per block.
+#ifndef GA_GV2_COL_ITEMS
+#define GA_GV2_COL_ITEMS 4
+#endif
+constexpr int kColItemsPerWave = GA_GV2_COL_ITEMS;
 constexpr int kReduceFan = 32;     // rows summed per block in each da reduction stage
 constexpr int kRowsUnroll = 3;     // edges in flight per lane group in the row pass (4 waves/SIMD)
 
@@ -46,24 +57,20 @@ struct BwdV2 : RowIO<T, G, LH> {
   using IO::R;
   using IO::VEC;
   using typename IO::acc_t;
-  static constexpr int kRowStride = 4 * F + (2 * H + 3) / 4 * 4;  // A1 B1 A2 B2 [F], D L [H]
+  static constexpr int kRowStride = 2 * F + (2 * H + 3) / 4 * 4;  // A1 B1 [F], D L [H]
   static constexpr int kColStride = 2 * F;                        // C1 C2 [F]
 
-  // A1, B1 (for dxd) are row-normalised fp32 sums. A2, B2, D, L feed dattn, a sum over
-  // every edge of the graph whose per-row terms cancel; for fp32 features they are kept in
-  // fp64 (acc_t) so the graph-wide sum keeps fp32-level accuracy.
+  // A1, B1, D, L feed dxd and, through R_i, dattn: a sum over the whole graph of per-row
+  // terms that cancel; for fp32 features they are kept in fp64 (acc_t) so that sum keeps
+  // fp32-level accuracy.
   struct RowAcc {
-    float A1[VEC], B1[VEC];
-    acc_t A2[VEC], B2[VEC];
+    acc_t A1[VEC], B1[VEC];
     acc_t D, L;
   };
 
   __device__ __forceinline__ static void zero(RowAcc& s) {
 #pragma unroll
-    for (int c = 0; c < VEC; ++c) {
-      s.A1[c] = s.B1[c] = 0.f;
-      s.A2[c] = s.B2[c] = 0;
-    }
+    for (int c = 0; c < VEC; ++c) s.A1[c] = s.B1[c] = 0;
     s.D = s.L = 0;
   }
 
@@ -121,13 +128,12 @@ struct BwdV2 : RowIO<T, G, LH> {
           float xs[VEC];
           L16::unpack(xr[u], xs);
           // g = LeakyReLU'(z) by one select, LeakyReLU(z) = z g exactly (g is 1 or the slope)
-          float g[VEC], lz[VEC], e = 0.f;
+          float g[VEC], e = 0.f;
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
             const float z = xd[c] + xs[c];
             g[c] = z >= 0.f ? 1.f : a.neg_slope;
-            lz[c] = z * g[c];
-            e = fmaf(av[c], lz[c], e);
+            e = fmaf(av[c], z * g[c], e);
           }
           const float s2 = head_sum<LH>(e) * a.sc2;
           const float dp = head_sum<LH>(L16::dot_packed(dor, xr[u]));
@@ -137,10 +143,8 @@ struct BwdV2 : RowIO<T, G, LH> {
           s.L += static_cast<acc_t>(p);
 #pragma unroll
           for (int c = 0; c < VEC; ++c) {
-            s.A1[c] = fmaf(pdp, g[c], s.A1[c]);
-            s.B1[c] = fmaf(p, g[c], s.B1[c]);
-            s.A2[c] += static_cast<acc_t>(pdp * lz[c]);
-            s.B2[c] += static_cast<acc_t>(p * lz[c]);
+            s.A1[c] = fma(static_cast<acc_t>(pdp), static_cast<acc_t>(g[c]), s.A1[c]);
+            s.B1[c] = fma(static_cast<acc_t>(p), static_cast<acc_t>(g[c]), s.B1[c]);
           }
         }
       }
@@ -151,16 +155,15 @@ struct BwdV2 : RowIO<T, G, LH> {
   __device__ __forceinline__ static void combine(RowAcc& s) {
     IO::template group_sum<NGS>(s.A1);
     IO::template group_sum<NGS>(s.B1);
-    IO::template group_sum<NGS>(s.A2);
-    IO::template group_sum<NGS>(s.B2);
     IO::template group_sum1<NGS>(s.D);
     IO::template group_sum1<NGS>(s.L);
   }
 
-  // Row epilogue: dxd, the record, and this row's da contribution added into `da`.
+  // Row epilogue: dxd, the record, and this row's dattn term scale xd R added into `da`.
   __device__ __forceinline__ static void finish_row(const BwdArgs& a, int row, int r, int h,
                                                     float lse2, const float* av,
-                                                    const RowAcc& s, acc_t* da) {
+                                                    const float* xd, const RowAcc& s,
+                                                    acc_t* da) {
     const acc_t inv = s.L > 0 ? acc_t(1) / s.L : acc_t(0);
     const acc_t Dn = s.D * inv;
     const acc_t f = static_cast<acc_t>(a.scale) * inv;
@@ -168,8 +171,9 @@ struct BwdV2 : RowIO<T, G, LH> {
     float x[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) {
-      x[c] = av[c] * fmaf(-Dn32, s.B1[c], s.A1[c]);
-      da[c] += f * (s.A2[c] - Dn * s.B2[c]);
+      const acc_t rc = s.A1[c] - Dn * s.B1[c];  // L R_i
+      x[c] = av[c] * static_cast<float>(rc);
+      da[c] += f * rc * static_cast<acc_t>(xd[c]);
     }
     IO::store(a.dq, row, r, x, static_cast<float>(f));
     if (r % LH == 0) {
@@ -182,21 +186,17 @@ struct BwdV2 : RowIO<T, G, LH> {
   __device__ __forceinline__ static void store_partial(float* p, int r, int h, const RowAcc& s) {
     IO::store_f32(p, r, s.A1);
     IO::store_f32(p + F, r, s.B1);
-    IO::store_f32(p + 2 * F, r, s.A2);
-    IO::store_f32(p + 3 * F, r, s.B2);
     if (r % LH == 0) {
-      st_stream(p + 4 * F + h, static_cast<float>(s.D));
-      st_stream(p + 4 * F + H + h, static_cast<float>(s.L));
+      st_stream(p + 2 * F + h, static_cast<float>(s.D));
+      st_stream(p + 2 * F + H + h, static_cast<float>(s.L));
     }
   }
 
   __device__ __forceinline__ static void add_partial(const float* p, int r, int h, RowAcc& s) {
     IO::add_f32(p, r, s.A1);
     IO::add_f32(p + F, r, s.B1);
-    IO::add_f32(p + 2 * F, r, s.A2);
-    IO::add_f32(p + 3 * F, r, s.B2);
-    s.D += static_cast<acc_t>(ld_stream(p + 4 * F + h));
-    s.L += static_cast<acc_t>(ld_stream(p + 4 * F + H + h));
+    s.D += static_cast<acc_t>(ld_stream(p + 2 * F + h));
+    s.L += static_cast<acc_t>(ld_stream(p + 2 * F + H + h));
   }
 
   // Column pass over transpose edges [e0, e1) of column j (xs_j held by the lane).
@@ -261,6 +261,16 @@ struct BwdV2 : RowIO<T, G, LH> {
       x[c] = static_cast<acc_t>(a.scale * av[c]) * C1[c] + C2[c];
     IO::store(a.dk, col, r, x, 1.f);
   }
+
+  // The column's dattn term scale xs_j C_j added into `da` (registers, or the lane's
+  // column of an LDS tile [VEC][64] when Stride = kWave).
+  template <int Stride = 1>
+  __device__ __forceinline__ static void add_col_da(const BwdArgs& a, const float* xs,
+                                                    const acc_t* C1, acc_t* da) {
+#pragma unroll
+    for (int c = 0; c < VEC; ++c)
+      da[c * Stride] += static_cast<acc_t>(a.scale) * C1[c] * static_cast<acc_t>(xs[c]);
+  }
 };
 
 template <typename T, int G, int LH, int U>
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdAr
         if (chunk)
           K::store_partial(a.ws_dq + static_cast<size_t>(item) * K::kRowStride, r, h, s);
         else
-          K::finish_row(a, row, r, h, lse2, av, s, da);
+          K::finish_row(a, row, r, h, lse2, av, xd, s, da);
       }
     } else {
       const int64_t li = (item - B.n_chunks - B.n_medium) * NG + g;
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdAr
         dor = ld_stream(K::R(a.dout) + off);
         lse2 = ld_stream(a.lse + static_cast<size_t>(row) * K::H + h) * kLog2e;
         K::template run_rows<1>(a, e0, e1, g * G, 0, r, xd, dor, av, lse2, s);
-        K::finish_row(a, row, r, h, lse2, av, s, da);
+        K::finish_row(a, row, r, h, lse2, av, xd, s, da);
       }
     }
   }
@@ -329,9 +339,9 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdAr
   if (g == 0) K::store_f32(a.ws_da + static_cast<size_t>(slot) * F, r, da);
 }
 
-// One wavefront per hub row; its da contribution goes to partial slot n_row_slots + hub.
+// One wavefront per hub row; its dattn term goes to partial slot slot0 + hub.
 template <typename T, int G, int LH>
-__global__ __launch_bounds__(kBlock) void bwd_gatv2_rows_merge(BwdArgs a, int n_row_slots) {
+__global__ __launch_bounds__(kBlock) void bwd_gatv2_rows_merge(BwdArgs a, int64_t slot0) {
   using K = BwdV2<T, G, LH, 1>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F, H = K::H;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -347,14 +357,15 @@ __global__ __launch_bounds__(kBlock) void bwd_gatv2_rows_merge(BwdArgs a, int n_
     K::add_partial(a.ws_dq + static_cast<size_t>(c) * K::kRowStride, r, h, s);
   K::template combine<NG>(s);
   if (g != 0) return;
-  float av[VEC];
+  float av[VEC], xd[VEC];
   typename K::acc_t da[VEC];
   K::load_attn(a, r, av);
+  K::L16::unpack(ld_stream(K::R(a.q) + static_cast<size_t>(row) * G + r), xd);
 #pragma unroll
   for (int c = 0; c < VEC; ++c) da[c] = 0;
   const float lse2 = ld_stream(a.lse + static_cast<size_t>(row) * H + h) * kLog2e;
-  K::finish_row(a, row, r, h, lse2, av, s, da);
-  K::store_f32(a.ws_da + static_cast<size_t>(n_row_slots + hub) * F, r, da);
+  K::finish_row(a, row, r, h, lse2, av, xd, s, da);
+  K::store_f32(a.ws_da + static_cast<size_t>(slot0 + hub) * F, r, da);
 }
 
 // One reduction stage: block b sums rows [b*kReduceFan, min((b+1)*kReduceFan, n)) of src
@@ -377,58 +388,92 @@ __global__ __launch_bounds__(kBlock) void bwd_gatv2_da_reduce(const S* __restric
   }
 }
 
+// Column pass, dealt like the row pass: wave w of W runs kColItemsPerWave items in snake
+// order; block b writes its waves' dattn partial to slot slot0 + b.
 template <typename T, int G, int LH, int U>
-__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdArgs a,
+                                                                       int64_t slot0) {
   using K = BwdV2<T, G, LH, U>;
-  constexpr int NG = K::NG, VEC = K::VEC;
+  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
   const int lane = threadIdx.x & (kWave - 1);
-  const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int slot = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.cols;
-  float av[VEC], xs[VEC];
-  typename K::acc_t C1[VEC], C2[VEC];
-#pragma unroll
-  for (int c = 0; c < VEC; ++c) C1[c] = C2[c] = 0;
+  const int64_t n_items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  const int64_t W = (n_items + kColItemsPerWave - 1) / kColItemsPerWave;
+  // Each wave's dattn sum lives in LDS, one column of [VEC][64] per lane (touched once per
+  // item, so the edge loop keeps its registers); the block's waves are summed at the end
+  // into one partial per block.
+  __shared__ typename K::acc_t da_lds[kWavesPerBlock][VEC][kWave];
+  typename K::acc_t* da = &da_lds[threadIdx.x >> 6][0][lane];
+  float av[VEC];
   K::load_attn(a, r, av);
-  if (item < B.n_chunks + B.n_medium) {
-    int col, e0, e1;
-    const bool chunk = item < B.n_chunks;
-    if (chunk) {
-      col = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) da[c * kWave] = 0;
+  // waves of the last block past the last slot take no item but still join the block sum
+  for (int k = 0; k < kColItemsPerWave && slot < W; ++k) {
+    const int64_t item = int64_t(k) * W + ((k & 1) ? W - 1 - slot : slot);
+    if (item >= n_items) continue;
+    float xs[VEC];
+    typename K::acc_t C1[VEC], C2[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) C1[c] = C2[c] = 0;
+    if (item < B.n_chunks + B.n_medium) {
+      int col, e0, e1;
+      const bool chunk = item < B.n_chunks;
+      if (chunk) {
+        col = B.chunk_row[item];
+        e0 = B.chunk_begin[item];
+        e1 = B.chunk_end[item];
+      } else {
+        col = B.medium[item - B.n_chunks];
+        e0 = a.colptr[col];
+        e1 = a.colptr[col + 1];
+      }
+      const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
+      K::L16::unpack(xsr, xs);
+      K::template run_cols<NG>(a, e0, e1, 0, g, r, h, xsr, xs, av, C1, C2);
+      K::template group_sum<NG>(C1);
+      K::template group_sum<NG>(C2);
+      if (g == 0) {
+        if (chunk) {
+          float* p = a.ws_dkv + static_cast<size_t>(item) * K::kColStride;
+          K::store_f32(p, r, C1);
+          K::store_f32(p + F, r, C2);
+        } else {
+          K::store_col(a, col, r, av, C1, C2);
+          K::template add_col_da<kWave>(a, xs, C1, da);
+        }
+      }
     } else {
-      col = B.medium[item - B.n_chunks];
-      e0 = a.colptr[col];
-      e1 = a.colptr[col + 1];
+      const int64_t li = (item - B.n_chunks - B.n_medium) * NG + g;
+      if (li < B.n_light) {
+        const int col = B.light[li];
+        const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
+        const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
+        K::L16::unpack(xsr, xs);
+        K::template run_cols<1>(a, e0, e1, g * G, 0, r, h, xsr, xs, av, C1, C2);
+        K::store_col(a, col, r, av, C1, C2);
+        K::template add_col_da<kWave>(a, xs, C1, da);
+      }
     }
-    const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
-    K::L16::unpack(xsr, xs);
-    K::template run_cols<NG>(a, e0, e1, 0, g, r, h, xsr, xs, av, C1, C2);
-    K::template group_sum<NG>(C1);
-    K::template group_sum<NG>(C2);
-    if (g != 0) return;
-    if (chunk) {
-      float* p = a.ws_dkv + static_cast<size_t>(item) * K::kColStride;
-      K::store_f32(p, r, C1);
-      K::store_f32(p + K::F, r, C2);
-    } else {
-      K::store_col(a, col, r, av, C1, C2);
-    }
-    return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
-  if (li >= B.n_light) return;
-  const int col = B.light[li];
-  const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
-  const typename K::raw_t xsr = ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r);
-  K::L16::unpack(xsr, xs);
-  K::template run_cols<1>(a, e0, e1, g * G, 0, r, h, xsr, xs, av, C1, C2);
-  K::store_col(a, col, r, av, C1, C2);
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  typename K::acc_t dsum[VEC];
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) {
+    dsum[c] = da_lds[0][c][lane];
+#pragma unroll
+    for (int w = 1; w < kWavesPerBlock; ++w) dsum[c] += da_lds[w][c][lane];
+  }
+  K::template group_sum<NG>(dsum);
+  if (g == 0) K::store_f32(a.ws_da + static_cast<size_t>(slot0 + blockIdx.x) * F, r, dsum);
 }
 
+// One wavefront per hub column; its dattn term goes to partial slot slot0 + hub.
 template <typename T, int G, int LH>
-__global__ __launch_bounds__(kBlock) void bwd_gatv2_cols_merge(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) void bwd_gatv2_cols_merge(BwdArgs a, int64_t slot0) {
   using K = BwdV2<T, G, LH, 1>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -449,9 +494,15 @@ __global__ __launch_bounds__(kBlock) void bwd_gatv2_cols_merge(BwdArgs a) {
   K::template group_sum<NG>(C1);
   K::template group_sum<NG>(C2);
   if (g != 0) return;
-  float av[VEC];
+  float av[VEC], xs[VEC];
+  typename K::acc_t da[VEC];
   K::load_attn(a, r, av);
+  K::L16::unpack(ld_stream(K::R(a.k) + static_cast<size_t>(col) * G + r), xs);
+#pragma unroll
+  for (int c = 0; c < VEC; ++c) da[c] = 0;
   K::store_col(a, col, r, av, C1, C2);
+  K::add_col_da(a, xs, C1, da);
+  K::store_f32(a.ws_da + static_cast<size_t>(slot0 + hub) * F, r, da);
 }
 
 template <typename T, int G, int LH>
@@ -459,30 +510,47 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   constexpr int NG = kWave / G;
   constexpr int F = G * Lane16<T>::VEC;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  auto items_of = [](const DevBins& B) {
-    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  auto waves_of = [](const DevBins& B, int per_wave) {
+    const int64_t items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+    return (items + per_wave - 1) / per_wave;
   };
-  const int64_t row_slots = (items_of(a.rows) + kItemsPerWave - 1) / kItemsPerWave;
-  const int64_t n_slots = row_slots + a.rows.n_hub;
+  auto blocks = [](int64_t waves) {
+    return dim3(static_cast<unsigned>((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+  };
+  // dattn partial slots: row waves, hub rows, column blocks, hub columns
+  const int64_t row_waves = waves_of(a.rows, kItemsPerWave);
+  const int64_t col_waves = waves_of(a.cols, kColItemsPerWave);
+  const int64_t col_blocks = (col_waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t slot_rh = row_waves, slot_cw = slot_rh + a.rows.n_hub;
+  const int64_t slot_ch = slot_cw + col_blocks, n_slots = slot_ch + a.cols.n_hub;
   int e;
   auto done = [&](const char* name) -> int {
     if (hook) hook(name, stream, 0);
     return static_cast<int>(hipGetLastError());
   };
-  if (row_slots > 0) {
+  if (row_waves > 0) {
     if (hook) hook("bwd_gatv2_rows_main", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, kRowsUnroll>),
-                       dim3(static_cast<unsigned>((row_slots + kWavesPerBlock - 1) /
-                                                  kWavesPerBlock)),
+    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, kRowsUnroll>), blocks(row_waves),
                        dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_rows_main"))) return e;
   }
   if (a.rows.n_hub > 0) {
     if (hook) hook("bwd_gatv2_rows_merge", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_rows_merge<T, G, LH>),
-                       dim3((a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                       s, a, static_cast<int>(row_slots));
+    hipLaunchKernelGGL((bwd_gatv2_rows_merge<T, G, LH>), blocks(a.rows.n_hub), dim3(kBlock), 0,
+                       s, a, slot_rh);
     if ((e = done("bwd_gatv2_rows_merge"))) return e;
+  }
+  if (col_waves > 0) {
+    if (hook) hook("bwd_gatv2_cols_main", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_cols_main<T, G, LH, GA_UNROLL_DKDV>), blocks(col_waves),
+                       dim3(kBlock), 0, s, a, slot_cw);
+    if ((e = done("bwd_gatv2_cols_main"))) return e;
+  }
+  if (a.cols.n_hub > 0) {
+    if (hook) hook("bwd_gatv2_cols_merge", stream, 1);
+    hipLaunchKernelGGL((bwd_gatv2_cols_merge<T, G, LH>), blocks(a.cols.n_hub), dim3(kBlock), 0,
+                       s, a, slot_ch);
+    if ((e = done("bwd_gatv2_cols_merge"))) return e;
   }
   {
     // fp32 slots -> fp64 rows, then fp64 stages until one block remains; that last stage
@@ -517,22 +585,6 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
     }
     if ((e = done("bwd_gatv2_da_reduce"))) return e;
   }
-  const int64_t col_items = items_of(a.cols);
-  if (col_items > 0) {
-    if (hook) hook("bwd_gatv2_cols_main", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_cols_main<T, G, LH, GA_UNROLL_DKDV>),
-                       dim3(static_cast<unsigned>((col_items + kWavesPerBlock - 1) /
-                                                  kWavesPerBlock)),
-                       dim3(kBlock), 0, s, a);
-    if ((e = done("bwd_gatv2_cols_main"))) return e;
-  }
-  if (a.cols.n_hub > 0) {
-    if (hook) hook("bwd_gatv2_cols_merge", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_cols_merge<T, G, LH>),
-                       dim3((a.cols.n_hub + kWavesPerBlock - 1) / kWavesPerBlock), dim3(kBlock), 0,
-                       s, a);
-    if ((e = done("bwd_gatv2_cols_merge"))) return e;
-  }
   return 0;
 }
 
@@ -554,9 +606,20 @@ int dispatch(const Geometry& g, const BwdArgs& a, void* stream, TimerHook hook) 
 
 int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g) {
   const int64_t NG = kWave / g.G;
-  const int64_t items = int64_t(p->rows.chunk_row.size()) + int64_t(p->rows.medium.size()) +
-                        (int64_t(p->rows.light.size()) + NG - 1) / NG;
-  return (items + kItemsPerWave - 1) / kItemsPerWave + int64_t(p->rows.hub.size());
+  auto waves = [&](const Bins& b, int per_wave) {
+    const int64_t items = int64_t(b.chunk_row.size()) + int64_t(b.medium.size()) +
+                          (int64_t(b.light.size()) + NG - 1) / NG;
+    return (items + per_wave - 1) / per_wave;
+  };
+  const int64_t col_blocks = (waves(p->cols, kColItemsPerWave) + kWavesPerBlock - 1) /
+                             kWavesPerBlock;
+  return waves(p->rows, kItemsPerWave) + int64_t(p->rows.hub.size()) + col_blocks +
+         int64_t(p->cols.hub.size());
+}
+
+int64_t gatv2_row_partial_floats(int heads, int dim) {
+  const int64_t F = int64_t(heads) * dim;
+  return 2 * F + (2 * int64_t(heads) + 3) / 4 * 4;
 }
 
 // fp64 rows of the two ping-pong buffers of the da reduction: the first stage writes

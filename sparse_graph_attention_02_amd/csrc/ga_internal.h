@@ -174,9 +174,11 @@ int launch_bwd_gat(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* strea
 // GATv2: q/k/dq/dk carry xd/xs/dxd/dxs ([N, H, d]); attn/dattn/ws_da/ws_da64 set.
 int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
                      TimerHook hook);
-// da partial slots of the GATv2 row pass, and the fp64 rows of its reduction buffers
-// (total, and the first buffer's share).
+// dattn partial slots of the GATv2 backward (row waves, hub rows, column waves, hub
+// columns), the floats of one row-chunk partial, and the fp64 rows of the dattn reduction
+// buffers (total, and the first buffer's share).
 int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g);
+int64_t gatv2_row_partial_floats(int heads, int dim);  // A1 B1 [H*d], D L [H] (padded)
 int64_t gatv2_reduce_rows(int64_t n_slots);
 int64_t gatv2_reduce_rows_a(int64_t n_slots);
 // Neighbourhood min / max reduction (reduce.hip). Rows of F elements are G lanes x 16 B.

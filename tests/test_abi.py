@@ -238,10 +238,12 @@ def test_bwd_gatv2_argument_checks():
     capi.graph_attn_bwd_gatv2_workspace_bytes(p.handle, capi.GA_BF16, 8, 32, byref(need))
     info = p.info()
     al = lambda x: (x + 255) // 256 * 256
-    items = info["n_row_chunks"] + info["n_row_medium"] + -(-info["n_row_light"] // 2)
-    slots = -(-items // 16) + info["n_row_hub"]
+    slots = 0
+    for side in ("row", "col"):     # one slot per 16 work items, plus one per hub
+        items = info[f"n_{side}_chunks"] + info[f"n_{side}_medium"] + -(-info[f"n_{side}_light"] // 2)
+        slots += -(-items // 16) + info[f"n_{side}_hub"]
     r64 = -(-slots // 32) + -(-slots // 1024)
-    assert need.value == al(64 * 8 * 8) + al(info["n_row_chunks"] * (4 * 256 + 16) * 4) + \
+    assert need.value == al(64 * 8 * 8) + al(info["n_row_chunks"] * (2 * 256 + 16) * 4) + \
         al(info["n_col_chunks"] * 2 * 256 * 4) + al(slots * 256 * 4) + al(r64 * 256 * 8)
 
     def call(ptrs=None, attn=FAKE, dattn=FAKE, ws=FAKE, wsb=1 << 30, plan=p):
