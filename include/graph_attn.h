@@ -274,7 +274,8 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t head
  * -0 equals +0). A row with no neighbours gives out = 0 and arg = -1. Optionally the
  * forward also writes slot[i,c] = the position within row i (k - indptr[i]) of the first
  * edge of that row from arg[i,c], as unsigned 16-bit values when no row has more than
- * 65536 edges, else 32-bit (graph_attn_reduce_slot_bytes); empty rows get all ones. The
+ * 65535 edges, else 32-bit (graph_attn_reduce_slot_bytes); an element without a winner
+ * (an empty row) gets all ones, which no position equals. The
  * backward reads slot (2 bytes per element per transpose edge) in place of arg (4), so a
  * training step should keep slot. NaN never wins a
  * comparison (a row whose candidates are all NaN reads as empty); inputs are meant to be
@@ -290,7 +291,7 @@ typedef enum { GA_REDUCE_MAX = 0, GA_REDUCE_MIN = 1 } ga_reduce;
 ga_status graph_attn_reduce_fwd_workspace_bytes(const ga_plan* plan, int32_t features,
                                                 size_t* bytes);
 
-/* Bytes per element of the plan's slot array: 2 when no row has more than 65536 edges,
+/* Bytes per element of the plan's slot array: 2 when no row has more than 65535 edges,
  * else 4. */
 ga_status graph_attn_reduce_slot_bytes(const ga_plan* plan, size_t* bytes);
 

@@ -209,8 +209,9 @@ struct RedArgs {
   void* dx;               // [N, F]
   float* ws_sum;          // hub column partial sums [n_col_chunks][F]
 };
-// Width of the slot array of a plan (2 bytes when no row has more than 65536 edges).
-inline int reduce_slot_bytes(int64_t max_in_degree) { return max_in_degree <= 65536 ? 2 : 4; }
+// Width of the slot array of a plan: 2 bytes when no row has more than 65535 edges, so
+// that every position (at most 65534) differs from the all-ones "no winner" slot.
+inline int reduce_slot_bytes(int64_t max_in_degree) { return max_in_degree <= 65535 ? 2 : 4; }
 bool reduce_supported(ga_dtype dt, int G);
 int launch_reduce(ga_dtype dt, bool backward, int op, int G, const RedArgs& a, void* stream,
                   TimerHook hook);

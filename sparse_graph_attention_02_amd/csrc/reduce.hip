@@ -10,7 +10,7 @@
 //   arg[i, c] = the source id attaining it; equal values go to the smallest id, so the
 //               result does not depend on neighbour order or on how a row is split.
 //   slot[i, c] (optional) = the position within row i of the first edge from that id,
-//               16-bit when every row has at most 65536 edges, else 32-bit.
+//               16-bit when every row has at most 65535 edges, else 32-bit.
 //   Empty rows: out = 0, arg = -1 (slot all ones).
 //
 // Forward (one launch over every row, the plan's row bins, like the attention forward):

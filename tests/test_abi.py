@@ -397,13 +397,14 @@ def test_reduce_argument_checks_before_any_hip_call():
     assert _rws(q, "graph_attn_reduce_bwd_workspace_bytes", 256) == 0
     assert _rfwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY
     assert _rbwd(q, ws=0, wsb=0) == capi.GA_ERR_NOT_READY
-    # slot width: 2 bytes unless some row has more than 65536 edges
+    # slot width: 2 bytes unless some row has more than 65535 edges (positions up to 65534,
+    # so none equals the all-ones slot of an element without a winner)
     b = c_size_t()
     capi.graph_attn_reduce_slot_bytes(p.handle, byref(b))
     assert b.value == 2
-    big = Plan(*gg.csr_from_edges(3, np.zeros(65537, np.int64), np.full(65537, 1)))
+    big = Plan(*gg.csr_from_edges(3, np.zeros(65536, np.int64), np.full(65536, 1)))
     capi.graph_attn_reduce_slot_bytes(big.handle, byref(b))
     assert b.value == 4
-    ok = Plan(*gg.csr_from_edges(3, np.zeros(65536, np.int64), np.full(65536, 1)))
+    ok = Plan(*gg.csr_from_edges(3, np.zeros(65535, np.int64), np.full(65535, 1)))
     capi.graph_attn_reduce_slot_bytes(ok.handle, byref(b))
     assert b.value == 2

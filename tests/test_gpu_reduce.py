@@ -248,8 +248,8 @@ def test_full_chunglu1m_sampled():
     assert np.all(np.abs(tot - dref) <= 2 ** -8 * scale)
 
 
-def test_wide_slots_for_rows_beyond_65536_edges():
-    """A row with more than 65536 edges makes the slots 32-bit; forward and backward in
+def test_wide_slots_for_rows_beyond_65535_edges():
+    """A row with more than 65535 edges makes the slots 32-bit; forward and backward in
     both match modes, with parallel edges in the long row."""
     rng = np.random.default_rng(21)
     n = 4000
@@ -262,6 +262,42 @@ def test_wide_slots_for_rows_beyond_65536_edges():
         plan, out, arg_slot, ra = fwd_exact("wide slots", ip, ix, x, "bf16", op)
         assert reduce_slot_dtype(plan) == torch.int32 and arg_slot[1].dtype == torch.int32
         bwd_parity("wide slots", plan, ip, ix, arg_slot, ra, dout, "bf16")
+
+
+def test_no_winner_slot_never_matches_a_position():
+    """A row of exactly 65536 edges has positions up to 65535 = 0xFFFF, the 16-bit form of
+    the all-ones slot of an element without a winner, so such a plan takes 32-bit slots.
+    Here one feature column is NaN on every node: that element has no winner in any row,
+    so its dx must stay exactly zero (with 16-bit slots the row's last edge would match);
+    the other columns follow the oracle, run with that column set to zero."""
+    rng = np.random.default_rng(23)
+    n = 3000
+    rs, rd = rng.integers(0, n, 9_000), rng.integers(0, n, 9_000)
+    keep = (rd != 7) & (rs != rd)                # row 7 gets exactly the 65536 long-row edges
+    src = np.concatenate([rng.integers(0, n, 65_536), rs[keep]])
+    dst = np.concatenate([np.full(65_536, 7), rd[keep]])
+    ip, ix = gg.csr_from_edges(n, src, dst)
+    assert ip[8] - ip[7] == 65_536
+    x = gg.f32_to_bf16_bits(rng.standard_normal((n, 32)).astype(np.float32))
+    dout = gg.normal_features(rng, (n, 32), "bf16")
+    c0 = 5
+    xn = x.copy()
+    xn[:, c0] = gg.f32_to_bf16_bits(np.full(n, np.nan, np.float32))
+    x0 = x.copy()
+    x0[:, c0] = 0
+    say("no-winner slots, long row", ip[8] - ip[7], "E", ix.size)
+    plan = Plan(ip, ix).upload()
+    assert reduce_slot_dtype(plan) == torch.int32
+    out, arg, slot = reduce_fwd(plan, dev(xn), op="max")
+    dx = reduce_bwd(plan, None, dev(dout), slot=slot)
+    torch.cuda.synchronize()
+    assert torch.all(arg[:, c0] == -1) and torch.all(slot[:, c0] == -1)
+    assert torch.all(dx[:, c0].float() == 0)
+    _, ra = R.reduce_rows(ip, ix, x0, np.arange(n), "max")
+    others = np.r_[0:c0, c0 + 1:32]
+    assert np.array_equal(arg[:, others].cpu().numpy(), ra[:, others])
+    rdx = R.reduce_backward(ra, dout, n)
+    check("no-winner slots dx", host64(dx[:, others]), rdx[:, others], "bf16")
 
 
 @pytest.mark.parametrize("dtype,F", [("bf16", 256), ("f32", 128), ("bf16", 64)])
