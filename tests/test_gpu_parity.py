@@ -522,6 +522,28 @@ def test_gatv2_forward_geometries(dtype, G, LH):
                    slope=0.2, light_max_deg=6, hub_min_deg_exclusive=24, hub_chunk=16)
 
 
+@pytest.mark.parametrize("dtype,H,d", [("bf16", 8, 32), ("f32", 4, 32), ("bf16", 2, 64)])
+def test_gatv2_forward_feature_slices(dtype, H, d):
+    """An explicit feature-slice count in the GATv2 forward: every element against the
+    oracle for each count, and the same bits again on a second call. (Counts differ in how
+    a row's edges are dealt to lane groups, so they differ from one another in rounding.)"""
+    rng = np.random.default_rng(H * 7 + d)
+    n = 1500
+    ip, ix = gg.random_multigraph(n, 15000, rng, hub_rows=(4, 9), hub_deg=700)
+    xd, xs = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    if dtype == "bf16":
+        xd, xs = gg.f32_to_bf16_bits(xd), gg.f32_to_bf16_bits(xs)
+    from sparse_graph_attention_02_amd import fwd_gatv2
+    kw = dict(light_max_deg=8, hub_min_deg_exclusive=64, hub_chunk=48)
+    for S in (1, 2, 4, 8):
+        plan, out, lse = gatv2_fwd_case(f"gatv2 slices {S} {dtype}", ip, ix, xd, xs, a, dtype,
+                                        feature_slices=S, **kw)
+        assert plan.info()["feature_slices"] == S
+        out2, lse2 = fwd_gatv2(plan, dev(xd), dev(xs), dev(a))
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
 def test_gatv2_forward_chunglu100k_every_row():
     w = gg.WORKLOADS["chunglu100k_gat_f32"]
     ip, ix = gg.make_graph(w)
