@@ -47,7 +47,7 @@ __all__ = [
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
     "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
     "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
-    "train_step_rows_gatv2",
+    "train_step_rows_gatv2", "forward_online_chunked",
 ]
 
 
@@ -115,6 +115,59 @@ def forward_rows(indptr, indices, a, b, v, rows, score="dot", scale=None, neg_sl
 def forward(indptr, indices, a, b, v, score="dot", scale=None, neg_slope=0.2):
     n = indptr.size - 1
     return forward_rows(indptr, indices, a, b, v, np.arange(n), score, scale, neg_slope)
+
+
+def _merge_states(x, y):
+    """Combine two running softmax states (m [H], l [H], acc [H, d]) over disjoint edge
+    sets: rescale both to the larger maximum and add. An empty state has m = -inf."""
+    (ma, la, aa), (mb, lb, ab) = x, y
+    m = np.maximum(ma, mb)
+    fa = np.where(np.isneginf(ma), 0.0, np.exp(ma - np.where(np.isneginf(m), 0.0, m)))
+    fb = np.where(np.isneginf(mb), 0.0, np.exp(mb - np.where(np.isneginf(m), 0.0, m)))
+    return m, la * fa + lb * fb, aa * fa[:, None] + ab * fb[:, None]
+
+
+def forward_online_chunked(indptr, indices, a, b, v, rng, score="dot", scale=None,
+                           neg_slope=0.2, max_chunk=None):
+    """The streaming form of the same forward ("On Efficient Scaling of GNNs via IO-Aware
+    Layers Implementations", Technical Summary > Methodology, attention-based layers,
+    forward pass: online softmax keeping running statistics instead of edge-wise logits).
+    Each row's edges are cut at random boundaries into chunks (at most max_chunk edges,
+    default: random lengths up to the degree); each chunk streams its edges one by one
+    into a running state (m = max score so far, l = sum of exp(e - m), acc = sum of
+    exp(e - m) v), starting empty; the chunk states are then merged in ascending order and
+    out = acc / l, lse = m + ln l. Exactly the two-pass softmax up to rounding; test pin
+    only (the hub-chunk partials and their ordered merge compute this)."""
+    n = indptr.size - 1
+    H, d = v.shape[1], v.shape[2]
+    out = np.zeros((n, H, d))
+    lse = np.full((n, H), -np.inf)
+    vf = widen(v)
+    empty = lambda: (np.full(H, -np.inf), np.zeros(H), np.zeros((H, d)))
+    for i in range(n):
+        J = _neighbours(indptr, indices, i)
+        if J.size == 0:
+            continue
+        e = row_scores(i, indptr, indices, a, b, score, scale, neg_slope)   # [deg, H]
+        cuts, pos = [0], 0
+        while pos < J.size:
+            pos += int(rng.integers(1, (max_chunk or J.size) + 1))
+            cuts.append(min(pos, J.size))
+        total = empty()
+        for c0, c1 in zip(cuts[:-1], cuts[1:]):
+            m, l, acc = empty()
+            for k in range(c0, c1):                     # one edge at a time
+                m_new = np.maximum(m, e[k])
+                f = np.exp(m - m_new)                   # 0 while the state is empty
+                w = np.exp(e[k] - m_new)
+                l = l * f + w
+                acc = acc * f[:, None] + w[:, None] * vf[J[k]]
+                m = m_new
+            total = _merge_states(total, (m, l, acc))
+        m, l, acc = total
+        out[i] = acc / l[:, None]
+        lse[i] = m + np.log(l)
+    return out, lse
 
 
 def _row_backward(i, indptr, indices, q, k, v, dout, scale):

@@ -278,3 +278,42 @@ def test_bf16_inputs_are_widened_exactly():
     # bf16 keeps 8 significant bits: exact for the first three, RNE for the last
     assert list(w[:3]) == [1.0, -2.5, 3.140625]
     assert abs(w[3] - 1e-3) <= 2 ** -9 * 1e-3 and w.dtype == np.float64
+
+
+@pytest.mark.parametrize("max_chunk", [None, 1, 3, 1000])
+@pytest.mark.parametrize("score", ["dot", "gat"])
+def test_online_chunked_equals_two_pass(score, max_chunk):
+    """The streaming form (running max, sum and accumulator per edge; rows cut into chunks
+    at random boundaries whose states merge in order) equals the two-pass definition to
+    1e-13: one chunk per row (max_chunk 1000: pure online), one edge per chunk, and mixes."""
+    rng = np.random.default_rng(5 if score == "dot" else 6)
+    n, H, d = 150, 3, 8
+    ip, ix = gg.random_multigraph(n, 1800, rng, hub_rows=(4, 40), hub_deg=300)
+    if score == "dot":
+        a, b = (rng.standard_normal((n, H, d)) * 1.5 for _ in range(2))
+    else:
+        a, b = (rng.standard_normal((n, H)) * 2 for _ in range(2))
+    v = rng.standard_normal((n, H, d))
+    ro, rl = A.forward(ip, ix, a, b, v, score)
+    co, cl = A.forward_online_chunked(ip, ix, a, b, v, np.random.default_rng(9), score,
+                                      max_chunk=max_chunk)
+    assert np.array_equal(np.isneginf(cl), np.isneginf(rl))
+    fin = ~np.isneginf(rl)
+    assert np.allclose(cl[fin], rl[fin], rtol=1e-13, atol=1e-13)
+    assert np.allclose(co, ro, rtol=1e-13, atol=1e-13)
+
+
+def test_online_chunked_keeps_empty_rows_and_large_scores():
+    """Rows without neighbours stay (0, -inf); scores in the hundreds (exp would overflow
+    without the running max) still match."""
+    ip = np.array([0, 0, 3, 3, 5])
+    ix = np.array([1, 2, 3, 0, 0])
+    rng = np.random.default_rng(2)
+    q, k = rng.standard_normal((4, 2, 4)) * 12, rng.standard_normal((4, 2, 4)) * 12
+    v = rng.standard_normal((4, 2, 4))
+    ro, rl = A.forward(ip, ix, q, k, v, "dot", scale=1.0)
+    assert np.abs(rl[np.isfinite(rl)]).max() > 100
+    co, cl = A.forward_online_chunked(ip, ix, q, k, v, rng, "dot", scale=1.0, max_chunk=1)
+    assert np.all(co[[0, 2]] == 0) and np.all(np.isneginf(cl[[0, 2]]))
+    assert np.allclose(co, ro, rtol=1e-13, atol=1e-13) and np.allclose(cl[[1, 3]], rl[[1, 3]],
+                                                                       rtol=1e-13)
