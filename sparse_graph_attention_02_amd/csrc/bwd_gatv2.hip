@@ -396,7 +396,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
   using K = BwdV2<T, G, LH, U>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
   const int lane = threadIdx.x & (kWave - 1);
-  const int slot = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+  const int wave = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.cols;
   const int64_t n_items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
@@ -410,9 +410,9 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
   K::load_attn(a, r, av);
 #pragma unroll
   for (int c = 0; c < VEC; ++c) da[c * kWave] = 0;
-  // waves of the last block past the last slot take no item but still join the block sum
-  for (int k = 0; k < kColItemsPerWave && slot < W; ++k) {
-    const int64_t item = int64_t(k) * W + ((k & 1) ? W - 1 - slot : slot);
+  // waves of the last block past wave W-1 take no item but still join the block sum
+  for (int k = 0; k < kColItemsPerWave && wave < W; ++k) {
+    const int64_t item = int64_t(k) * W + ((k & 1) ? W - 1 - wave : wave);
     if (item >= n_items) continue;
     float xs[VEC];
     typename K::acc_t C1[VEC], C2[VEC];

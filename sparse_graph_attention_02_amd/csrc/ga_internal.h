@@ -174,7 +174,7 @@ int launch_bwd_gat(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* strea
 // GATv2: q/k/dq/dk carry xd/xs/dxd/dxs ([N, H, d]); attn/dattn/ws_da/ws_da64 set.
 int launch_bwd_gatv2(ga_dtype dt, const Geometry& g, const BwdArgs& a, void* stream,
                      TimerHook hook);
-// dattn partial slots of the GATv2 backward (row waves, hub rows, column waves, hub
+// dattn partial slots of the GATv2 backward (row waves, hub rows, column blocks, hub
 // columns), the floats of one row-chunk partial, and the fp64 rows of the dattn reduction
 // buffers (total, and the first buffer's share).
 int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g);
