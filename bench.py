@@ -260,7 +260,7 @@ def main():
                          "before the run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the fused layer is measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
 
