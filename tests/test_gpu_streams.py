@@ -58,3 +58,29 @@ def test_two_streams_share_a_plan():
     for r, res in enumerate(results):
         for a, b in zip(serial[r % 2], res):
             assert torch.equal(a, b), f"concurrent call {r} differs from the serial result"
+
+
+def test_upload_again_retargets_the_plan():
+    """A second upload moves the plan to a new device buffer. The first buffer is then
+    zeroed (a zeroed plan reads as a graph whose rows and columns are all empty, so a
+    plan still pointing there would give different results without reading out of
+    bounds): fwd and bwd must give what they gave before, bit for bit."""
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    n = 5_000
+    ip, ix = gg.make_graph(w, n=n)
+    rng = np.random.default_rng(12)
+    print("[case] plan uploaded twice: N", n, "E", ix.size, flush=True)
+    q, k, v, do = (dev(gg.normal_features(rng, (n, 8, 32), "bf16")) for _ in range(4))
+    plan = ga.Plan(ip, ix, hub_min_deg_exclusive=64, hub_chunk=32).upload()
+    out1, lse1 = ga.fwd(plan, q, k, v)
+    g1 = ga.bwd(plan, q, k, v, do, lse1)
+    torch.cuda.synchronize()
+    first = plan.device_buffer
+    plan.upload()
+    assert plan.device_buffer.data_ptr() != first.data_ptr()
+    first.zero_()
+    out2, lse2 = ga.fwd(plan, q, k, v)
+    g2 = ga.bwd(plan, q, k, v, do, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
