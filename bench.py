@@ -52,6 +52,11 @@ def algorithmic_bytes(kernel, N, E, H, d, b, score="dot"):
         return csr + 2 * E * F * b + 2 * N * F * b + 4 * N * H + N * F * b + 8 * N * H
     if kernel == "bwd_dkdv_main":  # Q_i + dOut_i + record_i per edge; K, V; dK, dV
         return csr + E * (2 * F * b + 8 * H) + 2 * N * F * b + 2 * N * F * b
+    if kernel == "bwd_gat_rows_main":    # t_j + V_j per edge; s, dOut, lse; ds, record
+        return csr + E * (4 * H + F * b) + 4 * N * H + N * F * b + 4 * N * H + 4 * N * H \
+            + 8 * N * H
+    if kernel == "bwd_gat_cols_main":    # s_i + dOut_i + record_i per edge; t, V; dt, dV
+        return csr + E * (4 * H + F * b + 8 * H) + 4 * N * H + N * F * b + 4 * N * H + N * F * b
     if kernel == "bwd_gatv2_rows_main":  # xs_j per edge; xd, dOut, lse; dxd, record; attn
         return csr + E * F * b + 2 * N * F * b + 4 * N * H + N * F * b + 8 * N * H + 4 * F
     if kernel == "bwd_gatv2_cols_main":  # xd_i + dOut_i + record_i per edge; xs; dxs; attn
@@ -77,6 +82,9 @@ def step_bytes(N, E, H, d, b, backward, score="dot"):
     if backward and score == "gatv2":
         tot += algorithmic_bytes("bwd_gatv2_rows_main", N, E, H, d, b, score)
         tot += algorithmic_bytes("bwd_gatv2_cols_main", N, E, H, d, b, score)
+    elif backward and score == "gat":
+        tot += algorithmic_bytes("bwd_gat_rows_main", N, E, H, d, b, score)
+        tot += algorithmic_bytes("bwd_gat_cols_main", N, E, H, d, b, score)
     elif backward:
         tot += algorithmic_bytes("bwd_dq_main", N, E, H, d, b, score)
         tot += algorithmic_bytes("bwd_dkdv_main", N, E, H, d, b, score)
@@ -111,6 +119,9 @@ def _cpu_worker(args):
                     R.train_step_rows(g["ip"], g["ix"], g["q"], g["dout"], batch, g["score"])
                 else:
                     R.reduce_rows(g["ip"], g["ix"], g["q"], batch, g["score"])
+            elif backward and g["score"] == "gat":
+                A.train_step_rows_gat(g["ip"], g["ix"], g["q"], g["k"], g["v"], g["dout"],
+                                      batch, g["scale"], g["slope"])
             elif backward:
                 A.train_step_rows(g["ip"], g["ix"], g["q"], g["k"], g["v"], g["dout"], batch,
                                   g["scale"])
@@ -337,7 +348,8 @@ def main():
         bws = torch.empty(ga.bwd_gatv2_workspace_bytes(plan, vt.dtype, H, d), dtype=torch.uint8,
                           device="cuda")
     elif w.backward:
-        dq, dk, dv = (torch.empty_like(tens[0]) for _ in range(3))
+        # dot: dq, dk, dv like q, k, v; GAT-style: ds, dt like s, t and dv like v
+        dq, dk, dv = (torch.empty_like(x) for x in tens)
         bws = torch.empty(plan.bwd_workspace_bytes(H, d), dtype=torch.uint8, device="cuda")
 
     def step(backward=w.backward):
@@ -354,7 +366,8 @@ def main():
             return
         ga.fwd(plan, *tens, score=w.score, scale=scale, out=out, lse=lse, workspace=fws)
         if backward:
-            ga.bwd(plan, *tens, tdo, lse, scale=scale, dq=dq, dk=dk, dv=dv, workspace=bws)
+            ga.bwd(plan, *tens, tdo, lse, score=w.score, scale=scale, dq=dq, dk=dk, dv=dv,
+                   workspace=bws)
 
     for _ in range(args.warmup):
         step()

@@ -233,6 +233,8 @@ WORKLOADS = {
                  True, {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
         Workload(7, "chunglu1m_max_train_bf16", "chunglu", 1_000_000, 8, 32, "bf16", "max",
                  True, {"avg_deg": 50, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=3),
+        Workload(8, "chunglu100k_gat_train_f32", "chunglu", 100_000, 4, 64, "f32", "gat", True,
+                 {"avg_deg": 20, "gamma": 2.1, "max_over_mean": 500.0}, graph_wid=2),
     ]
 }
 

@@ -47,7 +47,7 @@ __all__ = [
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
     "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
     "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
-    "train_step_rows_gatv2", "forward_online_chunked",
+    "train_step_rows_gatv2", "forward_online_chunked", "train_step_rows_gat",
 ]
 
 
@@ -332,6 +332,42 @@ def backward_gat(indptr, indices, s, t, v, dout, scale=1.0, neg_slope=0.2):
         np.add.at(dt, J, sc * dS * g)
         np.add.at(dv, J, alpha[:, :, None] * widen(dout[i])[None])
     return ds, dt, dv
+
+
+def train_step_rows_gat(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slope=0.2):
+    """Forward and backward of the listed rows of the GAT-style layer, each row's work done
+    once (the GAT counterpart of ``train_step_rows``).
+
+    Returns (out [R,H,d], lse [R,H], ds [R,H], cols, dt_part [C,H], dv_part [C,H,d]):
+    ``cols`` are the source columns the rows touch (ascending), and dt_part and dv_part
+    hold those rows' contributions. With rows = all rows this is exactly ``forward``
+    plus ``backward_gat``."""
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = v.shape[1], v.shape[2]
+    segs = [indices[int(indptr[i]):int(indptr[i + 1])] for i in rows]
+    cols = np.unique(np.concatenate(segs)) if segs else np.zeros(0, np.int64)
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    ds = np.zeros((rows.size, H))
+    dt = np.zeros((cols.size, H))
+    dv = np.zeros((cols.size, H, d))
+    for r, i in enumerate(rows):
+        J = segs[r]
+        if J.size == 0:
+            continue
+        e = row_scores(i, indptr, indices, s, t, "gat", scale, neg_slope)
+        alpha, lse[r] = row_softmax(e)
+        vj = widen(v[J])
+        out[r] = np.einsum("kh,khc->hc", alpha, vj)
+        dp = np.einsum("hc,khc->kh", widen(dout[i]), vj)
+        D = (alpha * dp).sum(axis=0)
+        dS = alpha * (dp - D[None, :])
+        g = leaky_relu_grad(widen(s[i])[None, :] + widen(t[J]), float(neg_slope))
+        ds[r] = scale * (dS * g).sum(axis=0)
+        slot = np.searchsorted(cols, J)
+        np.add.at(dt, slot, scale * dS * g)
+        np.add.at(dv, slot, alpha[:, :, None] * widen(dout[i])[None])
+    return out, lse, ds, cols, dt, dv
 
 
 def grad_s_rows(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slope=0.2):

@@ -31,6 +31,10 @@ def _hand(kernel, H, d, b):
         "fwd_main": (4 + 2 * row, 4 + row + row + 4 * H, 4),                    # K,V | Q,out,lse
         "bwd_dq_main": (4 + 2 * row, 4 + 2 * row + 4 * H + row + 8 * H, 4),     # K,V | Q,dO,lse,dQ,rec
         "bwd_dkdv_main": (4 + 2 * row + 8 * H, 4 + 2 * row + 2 * row, 4),       # Q,dO,rec | K,V,dK,dV
+        "bwd_gat_rows_main": (4 + 4 * H + row, 4 + 4 * H + row + 4 * H + 4 * H + 8 * H, 4),
+        # t_j, V_j | s, dO, lse, ds, record
+        "bwd_gat_cols_main": (4 + 4 * H + row + 8 * H, 4 + 4 * H + row + 4 * H + row, 4),
+        # s_i, dO_i, record_i | t, V, dt, dV
         "bwd_gatv2_rows_main": (4 + row, 4 + 2 * row + 4 * H + row + 8 * H, 4 + 4 * F),
         "bwd_gatv2_cols_main": (4 + 2 * row + 8 * H, 4 + row + row, 4 + 4 * F),
         "reduce_fwd_main": (4 + row, 4 + row + 4 * F + 2 * F, 4),             # x | out,arg,slot
@@ -40,12 +44,14 @@ def _hand(kernel, H, d, b):
 
 
 @pytest.mark.parametrize("kernel", ["fwd_main", "bwd_dq_main", "bwd_dkdv_main",
+                                    "bwd_gat_rows_main", "bwd_gat_cols_main",
                                     "bwd_gatv2_rows_main", "bwd_gatv2_cols_main",
                                     "reduce_fwd_main", "reduce_bwd_main"])
 @pytest.mark.parametrize("N,E,H,d,b", [(1_000_000, 50_997_829, 8, 32, 2),
                                        (2_097_152, 65_008_926, 1, 128, 2), (10, 0, 4, 16, 4)])
 def test_byte_model_per_edge_and_node(kernel, N, E, H, d, b):
-    score = "gatv2" if "gatv2" in kernel else ("max" if kernel.startswith("reduce") else "dot")
+    score = ("gatv2" if "gatv2" in kernel else "gat" if "_gat_" in kernel
+             else "max" if kernel.startswith("reduce") else "dot")
     pe, pn, c = _hand(kernel, H, d, b)
     assert bench.algorithmic_bytes(kernel, N, E, H, d, b, score) == pe * E + pn * N + c
 
@@ -66,6 +72,9 @@ def test_byte_model_figures_of_the_configurations():
     N, E = 1000, 5000
     assert bench.step_bytes(N, E, 8, 32, 2, True) == sum(
         f(k, N, E, 8, 32, 2) for k in ("fwd_main", "bwd_dq_main", "bwd_dkdv_main"))
+    assert bench.step_bytes(N, E, 4, 64, 4, True, "gat") == sum(
+        f(k, N, E, 4, 64, 4, "gat") for k in ("fwd_main", "bwd_gat_rows_main",
+                                              "bwd_gat_cols_main"))
 
 
 @pytest.mark.parametrize("order", ["random", "out-degree", "rcm"])

@@ -478,11 +478,13 @@ def test_gat_backward_deterministic():
 
 @pytest.mark.slow
 def test_full_chunglu100k_gat_backward_sampled():
-    w = gg.WORKLOADS["chunglu100k_gat_f32"]
+    """The GAT training step as the bench runs it (same graph, features, dOut and default
+    plan): ds on sampled rows, dt and dV on sampled columns including the top hubs."""
+    w = gg.WORKLOADS["chunglu100k_gat_train_f32"]
     ip, ix = gg.make_graph(w)
     s, t, v = gg.make_features(w)
+    do = gg.make_dout(w)
     rng = np.random.default_rng(8)
-    do = rng.standard_normal(v.shape).astype(np.float32)
     rows = _sample_rows(ip, rng, k=500)
     odeg = np.bincount(ix, minlength=w.n)
     cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3], rng.choice(w.n, 200, replace=False)])

@@ -232,3 +232,35 @@ def test_gat_backward_sampled_forms_agree():
     gt, gv = A.grad_tv_cols(ip, ix, s, t, v, do, sel, 1.0, 0.2)
     np.testing.assert_allclose(gt, dt[sel], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(gv, dv[sel], rtol=1e-12, atol=1e-13)
+
+
+def test_train_step_rows_gat_is_the_plain_step():
+    """The GAT per-row training step over all rows is forward + backward_gat; over a subset
+    it gives those rows' outputs and ds, and two disjoint subsets' dt / dv shares add up to
+    the whole."""
+    rng = np.random.default_rng(17)
+    n, H, d = 40, 3, 5
+    ip, ix = gg.random_multigraph(n, 300, rng, hub_rows=(3,), hub_deg=60)
+    s_, t_ = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    v, do = rng.standard_normal((n, H, d)), rng.standard_normal((n, H, d))
+    out, lse = A.forward(ip, ix, s_, t_, v, "gat", 0.7, 0.15)
+    ds, dt, dv = A.backward_gat(ip, ix, s_, t_, v, do, 0.7, 0.15)
+    o2, l2, ds2, cols, dt2, dv2 = A.train_step_rows_gat(ip, ix, s_, t_, v, do, np.arange(n),
+                                                        0.7, 0.15)
+    np.testing.assert_allclose(o2, out, atol=1e-13)
+    np.testing.assert_allclose(l2, lse, atol=1e-13)
+    np.testing.assert_allclose(ds2, ds, atol=1e-12)
+    full_t, full_v = np.zeros_like(dt), np.zeros_like(dv)
+    full_t[cols], full_v[cols] = dt2, dv2
+    np.testing.assert_allclose(full_t, dt, atol=1e-12)
+    np.testing.assert_allclose(full_v, dv, atol=1e-12)
+    a, b = np.arange(0, n, 2), np.arange(1, n, 2)
+    acc_t, acc_v = np.zeros_like(dt), np.zeros_like(dv)
+    for rows in (a, b):
+        o3, _, ds3, c3, dt3, dv3 = A.train_step_rows_gat(ip, ix, s_, t_, v, do, rows, 0.7, 0.15)
+        np.testing.assert_allclose(o3, out[rows], atol=1e-13)
+        np.testing.assert_allclose(ds3, ds[rows], atol=1e-12)
+        np.add.at(acc_t, c3, dt3)
+        np.add.at(acc_v, c3, dv3)
+    np.testing.assert_allclose(acc_t, dt, atol=1e-12)
+    np.testing.assert_allclose(acc_v, dv, atol=1e-12)
