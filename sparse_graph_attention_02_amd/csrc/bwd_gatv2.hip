@@ -44,7 +44,13 @@ constexpr int kItemsPerWave = 16;  // row-pass work items per wavefront (bounds 
 #endif
 constexpr int kColItemsPerWave = GA_GV2_COL_ITEMS;
 constexpr int kReduceFan = 32;     // rows summed per block in each da reduction stage
-constexpr int kRowsUnroll = 3;     // edges in flight per lane group in the row pass (4 waves/SIMD)
+// Edges in flight per lane group in the row pass, as many as keep the kernel within 128
+// VGPRs (4 waves per SIMD) without spills: 5 for rows of at most 32 lanes with heads of at
+// most 4 lanes, 3 for wider rows or heads.
+template <int G, int LH>
+constexpr int rows_unroll() {
+  return (G <= 32 && LH <= 4) ? 5 : 3;
+}
 
 template <typename T, int G, int LH, int U>
 struct BwdV2 : RowIO<T, G, LH> {
@@ -530,7 +536,7 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   };
   if (row_waves > 0) {
     if (hook) hook("bwd_gatv2_rows_main", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, kRowsUnroll>), blocks(row_waves),
+    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, rows_unroll<G, LH>()>), blocks(row_waves),
                        dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_rows_main"))) return e;
   }
