@@ -515,7 +515,10 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
 }
 
 constexpr int kUnrollRed = 8;
-constexpr int kUnrollRedBwd = 4;
+#ifndef GA_UNROLL_RED_BWD
+#define GA_UNROLL_RED_BWD 4
+#endif
+constexpr int kUnrollRedBwd = GA_UNROLL_RED_BWD;
 
 template <typename Kern>
 int go(const char* name, Kern kernel, int64_t blocks, const RedArgs& a, void* stream,
