@@ -352,22 +352,29 @@ def main():
         dq, dk, dv = (torch.empty_like(x) for x in tens)
         bws = torch.empty(plan.bwd_workspace_bytes(H, d), dtype=torch.uint8, device="cuda")
 
-    def step(backward=w.backward):
+    def forward():
         if red:
             ga.reduce_fwd(plan, tens[0], op=w.score, out=out, arg=arg, slot=slot, workspace=fws)
-            if backward:
-                ga.reduce_bwd(plan, None, tdo, slot=slot, dx=dq, workspace=bws)
-            return
-        if w.score == "gatv2":
+        elif w.score == "gatv2":
             ga.fwd_gatv2(plan, *tens, scale=scale, out=out, lse=lse, workspace=fws)
-            if backward:
-                ga.bwd_gatv2(plan, *tens, tdo, lse, scale=scale, dxd=dq, dxs=dk, dattn=dv,
-                             workspace=bws)
-            return
-        ga.fwd(plan, *tens, score=w.score, scale=scale, out=out, lse=lse, workspace=fws)
-        if backward:
+        else:
+            ga.fwd(plan, *tens, score=w.score, scale=scale, out=out, lse=lse, workspace=fws)
+
+    def backward():
+        """The backward alone, from what the last forward saved (lse, or the slots)."""
+        if red:
+            ga.reduce_bwd(plan, None, tdo, slot=slot, dx=dq, workspace=bws)
+        elif w.score == "gatv2":
+            ga.bwd_gatv2(plan, *tens, tdo, lse, scale=scale, dxd=dq, dxs=dk, dattn=dv,
+                         workspace=bws)
+        else:
             ga.bwd(plan, *tens, tdo, lse, score=w.score, scale=scale, dq=dq, dk=dk, dv=dv,
                    workspace=bws)
+
+    def step(with_backward=w.backward):
+        forward()
+        if with_backward:
+            backward()
 
     for _ in range(args.warmup):
         step()
@@ -406,6 +413,9 @@ def main():
 
     dist_step = per_step(step, args.steps)
     dist_fwd = per_step(lambda: step(False), args.steps)
+    if w.backward:           # the last forward's lse / slots are in place
+        ms_bwd, _ = timed(backward, args.steps)
+        dist_bwd = per_step(backward, args.steps)
     # peak memory of one step above what is already allocated (inputs, outputs, plan and
     # workspaces are allocated before the timed region; a step allocates nothing)
     torch.cuda.synchronize()
@@ -473,10 +483,18 @@ def main():
         "cpu_baseline": cpu,
         "step_GBps_algorithmic": tot_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": tot_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step_frac_of_copy_probe": tot_bytes / (ms_step * 1e-3) / 1e9 / copy_gbps,
         "fwd": {"ms": ms_fwd, "ms_distribution": dist_fwd, "edges_per_s": E / (ms_fwd * 1e-3),
                 "GBps_algorithmic": fwd_bytes / (ms_fwd * 1e-3) / 1e9,
                 "frac_of_peak": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "frac_of_copy_probe": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / copy_gbps,
                 "fwd_main_ms": fwd_main_ms},
+        "bwd": ({"ms": ms_bwd, "ms_distribution": dist_bwd, "edges_per_s": E / (ms_bwd * 1e-3),
+                 "GBps_algorithmic": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9,
+                 "frac_of_peak": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "frac_of_copy_probe": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9 / copy_gbps,
+                 "note": "the backward alone, timed after a forward"}
+                if w.backward else None),
         "gather_floor": {
             "ms": ms_gather, "GBps_algorithmic": gather_bytes / (ms_gather * 1e-3) / 1e9,
             "fwd_main_frac_of_floor": ms_gather / fwd_main_ms,
