@@ -45,7 +45,8 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
-__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention", "reduce_fwd",
+__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention",
+           "graph_attention_gatv2", "reduce_fwd",
            "reduce_bwd", "reduce_slot_dtype", "graph_reduce", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
@@ -333,32 +334,61 @@ def _autograd_fn():
 
     class _GraphAttention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, plan, scale):
-            out, lse = fwd(plan, q.contiguous(), k.contiguous(), v.contiguous(), scale=scale)
+        def forward(ctx, q, k, v, plan, scale, score, neg_slope):
+            out, lse = fwd(plan, q.contiguous(), k.contiguous(), v.contiguous(), score=score,
+                           scale=scale, neg_slope=neg_slope)
             ctx.save_for_backward(q, k, v, lse)
-            ctx.plan, ctx.scale = plan, scale
+            ctx.plan, ctx.scale, ctx.score, ctx.neg_slope = plan, scale, score, neg_slope
             return out
 
         @staticmethod
         def backward(ctx, g):
             q, k, v, lse = ctx.saved_tensors
             dq, dk, dv = bwd(ctx.plan, q.contiguous(), k.contiguous(), v.contiguous(),
-                             g.contiguous(), lse, scale=ctx.scale)
-            return dq, dk, dv, None, None
+                             g.contiguous(), lse, score=ctx.score, scale=ctx.scale,
+                             neg_slope=ctx.neg_slope)
+            return dq, dk, dv, None, None, None, None
 
-    return _GraphAttention
+    class _GraphAttentionV2(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, xd, xs, attn, plan, scale, neg_slope):
+            out, lse = fwd_gatv2(plan, xd.contiguous(), xs.contiguous(), attn.contiguous(),
+                                 scale=scale, neg_slope=neg_slope)
+            ctx.save_for_backward(xd, xs, attn, lse)
+            ctx.plan, ctx.scale, ctx.neg_slope = plan, scale, neg_slope
+            return out
+
+        @staticmethod
+        def backward(ctx, g):
+            xd, xs, attn, lse = ctx.saved_tensors
+            dxd, dxs, dattn = bwd_gatv2(ctx.plan, xd.contiguous(), xs.contiguous(),
+                                        attn.contiguous(), g.contiguous(), lse, scale=ctx.scale,
+                                        neg_slope=ctx.neg_slope)
+            return dxd, dxs, dattn, None, None, None
+
+    return _GraphAttention, _GraphAttentionV2
 
 
 _FN = None
 
 
-def graph_attention(plan: Plan, q, k, v, scale=None):
-    """Dot-score graph attention as a differentiable torch op (forward saves lse; backward
-    recomputes the weights)."""
+def graph_attention(plan: Plan, q, k, v, scale=None, *, score="dot", neg_slope=0.2):
+    """Graph attention as a differentiable torch op (forward saves lse; backward recomputes
+    the weights). score "dot": q, k, v [N,H,d]; "gat": q = s, k = t (fp32 [N,H]) and
+    v [N,H,d], with the LeakyReLU slope neg_slope (scale defaults to 1 there)."""
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
-    return _FN.apply(q, k, v, plan, scale)
+    return _FN[0].apply(q, k, v, plan, scale, score, neg_slope)
+
+
+def graph_attention_gatv2(plan: Plan, xd, xs, attn, scale=1.0, *, neg_slope=0.2):
+    """GATv2 attention as a differentiable torch op: xd, xs [N,H,d] (destination and source
+    projections; xs is also the message), attn fp32 [H,d]; returns out [N,H,d]."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    return _FN[1].apply(xd, xs, attn, plan, scale, neg_slope)
 
 
 def _features_view(t, name, device=None):
