@@ -7,32 +7,56 @@
 // medium / hub) and hub chunks merge without atomics. The transpose follows the same
 // section's SpMM paragraph (transposed adjacency precomputed once for the backward).
 //
-// Everything is O(N + E) or O(N log N), runs once per graph, and is bit-exact by
-// construction (no floating point, no parallel reordering).
+// Everything is O(N + E) (or O(N log N) when one degree dwarfs N), runs once per graph, and
+// is bit-exact by construction: no floating point, and the threaded transpose writes every
+// entry where the sequential counting sort would.
 #include <algorithm>
 #include <new>
+#include <thread>
 
 #include "ga_internal.h"
 
 namespace ga {
 namespace {
 
+// Ids 0..n-1 ordered by degree descending, ties by ascending id: a stable counting sort on
+// the degree (a comparison sort when the largest degree is far beyond n).
+void order_by_degree(const std::vector<int32_t>& ptr, std::vector<int32_t>* order,
+                     int64_t* max_deg) {
+  const int64_t n = static_cast<int64_t>(ptr.size()) - 1;
+  order->resize(static_cast<size_t>(n));
+  int64_t mx = 0;
+  for (int64_t i = 0; i < n; ++i) mx = std::max<int64_t>(mx, ptr[i + 1] - ptr[i]);
+  *max_deg = mx;
+  if (mx <= 4 * n + 1024) {
+    std::vector<int64_t> start(static_cast<size_t>(mx) + 2, 0);  // start[d]: first slot of degree d
+    for (int64_t i = 0; i < n; ++i) start[ptr[i + 1] - ptr[i]]++;
+    int64_t at = 0;
+    for (int64_t d = mx; d >= 0; --d) {
+      const int64_t c = start[d];
+      start[d] = at;
+      at += c;
+    }
+    for (int64_t i = 0; i < n; ++i) (*order)[start[ptr[i + 1] - ptr[i]]++] = static_cast<int32_t>(i);
+    return;
+  }
+  for (int64_t i = 0; i < n; ++i) (*order)[i] = static_cast<int32_t>(i);
+  std::stable_sort(order->begin(), order->end(), [&](int32_t x, int32_t y) {
+    return ptr[x + 1] - ptr[x] > ptr[y + 1] - ptr[y];
+  });
+}
+
 // Rows of `ptr` binned by degree; each bin lists ids by degree descending, ties by id.
 void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins* b,
                    int64_t* max_deg) {
-  const int64_t n = static_cast<int64_t>(ptr.size()) - 1;
-  std::vector<int32_t> order(static_cast<size_t>(n));
-  for (int64_t i = 0; i < n; ++i) order[i] = static_cast<int32_t>(i);
+  std::vector<int32_t> order;
+  order_by_degree(ptr, &order, max_deg);
   auto deg = [&](int32_t i) { return ptr[i + 1] - ptr[i]; };
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t x, int32_t y) { return deg(x) > deg(y); });
   b->light.clear();
   b->medium.clear();
   b->hub.clear();
-  *max_deg = 0;
   for (int32_t i : order) {
     const int32_t d = deg(i);
-    if (d > *max_deg) *max_deg = d;
     if (d <= o.light_max_deg)
       b->light.push_back(i);
     else if (d <= o.hub_min_deg_exclusive)
@@ -53,6 +77,73 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins*
     }
     b->hub_chunk_ptr.push_back(static_cast<int32_t>(b->chunk_row.size()));
   }
+}
+
+// Threads for the transpose: up to 16, one when the graph is small; fewer when the
+// per-thread column counters (threads x N int32) would pass 1 GiB.
+int transpose_threads(int64_t n, int64_t e) {
+  if (e < (int64_t(1) << 16)) return 1;
+  const unsigned hw = std::thread::hardware_concurrency();
+  int t = hw ? static_cast<int>(std::min(hw, 16u)) : 1;
+  while (t > 1 && int64_t(t) * n * 4 > (int64_t(1) << 30)) t /= 2;
+  return t;
+}
+
+// Stable counting-sort transpose: colptr, and for every transpose entry its destination
+// row and its position within that row; destinations ascend within each column. Rows are
+// split into T contiguous blocks of about E/T edges. Block t counts its edges per column,
+// then writes them, in row order, from the column's start plus the counts of blocks before
+// it: the positions a single pass over the rows in order would use.
+void transpose(const std::vector<int32_t>& indptr, const std::vector<int32_t>& indices,
+               int64_t n, int64_t e, int T, std::vector<int32_t>* colptr,
+               std::vector<int32_t>* rowidx, std::vector<int32_t>* rel,
+               std::vector<int32_t>* cursor) {
+  std::vector<int64_t> rb(static_cast<size_t>(T) + 1, n);  // block t: rows [rb[t], rb[t+1])
+  rb[0] = 0;
+  for (int t = 1; t < T; ++t)
+    rb[t] = std::lower_bound(indptr.begin(), indptr.end(), static_cast<int32_t>(e * t / T)) -
+            indptr.begin();
+  for (int t = 1; t <= T; ++t) rb[t] = std::max(rb[t], rb[t - 1]);
+  rb[T] = n;
+  int32_t* cnt = cursor->data();  // [T][n]
+  // blocks 1..T-1 on their own threads, block 0 here; a block whose thread cannot be
+  // started runs here too (no exception leaves the planner)
+  auto run = [&](auto&& body) {
+    std::vector<std::thread> th;
+    th.reserve(static_cast<size_t>(T));
+    int t = 1;
+    try {
+      for (; t < T; ++t) th.emplace_back(body, t);
+    } catch (...) {
+    }
+    for (int u = t; u < T; ++u) body(u);
+    body(0);
+    for (auto& x : th) x.join();
+  };
+  run([&](int t) {
+    int32_t* c = cnt + static_cast<size_t>(t) * n;
+    for (int64_t k = indptr[rb[t]]; k < indptr[rb[t + 1]]; ++k) c[indices[k]]++;
+  });
+  (*colptr)[0] = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    int64_t at = (*colptr)[j];
+    for (int t = 0; t < T; ++t) {
+      int32_t& c = cnt[static_cast<size_t>(t) * n + j];
+      const int32_t k = c;
+      c = static_cast<int32_t>(at);  // block t's first slot in column j
+      at += k;
+    }
+    (*colptr)[j + 1] = static_cast<int32_t>(at);
+  }
+  run([&](int t) {
+    int32_t* c = cnt + static_cast<size_t>(t) * n;
+    for (int64_t i = rb[t]; i < rb[t + 1]; ++i)
+      for (int32_t k = indptr[i]; k < indptr[i + 1]; ++k) {
+        const int32_t at = c[indices[k]]++;
+        (*rowidx)[at] = static_cast<int32_t>(i);
+        (*rel)[at] = k - indptr[i];  // the edge's position within its CSR row
+      }
+  });
 }
 
 }  // namespace
@@ -118,20 +209,12 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
     p->has_csc = o.build_csc != 0;
     p->max_out = 0;
     if (p->has_csc) {
-      // stable counting-sort transpose: scanning rows in order leaves destinations
-      // ascending inside every column
+      const int T = transpose_threads(n, e);
       p->colptr.assign(static_cast<size_t>(n) + 1, 0);
-      for (int64_t k = 0; k < e; ++k) p->colptr[indices[k] + 1]++;
-      for (int64_t j = 0; j < n; ++j) p->colptr[j + 1] += p->colptr[j];
-      std::vector<int32_t> cursor(p->colptr.begin(), p->colptr.end() - 1);
       p->rowidx.assign(static_cast<size_t>(e), 0);
       p->csc_rel.assign(static_cast<size_t>(e), 0);
-      for (int64_t i = 0; i < n; ++i)
-        for (int32_t k = indptr[i]; k < indptr[i + 1]; ++k) {
-          const int32_t at = cursor[indices[k]]++;
-          p->rowidx[at] = static_cast<int32_t>(i);
-          p->csc_rel[at] = k - indptr[i];  // the edge's position within its CSR row
-        }
+      std::vector<int32_t> cursor(static_cast<size_t>(T) * static_cast<size_t>(n), 0);
+      transpose(p->indptr, p->indices, n, e, T, &p->colptr, &p->rowidx, &p->csc_rel, &cursor);
       ga_plan_opts oc = o;  // the transpose's columns use their own hub threshold / chunk
       oc.hub_min_deg_exclusive = o.col_hub_min_deg_exclusive;
       oc.hub_chunk = o.col_hub_chunk;

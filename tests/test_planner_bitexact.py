@@ -25,6 +25,10 @@ def _graphs():
     yield "no_nodes", (np.zeros(1, np.int32), np.zeros(0, np.int32))
     yield "chunglu30k", gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=30_000)
     yield "rmat2^14", gg.make_graph(gg.WORKLOADS["rmat21_dot_bf16"], n=1 << 14)
+    # one row holding nearly every edge: most of the transpose's row blocks are empty
+    yield "giant_row", gg.csr_from_edges(
+        1000, np.r_[rng.integers(0, 1000, 90_000), rng.integers(0, 1000, 500)],
+        np.r_[np.full(90_000, 5), rng.integers(0, 1000, 500)])
 
 
 THRESH = [(16, 1024, 512), (0, 0, 1), (2, 3, 2), (31, 32, 33), (8, 64, 64)]
