@@ -20,7 +20,8 @@ namespace ga {
 namespace {
 
 // Ids 0..n-1 ordered by degree descending, ties by ascending id: a stable counting sort on
-// the degree (a comparison sort when the largest degree is far beyond n).
+// the degree, whose buckets take 4 bytes per possible degree, when the largest degree is
+// at most about n; a stable comparison sort otherwise.
 void order_by_degree(const std::vector<int32_t>& ptr, std::vector<int32_t>* order,
                      int64_t* max_deg) {
   const int64_t n = static_cast<int64_t>(ptr.size()) - 1;
@@ -28,12 +29,12 @@ void order_by_degree(const std::vector<int32_t>& ptr, std::vector<int32_t>* orde
   int64_t mx = 0;
   for (int64_t i = 0; i < n; ++i) mx = std::max<int64_t>(mx, ptr[i + 1] - ptr[i]);
   *max_deg = mx;
-  if (mx <= 4 * n + 1024) {
-    std::vector<int64_t> start(static_cast<size_t>(mx) + 2, 0);  // start[d]: first slot of degree d
+  if (mx <= n + 1024) {
+    std::vector<int32_t> start(static_cast<size_t>(mx) + 1, 0);  // start[d]: first slot of degree d
     for (int64_t i = 0; i < n; ++i) start[ptr[i + 1] - ptr[i]]++;
-    int64_t at = 0;
+    int32_t at = 0;
     for (int64_t d = mx; d >= 0; --d) {
-      const int64_t c = start[d];
+      const int32_t c = start[d];
       start[d] = at;
       at += c;
     }
