@@ -233,9 +233,11 @@ def test_backward_chunglu5k_every_element(dtype):
     assert info["n_row_hub"] > 0
 
 
-@pytest.mark.parametrize("G,LH,dtype", [(8, 8, "f32"), (16, 16, "bf16"), (64, 16, "f32"),
-                                        (4, 2, "bf16"), (64, 64, "bf16"), (32, 32, "f32")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G,LH", GEOMS)
 def test_backward_geometries(G, LH, dtype):
+    """The dot backward on every element, for every compiled (lanes per row, lanes per head)
+    geometry, with a row hub and a column hub split into chunks."""
     eb = 4 if dtype == "f32" else 2
     H, d = G // LH, LH * 16 // eb
     rng = np.random.default_rng(G + LH)
@@ -502,9 +504,10 @@ def test_gat_backward_every_element(dtype):
     assert info["n_col_chunks"] > info["n_col_hub"] > 0
 
 
-@pytest.mark.parametrize("G,LH,dtype", [(8, 8, "f32"), (16, 2, "bf16"), (64, 64, "bf16"),
-                                        (4, 4, "f32"), (32, 8, "f32")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("G,LH", GEOMS)
 def test_gat_backward_geometries(G, LH, dtype):
+    """The GAT-style backward on every element, for every compiled geometry of V."""
     eb = 4 if dtype == "f32" else 2
     H, d = G // LH, LH * 16 // eb
     rng = np.random.default_rng(G * 7 + LH)
@@ -568,7 +571,7 @@ def gatv2_fwd_case(tag, ip, ix, xd, xs, a, dtype, scale=1.0, slope=0.2, rows=Non
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("G,LH", [(8, 8), (16, 4), (32, 4), (64, 16), (4, 2), (64, 64)])
+@pytest.mark.parametrize("G,LH", GEOMS)
 def test_gatv2_forward_geometries(dtype, G, LH):
     eb = 4 if dtype == "f32" else 2
     H, d = G // LH, LH * 16 // eb
@@ -641,7 +644,7 @@ def gatv2_bwd_case(tag, ip, ix, xd, xs, a, do, dtype, scale=1.0, slope=0.2, rows
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("G,LH", [(8, 8), (32, 4), (64, 16), (4, 2), (16, 16)])
+@pytest.mark.parametrize("G,LH", GEOMS)
 def test_gatv2_backward_every_element(dtype, G, LH):
     eb = 4 if dtype == "f32" else 2
     H, d = G // LH, LH * 16 // eb
