@@ -762,3 +762,26 @@ def test_binding_rejects_mismatched_rows():
                  lambda: gather_probe(plan, x, x)):
         with pytest.raises(ValueError):
             call()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_edge_chunks_in_every_layer(dtype):
+    """Thresholds (0, 0, 1): every non-empty row and column is a hub cut into one-edge
+    chunks, so each result comes out of the merge kernels alone. Dot, GAT-style and GATv2
+    forward and backward, every element, against the oracle."""
+    from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2
+    rng = np.random.default_rng(61)
+    n, H, d = 150, 2, 32 if dtype == "bf16" else 16
+    ip, ix = gg.random_multigraph(n, 1200, rng, hub_rows=(4,), hub_deg=300)
+    kw = dict(light_max_deg=0, hub_min_deg_exclusive=0, hub_chunk=1)
+    feats = [rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(4)]
+    if dtype == "bf16":
+        feats = [gg.f32_to_bf16_bits(x) for x in feats]
+    plan, _ = bwd_case(f"one-edge chunks dot {dtype}", ip, ix, *feats, dtype, **kw)
+    info = plan.info()
+    assert info["n_row_chunks"] == ix.size and info["n_col_chunks"] == ix.size
+    s_, t_ = (rng.standard_normal((n, H)).astype(np.float32) for _ in range(2))
+    gat_bwd_case(f"one-edge chunks gat {dtype}", ip, ix, s_, t_, feats[2], feats[3], dtype, **kw)
+    a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    gatv2_bwd_case(f"one-edge chunks gatv2 {dtype}", ip, ix, feats[0], feats[1], a, feats[3],
+                   dtype, **kw)
