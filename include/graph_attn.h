@@ -23,7 +23,8 @@
  *
  * Conventions shared by every call
  *   Graph: CSR with int32 indptr [N+1] and indices [E], row i = destination, indices =
- *     its sources. Parallel edges count with multiplicity. N, E < 2^31.
+ *     its sources. Parallel edges count with multiplicity. N < 2^31 and E <= 2^31 - 2^16
+ *     (kernels walk edge positions in 32-bit integers); larger graphs: GA_ERR_INVALID_ARG.
  *   Features: node-major, contiguous [N, H, d] in the call's dtype (fp32 or bf16), each
  *     pointer 16-byte aligned, H*d*sizeof(dtype) a multiple of 16 bytes and at most 1024
  *     bytes, d*sizeof(dtype) a power of two between 32 and 1024 bytes dividing the row.

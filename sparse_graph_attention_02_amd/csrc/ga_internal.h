@@ -57,6 +57,9 @@ struct ga_plan {
 
 namespace ga {
 
+// Largest edge count a plan accepts: 2^31 - 2^16.
+constexpr int64_t kMaxEdges = (int64_t(1) << 31) - (int64_t(1) << 16);
+
 // Planner (plan.cpp). Validates and builds every host array.
 ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, int64_t e,
                      const ga_plan_opts& opts, ga_plan* p);

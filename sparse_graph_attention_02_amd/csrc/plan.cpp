@@ -173,8 +173,9 @@ ga_plan_opts resolve_opts(const ga_plan_opts& in, int64_t e) {
 
 ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, int64_t e,
                      const ga_plan_opts& given, ga_plan* p) {
-  if (n < 0 || e < 0 || n >= (int64_t(1) << 31) || e >= (int64_t(1) << 31))
-    return GA_ERR_INVALID_ARG;
+  // Kernels step through edge positions in 32-bit integers, up to 64 past a row's end
+  // before the loop test: E keeps 2^16 of headroom below 2^31.
+  if (n < 0 || e < 0 || n >= (int64_t(1) << 31) || e > kMaxEdges) return GA_ERR_INVALID_ARG;
   if (!indptr || (e > 0 && !indices)) return GA_ERR_INVALID_ARG;
   if (given.light_max_deg < 0 || given.hub_min_deg_exclusive < -1 || given.hub_chunk < -1 ||
       given.hub_chunk == 0 || given.col_hub_min_deg_exclusive < -1 ||

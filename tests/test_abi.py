@@ -80,6 +80,16 @@ def test_bad_opts_are_rejected():
         capi.GA_ERR_INVALID_ARG
 
 
+def test_edge_count_limit():
+    """E must stay at or below 2^31 - 2^16 (edge positions are 32-bit in the kernels, with
+    room for a step past a row's end); larger counts are refused before any array is read."""
+    ip, ix = np.array([0, 1], np.int32), np.array([0], np.int32)
+    for e in (2 ** 31 - 2 ** 16 + 1, 2 ** 31, 2 ** 40):
+        assert capi.raw_status("graph_attn_plan_create", ip.ctypes.data_as(POINTER(c_int32)),
+                               ix.ctypes.data_as(POINTER(c_int32)), 1, e, None,
+                               ctypes.byref(ctypes.c_void_p())) == capi.GA_ERR_INVALID_ARG, e
+
+
 def test_empty_graph_plan():
     p = Plan(np.zeros(1, np.int32), np.zeros(0, np.int32))
     info = p.info()
