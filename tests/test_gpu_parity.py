@@ -785,3 +785,24 @@ def test_one_edge_chunks_in_every_layer(dtype):
     a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
     gatv2_bwd_case(f"one-edge chunks gatv2 {dtype}", ip, ix, feats[0], feats[1], a, feats[3],
                    dtype, **kw)
+
+
+@pytest.mark.parametrize("slope,scale", [(1.7, 0.6), (-0.3, 2.0), (0.0, 1.0)])
+def test_gat_and_gatv2_slopes_and_scales(slope, scale):
+    """LeakyReLU slopes above 1, negative and zero, and scales away from 1: the GAT-style and
+    GATv2 layers, forward and backward on every element (the per-node form of the GATv2
+    attention gradient relies on LeakyReLU(z) = g z, which holds for any slope)."""
+    rng = np.random.default_rng(int(slope * 10) + 100)
+    n, H, d = 300, 2, 16
+    ip, ix = gg.random_multigraph(n, 3000, rng, hub_rows=(2,), hub_deg=400)
+    kw = dict(light_max_deg=4, hub_min_deg_exclusive=48, hub_chunk=40)
+    s_, t_ = (rng.standard_normal((n, H)).astype(np.float32) for _ in range(2))
+    v, do = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    gat_bwd_case(f"gat slope {slope} scale {scale}", ip, ix, s_, t_, v, do, "f32", scale=scale,
+                 slope=slope, **kw)
+    xd, xs = (rng.standard_normal((n, H, d)).astype(np.float32) for _ in range(2))
+    a = (rng.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    gatv2_fwd_case(f"gatv2 slope {slope} scale {scale}", ip, ix, xd, xs, a, "f32", scale=scale,
+                   slope=slope, **kw)
+    gatv2_bwd_case(f"gatv2 slope {slope} scale {scale}", ip, ix, xd, xs, a, do, "f32",
+                   scale=scale, slope=slope, **kw)
