@@ -418,3 +418,23 @@ def test_reduce_argument_checks_before_any_hip_call():
     ok = Plan(*gg.csr_from_edges(3, np.zeros(65535, np.int64), np.full(65535, 1)))
     capi.graph_attn_reduce_slot_bytes(ok.handle, byref(b))
     assert b.value == 2
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library the package raises on first use: there is no CPU
+    fallback (a fresh process pointed at a library path that does not exist)."""
+    import subprocess
+    import sys
+    code = ("import numpy as np, sparse_graph_attention_02_amd as ga\n"
+            "try:\n"
+            "    ga.Plan(np.array([0, 1], np.int32), np.array([0], np.int32))\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    env = dict(os.environ, GRAPH_ATTN_LIB="/nonexistent/libgraph_attn.so")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "missing" in r.stdout, r.stdout
