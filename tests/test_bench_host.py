@@ -57,8 +57,8 @@ def test_byte_model_per_edge_and_node(kernel, N, E, H, d, b):
 
 
 def test_byte_model_figures_of_the_configurations():
-    """The per-edge / per-node figures of the survey's sizing table: 1,028 / 1,060 B for the
-    1M forward; 1,044 / 1,060 B for the GAT forward (fp32, H = 4, d = 64); 516 / 520 B for
+    """Per-edge / per-node byte figures worked out by hand from the layouts: 1,028 / 1,060 B
+    for the 1M forward; 1,044 / 1,060 B for the GAT forward (fp32, H = 4, d = 64); 516 / 520 B for
     the R-MAT forward; the 1M dK/dV pass 1,092 B per edge."""
     f = bench.algorithmic_bytes
     assert f("fwd_main", 1, 1, 8, 32, 2) - f("fwd_main", 1, 0, 8, 32, 2) == 1028
