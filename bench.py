@@ -33,6 +33,10 @@ import graphgen as gg  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# XCD split thresholds of the attention workloads' plans (rows, transpose columns): a sweep
+# on the 1M-node training step gave 19.19 ms unsplit, 17.54 ms at 256 / 1024, 17.71 ms at
+# 512 / 512 and 18.31 ms at 128 / 128 (chunk partials outgrow the L2 gain below ~256)
+XCD_SPLIT_ROWS, XCD_SPLIT_COLS = 256, 1024
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -262,6 +266,14 @@ def main():
     ap.add_argument("--chunk", type=int, default=None)
     ap.add_argument("--col-hub", type=int, default=None)
     ap.add_argument("--col-chunk", type=int, default=None)
+    ap.add_argument("--xcd-split", type=int, default=None,
+                    help="rows longer than this are regrouped by source id mod 8 and their "
+                         "chunks scheduled to the matching XCD (0 = off; default %d for the "
+                         "attention workloads, off for the reductions, whose slots are row "
+                         "positions)" % XCD_SPLIT_ROWS)
+    ap.add_argument("--col-xcd-split", type=int, default=None,
+                    help="the same for transpose columns (default %d for the attention "
+                         "workloads)" % XCD_SPLIT_COLS)
     ap.add_argument("--slices", type=int, default=None,
                     help="feature slices per XCD group (0 = automatic, 1 = off, 2, 4, 8)")
     ap.add_argument("--order", choices=["as-generated", "out-degree", "rcm"],
@@ -276,6 +288,11 @@ def main():
         sys.exit(2)
 
     w = gg.WORKLOADS[args.workload]
+    reduction = w.score in ("max", "min")
+    if args.xcd_split is None:
+        args.xcd_split = 0 if reduction else XCD_SPLIT_ROWS
+    if args.col_xcd_split is None:  # columns: at least the column default, 0 when rows are 0
+        args.col_xcd_split = 0 if args.xcd_split == 0 else max(XCD_SPLIT_COLS, args.xcd_split)
     t0 = time.perf_counter()
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)
@@ -303,7 +320,9 @@ def main():
     t0 = time.perf_counter()
     plan = ga.Plan(ip, ix, light_max_deg=args.light, hub_min_deg_exclusive=args.hub,
                    hub_chunk=args.chunk, build_csc=w.backward, feature_slices=args.slices,
-                   col_hub_min_deg_exclusive=args.col_hub, col_hub_chunk=args.col_chunk)
+                   col_hub_min_deg_exclusive=args.col_hub, col_hub_chunk=args.col_chunk,
+                   xcd_split_min_deg_exclusive=args.xcd_split,
+                   col_xcd_split_min_deg_exclusive=args.col_xcd_split)
     plan_host_s = time.perf_counter() - t0
     plan.upload("cuda")
     torch.cuda.synchronize()
@@ -475,7 +494,9 @@ def main():
                                           "n_row_chunks", "n_col_hub", "n_col_chunks",
                                           "max_in_degree", "max_out_degree", "rows_sorted",
                                           "feature_slices", "col_hub_min_deg_exclusive",
-                                          "col_hub_chunk")},
+                                          "col_hub_chunk", "xcd_split_min_deg_exclusive",
+                                          "col_xcd_split_min_deg_exclusive", "n_row_sched",
+                                          "n_col_sched")},
             "parallelism": "single GPU",
         },
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,

@@ -91,8 +91,19 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * the tail), at least light_max_deg; the row chunk max(256, threshold / 4); the column
  * threshold min(1024, row threshold) and column chunk min(512, row chunk), as the column
  * passes do more work per edge. graph_attn_plan_get_info reports the values used.
+ * xcd_split_min_deg_exclusive (rows) and col_xcd_split_min_deg_exclusive (transpose
+ * columns), 0 = off (the default): rows longer than this become hubs whose edges the plan
+ * regroups by source id mod 8 (stable within a group, in the plan's own copy of the CSR;
+ * columns: destinations by id mod 8), each group chunked separately, and the chunks are
+ * scheduled so that group p runs on the XCD whose workgroups have id = p mod 8. Each XCD's
+ * 4 MB L2 then holds hot rows of one eighth of the nodes instead of all of them. The
+ * forward (every score), the dot backward's dQ and dK/dV passes run this schedule; the
+ * other backward passes stay correct on such a plan without it. Their main kernels run
+ * unsliced on a split plan (feature_slices does not apply to them). Results agree with
+ * an unsplit plan to rounding (the sum order within a row changes). The min/max
+ * reduction, whose slots are row positions, refuses split plans (GA_ERR_UNSUPPORTED).
  * Constraints: light_max_deg >= 0; an explicit threshold >= light_max_deg; an explicit
- * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}. */
+ * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}; a split threshold 0 or >= light_max_deg. */
 typedef struct {
   int32_t light_max_deg;
   int32_t hub_min_deg_exclusive;
@@ -101,6 +112,8 @@ typedef struct {
   int32_t feature_slices;
   int32_t col_hub_min_deg_exclusive;
   int32_t col_hub_chunk;
+  int32_t xcd_split_min_deg_exclusive;
+  int32_t col_xcd_split_min_deg_exclusive;
 } ga_plan_opts;
 
 /* Counts describing a built plan (all int64 so the struct has no padding). */
@@ -116,6 +129,8 @@ typedef struct {
   int64_t rows_sorted;  /* 1 when every row's neighbour ids are non-decreasing */
   int64_t feature_slices;  /* the option as given (0 = automatic) */
   int64_t col_hub_min_deg_exclusive, col_hub_chunk;      /* as used */
+  int64_t xcd_split_min_deg_exclusive, col_xcd_split_min_deg_exclusive;
+  int64_t n_row_sched, n_col_sched;  /* scheduled chunk slots (0: chunk order) */
 } ga_plan_info;
 
 typedef struct ga_plan ga_plan; /* opaque; host metadata owned by the library */
@@ -127,15 +142,20 @@ const char* graph_attn_version(void);
 const char* graph_attn_status_string(ga_status status);
 
 /* Fill *opts with the defaults: light_max_deg 16, hub thresholds and chunks -1 (chosen
- * from the graph), build_csc 1, feature_slices 0 (automatic). */
+ * from the graph), build_csc 1, feature_slices 0 (automatic), both split thresholds 0
+ * (off). */
 ga_status graph_attn_plan_opts_default(ga_plan_opts* opts);
 
 /* Build a plan from a host CSR graph (the planner of the degree-aware tiling; runs on the
  * host, O(N + E), no HIP calls). The CSR is always validated; GA_ERR_BAD_GRAPH on failure.
  * Bins: each bin lists its rows by degree descending, ties by ascending row id. Hub row
- * chunks: [indptr[i] + k*C, min(indptr[i] + (k+1)*C, indptr[i+1])), listed hub by hub.
+ * chunks: [indptr[i] + k*C, min(indptr[i] + (k+1)*C, indptr[i+1])), listed hub by hub;
+ * a split row (see xcd_split_min_deg_exclusive) is listed by group, each group's range
+ * cut the same way, and "indices" is the regrouped CSR. "row_sched" / "col_sched": the
+ * chunk scheduled in each dispatch slot (-1 = none), empty when nothing is split.
  * Transpose (build_csc): colptr [N+1] and rowidx [E], destinations ascending within each
- * column (the order a stable scatter over rows produces), and csc_rel [E], for each
+ * column (the order a stable scatter over rows produces; split columns regrouped as
+ * above), and csc_rel [E], for each
  * transpose entry the position of that edge within its CSR row (k - indptr[i] for CSR
  * edge k of row i); column bins/chunks follow the same rules on out-degree.
  * indptr_host/indices_host are only read during the call (indices_host may be NULL when
@@ -162,7 +182,8 @@ ga_status graph_attn_plan_upload(ga_plan* plan, void* dev_buf, size_t bytes, voi
  * "row_light", "row_medium", "row_hub", "row_chunk_row", "row_chunk_begin",
  * "row_chunk_end", "row_hub_chunk_ptr", and with the transpose "colptr", "rowidx",
  * "col_light", "col_medium", "col_hub", "col_chunk_row", "col_chunk_begin",
- * "col_chunk_end", "col_hub_chunk_ptr", "csc_rel". *data stays valid until the plan is
+ * "col_chunk_end", "col_hub_chunk_ptr", "csc_rel", then "row_sched" and "col_sched"
+ * (the latter needs the transpose). *data stays valid until the plan is
  * destroyed (it may be NULL when *count == 0). GA_ERR_INVALID_ARG for an unknown name,
  * GA_ERR_NOT_READY for a transpose array of a plan built without it. */
 ga_status graph_attn_plan_array(const ga_plan* plan, const char* name, const int32_t** data,

@@ -62,11 +62,15 @@ class Plan:
     built on the host by the library's planner; ``upload`` copies it to the GPU.
 
     Thresholds left as None take the library defaults, except that the column hub
-    threshold and chunk follow explicitly given row values unless given themselves."""
+    threshold and chunk, and the column XCD split threshold, follow explicitly given row
+    values unless given themselves. ``xcd_split_min_deg_exclusive`` > 0 regroups longer
+    rows (columns) by neighbour id mod 8 and schedules their chunks to the matching XCD
+    (see graph_attn_plan_opts); 0, the default, leaves the CSR as given."""
 
     def __init__(self, indptr, indices, *, light_max_deg=None, hub_min_deg_exclusive=None,
                  hub_chunk=None, build_csc=True, feature_slices=None,
-                 col_hub_min_deg_exclusive=None, col_hub_chunk=None):
+                 col_hub_min_deg_exclusive=None, col_hub_chunk=None,
+                 xcd_split_min_deg_exclusive=None, col_xcd_split_min_deg_exclusive=None):
         ip = np.ascontiguousarray(indptr, dtype=np.int32)
         ix = np.ascontiguousarray(indices, dtype=np.int32)
         opts = capi.ga_plan_opts()
@@ -75,11 +79,15 @@ class Plan:
             col_hub_min_deg_exclusive = hub_min_deg_exclusive
         if col_hub_chunk is None:
             col_hub_chunk = hub_chunk
+        if col_xcd_split_min_deg_exclusive is None:
+            col_xcd_split_min_deg_exclusive = xcd_split_min_deg_exclusive
         for k, v in (("light_max_deg", light_max_deg),
                      ("hub_min_deg_exclusive", hub_min_deg_exclusive),
                      ("hub_chunk", hub_chunk), ("feature_slices", feature_slices),
                      ("col_hub_min_deg_exclusive", col_hub_min_deg_exclusive),
-                     ("col_hub_chunk", col_hub_chunk)):
+                     ("col_hub_chunk", col_hub_chunk),
+                     ("xcd_split_min_deg_exclusive", xcd_split_min_deg_exclusive),
+                     ("col_xcd_split_min_deg_exclusive", col_xcd_split_min_deg_exclusive)):
             if v is not None:
                 setattr(opts, k, int(v))
         opts.build_csc = 1 if build_csc else 0

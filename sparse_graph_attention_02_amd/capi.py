@@ -25,7 +25,9 @@ GA_REDUCE_MAX, GA_REDUCE_MIN = 0, 1
 class ga_plan_opts(Structure):
     _fields_ = [("light_max_deg", c_int32), ("hub_min_deg_exclusive", c_int32),
                 ("hub_chunk", c_int32), ("build_csc", c_int32), ("feature_slices", c_int32),
-                ("col_hub_min_deg_exclusive", c_int32), ("col_hub_chunk", c_int32)]
+                ("col_hub_min_deg_exclusive", c_int32), ("col_hub_chunk", c_int32),
+                ("xcd_split_min_deg_exclusive", c_int32),
+                ("col_xcd_split_min_deg_exclusive", c_int32)]
 
 
 class ga_plan_info(Structure):
@@ -34,7 +36,8 @@ class ga_plan_info(Structure):
         "has_csc", "n_col_light", "n_col_medium", "n_col_hub", "n_col_chunks",
         "max_in_degree", "max_out_degree", "light_max_deg", "hub_min_deg_exclusive",
         "hub_chunk", "device_bytes", "uploaded", "rows_sorted", "feature_slices",
-        "col_hub_min_deg_exclusive", "col_hub_chunk")]
+        "col_hub_min_deg_exclusive", "col_hub_chunk", "xcd_split_min_deg_exclusive",
+        "col_xcd_split_min_deg_exclusive", "n_row_sched", "n_col_sched")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -98,6 +98,8 @@ const ArrayRef kArrays[] = {
     GA_REF("col_chunk_end", p->cols.chunk_end, true),
     GA_REF("col_hub_chunk_ptr", p->cols.hub_chunk_ptr, true),
     GA_REF("csc_rel", p->csc_rel, true),
+    GA_REF("row_sched", p->rows.sched, false),
+    GA_REF("col_sched", p->cols.sched, true),
 };
 #undef GA_REF
 constexpr int kNumArrays = sizeof(kArrays) / sizeof(kArrays[0]);
@@ -186,6 +188,12 @@ size_t reduce_bwd_ws_bytes(const ga_plan* p, int32_t features) {
   return align_up(p->cols.chunk_row.size() * size_t(features) * 4);
 }
 
+// Plans that regroup rows or columns by XCD partition: their edge positions are not the
+// caller's, so the reduction (whose slots are row positions) does not take them.
+bool split_plan(const ga_plan* p) {
+  return p->opts.xcd_split_min_deg_exclusive > 0 || p->opts.col_xcd_split_min_deg_exclusive > 0;
+}
+
 ga_status check_device(const ga_plan* p) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
@@ -221,6 +229,8 @@ ga_status graph_attn_plan_opts_default(ga_plan_opts* o) {
   o->feature_slices = 0;
   o->col_hub_min_deg_exclusive = -1;
   o->col_hub_chunk = -1;
+  o->xcd_split_min_deg_exclusive = 0;  // off
+  o->col_xcd_split_min_deg_exclusive = 0;
   return GA_OK;
 }
 
@@ -267,6 +277,10 @@ ga_status graph_attn_plan_get_info(const ga_plan* p, ga_plan_info* info) {
   info->feature_slices = p->opts.feature_slices;
   info->col_hub_min_deg_exclusive = p->opts.col_hub_min_deg_exclusive;
   info->col_hub_chunk = p->opts.col_hub_chunk;
+  info->xcd_split_min_deg_exclusive = p->opts.xcd_split_min_deg_exclusive;
+  info->col_xcd_split_min_deg_exclusive = p->opts.col_xcd_split_min_deg_exclusive;
+  info->n_row_sched = static_cast<int64_t>(p->rows.sched.size());
+  info->n_col_sched = static_cast<int64_t>(p->cols.sched.size());
   info->uploaded = p->uploaded;
   return GA_OK;
 }
@@ -299,7 +313,7 @@ ga_status graph_attn_plan_upload(ga_plan* p, void* dev_buf, size_t bytes, void* 
       return GA_ERR_HIP;
   }
   if (hipStreamSynchronize(s) != hipSuccess) return GA_ERR_HIP;
-  auto bins = [&](int first, const ga::Bins& b) {
+  auto bins = [&](int first, int sched, const ga::Bins& b) {
     ga::DevBins d;
     d.light = ptrs[first];
     d.medium = ptrs[first + 1];
@@ -312,14 +326,16 @@ ga_status graph_attn_plan_upload(ga_plan* p, void* dev_buf, size_t bytes, void* 
     d.n_medium = static_cast<int32_t>(b.medium.size());
     d.n_hub = static_cast<int32_t>(b.hub.size());
     d.n_chunks = static_cast<int32_t>(b.chunk_row.size());
+    d.sched = b.sched.empty() ? nullptr : ptrs[sched];
+    d.n_sched = static_cast<int32_t>(b.sched.empty() ? b.chunk_row.size() : b.sched.size());
     return d;
   };
   p->d_indptr = ptrs[0];
   p->d_indices = ptrs[1];
-  p->d_rows = bins(2, p->rows);
+  p->d_rows = bins(2, 19, p->rows);
   p->d_colptr = ptrs[9];
   p->d_rowidx = ptrs[10];
-  p->d_cols = p->has_csc ? bins(11, p->cols) : ga::DevBins{};
+  p->d_cols = p->has_csc ? bins(11, 20, p->cols) : ga::DevBins{};
   p->d_csc_rel = ptrs[18];
   p->device = dev;
   p->uploaded = true;
@@ -409,10 +425,12 @@ ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.neg_slope = neg_slope;
   args.ld = g.G;
   args.hf = g.heads;
-  // GAT-style scores gather t_j per head, a partial line per slice: not sliced
-  args.slices = score == GA_SCORE_DOT ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
-                                                           ga::kAutoSliceLanesTwoRows)
-                                      : 1;
+  // GAT-style scores gather t_j per head, a partial line per slice: not sliced; nor are
+  // plans whose chunk slots are scheduled to XCDs
+  args.slices = score == GA_SCORE_DOT && p->rows.sched.empty()
+                    ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
+                                         ga::kAutoSliceLanesTwoRows)
+                    : 1;
   const int rc = ga::launch_fwd(dtype, score == GA_SCORE_DOT ? ga::kModeDot : ga::kModeGat, g,
                                 args, p->n, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
@@ -457,7 +475,9 @@ ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.neg_slope = neg_slope;
   args.ld = g.G;
   args.hf = g.heads;
-  args.slices = ga::feature_slices(g.G, g.LH, p->opts.feature_slices, 0);
+  args.slices = p->rows.sched.empty()
+                    ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices, 0)
+                    : 1;
   const int rc = ga::launch_fwd(dtype, ga::kModeGatV2, g, args, p->n, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
@@ -517,7 +537,10 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.neg_slope = neg_slope;
   args.ld = g.G;
   args.hf = g.heads;
-  args.slices = ga::feature_slices(g.G, g.LH, p->opts.feature_slices, ga::kAutoSliceLanesTwoRows);
+  args.slices = p->rows.sched.empty()
+                    ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
+                                         ga::kAutoSliceLanesTwoRows)
+                    : 1;
   args.dq_stride = static_cast<int>(ga::dq_partial_floats(heads, dim));
   const int rc = score == GA_SCORE_DOT ? ga::launch_bwd(dtype, g, args, p->n, stream, active_hook())
                                        : ga::launch_bwd_gat(dtype, g, args, stream, active_hook());
@@ -615,6 +638,7 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   int G = 0;
   ga_status s = reduce_geometry(dtype, features, &G);
   if (s != GA_OK) return s;
+  if (split_plan(p)) return GA_ERR_UNSUPPORTED;
   if (p->n > 0) {
     if ((s = check_ptr(x, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
         (s = check_ptr(arg, 16)) != GA_OK)
@@ -656,6 +680,7 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   int G = 0;
   ga_status s = reduce_geometry(dtype, features, &G);
   if (s != GA_OK) return s;
+  if (split_plan(p)) return GA_ERR_UNSUPPORTED;
   if (p->n > 0) {
     if ((s = check_ptr(slot ? slot : static_cast<const void*>(arg), 16)) != GA_OK ||
         (s = check_ptr(dout, 16)) != GA_OK || (s = check_ptr(dx, 16)) != GA_OK)

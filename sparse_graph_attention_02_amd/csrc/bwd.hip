@@ -199,15 +199,17 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
   float A[VEC], Bk[VEC], lse2, D = 0.f, Lp = 0.f;
 #pragma unroll
   for (int c = 0; c < VEC; ++c) A[c] = Bk[c] = 0.f;
-  if (item < B.n_chunks + B.n_medium) {
-    int row, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int row, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      row = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      row = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      row = B.medium[item - B.n_chunks];
+      row = B.medium[item - B.n_sched];
       e0 = a.indptr[row];
       e1 = a.indptr[row + 1];
     }
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
     if (g != 0) return;
     if (chunk) {
       const int Ff = a.ld * VEC;  // elements of the full row
-      float* p = a.ws_dq + static_cast<size_t>(item) * a.dq_stride;
+      float* p = a.ws_dq + static_cast<size_t>(c) * a.dq_stride;
       K::store_f32(p + so * VEC, r, A);
       K::store_f32(p + Ff + so * VEC, r, Bk);
       if (r % LH == 0) {
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
     }
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
@@ -285,15 +287,17 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) 
   typename K::acc_t dk[VEC], dv[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) dk[c] = dv[c] = 0;
-  if (item < B.n_chunks + B.n_medium) {
-    int col, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int col, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      col = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      col = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      col = B.medium[item - B.n_chunks];
+      col = B.medium[item - B.n_sched];
       e0 = a.colptr[col];
       e1 = a.colptr[col + 1];
     }
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) 
     K::template group_sum<NG>(dv);
     if (g != 0) return;
     if (chunk) {
-      float* p = a.ws_dkv + static_cast<size_t>(item) * 2 * F;
+      float* p = a.ws_dkv + static_cast<size_t>(c) * 2 * F;
       K::store_f32(p, r, dk);
       K::store_f32(p + F, r, dv);
     } else {
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) 
     }
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
@@ -356,7 +360,7 @@ template <typename T, int G, int LH>
 struct Launcher {
   static constexpr int NG = kWave / G;
   static int64_t items_of(const DevBins& B) {
-    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+    return int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   }
   template <typename Kern>
   static int go(const char* name, Kern kernel, int64_t blocks, const BwdArgs& a, void* stream,

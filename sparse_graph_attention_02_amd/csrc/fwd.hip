@@ -8,8 +8,9 @@
 // reduction paragraph (light rows feature-parallel, heavy rows as parallel edge chunks).
 //
 // One launch (fwd_main) covers every row. Its wavefront work items are, in order:
-//   [0, n_chunks)                hub-row chunks: one wavefront per chunk -> fp32 partial
-//                                (m, l, acc) in the workspace
+//   [0, n_sched)                 hub-row chunks: one wavefront per chunk -> fp32 partial
+//                                (m, l, acc) in the workspace; slot k runs chunk k, or
+//                                the chunk the plan's XCD schedule puts there (none: -1)
 //   [.., + n_medium)             medium rows: one wavefront per row
 //   [.., + ceil(n_light / NG))   light rows: one G-lane group per row, NG rows per wave
 // Bins are sorted by degree descending, so the longest items start first. A second
@@ -248,15 +249,17 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   typename K::State st;
   typename K::RowOp q;
   K::init(st);
-  if (item < B.n_chunks + B.n_medium) {
-    int row, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int row, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      row = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      row = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      row = B.medium[item - B.n_chunks];
+      row = B.medium[item - B.n_sched];
       e0 = a.indptr[row];
       e1 = a.indptr[row + 1];
     }
@@ -265,12 +268,12 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
     K::template combine<NG>(st);
     if (g != 0) return;
     if (chunk)
-      K::write_partial(a, item, r, h, st);
+      K::write_partial(a, c, r, h, st);
     else
       K::write_row(a, row, r, h, st);
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
@@ -325,7 +328,7 @@ int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
   constexpr int U = GA_UNROLL_FWD;
   constexpr int NG = kWave / G;
   const DevBins& B = a.bins;
-  const int64_t items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  const int64_t items = int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   if (items <= 0) return 0;
   const int64_t blocks = slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices);
   if (hook) hook("fwd_main", stream, 1);

@@ -11,6 +11,8 @@
 
 #include <type_traits>
 
+#include "ga_internal.h"
+
 namespace ga {
 
 constexpr int kWave = 64;
@@ -250,6 +252,13 @@ __device__ __forceinline__ SliceItem slice_of(int S) {
   const int blk = (blockIdx.x >> 3) * q + x % q;
   return {wave_uniform(x / q), wave_uniform(blk * kWavesPerBlock + wave)};
 }
+// Chunk run by chunk slot `slot` (< B.n_sched): the plan's XCD schedule when it has one
+// (-1 marks an unused slot), else the chunk of the same index.
+__device__ __forceinline__ int chunk_of(const DevBins& B, int slot) {
+  return B.sched ? wave_uniform(B.sched[slot]) : slot;
+}
+static_assert(kWavesPerBlock == kWavesPerSlotBlock, "chunk schedules assume 4-wave blocks");
+
 inline int64_t slice_blocks(int64_t blocks_per_slice, int S) {
   if (S == 1) return blocks_per_slice;
   const int q = 8 / S;

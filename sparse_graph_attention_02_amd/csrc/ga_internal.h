@@ -11,11 +11,17 @@
 
 namespace ga {
 
+// L2 partitions (XCDs) of the GPU; workgroups are dealt to them round-robin by id. Waves
+// per workgroup of the kernels that run scheduled chunk slots (kWavesPerBlock on device).
+constexpr int kXcds = 8;
+constexpr int kWavesPerSlotBlock = 4;
+
 // One degree-binned view of a CSR-like structure (the CSR itself, or its transpose).
 struct Bins {
   std::vector<int32_t> light, medium, hub;               // ids, degree desc / id asc
   std::vector<int32_t> chunk_row, chunk_begin, chunk_end;  // hub chunks, hub by hub
   std::vector<int32_t> hub_chunk_ptr;                      // [n_hub + 1]
+  std::vector<int32_t> sched;  // dispatch slot -> chunk id or -1 (empty: slot = chunk id)
 };
 
 // Device pointers of one Bins (into the caller's plan buffer).
@@ -27,7 +33,9 @@ struct DevBins {
   const int32_t* chunk_begin = nullptr;
   const int32_t* chunk_end = nullptr;
   const int32_t* hub_chunk_ptr = nullptr;
+  const int32_t* sched = nullptr;  // null: chunk slots run in chunk order
   int32_t n_light = 0, n_medium = 0, n_hub = 0, n_chunks = 0;
+  int32_t n_sched = 0;  // chunk slots: sched's length, or n_chunks without it
 };
 
 }  // namespace ga

@@ -48,11 +48,22 @@ void order_by_degree(const std::vector<int32_t>& ptr, std::vector<int32_t>* orde
 }
 
 // Rows of `ptr` binned by degree; each bin lists ids by degree descending, ties by id.
-void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins* b,
+// A hub is a row above the hub threshold or, when split > 0, above split. Rows above split
+// are regrouped in place: their entries of `key` (and of `comp`, when given, in step) are
+// stably ordered by key mod kXcds, and each nonempty group is chunked on its own, so every
+// chunk of such a row reads the sources of one partition. sched then deals the chunks to
+// dispatch slots: a slot s runs in workgroup s / kWavesPerSlotBlock, and workgroup w lands
+// on XCD w mod kXcds, so partition p's chunks go to slots of workgroups w = p (mod kXcds);
+// chunks of unsplit hubs are dealt to the partitions in turn. Within a partition chunks
+// run longest first (ties by chunk id); unused slots hold -1. sched stays empty when no
+// row is split.
+void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, int32_t split,
+                   std::vector<int32_t>* key, std::vector<int32_t>* comp, Bins* b,
                    int64_t* max_deg) {
   std::vector<int32_t> order;
   order_by_degree(ptr, &order, max_deg);
   auto deg = [&](int32_t i) { return ptr[i + 1] - ptr[i]; };
+  auto is_split = [&](int32_t d) { return split > 0 && d > split; };
   b->light.clear();
   b->medium.clear();
   b->hub.clear();
@@ -60,7 +71,7 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins*
     const int32_t d = deg(i);
     if (d <= o.light_max_deg)
       b->light.push_back(i);
-    else if (d <= o.hub_min_deg_exclusive)
+    else if (d <= o.hub_min_deg_exclusive && !is_split(d))
       b->medium.push_back(i);
     else
       b->hub.push_back(i);
@@ -68,16 +79,60 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, Bins*
   b->chunk_row.clear();
   b->chunk_begin.clear();
   b->chunk_end.clear();
+  b->sched.clear();
   b->hub_chunk_ptr.assign(1, 0);
-  for (int32_t i : b->hub) {
-    const int64_t beg = ptr[i], end = ptr[i + 1];
+  std::vector<int32_t> tk, tc;
+  std::vector<int8_t> part;  // per chunk: its partition, or -1 (unsplit hub)
+  auto cut = [&](int32_t row, int64_t beg, int64_t end, int8_t p) {
     for (int64_t s = beg; s < end; s += o.hub_chunk) {
-      b->chunk_row.push_back(i);
+      b->chunk_row.push_back(row);
       b->chunk_begin.push_back(static_cast<int32_t>(s));
       b->chunk_end.push_back(static_cast<int32_t>(std::min<int64_t>(s + o.hub_chunk, end)));
+      part.push_back(p);
+    }
+  };
+  for (int32_t i : b->hub) {
+    const int64_t beg = ptr[i], end = ptr[i + 1];
+    if (!is_split(deg(i))) {
+      cut(i, beg, end, -1);
+    } else {
+      int64_t at[kXcds + 1] = {0};
+      for (int64_t k = beg; k < end; ++k) at[((*key)[k] & (kXcds - 1)) + 1]++;
+      for (int p = 0; p < kXcds; ++p) at[p + 1] += at[p];
+      const int64_t n = end - beg;
+      tk.resize(static_cast<size_t>(n));
+      if (comp) tc.resize(static_cast<size_t>(n));
+      int64_t fill[kXcds];
+      for (int p = 0; p < kXcds; ++p) fill[p] = at[p];
+      for (int64_t k = beg; k < end; ++k) {
+        const int64_t t = fill[(*key)[k] & (kXcds - 1)]++;
+        tk[t] = (*key)[k];
+        if (comp) tc[t] = (*comp)[k];
+      }
+      std::copy(tk.begin(), tk.end(), key->begin() + beg);
+      if (comp) std::copy(tc.begin(), tc.end(), comp->begin() + beg);
+      for (int p = 0; p < kXcds; ++p) cut(i, beg + at[p], beg + at[p + 1], static_cast<int8_t>(p));
     }
     b->hub_chunk_ptr.push_back(static_cast<int32_t>(b->chunk_row.size()));
   }
+  if (std::find_if(part.begin(), part.end(), [](int8_t p) { return p >= 0; }) == part.end())
+    return;
+  std::vector<int32_t> q[kXcds];
+  int64_t turn = 0;
+  for (size_t c = 0; c < part.size(); ++c)
+    q[part[c] >= 0 ? part[c] : (turn++ % kXcds)].push_back(static_cast<int32_t>(c));
+  size_t blocks = 0;
+  for (auto& v : q) {
+    std::stable_sort(v.begin(), v.end(), [&](int32_t x, int32_t y) {
+      return b->chunk_end[x] - b->chunk_begin[x] > b->chunk_end[y] - b->chunk_begin[y];
+    });
+    blocks = std::max(blocks, (v.size() + kWavesPerSlotBlock - 1) / kWavesPerSlotBlock);
+  }
+  b->sched.assign(blocks * kXcds * kWavesPerSlotBlock, -1);
+  for (int p = 0; p < kXcds; ++p)
+    for (size_t k = 0; k < q[p].size(); ++k)
+      b->sched[((k / kWavesPerSlotBlock) * kXcds + p) * kWavesPerSlotBlock +
+               k % kWavesPerSlotBlock] = q[p][k];
 }
 
 // Threads for the transpose: up to 16, one when the graph is small; fewer when the
@@ -179,7 +234,12 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
   if (!indptr || (e > 0 && !indices)) return GA_ERR_INVALID_ARG;
   if (given.light_max_deg < 0 || given.hub_min_deg_exclusive < -1 || given.hub_chunk < -1 ||
       given.hub_chunk == 0 || given.col_hub_min_deg_exclusive < -1 ||
-      given.col_hub_chunk < -1 || given.col_hub_chunk == 0)
+      given.col_hub_chunk < -1 || given.col_hub_chunk == 0 ||
+      given.xcd_split_min_deg_exclusive < 0 || given.col_xcd_split_min_deg_exclusive < 0 ||
+      (given.xcd_split_min_deg_exclusive > 0 &&
+       given.xcd_split_min_deg_exclusive < given.light_max_deg) ||
+      (given.col_xcd_split_min_deg_exclusive > 0 &&
+       given.col_xcd_split_min_deg_exclusive < given.light_max_deg))
     return GA_ERR_INVALID_ARG;
   const ga_plan_opts o = resolve_opts(given, e);
   if (o.hub_min_deg_exclusive < o.light_max_deg || o.col_hub_min_deg_exclusive < o.light_max_deg)
@@ -200,7 +260,6 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
     p->opts = o;
     p->indptr.assign(indptr, indptr + n + 1);
     p->indices.assign(indices, indices + e);
-    bin_by_degree(p->indptr, o, &p->rows, &p->max_in);
     p->rows_sorted = true;
     for (int64_t i = 0; i < n && p->rows_sorted; ++i)
       for (int32_t k = indptr[i] + 1; k < indptr[i + 1]; ++k)
@@ -208,6 +267,9 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
           p->rows_sorted = false;
           break;
         }
+    // regroups split rows of p->indices; the transpose below is of that CSR
+    bin_by_degree(p->indptr, o, o.xcd_split_min_deg_exclusive, &p->indices, nullptr, &p->rows,
+                  &p->max_in);
     p->has_csc = o.build_csc != 0;
     p->max_out = 0;
     if (p->has_csc) {
@@ -220,7 +282,8 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
       ga_plan_opts oc = o;  // the transpose's columns use their own hub threshold / chunk
       oc.hub_min_deg_exclusive = o.col_hub_min_deg_exclusive;
       oc.hub_chunk = o.col_hub_chunk;
-      bin_by_degree(p->colptr, oc, &p->cols, &p->max_out);
+      bin_by_degree(p->colptr, oc, o.col_xcd_split_min_deg_exclusive, &p->rowidx, &p->csc_rel,
+                    &p->cols, &p->max_out);
     } else {
       p->colptr.clear();
       p->rowidx.clear();

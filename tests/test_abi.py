@@ -63,7 +63,7 @@ def test_bad_graphs_are_rejected(ip, ix):
 
 def test_bad_opts_are_rejected():
     # fields: light, hub threshold, hub chunk, build_csc, feature_slices, column hub
-    # threshold, column hub chunk
+    # threshold, column hub chunk, row / column XCD split thresholds
     assert _create([0, 1], [0], capi.ga_plan_opts(1, 4, 8, 1, 0, 4, 8))[0] == capi.GA_OK
     assert _create([0, 1], [0], capi.ga_plan_opts(1, -1, -1, 1, 0, -1, -1))[0] == capi.GA_OK
     for bad in [(5, 4, 16, 1, 0, 8, 8),       # light > hub threshold
@@ -74,7 +74,10 @@ def test_bad_opts_are_rejected():
                 (1, 4, 8, 1, 0, 4, 0),        # column chunk 0
                 (1, -4, 8, 1, 0, 4, 8),       # hub threshold below -1
                 (1, 4, 8, 1, 3, 4, 8),        # feature slices not a power of two
-                (1, 4, 8, 1, 16, 4, 8)]:      # too many feature slices
+                (1, 4, 8, 1, 16, 4, 8),       # too many feature slices
+                (4, 8, 8, 1, 0, 8, 8, 2, 0),  # split threshold below light
+                (4, 8, 8, 1, 0, 8, 8, 0, 3),  # column split threshold below light
+                (4, 8, 8, 1, 0, 8, 8, -1, 0)]:  # negative split threshold
         assert _create([0, 1], [0], capi.ga_plan_opts(*bad))[0] == capi.GA_ERR_INVALID_ARG, bad
     assert capi.raw_status("graph_attn_plan_create", None, None, 0, 0, None, None) == \
         capi.GA_ERR_INVALID_ARG
@@ -438,3 +441,15 @@ def test_missing_library_fails_loudly():
                        text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("raised:") and "missing" in r.stdout, r.stdout
+
+
+def test_reduce_refuses_xcd_split_plans():
+    """A plan that regroups rows or columns by XCD has edge positions that are not the
+    caller's, so the reduction (whose slots are row positions) refuses it."""
+    ip, ix = gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=5_000)
+    for xs, cxs in [(32, 0), (0, 32), (32, 32)]:
+        p = Plan(ip, ix, xcd_split_min_deg_exclusive=xs, col_xcd_split_min_deg_exclusive=cxs)
+        assert _rfwd(p) == capi.GA_ERR_UNSUPPORTED
+        assert _rbwd(p) == capi.GA_ERR_UNSUPPORTED
+    q = Plan(ip, ix)
+    assert _rfwd(q) != capi.GA_ERR_UNSUPPORTED   # not uploaded: a different refusal

@@ -100,3 +100,57 @@ def test_cpp_planner_column_thresholds(name, g, tl, th, c, cth, cc):
     for nm in _names():
         want = {"indptr": ip, "indices": ix}.get(nm, ref.get(nm))
         assert np.array_equal(p.array(nm), np.asarray(want, np.int32)), nm
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("tl,th,c,xs,cxs", [(16, 8192, 2048, 64, 64), (4, 64, 16, 8, 100),
+                                            (2, 3, 2, 2, 0), (0, 1000, 7, 0, 5),
+                                            (8, 16, 1, 300, 40)])
+def test_cpp_planner_xcd_split(name, g, tl, th, c, xs, cxs):
+    """Rows / columns regrouped by neighbour id mod 8, chunked per group and scheduled to
+    XCD slots: every array identical to the reference planner's."""
+    ip, ix = g
+    ref = P.plan(ip, ix, tl, th, c, build_csc=True, xcd_split=xs, col_xcd_split=cxs)
+    p = Plan(ip, ix, light_max_deg=tl, hub_min_deg_exclusive=th, hub_chunk=c,
+             xcd_split_min_deg_exclusive=xs, col_xcd_split_min_deg_exclusive=cxs)
+    for nm in _names():
+        assert np.array_equal(p.array(nm), np.asarray(ref[nm], np.int32)), nm
+    info = p.info()
+    assert info["n_row_sched"] == ref["row_sched"].size
+    assert info["n_col_sched"] == ref["col_sched"].size
+
+
+def test_xcd_split_invariants():
+    """What the split must keep, checked on the library's plan directly: each row's
+    neighbour multiset; each split chunk draws from one partition; the schedule runs every
+    chunk exactly once and puts partition p's chunks in workgroups w = p (mod 8); the
+    transpose is the transpose of the regrouped CSR."""
+    ip, ix = gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=30_000)
+    xs = 40
+    p = Plan(ip, ix, light_max_deg=8, hub_min_deg_exclusive=512, hub_chunk=128,
+             xcd_split_min_deg_exclusive=xs)
+    pix = p.array("indices")
+    deg = np.diff(ip)
+    for i in range(ip.size - 1):
+        a, b = ip[i], ip[i + 1]
+        assert np.array_equal(np.sort(pix[a:b]), np.sort(ix[a:b]))
+        if deg[i] <= xs:
+            assert np.array_equal(pix[a:b], ix[a:b])
+    cr, cb, ce = p.array("row_chunk_row"), p.array("row_chunk_begin"), p.array("row_chunk_end")
+    sched = p.array("row_sched")
+    assert sched.size % 32 == 0 and sched.size > 0
+    run = sched[sched >= 0]
+    assert np.array_equal(np.sort(run), np.arange(cr.size))
+    for slot, c in enumerate(sched):
+        if c < 0 or deg[cr[c]] <= xs:
+            continue
+        parts = np.unique(pix[cb[c]:ce[c]] % 8)
+        assert parts.size == 1 and parts[0] == (slot // 4) % 8
+    colptr, rowidx = P.transpose(ip, pix)
+    assert np.array_equal(p.array("colptr"), colptr)
+    # columns follow the row split threshold; their groups hold destinations of one class
+    cpix = p.array("rowidx")
+    for j in np.flatnonzero(np.diff(colptr) > xs)[:50]:
+        a, b = colptr[j], colptr[j + 1]
+        assert np.array_equal(np.sort(cpix[a:b]), np.sort(rowidx[a:b]))
+        assert np.all(np.diff(cpix[a:b] % 8) >= 0)
