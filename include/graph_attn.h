@@ -97,9 +97,10 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * columns: destinations by id mod 8), each group chunked separately, and the chunks are
  * scheduled so that group p runs on the XCD whose workgroups have id = p mod 8. Each XCD's
  * 4 MB L2 then holds hot rows of one eighth of the nodes instead of all of them. The
- * forward (every score), the dot backward's dQ and dK/dV passes run this schedule; the
- * other backward passes stay correct on such a plan without it. Their main kernels run
- * unsliced on a split plan (feature_slices does not apply to them). Results agree with
+ * forward (every score), the dot backward's dQ and dK/dV passes, both GAT-style backward
+ * passes and the GATv2 column pass run this schedule; the GATv2 row pass runs the chunks
+ * in order. The forward and dQ pass run unsliced on a split plan (feature_slices does not
+ * apply to them). Results agree with
  * an unsplit plan to rounding (the sum order within a row changes). The min/max
  * reduction, whose slots are row positions, refuses split plans (GA_ERR_UNSUPPORTED).
  * Constraints: light_max_deg >= 0; an explicit threshold >= light_max_deg; an explicit

@@ -182,15 +182,17 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_rows_main(BwdArgs
   const DevBins& B = a.rows;
   typename K::raw_t dor;
   float si, lse2, A = 0.f, Bg = 0.f, D = 0.f, Lp = 0.f;
-  if (item < B.n_chunks + B.n_medium) {
-    int row, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int row, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      row = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      row = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      row = B.medium[item - B.n_chunks];
+      row = B.medium[item - B.n_sched];
       e0 = a.indptr[row];
       e1 = a.indptr[row + 1];
     }
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_rows_main(BwdArgs
     if (g != 0) return;
     if (chunk) {
       if (r % LH == 0) {
-        float* p = a.ws_dq + static_cast<size_t>(item) * K::kRowStride;
+        float* p = a.ws_dq + static_cast<size_t>(c) * K::kRowStride;
         st_stream(p + h, A);
         st_stream(p + K::H + h, Bg);
         st_stream(p + 2 * K::H + h, D);
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_rows_main(BwdArgs
     }
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
@@ -264,15 +266,17 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_cols_main(BwdArgs
   typename K::acc_t dt = 0, dv[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) dv[c] = 0;
-  if (item < B.n_chunks + B.n_medium) {
-    int col, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int col, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      col = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      col = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      col = B.medium[item - B.n_chunks];
+      col = B.medium[item - B.n_sched];
       e0 = a.colptr[col];
       e1 = a.colptr[col + 1];
     }
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_cols_main(BwdArgs
     K::template group_sum<NG>(dv);
     if (g != 0) return;
     if (chunk) {
-      float* p = a.ws_dkv + static_cast<size_t>(item) * K::kColStride;
+      float* p = a.ws_dkv + static_cast<size_t>(c) * K::kColStride;
       K::store_f32(p, r, dv);
       if (r % LH == 0) st_stream(p + F + h, static_cast<float>(dt));
     } else {
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gat_cols_main(BwdArgs
     }
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
@@ -331,7 +335,7 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   constexpr int NG = kWave / G;
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto items_of = [](const DevBins& B) {
-    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+    return int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   };
   auto go = [&](const char* name, auto kernel, int64_t blocks) -> int {
     if (blocks <= 0) return 0;

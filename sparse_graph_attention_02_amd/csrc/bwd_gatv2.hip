@@ -43,6 +43,19 @@ constexpr int kItemsPerWave = 16;  // row-pass work items per wavefront (bounds 
 #define GA_GV2_COL_ITEMS 4
 #endif
 constexpr int kColItemsPerWave = GA_GV2_COL_ITEMS;
+// Column-pass waves W for `items` work items. With an XCD schedule W is a multiple of
+// kXcds * kWavesPerBlock, so that item k W + w runs on the XCD of slot w, the XCD its
+// scheduled chunk belongs to; the snake order's mirror then reverses whole groups of that
+// many waves, which keeps every wave's XCD.
+__host__ __device__ inline int64_t gv2_col_waves(int64_t items, bool sched) {
+  constexpr int64_t q = kXcds * kWavesPerBlock;
+  const int64_t w = (items + kColItemsPerWave - 1) / kColItemsPerWave;
+  return sched ? (w + q - 1) / q * q : w;
+}
+__host__ __device__ inline int64_t gv2_col_mirror(int64_t w, int64_t W, bool sched) {
+  constexpr int64_t q = kXcds * kWavesPerBlock;
+  return sched ? (W / q - 1 - w / q) * q + w % q : W - 1 - w;
+}
 constexpr int kReduceFan = 32;     // rows summed per block in each da reduction stage
 // Edges in flight per lane group in the row pass, as many as keep the kernel within 128
 // VGPRs (4 waves per SIMD) without spills: 5 for rows of at most 32 lanes with heads of at
@@ -395,7 +408,9 @@ __global__ __launch_bounds__(kBlock) void bwd_gatv2_da_reduce(const S* __restric
 }
 
 // Column pass, dealt like the row pass: wave w of W runs kColItemsPerWave items in snake
-// order; block b writes its waves' dattn partial to slot slot0 + b.
+// order; block b writes its waves' dattn partial to slot slot0 + b. Chunk items are slots
+// of the plan's XCD schedule when it has one (see gv2_col_waves); the row pass runs its
+// chunks in chunk order (it is bound by arithmetic, not by L2).
 template <typename T, int G, int LH, int U>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdArgs a,
                                                                        int64_t slot0) {
@@ -405,8 +420,9 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
   const int wave = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.cols;
-  const int64_t n_items = int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
-  const int64_t W = (n_items + kColItemsPerWave - 1) / kColItemsPerWave;
+  const bool sched = B.sched != nullptr;
+  const int64_t n_items = int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+  const int64_t W = gv2_col_waves(n_items, sched);
   // Each wave's dattn sum lives in LDS, one column of [VEC][64] per lane (touched once per
   // item, so the edge loop keeps its registers); the block's waves are summed at the end
   // into one partial per block.
@@ -418,21 +434,23 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
   for (int c = 0; c < VEC; ++c) da[c * kWave] = 0;
   // waves of the last block past wave W-1 take no item but still join the block sum
   for (int k = 0; k < kColItemsPerWave && wave < W; ++k) {
-    const int64_t item = int64_t(k) * W + ((k & 1) ? W - 1 - wave : wave);
+    const int64_t item = int64_t(k) * W + ((k & 1) ? gv2_col_mirror(wave, W, sched) : wave);
     if (item >= n_items) continue;
     float xs[VEC];
     typename K::acc_t C1[VEC], C2[VEC];
 #pragma unroll
     for (int c = 0; c < VEC; ++c) C1[c] = C2[c] = 0;
-    if (item < B.n_chunks + B.n_medium) {
-      int col, e0, e1;
-      const bool chunk = item < B.n_chunks;
+    if (item < B.n_sched + B.n_medium) {
+      int col, e0, e1, c = 0;
+      const bool chunk = item < B.n_sched;
       if (chunk) {
-        col = B.chunk_row[item];
-        e0 = B.chunk_begin[item];
-        e1 = B.chunk_end[item];
+        c = chunk_of(B, static_cast<int>(item));
+        if (c < 0) continue;  // unused slot of an XCD schedule
+        col = B.chunk_row[c];
+        e0 = B.chunk_begin[c];
+        e1 = B.chunk_end[c];
       } else {
-        col = B.medium[item - B.n_chunks];
+        col = B.medium[item - B.n_sched];
         e0 = a.colptr[col];
         e1 = a.colptr[col + 1];
       }
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
       K::template group_sum<NG>(C2);
       if (g == 0) {
         if (chunk) {
-          float* p = a.ws_dkv + static_cast<size_t>(item) * K::kColStride;
+          float* p = a.ws_dkv + static_cast<size_t>(c) * K::kColStride;
           K::store_f32(p, r, C1);
           K::store_f32(p + F, r, C2);
         } else {
@@ -452,7 +470,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_cols_main(BwdAr
         }
       }
     } else {
-      const int64_t li = (item - B.n_chunks - B.n_medium) * NG + g;
+      const int64_t li = (item - B.n_sched - B.n_medium) * NG + g;
       if (li < B.n_light) {
         const int col = B.light[li];
         const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
@@ -525,7 +543,9 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   };
   // dattn partial slots: row waves, hub rows, column blocks, hub columns
   const int64_t row_waves = waves_of(a.rows, kItemsPerWave);
-  const int64_t col_waves = waves_of(a.cols, kColItemsPerWave);
+  const int64_t col_waves = gv2_col_waves(
+      int64_t(a.cols.n_sched) + a.cols.n_medium + (int64_t(a.cols.n_light) + NG - 1) / NG,
+      a.cols.sched != nullptr);
   const int64_t col_blocks = (col_waves + kWavesPerBlock - 1) / kWavesPerBlock;
   const int64_t slot_rh = row_waves, slot_cw = slot_rh + a.rows.n_hub;
   const int64_t slot_ch = slot_cw + col_blocks, n_slots = slot_ch + a.cols.n_hub;
@@ -617,8 +637,12 @@ int64_t gatv2_da_slots(const ga_plan* p, const Geometry& g) {
                           (int64_t(b.light.size()) + NG - 1) / NG;
     return (items + per_wave - 1) / per_wave;
   };
-  const int64_t col_blocks = (waves(p->cols, kColItemsPerWave) + kWavesPerBlock - 1) /
-                             kWavesPerBlock;
+  const Bins& c = p->cols;
+  const int64_t col_items =
+      int64_t(c.sched.empty() ? c.chunk_row.size() : c.sched.size()) + int64_t(c.medium.size()) +
+      (int64_t(c.light.size()) + NG - 1) / NG;
+  const int64_t col_blocks =
+      (gv2_col_waves(col_items, !c.sched.empty()) + kWavesPerBlock - 1) / kWavesPerBlock;
   return waves(p->rows, kItemsPerWave) + int64_t(p->rows.hub.size()) + col_blocks +
          int64_t(p->cols.hub.size());
 }

@@ -394,6 +394,20 @@ def test_no_edge_sized_allocation():
 
 # ------------------------------------------------------------------ full workload sizes
 
+# Plans of the full-size tests: the library default, and the XCD split bench.py uses for
+# the attention workloads (rows above 256 and columns above 1024 edges regrouped)
+FULL_PLANS = [pytest.param({}, id="default-plan"),
+              pytest.param(dict(xcd_split_min_deg_exclusive=256,
+                                col_xcd_split_min_deg_exclusive=1024), id="bench-split-plan")]
+
+
+def test_full_plans_match_the_bench():
+    import bench
+    assert FULL_PLANS[1].values[0] == dict(
+        xcd_split_min_deg_exclusive=bench.XCD_SPLIT_ROWS,
+        col_xcd_split_min_deg_exclusive=bench.XCD_SPLIT_COLS)
+
+
 def _sample_rows(ip, rng, k=256):
     deg = np.diff(ip)
     top = np.argsort(-deg, kind="stable")[:8]
@@ -402,37 +416,42 @@ def _sample_rows(ip, rng, k=256):
 
 
 @pytest.mark.slow
-def test_full_chunglu1m_bf16_forward_sampled():
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_chunglu1m_bf16_forward_sampled(plan_kw):
     w = gg.WORKLOADS["chunglu1m_dot_bf16"]
     ip, ix = gg.make_graph(w)
     q, k, v = gg.make_features(w)
     rows = _sample_rows(ip, np.random.default_rng(3))
-    fwd_parity("full chunglu1m bf16 dot (sampled rows)", ip, ix, q, k, v, "bf16", rows=rows)
+    fwd_parity("full chunglu1m bf16 dot (sampled rows)", ip, ix, q, k, v, "bf16", rows=rows,
+               build_csc=False, **plan_kw)
 
 
 @pytest.mark.slow
-def test_full_rmat21_bf16_forward_sampled():
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_rmat21_bf16_forward_sampled(plan_kw):
     w = gg.WORKLOADS["rmat21_dot_bf16"]
     ip, ix = gg.make_graph(w)
     q, k, v = gg.make_features(w)
     rows = _sample_rows(ip, np.random.default_rng(4))
     plan, *_ = fwd_parity("full rmat21 bf16 dot (sampled rows)", ip, ix, q, k, v, "bf16",
-                          rows=rows)
+                          rows=rows, build_csc=False, **plan_kw)
     assert plan.info()["max_in_degree"] > 100_000
 
 
 @pytest.mark.slow
-def test_full_chunglu100k_gat_f32_default_plan():
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_chunglu100k_gat_f32_forward_sampled(plan_kw):
     w = gg.WORKLOADS["chunglu100k_gat_f32"]
     ip, ix = gg.make_graph(w)
     s, t, v = gg.make_features(w)
     rows = _sample_rows(ip, np.random.default_rng(5), k=2000)
     fwd_parity("full chunglu100k gat (sampled rows)", ip, ix, s, t, v, "f32", score="gat",
-               scale=1.0, rows=rows)
+               scale=1.0, rows=rows, build_csc=False, **plan_kw)
 
 
 @pytest.mark.slow
-def test_full_chunglu1m_training_step_sampled():
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_chunglu1m_training_step_sampled(plan_kw):
     w = gg.WORKLOADS["chunglu1m_train_bf16"]
     ip, ix = gg.make_graph(w)
     q, k, v = gg.make_features(w)
@@ -442,8 +461,12 @@ def test_full_chunglu1m_training_step_sampled():
     odeg = np.bincount(ix, minlength=w.n)
     cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3],
                            np.flatnonzero(odeg == 1)[:4], rng.choice(w.n, 48, replace=False)])
-    bwd_case("full chunglu1m training step (sampled rows/cols)", ip, ix, q, k, v, dout, "bf16",
-             rows=rows, cols=cols)
+    plan, r = bwd_case("full chunglu1m training step (sampled rows/cols)", ip, ix, q, k, v,
+                       dout, "bf16", rows=rows, cols=cols, **plan_kw)
+    ro, rl = A.forward_rows(ip, ix, q, k, v, rows, "dot", f32(1 / math.sqrt(w.dim)))
+    rt = torch.from_numpy(rows).cuda()
+    check("full chunglu1m training step out", host64(r[0][rt]), ro, "bf16")
+    check_lse("full chunglu1m training step lse", host64(r[1][rt]), rl)
 
 
 def test_gather_probe_runs_on_the_plan_graph():
@@ -539,9 +562,11 @@ def test_gat_backward_deterministic():
 
 
 @pytest.mark.slow
-def test_full_chunglu100k_gat_backward_sampled():
-    """The GAT training step as the bench runs it (same graph, features, dOut and default
-    plan): ds on sampled rows, dt and dV on sampled columns including the top hubs."""
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_chunglu100k_gat_backward_sampled(plan_kw):
+    """The GAT training step as the bench runs it (same graph, features, dOut; the default
+    and the bench's split plan): ds on sampled rows, dt and dV on sampled columns including
+    the top hubs."""
     w = gg.WORKLOADS["chunglu100k_gat_train_f32"]
     ip, ix = gg.make_graph(w)
     s, t, v = gg.make_features(w)
@@ -551,7 +576,7 @@ def test_full_chunglu100k_gat_backward_sampled():
     odeg = np.bincount(ix, minlength=w.n)
     cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3], rng.choice(w.n, 200, replace=False)])
     gat_bwd_case("full chunglu100k gat bwd (sampled)", ip, ix, s, t, v, do, "f32", rows=rows,
-                 cols=cols)
+                 cols=cols, **plan_kw)
 
 
 # ------------------------------------------------------------------ GATv2
@@ -708,9 +733,10 @@ def test_full_chunglu100k_gatv2_backward_sampled():
 
 
 @pytest.mark.slow
-def test_full_chunglu1m_gatv2_training_step_sampled():
-    """The GATv2 training step at full size in the bench's launch configuration (default
-    plan): forward and dxd on sampled rows (top hubs, single-neighbour rows, random rows),
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_full_chunglu1m_gatv2_training_step_sampled(plan_kw):
+    """The GATv2 training step at full size (the default plan and the bench's split plan):
+    forward and dxd on sampled rows (top hubs, single-neighbour rows, random rows),
     dxs on sampled columns, against the oracle; dattn, a sum over all 51M edges that the
     oracle cannot form here, by linearity: doubling dout doubles every gradient exactly."""
     from sparse_graph_attention_02_amd import bwd_gatv2, fwd_gatv2
@@ -718,8 +744,8 @@ def test_full_chunglu1m_gatv2_training_step_sampled():
     ip, ix = gg.make_graph(w)
     xd, xs, a = gg.make_features(w)
     do = gg.make_dout(w)
-    say("full chunglu1m gatv2 training step (sampled)", "E", ix.size)
-    plan = Plan(ip, ix).upload()
+    say("full chunglu1m gatv2 training step (sampled)", "E", ix.size, plan_kw)
+    plan = Plan(ip, ix, **plan_kw).upload()
     txd, txs, ta, td = dev(xd), dev(xs), dev(a), dev(do)
     out, lse = fwd_gatv2(plan, txd, txs, ta)
     dxd, dxs, da = bwd_gatv2(plan, txd, txs, ta, td, lse)

@@ -1,8 +1,8 @@
 """GPU parity on plans that regroup long rows / columns by neighbour id mod 8 and schedule
 their chunks to the matching XCD (xcd_split_min_deg_exclusive): the dot forward and
 backward, the GAT-style and GATv2 layers, against the fp64 oracle on the caller's CSR
-(the regrouping must not change results beyond rounding); full size in the bench's split
-configuration on sampled rows and columns.
+(the regrouping must not change results beyond rounding). The full-size cases in the
+bench's split configuration are in test_gpu_parity.py (FULL_PLANS).
 """
 import math
 
@@ -14,7 +14,7 @@ import graphgen as gg
 from oracle import attention as A
 from sparse_graph_attention_02_amd import Plan, bwd, fwd
 from tests.gpu_util import check, check_lse, dev, host64
-from tests.test_gpu_parity import (GEOMS, _sample_rows, bwd_case, f32, fwd_parity,
+from tests.test_gpu_parity import (GEOMS, bwd_case, f32, fwd_parity,
                                    gat_bwd_case, gatv2_bwd_case, say)
 
 pytestmark = pytest.mark.gpu
@@ -147,42 +147,3 @@ def test_split_agrees_with_unsplit_and_is_deterministic():
         rms = r.pow(2).mean().sqrt()
         tol = 1e-5 + 1e-4 * r.abs() if name == "lse" else 2e-2 * torch.maximum(r.abs(), rms)
         assert torch.all((x - r).abs() <= tol), name
-
-
-@pytest.mark.slow
-def test_full_chunglu1m_training_step_split_sampled():
-    """The 1M-node training step in the bench's split configuration (rows above 256 and
-    columns above 1024 edges regrouped), on sampled rows and columns against the oracle."""
-    import bench
-    w = gg.WORKLOADS["chunglu1m_train_bf16"]
-    ip, ix = gg.make_graph(w)
-    q, k, v = gg.make_features(w)
-    dout = gg.make_dout(w)
-    rng = np.random.default_rng(76)
-    rows = _sample_rows(ip, rng, k=128)
-    odeg = np.bincount(ix, minlength=w.n)
-    cols = np.unique(np.r_[np.argsort(-odeg, kind="stable")[:3],
-                           rng.choice(np.flatnonzero(odeg > 1024), 8, replace=False),
-                           np.flatnonzero(odeg == 1)[:4], rng.choice(w.n, 40, replace=False)])
-    plan, r = bwd_case("full chunglu1m training step, split plan (sampled rows/cols)", ip, ix,
-                       q, k, v, dout, "bf16", rows=rows, cols=cols,
-                       xcd_split_min_deg_exclusive=bench.XCD_SPLIT_ROWS,
-                       col_xcd_split_min_deg_exclusive=bench.XCD_SPLIT_COLS)
-    _fwd_ok("full chunglu1m split fwd", ip, ix, q, k, v, r[0], r[1], "bf16", rows=rows)
-    _scheduled(plan)
-
-
-@pytest.mark.slow
-def test_full_rmat21_forward_split_sampled():
-    """The R-MAT 2^21 forward (d = 128) in the bench's split configuration, on sampled rows
-    (the top hubs among them) against the oracle."""
-    import bench
-    w = gg.WORKLOADS["rmat21_dot_bf16"]
-    ip, ix = gg.make_graph(w)
-    q, k, v = gg.make_features(w)
-    rng = np.random.default_rng(77)
-    rows = _sample_rows(ip, rng, k=96)
-    plan, out, lse, _ = fwd_parity("full rmat21 forward, split plan (sampled rows)", ip, ix,
-                                   q, k, v, "bf16", rows=rows, build_csc=False,
-                                   xcd_split_min_deg_exclusive=bench.XCD_SPLIT_ROWS)
-    assert plan.info()["n_row_sched"] > 0
