@@ -104,7 +104,9 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * an unsplit plan to rounding (the sum order within a row changes). The min/max
  * reduction, whose slots are row positions, refuses split plans (GA_ERR_UNSUPPORTED).
  * Constraints: light_max_deg >= 0; an explicit threshold >= light_max_deg; an explicit
- * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}; a split threshold 0 or >= light_max_deg. */
+ * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}; a split threshold 0 or >= light_max_deg.
+ * A plan whose work items (scheduled chunk slots, medium and light rows) would exceed
+ * 2^31 - 1 is refused with GA_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t light_max_deg;
   int32_t hub_min_deg_exclusive;

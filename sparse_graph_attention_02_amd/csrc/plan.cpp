@@ -11,6 +11,7 @@
 // is bit-exact by construction: no floating point, and the threaded transpose writes every
 // entry where the sequential counting sort would.
 #include <algorithm>
+#include <climits>
 #include <new>
 #include <thread>
 
@@ -56,8 +57,10 @@ void order_by_degree(const std::vector<int32_t>& ptr, std::vector<int32_t>* orde
 // on XCD w mod kXcds, so partition p's chunks go to slots of workgroups w = p (mod kXcds);
 // chunks of unsplit hubs are dealt to the partitions in turn. Within a partition chunks
 // run longest first (ties by chunk id); unused slots hold -1. sched stays empty when no
-// row is split.
-void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, int32_t split,
+// row is split. Returns false when the work items (chunk slots, medium rows, light rows)
+// would not fit the kernels' 32-bit item index (a schedule can be up to 8 times longer
+// than the chunk list when one partition holds every chunk).
+bool bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, int32_t split,
                    std::vector<int32_t>* key, std::vector<int32_t>* comp, Bins* b,
                    int64_t* max_deg) {
   std::vector<int32_t> order;
@@ -115,8 +118,10 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, int32
     }
     b->hub_chunk_ptr.push_back(static_cast<int32_t>(b->chunk_row.size()));
   }
+  const size_t rest = b->medium.size() + b->light.size();
+  auto fits = [&](size_t slots) { return slots + rest <= size_t(INT32_MAX); };
   if (std::find_if(part.begin(), part.end(), [](int8_t p) { return p >= 0; }) == part.end())
-    return;
+    return fits(part.size());
   std::vector<int32_t> q[kXcds];
   int64_t turn = 0;
   for (size_t c = 0; c < part.size(); ++c)
@@ -128,11 +133,13 @@ void bin_by_degree(const std::vector<int32_t>& ptr, const ga_plan_opts& o, int32
     });
     blocks = std::max(blocks, (v.size() + kWavesPerSlotBlock - 1) / kWavesPerSlotBlock);
   }
+  if (!fits(blocks * kXcds * kWavesPerSlotBlock)) return false;
   b->sched.assign(blocks * kXcds * kWavesPerSlotBlock, -1);
   for (int p = 0; p < kXcds; ++p)
     for (size_t k = 0; k < q[p].size(); ++k)
       b->sched[((k / kWavesPerSlotBlock) * kXcds + p) * kWavesPerSlotBlock +
                k % kWavesPerSlotBlock] = q[p][k];
+  return true;
 }
 
 // Threads for the transpose: up to 16, one when the graph is small; fewer when the
@@ -268,8 +275,9 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
           break;
         }
     // regroups split rows of p->indices; the transpose below is of that CSR
-    bin_by_degree(p->indptr, o, o.xcd_split_min_deg_exclusive, &p->indices, nullptr, &p->rows,
-                  &p->max_in);
+    if (!bin_by_degree(p->indptr, o, o.xcd_split_min_deg_exclusive, &p->indices, nullptr,
+                       &p->rows, &p->max_in))
+      return GA_ERR_UNSUPPORTED;
     p->has_csc = o.build_csc != 0;
     p->max_out = 0;
     if (p->has_csc) {
@@ -282,8 +290,9 @@ ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, i
       ga_plan_opts oc = o;  // the transpose's columns use their own hub threshold / chunk
       oc.hub_min_deg_exclusive = o.col_hub_min_deg_exclusive;
       oc.hub_chunk = o.col_hub_chunk;
-      bin_by_degree(p->colptr, oc, o.col_xcd_split_min_deg_exclusive, &p->rowidx, &p->csc_rel,
-                    &p->cols, &p->max_out);
+      if (!bin_by_degree(p->colptr, oc, o.col_xcd_split_min_deg_exclusive, &p->rowidx,
+                         &p->csc_rel, &p->cols, &p->max_out))
+        return GA_ERR_UNSUPPORTED;
     } else {
       p->colptr.clear();
       p->rowidx.clear();
