@@ -57,13 +57,20 @@ def _graph(n=20_000):
     return gg.make_graph(w, n=n)
 
 
-def test_dot_training_step_captures():
+# plans: the library default, and the XCD split bench.py uses for the attention workloads
+PLANS = [pytest.param({}, id="default-plan"),
+         pytest.param(dict(xcd_split_min_deg_exclusive=256,
+                           col_xcd_split_min_deg_exclusive=1024), id="split-plan")]
+
+
+@pytest.mark.parametrize("plan_kw", PLANS)
+def test_dot_training_step_captures(plan_kw):
     ip, ix = _graph()
     n = ip.size - 1
     rng = np.random.default_rng(1)
     q, k, v, do = (dev(gg.normal_features(rng, (n, 8, 32), "bf16")) for _ in range(4))
-    say("graph capture: dot training step, N", n, "E", ix.size)
-    plan = ga.Plan(ip, ix).upload()
+    say("graph capture: dot training step, N", n, "E", ix.size, plan_kw)
+    plan = ga.Plan(ip, ix, **plan_kw).upload()
     out, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((n, 8), device="cuda")
     fws = torch.empty(max(plan.fwd_workspace_bytes(8, 32), 1), dtype=torch.uint8, device="cuda")
@@ -78,14 +85,15 @@ def test_dot_training_step_captures():
     _replays_match(step, [out, lse, dq, dk, dv], lambda: (x @ x).sum().item())
 
 
-def test_gatv2_training_step_captures():
+@pytest.mark.parametrize("plan_kw", PLANS)
+def test_gatv2_training_step_captures(plan_kw):
     ip, ix = _graph()
     n = ip.size - 1
     rng = np.random.default_rng(2)
     xd, xs, do = (dev(gg.normal_features(rng, (n, 8, 32), "bf16")) for _ in range(3))
     attn = torch.from_numpy(rng.standard_normal((8, 32)).astype(np.float32) / 6).cuda()
-    say("graph capture: GATv2 training step, N", n, "E", ix.size)
-    plan = ga.Plan(ip, ix).upload()
+    say("graph capture: GATv2 training step, N", n, "E", ix.size, plan_kw)
+    plan = ga.Plan(ip, ix, **plan_kw).upload()
     out, dxd, dxs = (torch.empty_like(xs) for _ in range(3))
     lse = torch.empty((n, 8), device="cuda")
     dattn = torch.empty((8, 32), device="cuda")

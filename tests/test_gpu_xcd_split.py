@@ -147,3 +147,20 @@ def test_split_agrees_with_unsplit_and_is_deterministic():
         rms = r.pow(2).mean().sqrt()
         tol = 1e-5 + 1e-4 * r.abs() if name == "lse" else 2e-2 * torch.maximum(r.abs(), rms)
         assert torch.all((x - r).abs() <= tol), name
+
+
+@pytest.mark.parametrize("S", [2, 8])
+def test_split_plan_overrides_feature_slices(S):
+    """On a split plan the forward and the dQ pass run unsliced whatever feature_slices
+    asks for; every result still matches the oracle."""
+    w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    n = 4000
+    ip, ix = gg.make_graph(w, n=n)
+    rng = np.random.default_rng(78 + S)
+    feats = [gg.f32_to_bf16_bits(rng.standard_normal((n, 8, 32)).astype(np.float32))
+             for _ in range(4)]
+    plan, r = bwd_case(f"split plan, feature_slices {S}", ip, ix, *feats, "bf16",
+                       light_max_deg=8, hub_min_deg_exclusive=512, hub_chunk=64,
+                       xcd_split_min_deg_exclusive=24, feature_slices=S)
+    _fwd_ok(f"split plan, feature_slices {S}", ip, ix, *feats[:3], r[0], r[1], "bf16")
+    _scheduled(plan)
