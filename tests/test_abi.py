@@ -453,3 +453,26 @@ def test_reduce_refuses_xcd_split_plans():
         assert _rbwd(p) == capi.GA_ERR_UNSUPPORTED
     q = Plan(ip, ix)
     assert _rfwd(q) != capi.GA_ERR_UNSUPPORTED   # not uploaded: a different refusal
+
+
+def test_xcd_split_defaults_and_info():
+    """The split is off by default; a split plan reports its thresholds and schedule sizes
+    (multiples of 8 XCDs x 4 wavefronts), and the workspace formulas follow its chunks."""
+    from sparse_graph_attention_02_amd import default_opts
+    d = default_opts()
+    assert d["xcd_split_min_deg_exclusive"] == 0 and d["col_xcd_split_min_deg_exclusive"] == 0
+    ip, ix = gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=5_000)
+    plain = Plan(ip, ix).info()
+    assert plain["n_row_sched"] == 0 and plain["n_col_sched"] == 0
+    p = Plan(ip, ix, xcd_split_min_deg_exclusive=32, col_xcd_split_min_deg_exclusive=64)
+    info = p.info()
+    assert info["xcd_split_min_deg_exclusive"] == 32
+    assert info["col_xcd_split_min_deg_exclusive"] == 64
+    assert info["n_row_sched"] > 0 and info["n_row_sched"] % 32 == 0
+    assert info["n_col_sched"] > 0 and info["n_col_sched"] % 32 == 0
+    assert p.array("row_sched").size == info["n_row_sched"]
+    deg = np.diff(ip)
+    assert info["n_row_hub"] == int(np.sum(deg > 32))
+    al = lambda x: (x + 255) // 256 * 256
+    nc = info["n_row_chunks"]
+    assert p.fwd_workspace_bytes(8, 32) == al(nc * 8 * 2 * 4) + al(nc * 256 * 4)
