@@ -80,3 +80,70 @@ def test_validate_csr():
     assert not P.validate_csr(np.array([0, 2, 4]), ix)           # indptr[N] != E
     assert not P.validate_csr(ip, np.array([1, 0, 2], np.int32))  # index out of range
     assert not P.validate_csr(ip, np.array([1, -1, 0], np.int32))
+
+
+def test_xcd_split_worked_example():
+    """The reference planner's XCD split against a hand-worked example
+    (tests/golden/xcd_split_example.json)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "xcd_split_example.json")))
+    o = g["options"]
+    got = P.plan(g["indptr"], g["indices"], o["light_max_deg"], o["hub_min_deg_exclusive"],
+                 o["hub_chunk"], build_csc=False, xcd_split=o["xcd_split"])
+    for name, want in g["expected"].items():
+        assert np.array_equal(got[name], np.asarray(want, np.int32)), name
+
+
+@pytest.mark.parametrize("name,g", list(_graphs()), ids=lambda x: x if isinstance(x, str) else "")
+@pytest.mark.parametrize("xs,cxs,chunk", [(8, 8, 5), (40, 16, 1000), (2, 0, 1)])
+def test_xcd_split_invariants_of_the_reference_planner(name, g, xs, cxs, chunk):
+    """What the split must keep, on the reference planner itself: each row's and column's
+    multiset; rows / columns above the threshold are hubs grouped by residue mod 8 (stable
+    within a group) and every chunk lies inside one group; unsplit rows keep their order;
+    the schedule runs every chunk once, partition p's chunks in workgroups = p (mod 8),
+    each partition's chunks longest first; the transpose is that of the regrouped CSR."""
+    ip, ix = g
+    ip64, ix64 = np.asarray(ip, np.int64), np.asarray(ix, np.int64)
+    n = ip64.size - 1
+    out = P.plan(ip, ix, 0, 10**9, chunk, build_csc=True, xcd_split=xs, col_xcd_split=cxs)
+    for side, ptr, orig, key, thr in (("row", ip64, ix64, out["indices"], xs),
+                                      ("col", out["colptr"].astype(np.int64),
+                                       P.transpose(ip, out["indices"])[1], out["rowidx"], cxs)):
+        deg = np.diff(ptr)
+        cr, cb, ce = out[f"{side}_chunk_row"], out[f"{side}_chunk_begin"], out[f"{side}_chunk_end"]
+        part = np.full(cr.size, -1)
+        for i in range(n):
+            a, b = ptr[i], ptr[i + 1]
+            assert np.array_equal(np.sort(key[a:b]), np.sort(orig[a:b]))
+            if thr > 0 and deg[i] > thr:
+                res = key[a:b] % 8
+                assert np.all(np.diff(res) >= 0)
+                for p in range(8):      # stable: each group keeps the original order
+                    assert np.array_equal(key[a:b][res == p], orig[a:b][orig[a:b] % 8 == p])
+            else:
+                assert np.array_equal(key[a:b], orig[a:b])
+        for c in range(cr.size):
+            assert cb[c] < ce[c] <= cb[c] + chunk
+            i = cr[c]
+            assert ptr[i] <= cb[c] and ce[c] <= ptr[i + 1]
+            if thr > 0 and deg[i] > thr:
+                res = np.unique(key[cb[c]:ce[c]] % 8)
+                assert res.size == 1
+                part[c] = res[0]
+        hub = out[f"{side}_hub"]
+        assert np.array_equal(np.sort(hub), np.flatnonzero(deg > thr) if thr > 0 else hub)
+        sched = out[f"{side}_sched"]
+        if not np.any(part >= 0):
+            assert sched.size == 0
+            continue
+        assert sched.size % 32 == 0
+        assert np.array_equal(np.sort(sched[sched >= 0]), np.arange(cr.size))
+        for p in range(8):
+            slots = np.flatnonzero(np.isin(sched, np.flatnonzero(part == p)))
+            assert np.all((slots // 4) % 8 == p)
+            sizes = (ce - cb)[sched[slots]]
+            assert np.all(np.diff(sizes) <= 0)
+    colptr, rowidx = P.transpose(ip, out["indices"])
+    assert np.array_equal(out["colptr"], colptr)
