@@ -37,6 +37,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # on the 1M-node training step gave 19.19 ms unsplit, 17.54 ms at 256 / 1024, 17.71 ms at
 # 512 / 512 and 18.31 ms at 128 / 128 (chunk partials outgrow the L2 gain below ~256)
 XCD_SPLIT_ROWS, XCD_SPLIT_COLS = 256, 1024
+# the min / max reduction's chunk partials (value, id, edge) are larger, so its merge is
+# dearer: 7.85 ms unsplit, 7.56 ms at 256 / 1024, 7.40 ms at 512 / 512 on the 1M max step
+XCD_SPLIT_REDUCE = 512
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -271,11 +274,11 @@ def main():
     ap.add_argument("--xcd-split", type=int, default=None,
                     help="rows longer than this are regrouped by source id mod 8 and their "
                          "chunks scheduled to the matching XCD (0 = off; default %d for the "
-                         "attention workloads, off for the reductions, whose slots are row "
-                         "positions)" % XCD_SPLIT_ROWS)
+                         "attention workloads, %d for the reductions)"
+                         % (XCD_SPLIT_ROWS, XCD_SPLIT_REDUCE))
     ap.add_argument("--col-xcd-split", type=int, default=None,
                     help="the same for transpose columns (default %d for the attention "
-                         "workloads)" % XCD_SPLIT_COLS)
+                         "workloads, %d for the reductions)" % (XCD_SPLIT_COLS, XCD_SPLIT_REDUCE))
     ap.add_argument("--slices", type=int, default=None,
                     help="feature slices per XCD group (0 = automatic, 1 = off, 2, 4, 8)")
     ap.add_argument("--order", choices=["as-generated", "out-degree", "rcm"],
@@ -292,9 +295,10 @@ def main():
     w = gg.WORKLOADS[args.workload]
     reduction = w.score in ("max", "min")
     if args.xcd_split is None:
-        args.xcd_split = 0 if reduction else XCD_SPLIT_ROWS
+        args.xcd_split = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_ROWS
     if args.col_xcd_split is None:  # columns: at least the column default, 0 when rows are 0
-        args.col_xcd_split = 0 if args.xcd_split == 0 else max(XCD_SPLIT_COLS, args.xcd_split)
+        col_default = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_COLS
+        args.col_xcd_split = 0 if args.xcd_split == 0 else max(col_default, args.xcd_split)
     t0 = time.perf_counter()
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)

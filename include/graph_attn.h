@@ -98,11 +98,11 @@ typedef enum { GA_SCORE_DOT = 0, GA_SCORE_GAT = 1 } ga_score;
  * scheduled so that group p runs on the XCD whose workgroups have id = p mod 8. Each XCD's
  * 4 MB L2 then holds hot rows of one eighth of the nodes instead of all of them. The
  * forward (every score), the dot backward's dQ and dK/dV passes, both GAT-style backward
- * passes and the GATv2 column pass run this schedule; the GATv2 row pass runs the chunks
- * in order. The forward and dQ pass run unsliced on a split plan (feature_slices does not
- * apply to them). Results agree with
- * an unsplit plan to rounding (the sum order within a row changes). The min/max
- * reduction, whose slots are row positions, refuses split plans (GA_ERR_UNSUPPORTED).
+ * passes, the GATv2 column pass and both min/max reduction passes run this schedule; the
+ * GATv2 row pass runs the chunks in order. The scheduled passes run unsliced on a split
+ * plan (feature_slices does not apply to them). Attention results agree with an unsplit
+ * plan to rounding (the sum order within a row changes); the reduction's out and arg are
+ * identical, and its slots are positions in the plan's rows (the exported "indices").
  * Constraints: light_max_deg >= 0; an explicit threshold >= light_max_deg; an explicit
  * chunk >= 1; feature_slices in {0, 1, 2, 4, 8}; a split threshold 0 or >= light_max_deg.
  * A plan whose work items (scheduled chunk slots, medium and light rows) would exceed
@@ -298,7 +298,8 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* plan, ga_dtype dtype, int32_t head
  * row's neighbours. out[i,c] is x[arg[i,c],c] bit for bit (values compare as numbers:
  * -0 equals +0). A row with no neighbours gives out = 0 and arg = -1. Optionally the
  * forward also writes slot[i,c] = the position within row i (k - indptr[i]) of the first
- * edge of that row from arg[i,c], as unsigned 16-bit values when no row has more than
+ * edge of that row from arg[i,c], in the plan's CSR (the caller's, unless the plan has an
+ * XCD split, which regroups long rows: see graph_attn_plan_array "indices"), as unsigned 16-bit values when no row has more than
  * 65535 edges, else 32-bit (graph_attn_reduce_slot_bytes); an element without a winner
  * (an empty row) gets all ones, which no position equals. The
  * backward reads slot (2 bytes per element per transpose edge) in place of arg (4), so a

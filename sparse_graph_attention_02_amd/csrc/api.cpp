@@ -188,12 +188,6 @@ size_t reduce_bwd_ws_bytes(const ga_plan* p, int32_t features) {
   return align_up(p->cols.chunk_row.size() * size_t(features) * 4);
 }
 
-// Plans that regroup rows or columns by XCD partition: their edge positions are not the
-// caller's, so the reduction (whose slots are row positions) does not take them.
-bool split_plan(const ga_plan* p) {
-  return p->opts.xcd_split_min_deg_exclusive > 0 || p->opts.col_xcd_split_min_deg_exclusive > 0;
-}
-
 ga_status check_device(const ga_plan* p) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GA_ERR_HIP;
@@ -638,7 +632,6 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   int G = 0;
   ga_status s = reduce_geometry(dtype, features, &G);
   if (s != GA_OK) return s;
-  if (split_plan(p)) return GA_ERR_UNSUPPORTED;
   if (p->n > 0) {
     if ((s = check_ptr(x, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
         (s = check_ptr(arg, 16)) != GA_OK)
@@ -661,7 +654,7 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.rows_sorted = p->rows_sorted;
   args.ld = G;
-  args.slices = ga::feature_slices(G, 1, p->opts.feature_slices, 0);
+  args.slices = p->rows.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   if (need > 0) {
     args.ws_val = static_cast<float*>(ws);
     args.ws_idx = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 3);
@@ -680,7 +673,6 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   int G = 0;
   ga_status s = reduce_geometry(dtype, features, &G);
   if (s != GA_OK) return s;
-  if (split_plan(p)) return GA_ERR_UNSUPPORTED;
   if (p->n > 0) {
     if ((s = check_ptr(slot ? slot : static_cast<const void*>(arg), 16)) != GA_OK ||
         (s = check_ptr(dout, 16)) != GA_OK || (s = check_ptr(dx, 16)) != GA_OK)
@@ -701,7 +693,7 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   args.csc_rel = p->d_csc_rel;
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.ld = G;
-  args.slices = ga::feature_slices(G, 1, p->opts.feature_slices, 0);
+  args.slices = p->cols.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   args.dout = dout;
   args.dx = dx;
   args.ws_sum = need > 0 ? static_cast<float*>(ws) : nullptr;

@@ -221,11 +221,21 @@ struct Red : RowIO<T, G, G> {
                              static_cast<unsigned>(x[4 * k + 3])});
   }
 
+  // Chunk partials always carry the winner's id: the merge compares ids, since the chunks
+  // of a row regrouped by an XCD split are not in id order (sorted rows track only the
+  // edge, so the id is read back from the chunk's own, just-streamed, indices).
   __device__ __forceinline__ static void write_partial(const RedArgs& a, int chunk, int r,
                                                        const State& s) {
     const size_t c0 = static_cast<size_t>(chunk) * a.ld * VEC;  // partials span full rows
     IO::store_f32(a.ws_val + c0, r, s.v);
-    if constexpr (!SORTED) st_int(a.ws_idx + c0, r, s.id);
+    if constexpr (SORTED) {
+      int id[VEC];
+#pragma unroll
+      for (int c = 0; c < VEC; ++c) id[c] = s.pos[c] == INT_MAX ? kNoArg : a.indices[s.pos[c]];
+      st_int(a.ws_idx + c0, r, id);
+    } else {
+      st_int(a.ws_idx + c0, r, s.id);
+    }
     st_int(a.ws_pos + c0, r, s.pos);
   }
 
@@ -395,15 +405,17 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a0) {
   const DevBins& B = a.rows;
   typename K::State s;
   K::init(s);
-  if (item < B.n_chunks + B.n_medium) {
-    int row, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int row, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      row = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      row = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      row = B.medium[item - B.n_chunks];
+      row = B.medium[item - B.n_sched];
       e0 = a.indptr[row];
       e1 = a.indptr[row + 1];
     }
@@ -411,12 +423,12 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a0) {
     K::template combine<NG>(s);
     if (g != 0) return;
     if (chunk)
-      K::write_partial(a, item, r, s);
+      K::write_partial(a, c, r, s);
     else
       K::write_row(a, row, e0, r, s);
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row];
@@ -424,10 +436,11 @@ __global__ __launch_bounds__(kBlock) void reduce_fwd_main(RedArgs a0) {
   K::write_row(a, row, e0, r, s);
 }
 
-// One wavefront per hub row: group g folds chunks c0+g, c0+g+NG, ..., then the butterfly.
-template <typename T, int G, int OP, bool SORTED>
+// One wavefront per hub row: group g folds chunks c0+g, c0+g+NG, ..., then the butterfly,
+// always by the full (value, id, edge) rule.
+template <typename T, int G, int OP>
 __global__ __launch_bounds__(kBlock) void reduce_fwd_merge(RedArgs a) {
-  using K = Red<T, G, OP, 1, SORTED>;
+  using K = Red<T, G, OP, 1, false>;
   constexpr int NG = K::NG;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int lane = threadIdx.x & (kWave - 1);
@@ -465,15 +478,17 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a0) {
   typename K::acc_t s[VEC];
 #pragma unroll
   for (int c = 0; c < VEC; ++c) s[c] = 0;
-  if (item < B.n_chunks + B.n_medium) {
-    int col, e0, e1;
-    const bool chunk = item < B.n_chunks;
+  if (item < B.n_sched + B.n_medium) {
+    int col, e0, e1, c = 0;
+    const bool chunk = item < B.n_sched;
     if (chunk) {
-      col = B.chunk_row[item];
-      e0 = B.chunk_begin[item];
-      e1 = B.chunk_end[item];
+      c = chunk_of(B, item);
+      if (c < 0) return;  // unused slot of an XCD schedule
+      col = B.chunk_row[c];
+      e0 = B.chunk_begin[c];
+      e1 = B.chunk_end[c];
     } else {
-      col = B.medium[item - B.n_chunks];
+      col = B.medium[item - B.n_sched];
       e0 = a.colptr[col];
       e1 = a.colptr[col + 1];
     }
@@ -481,12 +496,12 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a0) {
     K::template group_sum<NG>(s);
     if (g != 0) return;
     if (chunk)
-      K::store_f32(a.ws_sum + static_cast<size_t>(item) * a.ld * VEC, r, s);
+      K::store_f32(a.ws_sum + static_cast<size_t>(c) * a.ld * VEC, r, s);
     else
       K::store(a.dx, col, r, s, 1.f, a.ld);
     return;
   }
-  const int li = (item - B.n_chunks - B.n_medium) * NG + g;
+  const int li = (item - B.n_sched - B.n_medium) * NG + g;
   if (li >= B.n_light) return;
   const int col = B.light[li];
   const int e0 = a.colptr[col], e1 = a.colptr[col + 1];
@@ -538,7 +553,7 @@ template <typename T, int G>
 int launch_main(bool backward, int op, const RedArgs& a, void* stream, TimerHook hook) {
   constexpr int NG = kWave / G;
   auto items_of = [](const DevBins& B) {
-    return int64_t(B.n_chunks) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
+    return int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   };
   if (backward) {
     const int64_t b = slice_blocks(blocks_of(items_of(a.cols)), a.slices);
@@ -574,16 +589,9 @@ int launch_merge(bool backward, int op, const RedArgs& a, void* stream, TimerHoo
     return go("reduce_bwd_merge", reduce_bwd_merge<T, G>, blocks_of(a.cols.n_hub), a, stream,
               hook);
   const int64_t b = blocks_of(a.rows.n_hub);
-  if (op == kReduceMax)
-    return a.rows_sorted
-               ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, true>, b, a, stream,
-                    hook)
-               : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax, false>, b, a, stream,
-                    hook);
-  return a.rows_sorted
-             ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin, true>, b, a, stream, hook)
-             : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin, false>, b, a, stream,
-                  hook);
+  return op == kReduceMax
+             ? go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMax>, b, a, stream, hook)
+             : go("reduce_fwd_merge", reduce_fwd_merge<T, G, kReduceMin>, b, a, stream, hook);
 }
 
 template <typename T>

@@ -443,16 +443,13 @@ def test_missing_library_fails_loudly():
     assert r.stdout.startswith("raised:") and "missing" in r.stdout, r.stdout
 
 
-def test_reduce_refuses_xcd_split_plans():
-    """A plan that regroups rows or columns by XCD has edge positions that are not the
-    caller's, so the reduction (whose slots are row positions) refuses it."""
+def test_reduce_accepts_xcd_split_plans():
+    """Split plans pass the reduction's argument checks (an upload is what is missing)."""
     ip, ix = gg.make_graph(gg.WORKLOADS["chunglu100k_gat_f32"], n=5_000)
     for xs, cxs in [(32, 0), (0, 32), (32, 32)]:
         p = Plan(ip, ix, xcd_split_min_deg_exclusive=xs, col_xcd_split_min_deg_exclusive=cxs)
-        assert _rfwd(p) == capi.GA_ERR_UNSUPPORTED
-        assert _rbwd(p) == capi.GA_ERR_UNSUPPORTED
-    q = Plan(ip, ix)
-    assert _rfwd(q) != capi.GA_ERR_UNSUPPORTED   # not uploaded: a different refusal
+        assert _rfwd(p) == capi.GA_ERR_NOT_READY
+        assert _rbwd(p) == capi.GA_ERR_NOT_READY
 
 
 def test_xcd_split_defaults_and_info():

@@ -69,7 +69,11 @@ def fwd_exact(tag, ip, ix, x, dtype, op, rows=None, **plan_kw):
     gb = bits(out[rt].reshape(len(rows), F))
     assert np.array_equal(gb, oracle_bits(ro, dtype)), f"{tag}: out bits differ"
     gs = slot_values(slot[rt].reshape(len(rows), F))
-    assert np.array_equal(gs, R.slots_of(ip, ix, rows, ra)), f"{tag}: slots differ"
+    # slots are positions in the plan's CSR (regrouped on XCD-split plans)
+    pix = plan.array("indices")
+    assert np.array_equal(np.sort(pix), np.sort(ix)) and (
+        plan.info()["n_row_sched"] > 0 or np.array_equal(pix, ix))
+    assert np.array_equal(gs, R.slots_of(ip, pix, rows, ra)), f"{tag}: slots differ"
     return plan, out, (arg, slot), ra
 
 
@@ -89,10 +93,12 @@ def bwd_parity(tag, plan, ip, ix, arg_slot, ref_arg, dout, dtype):
 
 
 SMALL_BINS = dict(light_max_deg=4, hub_min_deg_exclusive=9, hub_chunk=3)
+SPLIT_BINS = dict(light_max_deg=4, hub_min_deg_exclusive=64, hub_chunk=5,
+                  xcd_split_min_deg_exclusive=8)
 
 
 @pytest.mark.parametrize("op", ["max", "min"])
-@pytest.mark.parametrize("bins", [{}, SMALL_BINS])
+@pytest.mark.parametrize("bins", [{}, SMALL_BINS, SPLIT_BINS])
 def test_er2k_f32_every_row(op, bins):
     w = gg.WORKLOADS["er2k_dot_f32"]
     ip, ix = gg.make_graph(w)
@@ -114,6 +120,25 @@ def test_chunglu20k_bf16_every_row_and_backward(tl, th, c):
         info = plan.info()
         assert info["n_row_hub"] > 0 and info["n_col_hub"] > 0
         bwd_parity(f"chunglu20k bf16 {op}", plan, ip, ix, arg, ra, dout, "bf16")
+
+
+@pytest.mark.parametrize("xs,cxs", [(16, 16), (40, 0), (0, 24)])
+def test_chunglu20k_split_plans(xs, cxs):
+    """Forward and backward on every row and element of a plan whose long rows and / or
+    columns are regrouped by XCD: out and arg bit-exact, slots as positions in the plan's
+    CSR, dx to the float criteria."""
+    w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
+    ip, ix = gg.make_graph(w, n=20_000)
+    (x,) = gg.make_features(w, n=20_000)
+    dout = gg.make_dout(w, n=20_000)
+    for op in ("max", "min"):
+        plan, out, arg, ra = fwd_exact(f"chunglu20k split {xs}/{cxs}", ip, ix, x, "bf16", op,
+                                       light_max_deg=8, hub_min_deg_exclusive=512, hub_chunk=16,
+                                       xcd_split_min_deg_exclusive=xs,
+                                       col_xcd_split_min_deg_exclusive=cxs)
+        info = plan.info()
+        assert (info["n_row_sched"] > 0) == (xs > 0) and (info["n_col_sched"] > 0) == (cxs > 0)
+        bwd_parity(f"chunglu20k split {xs}/{cxs} {op}", plan, ip, ix, arg, ra, dout, "bf16")
 
 
 @pytest.mark.parametrize("dtype,F", [("f32", 16), ("f32", 32), ("f32", 64), ("f32", 128),
@@ -155,7 +180,9 @@ def test_ties_signed_zeros_and_infinities(dtype, order):
     xv[pick] = special[rng.integers(0, 4, pick.sum())]
     x = gg.f32_to_bf16_bits(xv) if dtype == "bf16" else xv
     for op in ("max", "min"):
-        for bins in ({}, dict(light_max_deg=2, hub_min_deg_exclusive=20, hub_chunk=7)):
+        for bins in ({}, dict(light_max_deg=2, hub_min_deg_exclusive=20, hub_chunk=7),
+                     dict(light_max_deg=2, hub_min_deg_exclusive=20, hub_chunk=7,
+                          xcd_split_min_deg_exclusive=10)):
             plan, out, arg, ra = fwd_exact(f"ties {dtype}", ip, ix, x, dtype, op, **bins)
             # backward: each parallel edge is one variable; gradient finite everywhere
             dout = gg.normal_features(rng, (n, F), dtype)
@@ -208,10 +235,15 @@ def test_deterministic_and_autograd():
 
 
 @pytest.mark.slow
-def test_full_chunglu1m_sampled():
-    """Full workload size: the forward on sampled rows (hub, medium and light), the
-    backward on sampled columns (one of them a hub column), against the oracle computed
-    row by row; and the gradient-mass identity over the whole graph."""
+@pytest.mark.parametrize("plan_kw", [
+    pytest.param({}, id="default-plan"),
+    pytest.param(dict(xcd_split_min_deg_exclusive=512, col_xcd_split_min_deg_exclusive=512),
+                 id="bench-split-plan")])
+def test_full_chunglu1m_sampled(plan_kw):
+    """Full workload size (the default plan and the bench's split plan): the forward on
+    sampled rows (hub, medium and light), the backward on sampled columns (one of them a
+    hub column), against the oracle computed row by row; and the gradient-mass identity
+    over the whole graph."""
     w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
     ip, ix = gg.make_graph(w)
     (x,) = gg.make_features(w)
@@ -224,7 +256,7 @@ def test_full_chunglu1m_sampled():
     light = rng.choice(np.nonzero(deg <= 16)[0], 40, replace=False)
     rows = np.concatenate([hub_rows, med, light])
     plan, out, (arg, slot), _ = fwd_exact("chunglu1m bf16 sampled", ip, ix, x, "bf16", "max",
-                                          rows=rows)
+                                          rows=rows, **plan_kw)
     assert slot.dtype == torch.int16
     say("chunglu1m backward sampled columns")
     dx = reduce_bwd(plan, None, dev(dout), slot=slot)
@@ -346,3 +378,8 @@ def test_rows_of_only_infinities_and_nan(op, order):
     assert np.all(o[1] == inf) and np.all(a[1] == 0)
     assert np.all(o[2] == 0) and np.all(a[2] == -1)
     assert np.all(o[3] == 0) and np.all(a[3] == -1)
+
+
+def test_full_split_plan_matches_the_bench():
+    import bench
+    assert bench.XCD_SPLIT_REDUCE == 512
