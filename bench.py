@@ -232,6 +232,20 @@ def to_dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
 
 
+def xcd_split_of(w, rows=None, cols=None):
+    """(row, column) XCD split thresholds of the plan for workload w: the given values, else
+    the defaults (attention: rows 256 / columns 1024; min / max reduction: 512 / 512). A
+    column threshold left open follows the rows: 0 when they are 0, else at least the
+    column default and at least the row threshold."""
+    reduction = w.score in ("max", "min")
+    if rows is None:
+        rows = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_ROWS
+    if cols is None:
+        col_default = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_COLS
+        cols = 0 if rows == 0 else max(col_default, rows)
+    return rows, cols
+
+
 def source_digest():
     """Digest of the device sources (kernels and the headers they include); host-only
     files (the planner, the C-ABI layer) do not change what the counters measured."""
@@ -293,12 +307,7 @@ def main():
         sys.exit(2)
 
     w = gg.WORKLOADS[args.workload]
-    reduction = w.score in ("max", "min")
-    if args.xcd_split is None:
-        args.xcd_split = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_ROWS
-    if args.col_xcd_split is None:  # columns: at least the column default, 0 when rows are 0
-        col_default = XCD_SPLIT_REDUCE if reduction else XCD_SPLIT_COLS
-        args.col_xcd_split = 0 if args.xcd_split == 0 else max(col_default, args.xcd_split)
+    args.xcd_split, args.col_xcd_split = xcd_split_of(w, args.xcd_split, args.col_xcd_split)
     t0 = time.perf_counter()
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)

@@ -101,3 +101,14 @@ def test_relabel_keeps_the_graph_and_moves_node_arrays(order):
     if order == "out-degree":
         odeg = np.bincount(ix2, minlength=n)
         assert np.all(np.diff(odeg) <= 0)
+
+
+def test_xcd_split_defaults_of_the_workloads():
+    W = gg.WORKLOADS
+    assert bench.xcd_split_of(W["chunglu1m_train_bf16"]) == (256, 1024)
+    assert bench.xcd_split_of(W["rmat21_dot_bf16"]) == (256, 1024)
+    assert bench.xcd_split_of(W["chunglu1m_gatv2_train_bf16"]) == (256, 1024)
+    assert bench.xcd_split_of(W["chunglu1m_max_train_bf16"]) == (512, 512)
+    assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 0) == (0, 0)
+    assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 2048) == (2048, 2048)
+    assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 128, 0) == (128, 0)
