@@ -108,13 +108,17 @@ def test_gatv2_training_step_captures(plan_kw):
     _replays_match(step, [out, lse, dxd, dxs, dattn], lambda: torch.cuda.synchronize())
 
 
-def test_reduction_training_step_captures():
+@pytest.mark.parametrize("plan_kw", [
+    pytest.param({}, id="default-plan"),
+    pytest.param(dict(xcd_split_min_deg_exclusive=512, col_xcd_split_min_deg_exclusive=512),
+                 id="split-plan")])
+def test_reduction_training_step_captures(plan_kw):
     ip, ix = _graph()
     n = ip.size - 1
     rng = np.random.default_rng(3)
     x, do = (dev(gg.normal_features(rng, (n, 256), "bf16")) for _ in range(2))
-    say("graph capture: max-pooling training step, N", n, "E", ix.size)
-    plan = ga.Plan(ip, ix).upload()
+    say("graph capture: max-pooling training step, N", n, "E", ix.size, plan_kw)
+    plan = ga.Plan(ip, ix, **plan_kw).upload()
     out = torch.empty_like(x)
     arg = torch.empty(x.shape, dtype=torch.int32, device="cuda")
     slot = torch.empty(x.shape, dtype=ga.reduce_slot_dtype(plan), device="cuda")
