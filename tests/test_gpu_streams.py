@@ -20,13 +20,17 @@ def _need_gpu():
         pytest.skip("needs an MI355X")
 
 
-def test_two_streams_share_a_plan():
+@pytest.mark.parametrize("plan_kw", [
+    pytest.param({}, id="default-plan"),
+    pytest.param(dict(xcd_split_min_deg_exclusive=256, col_xcd_split_min_deg_exclusive=1024),
+                 id="split-plan")])
+def test_two_streams_share_a_plan(plan_kw):
     w = gg.WORKLOADS["chunglu1m_train_bf16"]
     n = 30_000
     ip, ix = gg.make_graph(w, n=n)
     rng = np.random.default_rng(8)
     print("[case] two streams, one plan: N", n, "E", ix.size, flush=True)
-    plan = ga.Plan(ip, ix).upload()
+    plan = ga.Plan(ip, ix, **plan_kw).upload()
     scale = 1 / math.sqrt(32)
     sets = [[dev(gg.normal_features(rng, (n, 8, 32), "bf16")) for _ in range(4)]
             for _ in range(2)]
