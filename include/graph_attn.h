@@ -33,7 +33,8 @@
  *     every per-node array must hold N rows (kernels index them by node id).
  *   Ownership: the caller allocates and frees every device buffer (features, outputs,
  *     the plan's device copy, workspaces). The library never calls hipMalloc/hipFree;
- *     it owns only the host-side plan metadata.
+ *     it owns only the host-side plan metadata, and the fixed scratch array of
+ *     graph_attn_fwd_noalloc (part of its device code, not an allocation).
  *   Streams: `stream` is a hipStream_t (NULL = the default stream). fwd/bwd only enqueue
  *     work and return; results are ready when the stream reaches them. They neither
  *     allocate nor synchronise nor memset, so they can be captured into a HIP graph
@@ -62,7 +63,9 @@ typedef enum {
   GA_ERR_WORKSPACE = 4,    /* workspace pointer null or smaller than required */
   GA_ERR_NOT_READY = 5,    /* plan not uploaded, or transpose missing for backward */
   GA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed */
-  GA_ERR_HOST_ALLOC = 7    /* host memory for the plan could not be allocated */
+  GA_ERR_HOST_ALLOC = 7,   /* host memory for the plan could not be allocated */
+  GA_ERR_TOO_LARGE = 8     /* the call needs more scratch memory than the library's fixed
+                              scratch holds (graph_attn_fwd_noalloc) */
 } ga_status;
 
 typedef enum { GA_F32 = 0, GA_BF16 = 1 } ga_dtype;
@@ -216,6 +219,24 @@ ga_status graph_attn_fwd(const ga_plan* plan, ga_score score, ga_dtype dtype, in
                          int32_t dim, float scale, float neg_slope, const void* q_or_s,
                          const void* k_or_t, const void* v, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same computation, arguments, kernels and results (bit for bit) as
+ * graph_attn_fwd, without the workspace arguments: the hub-chunk partial states go to a
+ * scratch array of GA_FWD_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU, from the first such call on that GPU until the process ends. A call whose
+ * graph_attn_fwd_workspace_bytes exceeds that size is rejected with GA_ERR_TOO_LARGE
+ * before any HIP call. Calls never allocate, free or memset device memory; each GPU's
+ * scratch keeps the last call's partials (every partial a call reads it writes first, so
+ * nothing needs clearing). All calls on one GPU share its scratch: calls that may overlap
+ * on one GPU (different streams, or different host threads) race and must be serialised
+ * by the caller; calls on one stream are ordered by the stream. */
+#define GA_FWD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ga_status graph_attn_fwd_noalloc(const ga_plan* plan, ga_score score, ga_dtype dtype,
+                                 int32_t heads, int32_t dim, float scale, float neg_slope,
+                                 const void* q_or_s, const void* k_or_t, const void* v, void* out,
+                                 float* lse, void* stream);
 
 /* GATv2 forward (the GATv2 layer the Methodology names; the textbook score, not printed on
  * the pages): per head h,

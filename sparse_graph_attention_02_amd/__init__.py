@@ -35,7 +35,8 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    graph_attn_reduce_slot_bytes,
                    graph_attn_bwd, graph_attn_bwd_gatv2, graph_attn_bwd_gatv2_workspace_bytes,
                    graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
-                   graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_workspace_bytes,
+                   graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_noalloc,
+                   graph_attn_fwd_workspace_bytes,
                    graph_attn_gather_probe,
                    graph_attn_plan_array,
                    graph_attn_plan_array_count, graph_attn_plan_array_name,
@@ -45,7 +46,7 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    graph_attn_status_string, graph_attn_timer_count, graph_attn_timer_enable,
                    graph_attn_timer_read, graph_attn_timer_reset, graph_attn_version)
 
-__all__ = ["Plan", "fwd", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention",
+__all__ = ["Plan", "fwd", "fwd_noalloc", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention",
            "graph_attention_gatv2", "reduce_fwd",
            "reduce_bwd", "reduce_slot_dtype", "graph_reduce", "copy_probe", "timers", "default_opts",
            "GraphAttnError", "capi"]
@@ -197,13 +198,8 @@ def _workspace(nbytes, device, ws):
     return ws, ws.numel() * ws.element_size()
 
 
-def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2, out=None,
-        lse=None, workspace=None, stream=None):
-    """Forward of the fused layer; returns (out [N,H,d], lse [N,H] fp32).
-
-    dot: q, k, v [N,H,d] (fp32 or bf16), scale defaults to 1/sqrt(d).
-    gat: s, t fp32 [N,H], v [N,H,d], scale defaults to 1, neg_slope to 0.2.
-    """
+def _fwd_args(plan, q_or_s, k_or_t, v, score, scale, out, lse):
+    """Checked forward arguments: (score code, scale, out, lse, N, H, d, device)."""
     import torch
     if plan.device_buffer is None:
         raise RuntimeError("plan is not uploaded")
@@ -226,11 +222,40 @@ def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2
     lse = torch.empty((N, H), dtype=torch.float32, device=dev) if lse is None else lse
     _need(out, "out", (N, H, d), v.dtype, dev)
     _need(lse, "lse", (N, H), torch.float32, dev)
+    return sc, scale, out, lse, N, H, d, dev
+
+
+def fwd(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2, out=None,
+        lse=None, workspace=None, stream=None):
+    """Forward of the fused layer; returns (out [N,H,d], lse [N,H] fp32).
+
+    dot: q, k, v [N,H,d] (fp32 or bf16), scale defaults to 1/sqrt(d).
+    gat: s, t fp32 [N,H], v [N,H,d], scale defaults to 1, neg_slope to 0.2.
+    """
+    import torch
+    sc, scale, out, lse, N, H, d, dev = _fwd_args(plan, q_or_s, k_or_t, v, score, scale, out,
+                                                  lse)
     ws, wsb = _workspace(plan.fwd_workspace_bytes(H, d), dev, workspace)
     with torch.cuda.device(dev):
         graph_attn_fwd(plan.handle, sc, _dtype_code(v), H, d, float(scale), float(neg_slope),
                        _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                        wsb, _stream(stream))
+    return out, lse
+
+
+def fwd_noalloc(plan: Plan, q_or_s, k_or_t, v, *, score="dot", scale=None, neg_slope=0.2,
+                out=None, lse=None, stream=None):
+    """The forward of ``fwd`` through graph_attn_fwd_noalloc: the library takes the hub
+    partials from its fixed per-GPU scratch (GA_FWD_NOALLOC_SCRATCH_BYTES) instead of a
+    workspace. Pass ``out`` and ``lse`` to allocate nothing at all. Calls that may overlap
+    on one GPU share that scratch and must not run concurrently."""
+    import torch
+    sc, scale, out, lse, N, H, d, dev = _fwd_args(plan, q_or_s, k_or_t, v, score, scale, out,
+                                                  lse)
+    with torch.cuda.device(dev):
+        graph_attn_fwd_noalloc(plan.handle, sc, _dtype_code(v), H, d, float(scale),
+                               float(neg_slope), _ptr(q_or_s), _ptr(k_or_t), _ptr(v), _ptr(out),
+                               _ptr(lse), _stream(stream))
     return out, lse
 
 

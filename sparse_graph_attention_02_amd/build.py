@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libgraph_attn.so")
 ARCH = os.environ.get("GA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["plan.cpp", "api.cpp", "fwd.hip", "bwd.hip", "bwd_gat.hip", "bwd_gatv2.hip",
-           "reduce.hip", "probe.hip"]
+           "reduce.hip", "probe.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -17,6 +17,9 @@ LIB_PATH = os.environ.get("GRAPH_ATTN_LIB") or os.path.join(
 
 GA_OK, GA_ERR_INVALID_ARG, GA_ERR_BAD_GRAPH, GA_ERR_UNSUPPORTED = 0, 1, 2, 3
 GA_ERR_WORKSPACE, GA_ERR_NOT_READY, GA_ERR_HIP, GA_ERR_HOST_ALLOC = 4, 5, 6, 7
+GA_ERR_TOO_LARGE = 8
+# bytes of the fixed scratch of graph_attn_fwd_noalloc (GA_FWD_NOALLOC_SCRATCH_BYTES)
+GA_FWD_NOALLOC_SCRATCH_BYTES = 64 << 20
 GA_F32, GA_BF16 = 0, 1
 GA_SCORE_DOT, GA_SCORE_GAT = 0, 1
 GA_REDUCE_MAX, GA_REDUCE_MIN = 0, 1
@@ -67,6 +70,9 @@ _SIGS = {
     "graph_attn_fwd": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float, c_float,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]),
+    "graph_attn_fwd_noalloc": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_float,
+                                         c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p]),
     "graph_attn_fwd_gatv2": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_float, c_float,
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
@@ -154,6 +160,7 @@ graph_attn_plan_array_name = _wrap("graph_attn_plan_array_name")
 graph_attn_plan_destroy = _wrap("graph_attn_plan_destroy")
 graph_attn_fwd_workspace_bytes = _wrap("graph_attn_fwd_workspace_bytes")
 graph_attn_fwd = _wrap("graph_attn_fwd")
+graph_attn_fwd_noalloc = _wrap("graph_attn_fwd_noalloc")
 graph_attn_fwd_gatv2 = _wrap("graph_attn_fwd_gatv2")
 graph_attn_bwd_workspace_bytes = _wrap("graph_attn_bwd_workspace_bytes")
 graph_attn_bwd = _wrap("graph_attn_bwd")

@@ -196,6 +196,68 @@ ga_status check_device(const ga_plan* p) {
 
 }  // namespace
 
+namespace ga {
+
+ga_status plan_device_check(const ga_plan* p) { return check_device(p); }
+
+ga_status fwd_check(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads, int32_t dim,
+                    const void* a, const void* b, const void* v, const void* out,
+                    const float* lse, size_t* need) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  if (score != GA_SCORE_DOT && score != GA_SCORE_GAT) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (!ga::fwd_supported(dtype, score, g)) return GA_ERR_UNSUPPORTED;
+  if (p->n > 0) {
+    const size_t score_align = score == GA_SCORE_DOT ? 16 : 4;
+    if ((s = check_ptr(a, score_align)) != GA_OK || (s = check_ptr(b, score_align)) != GA_OK ||
+        (s = check_ptr(v, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
+        (s = check_ptr(lse, 4)) != GA_OK)
+      return s;
+  }
+  *need = fwd_ws_bytes(p, g);
+  return GA_OK;
+}
+
+ga_status fwd_enqueue(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads,
+                      int32_t dim, float scale, float neg_slope, const void* a, const void* b,
+                      const void* v, void* out, float* lse, void* ws, void* stream) {
+  ga_status s = check_device(p);
+  if (s != GA_OK) return s;
+  ga::Geometry g;
+  if ((s = make_geometry(dtype, heads, dim, &g)) != GA_OK) return s;
+  ga::FwdArgs args{};
+  args.indptr = p->d_indptr;
+  args.indices = p->d_indices;
+  args.bins = p->d_rows;
+  args.a = a;
+  args.b = b;
+  args.v = v;
+  args.out = out;
+  args.lse = lse;
+  const size_t nc = p->rows.chunk_row.size();
+  args.ws_ml = static_cast<float*>(ws);
+  args.ws_acc = nc ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              align_up(nc * heads * 2 * sizeof(float)))
+                   : nullptr;
+  args.sc2 = scale * 1.4426950408889634f;
+  args.neg_slope = neg_slope;
+  args.ld = g.G;
+  args.hf = g.heads;
+  // GAT-style scores gather t_j per head, a partial line per slice: not sliced; nor are
+  // plans whose chunk slots are scheduled to XCDs
+  args.slices = score == GA_SCORE_DOT && p->rows.sched.empty()
+                    ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
+                                         ga::kAutoSliceLanesTwoRows)
+                    : 1;
+  const int rc = ga::launch_fwd(dtype, score == GA_SCORE_DOT ? ga::kModeDot : ga::kModeGat, g,
+                                args, p->n, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+}  // namespace ga
+
 extern "C" {
 
 const char* graph_attn_version(void) { return "graph_attn 0.1 gfx950"; }
@@ -210,6 +272,8 @@ const char* graph_attn_status_string(ga_status s) {
     case GA_ERR_NOT_READY: return "GA_ERR_NOT_READY: plan not uploaded or transpose missing";
     case GA_ERR_HIP: return "GA_ERR_HIP: HIP runtime error";
     case GA_ERR_HOST_ALLOC: return "GA_ERR_HOST_ALLOC: host allocation failed";
+    case GA_ERR_TOO_LARGE:
+      return "GA_ERR_TOO_LARGE: the call needs more than the library's fixed scratch";
   }
   return "unknown ga_status";
 }
@@ -382,52 +446,14 @@ ga_status graph_attn_fwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
                          int32_t dim, float scale, float neg_slope, const void* a, const void* b,
                          const void* v, void* out, float* lse, void* ws, size_t ws_bytes,
                          void* stream) {
-  if (!p) return GA_ERR_INVALID_ARG;
-  if (score != GA_SCORE_DOT && score != GA_SCORE_GAT) return GA_ERR_INVALID_ARG;
-  ga::Geometry g;
-  ga_status s = make_geometry(dtype, heads, dim, &g);
+  size_t need = 0;
+  ga_status s = ga::fwd_check(p, score, dtype, heads, dim, a, b, v, out, lse, &need);
   if (s != GA_OK) return s;
-  if (!ga::fwd_supported(dtype, score, g)) return GA_ERR_UNSUPPORTED;
-  if (p->n > 0) {
-    const size_t score_align = score == GA_SCORE_DOT ? 16 : 4;
-    if ((s = check_ptr(a, score_align)) != GA_OK || (s = check_ptr(b, score_align)) != GA_OK ||
-        (s = check_ptr(v, 16)) != GA_OK || (s = check_ptr(out, 16)) != GA_OK ||
-        (s = check_ptr(lse, 4)) != GA_OK)
-      return s;
-  }
-  const size_t need = fwd_ws_bytes(p, g);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return GA_ERR_WORKSPACE;
   if (!p->uploaded) return GA_ERR_NOT_READY;
   if (p->n == 0) return GA_OK;
-  if ((s = check_device(p)) != GA_OK) return s;
-
-  ga::FwdArgs args{};
-  args.indptr = p->d_indptr;
-  args.indices = p->d_indices;
-  args.bins = p->d_rows;
-  args.a = a;
-  args.b = b;
-  args.v = v;
-  args.out = out;
-  args.lse = lse;
-  const size_t nc = p->rows.chunk_row.size();
-  args.ws_ml = static_cast<float*>(ws);
-  args.ws_acc = nc ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                              align_up(nc * heads * 2 * sizeof(float)))
-                   : nullptr;
-  args.sc2 = scale * 1.4426950408889634f;
-  args.neg_slope = neg_slope;
-  args.ld = g.G;
-  args.hf = g.heads;
-  // GAT-style scores gather t_j per head, a partial line per slice: not sliced; nor are
-  // plans whose chunk slots are scheduled to XCDs
-  args.slices = score == GA_SCORE_DOT && p->rows.sched.empty()
-                    ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
-                                         ga::kAutoSliceLanesTwoRows)
-                    : 1;
-  const int rc = ga::launch_fwd(dtype, score == GA_SCORE_DOT ? ga::kModeDot : ga::kModeGat, g,
-                                args, p->n, stream, active_hook());
-  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+  return ga::fwd_enqueue(p, score, dtype, heads, dim, scale, neg_slope, a, b, v, out, lse, ws,
+                         stream);
 }
 
 ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, int32_t dim,

@@ -68,6 +68,19 @@ namespace ga {
 // Largest edge count a plan accepts: 2^31 - 2^16.
 constexpr int64_t kMaxEdges = (int64_t(1) << 31) - (int64_t(1) << 16);
 
+// Forward entry points (api.cpp), shared by graph_attn_fwd and graph_attn_fwd_noalloc.
+// fwd_check runs every argument check that needs no HIP call and reports the workspace
+// bytes the call needs; fwd_enqueue checks that the current device is the plan's and
+// launches the forward with workspace `ws` (the plan uploaded, N > 0). plan_device_check
+// is the device check alone.
+ga_status fwd_check(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads, int32_t dim,
+                    const void* a, const void* b, const void* v, const void* out,
+                    const float* lse, size_t* need);
+ga_status fwd_enqueue(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t heads,
+                      int32_t dim, float scale, float neg_slope, const void* a, const void* b,
+                      const void* v, void* out, float* lse, void* ws, void* stream);
+ga_status plan_device_check(const ga_plan* p);
+
 // Planner (plan.cpp). Validates and builds every host array.
 ga_status build_plan(const int32_t* indptr, const int32_t* indices, int64_t n, int64_t e,
                      const ga_plan_opts& opts, ga_plan* p);

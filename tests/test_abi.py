@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert capi.graph_attn_version().decode().startswith("graph_attn")
-    for s in range(8):
+    for s in range(9):
         assert capi.lib().graph_attn_status_string(s).decode().startswith("GA_")
     assert capi.lib().graph_attn_status_string(99) == b"unknown ga_status"
 
@@ -136,6 +136,35 @@ def test_fwd_argument_checks_before_any_hip_call():
     assert need > 0
     assert _fwd(p, wsb=need - 1) == capi.GA_ERR_WORKSPACE
     assert _fwd(p, wsb=need) == capi.GA_ERR_NOT_READY        # valid, but not uploaded
+
+
+def _fwd_noalloc(p, score=capi.GA_SCORE_DOT, dtype=capi.GA_BF16, H=8, d=32, a=FAKE, b=FAKE,
+                 v=FAKE, out=FAKE, lse=FAKE):
+    return capi.raw_status("graph_attn_fwd_noalloc", p.handle if p else None, score, dtype, H,
+                           d, ctypes.c_float(0.1), ctypes.c_float(0.2), c_void_p(a),
+                           c_void_p(b), c_void_p(v), c_void_p(out), c_void_p(lse), None)
+
+
+def test_fwd_noalloc_checks_and_scratch_limit_before_any_hip_call():
+    p, _, _ = _hub_plan()
+    assert _fwd_noalloc(None) == capi.GA_ERR_INVALID_ARG
+    assert _fwd_noalloc(p, score=7) == capi.GA_ERR_INVALID_ARG
+    assert _fwd_noalloc(p, d=12) == capi.GA_ERR_UNSUPPORTED
+    assert _fwd_noalloc(p, a=0) == capi.GA_ERR_INVALID_ARG
+    assert _fwd_noalloc(p, out=FAKE + 8) == capi.GA_ERR_INVALID_ARG
+    assert _fwd_noalloc(p) == capi.GA_ERR_NOT_READY     # fits the scratch; not uploaded
+    # a plan whose hub partials need more than the fixed scratch is refused as too large:
+    # one hub row of one-edge chunks, each chunk's partial (m, l) and acc taking
+    # (2 * 8 + 256) * 4 bytes at H = 8, d = 32
+    n_chunks = capi.GA_FWD_NOALLOC_SCRATCH_BYTES // (256 * 4) + 1
+    ip = np.array([0, n_chunks], np.int64)
+    big = Plan(ip, np.zeros(n_chunks, np.int32), light_max_deg=0, hub_min_deg_exclusive=0,
+               hub_chunk=1, build_csc=False)
+    assert big.info()["n_row_chunks"] == n_chunks
+    assert big.fwd_workspace_bytes(8, 32) > capi.GA_FWD_NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(big) == capi.GA_ERR_TOO_LARGE
+    # the regular forward takes the same plan with a workspace of that size
+    assert _fwd(big, wsb=big.fwd_workspace_bytes(8, 32)) == capi.GA_ERR_NOT_READY
 
 
 def _bwd(p, score=capi.GA_SCORE_DOT, dtype=capi.GA_BF16, H=8, d=32, ptrs=None, ws=FAKE,
