@@ -47,7 +47,8 @@ __all__ = [
     "backward", "backward_by_columns", "grad_q_rows", "grad_kv_cols", "train_step_rows",
     "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
     "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
-    "train_step_rows_gatv2", "forward_online_chunked", "train_step_rows_gat",
+    "train_step_rows_gatv2", "forward_online_chunked", "train_step_rows_gat", "row_pass",
+    "transpose_order", "column_pass",
 ]
 
 
@@ -299,6 +300,72 @@ def train_step_rows(indptr, indices, q, k, v, dout, rows, scale=None):
         np.add.at(dk, slot, sc * dS[:, :, None] * widen(q[i])[None])
         np.add.at(dv, slot, alpha[:, :, None] * widen(dout[i])[None])
     return out, lse, dq, cols, dk, dv
+
+
+def row_pass(indptr, indices, q, k, v, dout, rows, scale=None):
+    """The row half of the training step for the listed rows (the forward and the per-row
+    loop of ``backward_by_columns``): out [R,H,d], lse [R,H] and dq [R,H,d] of each row,
+    and the attention weight alpha [M,H] and score gradient dS [M,H] of each of its edges,
+    the rows' edges concatenated in the order of ``rows`` (for a contiguous, ascending
+    block of rows: the block's CSR positions).  With ``column_pass`` over every column this
+    is ``forward`` plus ``backward``; the two halves let blocks of rows and of columns run
+    apart."""
+    sc = _scale_of(q, scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = q.shape[1], q.shape[2]
+    deg = (indptr[rows + 1] - indptr[rows]).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(deg)])
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    dq = np.zeros((rows.size, H, d))
+    e_alpha = np.zeros((int(start[-1]), H))
+    e_ds = np.zeros((int(start[-1]), H))
+    for r, i in enumerate(rows):
+        if deg[r] == 0:
+            continue
+        J = _neighbours(indptr, indices, i)
+        e = row_scores(i, indptr, indices, q, k, "dot", sc)
+        alpha, lse[r] = row_softmax(e)
+        vj = widen(v[J])
+        out[r] = np.einsum("kh,khc->hc", alpha, vj)
+        dp = np.einsum("hc,khc->kh", widen(dout[i]), vj)
+        D = (alpha * dp).sum(axis=0)
+        dS = alpha * (dp - D[None, :])
+        dq[r] = sc * np.einsum("kh,khc->hc", dS, widen(k[J]))
+        e_alpha[start[r]:start[r + 1]] = alpha
+        e_ds[start[r]:start[r + 1]] = dS
+    return out, lse, dq, e_alpha, e_ds
+
+
+def transpose_order(indptr, indices):
+    """The transpose as a stable sort of CSR positions by source: (order, col_start,
+    edge_row), where column j's edges are the CSR positions order[col_start[j]:
+    col_start[j+1]] (destinations ascending) and edge_row[p] is the destination row of
+    CSR position p."""
+    n = indptr.size - 1
+    order = np.argsort(indices, kind="stable")
+    col_start = np.searchsorted(indices[order], np.arange(n + 1))
+    edge_row = np.repeat(np.arange(n), np.diff(indptr))
+    return order, col_start, edge_row
+
+
+def column_pass(q, dout, e_alpha, e_ds, order, col_start, edge_row, cols, scale=None):
+    """dk, dv [C,H,d] of the listed source columns from every edge's alpha and dS (indexed
+    by CSR position, as ``row_pass`` gives them for all rows): for column j and each edge
+    (i -> j), dk_j += scale dS q_i and dv_j += alpha dout_i (the per-column loop of
+    ``backward_by_columns``)."""
+    sc = _scale_of(q, scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    dk = np.zeros((cols.size,) + tuple(q.shape[1:]))
+    dv = np.zeros((cols.size,) + tuple(dout.shape[1:]))
+    for c, j in enumerate(cols):
+        es = order[col_start[j]:col_start[j + 1]]
+        if es.size == 0:
+            continue
+        rows = edge_row[es]
+        dk[c] = sc * np.einsum("eh,ehc->hc", e_ds[es], widen(q[rows]))
+        dv[c] = np.einsum("eh,ehc->hc", e_alpha[es], widen(dout[rows]))
+    return dk, dv
 
 
 def leaky_relu_grad(x: np.ndarray, neg_slope: float) -> np.ndarray:

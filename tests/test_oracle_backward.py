@@ -5,7 +5,8 @@
 * torch fp64 autograd through dense masked attention (boolean / log-count mask),
 * invariants: sum_j dK_j = 0 per head, sum_j dV_j = sum of dOut over non-empty rows,
   dQ = 0 on single-neighbour rows and on rows whose neighbour keys are all equal,
-* agreement of the CSR-scatter, CSC-gather, sampled and per-row training-step forms.
+* agreement of the CSR-scatter, CSC-gather, sampled and per-row training-step forms, and
+  of the row-pass / column-pass halves run over blocks of rows and columns.
 """
 import json
 import os
@@ -264,3 +265,40 @@ def test_train_step_rows_gat_is_the_plain_step():
         np.add.at(acc_v, c3, dv3)
     np.testing.assert_allclose(acc_t, dt, atol=1e-12)
     np.testing.assert_allclose(acc_v, dv, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_row_and_column_passes_in_blocks_are_the_plain_step(seed):
+    """The halves the full-size parity runs in worker blocks: rows in contiguous blocks
+    give out, lse, dq and every edge's (alpha, dS) at its CSR position; columns in blocks
+    give dk, dv. Composed they equal forward + backward (pinned above), with an empty row
+    and an empty column in the graph."""
+    rng = np.random.default_rng(seed)
+    n, H, d = 70, 3, 5
+    ip, ix = gg.random_multigraph(n, 900, rng, self_loops=False, hub_rows=(4,), hub_deg=120)
+    keep = (np.repeat(np.arange(n), np.diff(ip)) != 9) & (ix != 11)   # row 9, column 11 empty
+    dst = np.repeat(np.arange(n), np.diff(ip))[keep]
+    ip, ix = gg.csr_from_edges(n, ix[keep], dst)
+    q, k, v, do = (rng.standard_normal((n, H, d)) for _ in range(4))
+    fo, fl = A.forward(ip, ix, q, k, v, "dot", None)
+    dq0, dk0, dv0 = A.backward(ip, ix, q, k, v, do, None)
+    E = ix.size
+    ea, ed = np.full((E, H), np.nan), np.full((E, H), np.nan)
+    cuts = np.unique(np.r_[0, rng.choice(n, 6), n])
+    for r0, r1 in zip(cuts[:-1], cuts[1:]):
+        out, lse, dq, a, s = A.row_pass(ip, ix, q, k, v, do, np.arange(r0, r1), None)
+        np.testing.assert_allclose(out, fo[r0:r1], rtol=1e-13, atol=1e-14)
+        np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(fl[r0:r1]))
+        np.testing.assert_allclose(lse[~np.isneginf(lse)], fl[r0:r1][~np.isneginf(lse)],
+                                   rtol=1e-13)
+        np.testing.assert_allclose(dq, dq0[r0:r1], rtol=1e-12, atol=1e-12)
+        ea[ip[r0]:ip[r1]], ed[ip[r0]:ip[r1]] = a, s
+    assert not np.isnan(ea).any() and not np.isnan(ed).any()     # every edge written once
+    np.testing.assert_allclose(ea[ip[4]:ip[5]].sum(axis=0), 1.0, rtol=1e-13)   # row 4's weights
+    order, col_start, edge_row = A.transpose_order(ip, ix)
+    assert np.array_equal(np.sort(ix[order], kind="stable"), ix[order])
+    for c0, c1 in ((0, 23), (23, 24), (24, n)):
+        dk, dv = A.column_pass(q, do, ea, ed, order, col_start, edge_row, np.arange(c0, c1))
+        np.testing.assert_allclose(dk, dk0[c0:c1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dv, dv0[c0:c1], rtol=1e-12, atol=1e-12)
+    assert np.all(dk0[11] == 0) and np.all(dq0[9] == 0)
