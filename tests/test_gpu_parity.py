@@ -408,6 +408,9 @@ def test_full_plans_match_the_bench():
         col_xcd_split_min_deg_exclusive=bench.XCD_SPLIT_COLS)
 
 
+# The 1M training step (and so the 1M forward) and the R-MAT forward are checked on every
+# element in the bench's split plan by tests/test_gpu_fullsize.py; on the default plan
+# their full-size checks below sample rows and columns.
 def _sample_rows(ip, rng, k=256):
     deg = np.diff(ip)
     top = np.argsort(-deg, kind="stable")[:8]
@@ -416,7 +419,7 @@ def _sample_rows(ip, rng, k=256):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+@pytest.mark.parametrize("plan_kw", FULL_PLANS[:1])
 def test_full_chunglu1m_bf16_forward_sampled(plan_kw):
     w = gg.WORKLOADS["chunglu1m_dot_bf16"]
     ip, ix = gg.make_graph(w)
@@ -427,7 +430,7 @@ def test_full_chunglu1m_bf16_forward_sampled(plan_kw):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+@pytest.mark.parametrize("plan_kw", FULL_PLANS[:1])
 def test_full_rmat21_bf16_forward_sampled(plan_kw):
     w = gg.WORKLOADS["rmat21_dot_bf16"]
     ip, ix = gg.make_graph(w)
@@ -450,7 +453,7 @@ def test_full_chunglu100k_gat_f32_forward_sampled(plan_kw):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+@pytest.mark.parametrize("plan_kw", FULL_PLANS[:1])
 def test_full_chunglu1m_training_step_sampled(plan_kw):
     w = gg.WORKLOADS["chunglu1m_train_bf16"]
     ip, ix = gg.make_graph(w)
