@@ -383,15 +383,42 @@ ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launc
  * measure copy bandwidth and to calibrate traffic counters against a known byte count. */
 ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
-/* Gather-only pass over the plan's CSR: for every edge, load the source's K and V rows with
- * the forward's lane pattern (16 bytes per lane, G = H*d*sizeof(dtype)/16 lanes per row)
- * and do no arithmetic. Its duration is the memory system's floor for the forward's
- * neighbour gathers on this graph (the roofline of a gather-bound kernel, measured rather
- * than assumed). k, v as for graph_attn_fwd; sink: 1 KiB of device memory, 16-byte aligned,
- * that the probe may write. The plan must be uploaded. */
+/* Gather-only probes: the loads of an attention pass with its arithmetic taken out, on
+ * the same plan and in the same order (work items, lanes of 16 bytes, edges in flight),
+ * folded into an XOR so they stay live, with no stores (but an improbable one to `sink`).
+ * Their durations bound the passes' times from below on that graph: the time the memory
+ * system takes to deliver the pass's reads. sink: 1 KiB of device memory, 16-byte aligned.
+ * Rows, dtype and geometry as for graph_attn_fwd; pointers that may be NULL mean "not
+ * read". The plan must be uploaded (and, for the columns probe, built with the transpose).
+ *
+ * graph_attn_gather_probe: the work list of graph_attn_fwd and of the backward's dQ pass:
+ * the plan's hub-chunk slots (in its XCD schedule), medium rows, then light rows, with the
+ * forward's feature slices. Per work item it reads row_a[i] and row_b[i] (the row-side
+ * operands: q for the forward, q and dout for the dQ pass; either may be NULL); per edge
+ * (i <- j) k[j] and v[j] (v NULL: one row per edge, as the GATv2 forward gathers). */
 ga_status graph_attn_gather_probe(const ga_plan* plan, ga_dtype dtype, int32_t heads,
-                                  int32_t dim, const void* k, const void* v, void* sink,
-                                  void* stream);
+                                  int32_t dim, const void* row_a, const void* row_b,
+                                  const void* k, const void* v, void* sink, void* stream);
+
+/* graph_attn_gather_probe_cols: the work list of the backward's dK/dV pass over the
+ * transpose: hub-column chunk slots (in the plan's column XCD schedule), medium columns,
+ * then light columns. Per column j it reads k[j] and v[j] (either may be NULL); per
+ * transpose edge (i -> j) dout[i], q[i] (q may be NULL) and the fp32 (lse, D) record
+ * pair of i's head, record [N, heads, 2] (may be NULL; 8-byte aligned). */
+ga_status graph_attn_gather_probe_cols(const ga_plan* plan, ga_dtype dtype, int32_t heads,
+                                       int32_t dim, const void* k, const void* v, const void* q,
+                                       const void* dout, const float* record, void* sink,
+                                       void* stream);
+
+/* graph_attn_gather_probe_random: n_gathers rows of row_bytes bytes (64, 128, 256, 512 or
+ * 1024) drawn uniformly at random from a table of table_rows rows (1 <= table_rows <
+ * 2^32; the table holds table_rows * row_bytes bytes, 16-byte aligned), gather k reading
+ * the row picked by the k-th output of the SplitMix64 generator seeded with `seed`; 16 bytes
+ * per lane, 8 rows in flight per lane group. Its rate at a given table size is the gather
+ * ceiling of the memory hierarchy at that footprint (L2, the MALL, HBM). Needs no plan. */
+ga_status graph_attn_gather_probe_random(int32_t row_bytes, const void* table,
+                                         int64_t table_rows, int64_t n_gathers, uint64_t seed,
+                                         void* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,8 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
                    graph_attn_bwd_workspace_bytes, graph_attn_copy_probe,
                    graph_attn_fwd, graph_attn_fwd_gatv2, graph_attn_fwd_noalloc,
                    graph_attn_fwd_workspace_bytes,
-                   graph_attn_gather_probe,
+                   graph_attn_gather_probe, graph_attn_gather_probe_cols,
+                   graph_attn_gather_probe_random,
                    graph_attn_plan_array,
                    graph_attn_plan_array_count, graph_attn_plan_array_name,
                    graph_attn_plan_create, graph_attn_plan_destroy,
@@ -48,7 +49,8 @@ from .capi import (GA_BF16, GA_F32, GA_REDUCE_MAX, GA_REDUCE_MIN,  # noqa: F401
 
 __all__ = ["Plan", "fwd", "fwd_noalloc", "fwd_gatv2", "bwd", "bwd_gatv2", "graph_attention",
            "graph_attention_gatv2", "reduce_fwd",
-           "reduce_bwd", "reduce_slot_dtype", "graph_reduce", "copy_probe", "timers", "default_opts",
+           "reduce_bwd", "reduce_slot_dtype", "graph_reduce", "copy_probe", "gather_probe", "gather_probe_cols",
+           "gather_probe_random", "timers", "default_opts",
            "GraphAttnError", "capi"]
 
 
@@ -544,17 +546,64 @@ def copy_probe(dst, src, stream=None):
         graph_attn_copy_probe(_ptr(dst), _ptr(src), nbytes, _stream(stream))
 
 
-def gather_probe(plan: Plan, k, v, sink=None, stream=None):
-    """Gather-only pass over the plan's CSR with the forward's lane pattern (see
-    graph_attn_gather_probe); returns the sink tensor."""
+def _probe_rows(x, name, N, H, d, dtype, device):
+    if x is not None:
+        _need(x, name, (N, H, d), dtype, device)
+    return _ptr(x)
+
+
+def gather_probe(plan: Plan, k, v=None, *, row_a=None, row_b=None, sink=None, stream=None):
+    """Loads of the forward's (or the dQ pass's) work list without the arithmetic (see
+    graph_attn_gather_probe): per work item row_a[i], row_b[i]; per edge k[j] and v[j] (v
+    None: one row per edge). Returns the sink tensor."""
     import torch
-    if sink is None:
-        sink = torch.empty(1024, dtype=torch.uint8, device=k.device)
     N, H, d = k.shape
     _rows_match(plan, N)
+    if sink is None:
+        sink = torch.zeros(1024, dtype=torch.uint8, device=k.device)
+    ptrs = [_probe_rows(x, n, N, H, d, k.dtype, k.device)
+            for x, n in ((row_a, "row_a"), (row_b, "row_b"), (k, "k"), (v, "v"))]
     with torch.cuda.device(k.device):
-        graph_attn_gather_probe(plan.handle, _dtype_code(k), H, d, _ptr(k), _ptr(v), _ptr(sink),
+        graph_attn_gather_probe(plan.handle, _dtype_code(k), H, d, *ptrs, _ptr(sink),
                                 _stream(stream))
+    return sink
+
+
+def gather_probe_cols(plan: Plan, dout, *, q=None, record=None, k=None, v=None, sink=None,
+                      stream=None):
+    """Loads of the dK/dV pass's work list over the transpose without the arithmetic (see
+    graph_attn_gather_probe_cols): per column k[j], v[j]; per transpose edge dout[i], q[i]
+    and record[i] (fp32 [N, H, 2]). Returns the sink tensor."""
+    import torch
+    N, H, d = dout.shape
+    _rows_match(plan, N)
+    if record is not None:
+        _need(record, "record", (N, H, 2), torch.float32, dout.device)
+    if sink is None:
+        sink = torch.zeros(1024, dtype=torch.uint8, device=dout.device)
+    ptrs = [_probe_rows(x, n, N, H, d, dout.dtype, dout.device)
+            for x, n in ((k, "k"), (v, "v"), (q, "q"), (dout, "dout"))]
+    with torch.cuda.device(dout.device):
+        graph_attn_gather_probe_cols(plan.handle, _dtype_code(dout), H, d, *ptrs, _ptr(record),
+                                     _ptr(sink), _stream(stream))
+    return sink
+
+
+def gather_probe_random(table, row_bytes, n_gathers, *, table_rows=None, seed=1, sink=None,
+                        stream=None):
+    """n_gathers uniformly random rows of row_bytes bytes from the first table_rows rows
+    of ``table`` (a device tensor; default: all of it) (graph_attn_gather_probe_random).
+    Returns the sink tensor."""
+    import torch
+    nbytes = table.numel() * table.element_size()
+    rows = nbytes // row_bytes if table_rows is None else int(table_rows)
+    if not table.is_cuda or not table.is_contiguous() or rows * row_bytes > nbytes:
+        raise ValueError("table: a contiguous device tensor of at least table_rows rows")
+    if sink is None:
+        sink = torch.zeros(1024, dtype=torch.uint8, device=table.device)
+    with torch.cuda.device(table.device):
+        graph_attn_gather_probe_random(int(row_bytes), _ptr(table), rows, int(n_gathers),
+                                       int(seed), _ptr(sink), _stream(stream))
     return sink
 
 

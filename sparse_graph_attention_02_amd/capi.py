@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 from ctypes import (POINTER, Structure, c_char_p, c_double, c_float, c_int32, c_int64,
-                    c_size_t, c_void_p)
+                    c_size_t, c_uint64, c_void_p)
 
 # GRAPH_ATTN_LIB selects another build of the same library (tuning variants).
 LIB_PATH = os.environ.get("GRAPH_ATTN_LIB") or os.path.join(
@@ -100,7 +100,12 @@ _SIGS = {
                                         POINTER(c_double)]),
     "graph_attn_copy_probe": (c_int32, [c_void_p, c_void_p, c_size_t, c_void_p]),
     "graph_attn_gather_probe": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p,
-                                          c_void_p, c_void_p]),
+                                          c_void_p, c_void_p, c_void_p, c_void_p]),
+    "graph_attn_gather_probe_cols": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p]),
+    "graph_attn_gather_probe_random": (c_int32, [c_int32, c_void_p, c_int64, c_int64, c_uint64,
+                                                 c_void_p, c_void_p]),
 }
 
 _lib = None
@@ -177,6 +182,8 @@ graph_attn_timer_count = _wrap("graph_attn_timer_count")
 graph_attn_timer_read = _wrap("graph_attn_timer_read")
 graph_attn_copy_probe = _wrap("graph_attn_copy_probe")
 graph_attn_gather_probe = _wrap("graph_attn_gather_probe")
+graph_attn_gather_probe_cols = _wrap("graph_attn_gather_probe_cols")
+graph_attn_gather_probe_random = _wrap("graph_attn_gather_probe_random")
 
 
 def raw_status(name: str, *args) -> int:

@@ -778,20 +778,96 @@ ga_status graph_attn_timer_read(int32_t index, const char** name, int64_t* launc
 }
 
 ga_status graph_attn_gather_probe(const ga_plan* p, ga_dtype dtype, int32_t heads, int32_t dim,
-                                  const void* k, const void* v, void* sink, void* stream) {
+                                  const void* row_a, const void* row_b, const void* k,
+                                  const void* v, void* sink, void* stream) {
   if (!p) return GA_ERR_INVALID_ARG;
   ga::Geometry g;
   ga_status s = make_geometry(dtype, heads, dim, &g);
   if (s != GA_OK) return s;
   if (g.G < 4) return GA_ERR_UNSUPPORTED;
-  if (p->n > 0 && ((s = check_ptr(k, 16)) != GA_OK || (s = check_ptr(v, 16)) != GA_OK)) return s;
+  if (p->n > 0) {
+    if ((s = check_ptr(k, 16)) != GA_OK) return s;
+    for (const void* x : {row_a, row_b, v})
+      if (x && !aligned(x, 16)) return GA_ERR_INVALID_ARG;
+  }
   if ((s = check_ptr(sink, 16)) != GA_OK) return s;
   if (!p->uploaded) return GA_ERR_NOT_READY;
-  if (p->e == 0) return GA_OK;
+  if (p->n == 0) return GA_OK;
   if ((s = check_device(p)) != GA_OK) return s;
-  const int rc =
-      ga::launch_gather_probe(p->d_indices, p->e, g.G, k, v, sink, stream, active_hook());
-  return rc == 0 ? GA_OK : GA_ERR_HIP;
+  ga::ProbeLaunch L{};
+  L.ptr = p->d_indptr;
+  L.idx = p->d_indices;
+  L.bins = p->d_rows;
+  L.side_a = row_a;
+  L.side_b = row_b;
+  L.gx = k;
+  L.gy = v;
+  L.sink = sink;
+  L.G = g.G;
+  L.LH = g.LH;
+  L.heads = g.heads;
+  // the forward's feature slices: automatic 256-byte slices when two rows are gathered per
+  // edge, none for one row; none on a plan with an XCD schedule
+  L.slices = p->rows.sched.empty()
+                 ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
+                                      v ? ga::kAutoSliceLanesTwoRows : 0)
+                 : 1;
+  const int rc = ga::launch_gather_probe_rows(L, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_gather_probe_cols(const ga_plan* p, ga_dtype dtype, int32_t heads,
+                                       int32_t dim, const void* k, const void* v, const void* q,
+                                       const void* dout, const float* record, void* sink,
+                                       void* stream) {
+  if (!p) return GA_ERR_INVALID_ARG;
+  ga::Geometry g;
+  ga_status s = make_geometry(dtype, heads, dim, &g);
+  if (s != GA_OK) return s;
+  if (g.G < 4) return GA_ERR_UNSUPPORTED;
+  if (p->n > 0) {
+    if ((s = check_ptr(dout, 16)) != GA_OK) return s;
+    for (const void* x : {k, v, q})
+      if (x && !aligned(x, 16)) return GA_ERR_INVALID_ARG;
+    if (record && !aligned(record, 8)) return GA_ERR_INVALID_ARG;
+  }
+  if ((s = check_ptr(sink, 16)) != GA_OK) return s;
+  if (!p->has_csc) return GA_ERR_NOT_READY;
+  if (!p->uploaded) return GA_ERR_NOT_READY;
+  if (p->n == 0) return GA_OK;
+  if ((s = check_device(p)) != GA_OK) return s;
+  ga::ProbeLaunch L{};
+  L.ptr = p->d_colptr;
+  L.idx = p->d_rowidx;
+  L.bins = p->d_cols;
+  L.side_a = k;
+  L.side_b = v;
+  L.gx = dout;
+  L.gy = q;
+  L.rec = record;
+  L.sink = sink;
+  L.G = g.G;
+  L.LH = g.LH;
+  L.heads = g.heads;
+  L.slices = 1;
+  const int rc = ga::launch_gather_probe_cols(L, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
+}
+
+ga_status graph_attn_gather_probe_random(int32_t row_bytes, const void* table, int64_t table_rows,
+                                         int64_t n_gathers, uint64_t seed, void* sink,
+                                         void* stream) {
+  if (row_bytes != 64 && row_bytes != 128 && row_bytes != 256 && row_bytes != 512 &&
+      row_bytes != 1024)
+    return GA_ERR_UNSUPPORTED;
+  if (table_rows < 1 || table_rows > int64_t(0xffffffff) || n_gathers < 0)
+    return GA_ERR_INVALID_ARG;
+  ga_status s;
+  if ((s = check_ptr(table, 16)) != GA_OK || (s = check_ptr(sink, 16)) != GA_OK) return s;
+  if (n_gathers == 0) return GA_OK;
+  const int rc = ga::launch_gather_probe_random(row_bytes / 16, table, table_rows, n_gathers,
+                                                seed, sink, stream, active_hook());
+  return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
 
 ga_status graph_attn_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {

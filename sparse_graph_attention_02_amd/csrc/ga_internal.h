@@ -240,7 +240,28 @@ bool reduce_supported(ga_dtype dt, int G);
 int launch_reduce(ga_dtype dt, bool backward, int op, int G, const RedArgs& a, void* stream,
                   TimerHook hook);
 int launch_copy(void* dst, const void* src, size_t bytes, void* stream, TimerHook hook);
-int launch_gather_probe(const int32_t* indices, int64_t e, int G, const void* k, const void* v,
-                        void* sink, void* stream, TimerHook hook);
+// Gather-only probes (probe.hip). Rows: the forward's / dQ pass's work list over
+// (ptr, idx) = (indptr, indices) with the row bins; columns: the dK/dV pass's work list over
+// (colptr, rowidx) with the column bins. side_a / side_b: operand rows read once per work
+// item; gx / gy: rows gathered per edge (gy may be null); rec: the columns' per-edge
+// (lse, D) record [N][heads] (may be null). G lanes per feature row, LH per head; the rows
+// probe runs in `slices` feature slices.
+struct ProbeLaunch {
+  const int32_t* ptr;
+  const int32_t* idx;
+  DevBins bins;
+  const void* side_a;
+  const void* side_b;
+  const void* gx;
+  const void* gy;
+  const void* rec;
+  void* sink;
+  int G, LH, heads, slices;
+};
+int launch_gather_probe_rows(const ProbeLaunch& p, void* stream, TimerHook hook);
+int launch_gather_probe_cols(const ProbeLaunch& p, void* stream, TimerHook hook);
+// Random rows of a table of `rows` rows of G lanes, n gathers.
+int launch_gather_probe_random(int G, const void* table, int64_t rows, int64_t n, uint64_t seed,
+                               void* sink, void* stream, TimerHook hook);
 
 }  // namespace ga

@@ -249,15 +249,35 @@ def test_timers_and_copy_probe_host_paths():
 
 
 def test_gather_probe_argument_checks():
-    p, _, _ = _hub_plan()
-    call = lambda plan, H=8, d=32, k=FAKE, v=FAKE, sink=FAKE: capi.raw_status(
+    p, ip, ix = _hub_plan()
+    call = lambda plan, H=8, d=32, a=FAKE, b=0, k=FAKE, v=FAKE, sink=FAKE: capi.raw_status(
         "graph_attn_gather_probe", plan.handle if plan else None, capi.GA_BF16, H, d,
-        c_void_p(k), c_void_p(v), c_void_p(sink), None)
+        c_void_p(a), c_void_p(b), c_void_p(k), c_void_p(v), c_void_p(sink), None)
     assert call(None) == capi.GA_ERR_INVALID_ARG
     assert call(p, d=12) == capi.GA_ERR_UNSUPPORTED
     assert call(p, k=0) == capi.GA_ERR_INVALID_ARG
+    assert call(p, a=FAKE + 8) == capi.GA_ERR_INVALID_ARG
     assert call(p, sink=FAKE + 4) == capi.GA_ERR_INVALID_ARG
     assert call(p) == capi.GA_ERR_NOT_READY
+    assert call(p, a=0, v=0) == capi.GA_ERR_NOT_READY          # optional operands
+    cols = lambda plan, k=0, v=0, q=FAKE, dout=FAKE, rec=FAKE, sink=FAKE: capi.raw_status(
+        "graph_attn_gather_probe_cols", plan.handle if plan else None, capi.GA_BF16, 8, 32,
+        c_void_p(k), c_void_p(v), c_void_p(q), c_void_p(dout), c_void_p(rec), c_void_p(sink),
+        None)
+    assert cols(None) == capi.GA_ERR_INVALID_ARG
+    assert cols(p, dout=0) == capi.GA_ERR_INVALID_ARG
+    assert cols(p, rec=FAKE + 4) == capi.GA_ERR_INVALID_ARG
+    assert cols(p, q=FAKE + 8) == capi.GA_ERR_INVALID_ARG
+    assert cols(p) == capi.GA_ERR_NOT_READY
+    assert cols(Plan(ip, ix, build_csc=False)) == capi.GA_ERR_NOT_READY
+    rnd = lambda rb=512, t=FAKE, rows=100, n=10, sink=FAKE: capi.raw_status(
+        "graph_attn_gather_probe_random", rb, c_void_p(t), rows, n, 7, c_void_p(sink), None)
+    assert rnd(rb=48) == capi.GA_ERR_UNSUPPORTED
+    assert rnd(rows=0) == capi.GA_ERR_INVALID_ARG
+    assert rnd(rows=1 << 32) == capi.GA_ERR_INVALID_ARG
+    assert rnd(n=-1) == capi.GA_ERR_INVALID_ARG
+    assert rnd(t=FAKE + 8) == capi.GA_ERR_INVALID_ARG
+    assert rnd(n=0) == capi.GA_OK                               # nothing to launch
 
 
 def test_fwd_gatv2_argument_checks():

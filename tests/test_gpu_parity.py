@@ -472,17 +472,27 @@ def test_full_chunglu1m_training_step_sampled(plan_kw):
     check_lse("full chunglu1m training step lse", host64(r[1][rt]), rl)
 
 
-def test_gather_probe_runs_on_the_plan_graph():
+@pytest.mark.parametrize("plan_kw", FULL_PLANS)
+def test_gather_probes_run_on_the_plan_graph(plan_kw):
+    """The probes run over the plan's own work lists (rows and, with the transpose,
+    columns) and the random-table probe over a table; none writes its sink."""
     w = gg.WORKLOADS["chunglu1m_dot_bf16"]
     ip, ix = gg.make_graph(w, n=20_000)
     q, k, v = gg.make_features(w, n=20_000)
-    say("gather probe chunglu20k")
-    from sparse_graph_attention_02_amd import gather_probe
-    plan = Plan(ip, ix).upload()
-    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
-    gather_probe(plan, dev(k), dev(v), sink=sink)
+    say("gather probes chunglu20k", plan_kw)
+    from sparse_graph_attention_02_amd import gather_probe, gather_probe_cols, gather_probe_random
+    plan = Plan(ip, ix, **plan_kw).upload()
+    tq, tk, tv = dev(q), dev(k), dev(v)
+    rec = torch.zeros((20_000, 8, 2), dtype=torch.float32, device="cuda")
+    sinks = [gather_probe(plan, tk, tv, row_a=tq),
+             gather_probe(plan, tk, row_a=tq, row_b=tv),
+             gather_probe_cols(plan, tv, q=tq, record=rec, k=tk, v=tv),
+             gather_probe_cols(plan, tv),
+             gather_probe_random(tk, 512, 100_000),
+             gather_probe_random(tk, 64, 1000, table_rows=7)]
     torch.cuda.synchronize()
-    assert int(sink.sum()) == 0   # the probe writes its sink only on a 64-bit XOR collision
+    for s in sinks:   # a probe writes its sink only on a 96-bit XOR collision
+        assert int(s.sum()) == 0
 
 
 # ------------------------------------------------------------------ GAT-style backward
