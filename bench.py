@@ -7,11 +7,17 @@ the backward (dQ over CSR, dK/dV over the cached transpose).  The graph plan is 
 once per graph, before the timed region, as the method caches graph metadata.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+    python bench.py --ingest-counters DIR --workload NAME   # rocprofv3 CSV -> profiles/
 
 Prints one JSON line.  ``value`` is edges/s of the whole step (E / step time) with
-inputs resident in HBM; ``roofline`` is the dominant kernel's algorithmic bytes per
-launch over its measured average duration (HIP events recorded by the library on the
-launch stream); ``cpu_baseline`` is the fp64 oracle timed on this host on a time-boxed
+inputs resident in HBM.  ``roofline`` rates the dominant kernel against the 8 TB/s HBM
+peak by the L2-miss bytes its launches move (rocprofv3 FETCH_SIZE and WRITE_SIZE, from
+the committed counter runs of the same kernel sources and plan) over its average
+duration measured here with HIP events on the launch stream: an upper bound on its HBM
+rate, as the 256 MB MALL may serve some of those misses; ``compulsory`` beside it is the
+lower bound (every operand and output row once).  ``floors`` time gather-only probes
+over the same plan's work lists; ``gather_ceiling`` gathers random rows from tables of
+growing size.  ``cpu_baseline`` is the fp64 oracle timed on this host on a time-boxed
 uniform sample of rows (same edges/s unit).
 """
 from __future__ import annotations
@@ -32,6 +38,9 @@ if ROOT not in sys.path:
 import graphgen as gg  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# oracle worker processes: every CPU this process may run on, at most the 16 host CPUs
+# allotted to each GPU
+HOST_CPUS_PER_GPU = 16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # XCD split thresholds of the attention workloads' plans (rows, transpose columns): a sweep
 # on the 1M-node training step gave 19.19 ms unsplit, 17.54 ms at 256 / 1024, 17.71 ms at
@@ -45,8 +54,10 @@ XCD_SPLIT_REDUCE = 512
 # ---------------------------------------------------------------- algorithmic bytes
 
 def algorithmic_bytes(kernel, N, E, H, d, b, score="dot"):
-    """Bytes a launch must move at minimum: the CSR (or transpose) once, one read of each
-    gathered row per edge, each per-node operand once and each output once."""
+    """Logical bytes of a launch: the CSR (or transpose) once, one read of each gathered
+    row per edge, each per-node operand once and each output once.  Power-law graphs
+    re-gather hot rows, which the L2 and the MALL serve, so these bytes over the time can
+    exceed the HBM peak: a work rate, not a fraction of any memory roofline."""
     F = H * d
     csr = 4 * (N + 1) + 4 * E
     if kernel == "fwd_main":
@@ -98,6 +109,39 @@ def step_bytes(N, E, H, d, b, backward, score="dot"):
     return tot
 
 
+def compulsory_bytes(kernel, N, E, H, d, b, score="dot"):
+    """Bytes a launch cannot avoid moving from HBM: the CSR (or transpose) once and every
+    operand and output row once, however often the pass gathers it.  Over the launch's
+    time, a lower bound on its HBM rate."""
+    F = H * d
+    row = N * F * b               # one [N, H, d] operand
+    nh = 4 * N * H                # one fp32 [N, H] array
+    csr = 4 * (N + 1) + 4 * E
+    if kernel == "fwd_main":
+        if score == "gat":      # s, t, V; out, lse
+            return csr + 2 * nh + row + row + nh
+        if score == "gatv2":    # xd, xs; out, lse; attn
+            return csr + 2 * row + row + nh + 4 * F
+        return csr + 3 * row + row + nh                       # Q, K, V; out, lse
+    if kernel == "bwd_dq_main":    # Q, K, V, dOut, lse; dQ, record
+        return csr + 4 * row + nh + row + 2 * nh
+    if kernel == "bwd_dkdv_main":  # Q, dOut, record, K, V; dK, dV
+        return csr + 4 * row + 2 * nh + 2 * row
+    if kernel == "bwd_gat_rows_main":    # s, t, V, dOut, lse; ds, record
+        return csr + 2 * nh + 2 * row + nh + nh + 2 * nh
+    if kernel == "bwd_gat_cols_main":    # s, dOut, record, t, V; dt, dV
+        return csr + nh + row + 2 * nh + nh + row + nh + row
+    if kernel == "bwd_gatv2_rows_main":  # xs, xd, dOut, lse, attn; dxd, record
+        return csr + 3 * row + nh + 4 * F + row + 2 * nh
+    if kernel == "bwd_gatv2_cols_main":  # xd, dOut, record, xs, attn; dxs
+        return csr + 3 * row + 2 * nh + 4 * F + row
+    if kernel == "reduce_fwd_main":      # x; out, int32 arg, 16-bit slot
+        return csr + row + row + 4 * N * F + 2 * N * F
+    if kernel == "reduce_bwd_main":      # csc_rel, slots, dOut; dx
+        return csr + 4 * E + 2 * N * F + row + row
+    return None
+
+
 # ---------------------------------------------------------------- CPU baseline (oracle)
 
 _SHARED = {}
@@ -144,7 +188,8 @@ def _cpu_worker(args):
 
 def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     import multiprocessing as mp
-    cores = min(16, len(os.sched_getaffinity(0)))
+    affinity = len(os.sched_getaffinity(0))
+    cores = min(HOST_CPUS_PER_GPU, affinity)
     red = w.score in REDUCTIONS
     _SHARED.update(ip=ip, ix=ix, q=feats[0], k=None if red else feats[1],
                    v=None if red else feats[2], dout=dout, scale=scale, score=w.score, slope=0.2)
@@ -173,7 +218,8 @@ def cpu_baseline(ip, ix, feats, dout, w, scale, budget_s):
     if red:
         what = f"{w.score}-pooling {what} (backward: the rows' routed gradient)"
     return {
-        "value": e / longest, "unit": "edges/s", "cores": cores, "kind": "oracle",
+        "value": e / longest, "unit": "edges/s", "cores": cores, "affinity_cpus": affinity,
+        "kind": "oracle",
         "sample": f"{what} of {r} uniformly sampled rows ({e} edges) of the same graph, "
                   f"time-boxed to {budget_s:.0f} s per worker on {cores} fork workers "
                   f"(fp64 numpy per-row oracle, 1 BLAS thread each); wall {wall:.1f} s; "
@@ -247,8 +293,8 @@ def xcd_split_of(w, rows=None, cols=None):
 
 
 def source_digest():
-    """Digest of the device sources (kernels and the headers they include); host-only
-    files (the planner, the C-ABI layer) do not change what the counters measured."""
+    """Digest of the device sources (kernels and the headers they include): counters
+    taken on other kernel sources do not describe these kernels."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_graph_attention_02_amd", "csrc")
@@ -259,17 +305,214 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
-    the current kernel sources (else None)."""
+# what fixes the work a kernel launch does besides its sources: the plan (bins, chunks,
+# schedules, slices) and the node order
+PLAN_KEYS = ("light_max_deg", "hub_min_deg_exclusive", "hub_chunk", "n_row_light",
+             "n_row_medium", "n_row_hub", "n_row_chunks", "n_col_hub", "n_col_chunks",
+             "max_in_degree", "max_out_degree", "rows_sorted", "feature_slices",
+             "col_hub_min_deg_exclusive", "col_hub_chunk", "xcd_split_min_deg_exclusive",
+             "col_xcd_split_min_deg_exclusive", "n_row_sched", "n_col_sched")
+
+
+def measured_traffic(workload, kernel, plan, node_order, path=None):
+    """L2-miss bytes per launch of `kernel` from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources, the same plan and node order (else
+    None)."""
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(path or TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     rec = t.get(workload, {}).get(kernel)
     if not rec or rec.get("source_digest") != source_digest():
         return None
+    if rec.get("plan") != {k: plan[k] for k in PLAN_KEYS} or \
+            rec.get("node_order", "as-generated") != node_order:
+        return None
     return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- counter ingestion
+
+def _kernel_short(name):
+    """`void ga::(anonymous namespace)::fwd_main<unsigned short, 32, 4, 0, 8>(ga::FwdArgs)`
+    -> `fwd_main<unsigned short, 32, 4, 0, 8>`."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("ga::(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:i]
+    return n
+
+
+def _kernel_base(n):
+    return n.split("<")[0]
+
+
+def _last_json_line(path):
+    last = None
+    for line in open(path):
+        if line.startswith("{"):
+            last = line
+    if last is None:
+        raise ValueError(f"{path}: no bench line")
+    return json.loads(last)
+
+
+def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
+    """Summarise one workload's rocprofv3 runs of this script into profiles/.
+
+    run_dir holds `kt.log` (the output of the kernel-trace run, whose last line is its
+    bench line), `kt/**/*kernel_stats.csv` (rocprofv3 --kernel-trace --stats), and one
+    folder per counter pass `p<k>/**/*counter_collection.csv` with `p<k>.counters` naming
+    its counters.  Writes <workload>.kernel_trace.txt and <workload>.counters.txt and the
+    workload's records in traffic.json: per kernel, L2-miss bytes per launch =
+    FETCH_SIZE * 1024 * f + WRITE_SIZE * 1024 * w, where f and w make the library's copy
+    kernel, which reads and writes exactly 1 GiB per launch in every bench run, read 1 GiB
+    each; with the counters' source digest, plan and node order.  Returns the records."""
+    import csv
+    import glob
+    from collections import defaultdict
+    prof = profiles_dir or os.path.join(ROOT, "profiles")
+    tpath = traffic_path or os.path.join(prof, "traffic.json")
+    bl = _last_json_line(os.path.join(run_dir, "kt.log"))
+    cfg = bl["config"]
+    if cfg["workload"] != workload:
+        raise ValueError(f"{run_dir}: bench line of {cfg['workload']}, not {workload}")
+    N, E, H, dim = cfg["nodes"], cfg["edges"], cfg["heads"], cfg["dim"]
+    desc = f"{workload} (N={N}, E={E}, H={H}, d={dim}, {bl['dtype']}, {cfg['step']})"
+    plan = cfg["plan"]
+    split = (f"xcd split rows {plan.get('xcd_split_min_deg_exclusive', 0)} / columns "
+             f"{plan.get('col_xcd_split_min_deg_exclusive', 0)}; node order "
+             f"{cfg.get('node_order', 'as-generated')}")
+    stats = glob.glob(os.path.join(run_dir, "kt", "**", "*kernel_stats.csv"), recursive=True)
+    if len(stats) != 1:
+        raise ValueError(f"{run_dir}/kt: expected one kernel_stats.csv, found {len(stats)}")
+    st = [(_kernel_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e6,
+           float(r["MinNs"]) / 1e6, float(r["MaxNs"]) / 1e6, float(r["Percentage"]))
+          for r in csv.DictReader(open(stats[0]))]
+    lib = {k: v["avg_ms"] for k, v in bl["kernels"].items()}
+    cmd_kt = ("rocprofv3 --kernel-trace --stats --output-format csv -d <run>/kt -o kt -- "
+              f"python3 bench.py --cpu-budget 0 --workload {workload}")
+    if cfg.get("node_order", "as-generated") != "as-generated":
+        cmd_kt += f" --order {cfg['node_order']}"
+    out = [f"# rocprofv3 kernel trace: {desc}",
+           f"# command (repo root): {cmd_kt} > <run>/kt.log",
+           f"# plan: {split}",
+           f"# bench line of the same run: ms_per_step={bl['ms_per_step']:.3f}  "
+           f"value={bl['value']:.4g} edges/s",
+           "# library event timers of the same run (avg ms): "
+           + ", ".join(f"{k}={v:.4f}" for k, v in lib.items()),
+           f"# written by: python3 bench.py --ingest-counters <run> --workload {workload}",
+           "", f"{'kernel':52s} {'calls':>6s} {'avg_ms':>9s} {'min_ms':>9s} {'max_ms':>9s} "
+           f"{'pct':>6s}"]
+    for n, c, a, mn, mx, pc in st:
+        out.append(f"{n:52s} {c:6d} {a:9.4f} {mn:9.4f} {mx:9.4f} {pc:6.2f}")
+    os.makedirs(prof, exist_ok=True)
+    open(os.path.join(prof, f"{workload}.kernel_trace.txt"), "w").write("\n".join(out) + "\n")
+    avg = {_kernel_base(n): a for n, c, a, mn, mx, pc in st}
+    # counters: kernel -> counter -> mean over its dispatches
+    vals = defaultdict(lambda: defaultdict(list))
+    passes = []
+    for cf in sorted(glob.glob(os.path.join(run_dir, "p*.counters"))):
+        pname = os.path.basename(cf)[:-len(".counters")]
+        passes.append(open(cf).read().strip())
+        for f in glob.glob(os.path.join(run_dir, pname, "**", "*counter_collection.csv"),
+                           recursive=True):
+            for r in csv.DictReader(open(f)):
+                vals[_kernel_short(r["Kernel_Name"])][r["Counter_Name"]].append(
+                    float(r["Counter_Value"]))
+    cnt = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    cp = next((c for k, c in cnt.items() if _kernel_base(k) == "copy_probe"), None)
+    if not cp or "FETCH_SIZE" not in cp or "WRITE_SIZE" not in cp:
+        raise ValueError(f"{run_dir}: no FETCH_SIZE / WRITE_SIZE of copy_probe to calibrate")
+    ff = (1 << 30) / (cp["FETCH_SIZE"] * 1024)
+    wf = (1 << 30) / (cp["WRITE_SIZE"] * 1024)
+    order_arg = "" if cfg.get("node_order", "as-generated") == "as-generated" \
+        else f" --order {cfg['node_order']}"
+    o = [f"# rocprofv3 counters: {desc}", f"# plan: {split}",
+         "# one run per pass (repo root):"]
+    o += [f"#   timeout -s KILL 240 rocprofv3 --pmc {p} --output-format csv -d <run>/p{k + 1} "
+          f"-o p{k + 1} -- python3 bench.py --cpu-budget 0 --workload {workload}{order_arg} "
+          "--steps 1 --warmup 1" for k, p in enumerate(passes)]
+    o += [f"# written by: python3 bench.py --ingest-counters <run> --workload {workload}",
+          "#", "# calibration with the library copy kernel (1 GiB read + 1 GiB written per "
+          "launch, in every run):",
+          f"#   FETCH_SIZE reads {cp['FETCH_SIZE']:.0f} KiB -> fetch factor {ff:.4f};  "
+          f"WRITE_SIZE reads {cp['WRITE_SIZE']:.0f} KiB -> write factor {wf:.4f}",
+          "# traffic = FETCH_SIZE*1024*fetch_factor + WRITE_SIZE*1024*write_factor, bytes per "
+          "launch: L2 misses (TCC to EA requests), which the 256 MB MALL in front of HBM may "
+          "serve, so an upper bound on HBM bytes; compulsory = every operand and output row "
+          "once, a lower bound.", ""]
+    b = 2 if bl["dtype"] == "bf16" else 4
+    score = cfg["score"]
+    recs = {}
+    dig = source_digest()
+    for k in sorted(cnt):
+        c = cnt[k]
+        kb = _kernel_base(k)
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        fb, wb = c["FETCH_SIZE"] * 1024 * ff, c["WRITE_SIZE"] * 1024 * wf
+        t = fb + wb
+        line = f"   fetch {fb / 1e9:9.3f} GB   write {wb / 1e9:8.3f} GB   traffic " \
+               f"{t / 1e9:9.3f} GB/launch"
+        logical = algorithmic_bytes(kb, N, E, H, dim, b, score)
+        comp = compulsory_bytes(kb, N, E, H, dim, b, score)
+        if logical:
+            line += f"   logical {logical / 1e9:9.3f} GB  compulsory {comp / 1e9:7.3f} GB  " \
+                    f"traffic/logical {t / logical:.3f}"
+        o += [k, line]
+        a = avg.get(kb)
+        if a:
+            l2 = f"   avg {a:.4f} ms -> traffic rate {t / (a * 1e-3) / 1e9:8.1f} GB/s " \
+                 f"({t / (a * 1e-3) / 1e9 / HBM_PEAK_GBPS:.3f} of 8 TB/s)"
+            if logical:
+                l2 += f", compulsory rate {comp / (a * 1e-3) / 1e9:7.1f} GB/s, logical rate " \
+                      f"{logical / (a * 1e-3) / 1e9:8.1f} GB/s"
+            o.append(l2)
+        hr = None
+        if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c:
+            hr = c["TCC_HIT_sum"] / max(1.0, c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+            extra = ""
+            if "TCC_EA0_RDREQ_sum" in c:
+                extra = f"   EA read requests {c['TCC_EA0_RDREQ_sum']:.4g}"
+                if "TCC_EA0_RDREQ_128B_sum" in c:
+                    extra += f" (128B {c['TCC_EA0_RDREQ_128B_sum']:.4g})"
+            o.append(f"{extra}   L2 hit {c['TCC_HIT_sum']:.4g} miss {c['TCC_MISS_sum']:.4g} -> "
+                     f"hit rate {hr:.3f}")
+        sq = [x for x in ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_LDS",
+                          "SQ_INSTS_SALU", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
+                          "SQ_ACTIVE_INST_VALU") if x in c]
+        if sq:
+            o.append("   SQ: " + "  ".join(f"{x[3:].lower()} {c[x]:.4g}" for x in sq))
+            if "SQ_INSTS_VALU" in c and logical and E:
+                o.append(f"   VALU wave-instructions per edge {c['SQ_INSTS_VALU'] / E:.2f}")
+        o.append("")
+        if kb not in ("copy_probe", "__amd_rocclr_copyBuffer") and not kb.startswith("__amd"):
+            recs[kb] = {"bytes_per_launch": t, "fetch_bytes": fb, "write_bytes": wb,
+                        "fetch_factor": ff, "write_factor": wf, "l2_hit_rate": hr,
+                        "source_digest": dig, "plan": {q: plan[q] for q in PLAN_KEYS},
+                        "node_order": cfg.get("node_order", "as-generated")}
+    open(os.path.join(prof, f"{workload}.counters.txt"), "w").write("\n".join(o))
+    try:
+        tj = json.load(open(tpath))
+    except (OSError, ValueError):
+        tj = {}
+    tj[workload] = recs
+    with open(tpath, "w") as f:
+        json.dump(tj, f, indent=1, sort_keys=True)
+    return recs
+
+
+# ---------------------------------------------------------------- main
+
+def _rates(bytes_, ms):
+    return None if bytes_ is None or not ms else bytes_ / (ms * 1e-3) / 1e9
 
 
 def main():
@@ -300,11 +543,20 @@ def main():
                     help="node order ablation: relabel nodes by descending out-degree (hot "
                          "source rows contiguous) or by reverse Cuthill-McKee (locality) "
                          "before the run")
+    ap.add_argument("--ceiling-gathers", type=int, default=1 << 25,
+                    help="rows gathered per table size by the random-table ceiling (0 = skip)")
+    ap.add_argument("--ingest-counters", metavar="DIR", default=None,
+                    help="summarise the rocprofv3 runs in DIR for --workload into profiles/ "
+                         "(no GPU)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
               "(the fused layer is measured on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.ingest_counters:
+        recs = ingest_counters(args.ingest_counters, args.workload)
+        print(json.dumps({k: round(v["bytes_per_launch"] / 1e9, 3) for k, v in recs.items()}))
+        return
 
     w = gg.WORKLOADS[args.workload]
     args.xcd_split, args.col_xcd_split = xcd_split_of(w, args.xcd_split, args.col_xcd_split)
@@ -325,8 +577,8 @@ def main():
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(ip, ix, feats, dout, w, scale, args.cpu_budget)
-        print(f"[bench] cpu oracle: {cpu['value']:.3g} edges/s on {cpu['cores']} cores",
-              file=sys.stderr, flush=True)
+        print(f"[bench] cpu oracle: {cpu['value']:.3g} edges/s on {cpu['cores']} cores "
+              f"(affinity {cpu['affinity_cpus']})", file=sys.stderr, flush=True)
 
     # ---- GPU from here on
     import torch
@@ -347,7 +599,8 @@ def main():
     tdo = to_dev(dout) if dout is not None else None
     stream = torch.cuda.current_stream()
 
-    # copy-kernel bandwidth on this device (the measured ceiling next to the 8 TB/s spec)
+    # copy-kernel bandwidth on this device (the measured ceiling next to the 8 TB/s spec;
+    # also the calibration kernel of the traffic counters)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -458,32 +711,93 @@ def main():
     step()
     torch.cuda.synchronize()
     step_peak_extra = torch.cuda.max_memory_allocated() - base_alloc
-    # gather floor: the forward's neighbour gathers alone (same graph, same lane pattern)
-    sink = torch.empty(1024, dtype=torch.uint8, device="cuda")
-    # dot gathers two rows per edge (K_j, V_j); the other forms one (the probe then loads
-    # the same row twice and the second load hits in cache)
-    kv = (tens[1], tens[2]) if w.score == "dot" else (vt, vt)
-    ga.gather_probe(plan, *kv, sink=sink)
-    ms_gather, _ = timed(lambda: ga.gather_probe(plan, *kv, sink=sink), args.steps)
-    rows_per_edge = 2 if w.score == "dot" else 1
-    gather_bytes = rows_per_edge * E * H * d * b + 4 * E
-    main_fwd = "reduce_fwd_main" if red else "fwd_main"
 
+    # floors: the passes' loads alone, over the same plan's work lists (gather-only probes)
+    sink = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    probes = {}
+    if red:
+        probes["reduce_fwd_main"] = ("rows", lambda: ga.gather_probe(plan, tens[0], sink=sink))
+    elif w.score == "gatv2":
+        probes["fwd_main"] = ("rows", lambda: ga.gather_probe(plan, tens[1], row_a=tens[0],
+                                                              sink=sink))
+    elif w.score == "gat":
+        probes["fwd_main"] = ("rows", lambda: ga.gather_probe(plan, tens[2], sink=sink))
+    else:
+        probes["fwd_main"] = ("rows", lambda: ga.gather_probe(plan, tens[1], tens[2],
+                                                              row_a=tens[0], sink=sink))
+    if w.backward and not red:
+        rec = torch.zeros((N, H, 2), dtype=torch.float32, device="cuda")
+        if w.score == "dot":
+            probes["bwd_dq_main"] = ("rows", lambda: ga.gather_probe(
+                plan, tens[1], tens[2], row_a=tens[0], row_b=tdo, sink=sink))
+            probes["bwd_dkdv_main"] = ("cols", lambda: ga.gather_probe_cols(
+                plan, tdo, q=tens[0], record=rec, k=tens[1], v=tens[2], sink=sink))
+        elif w.score == "gatv2":
+            probes["bwd_gatv2_cols_main"] = ("cols", lambda: ga.gather_probe_cols(
+                plan, tdo, q=tens[0], record=rec, k=tens[1], sink=sink))
+    floor_ms = {}
+    for name, (kind, fn) in probes.items():
+        fn()
+        pm, pk = timed(fn, args.steps)
+        floor_ms[name] = next(t / n for n, t in pk.values())
+
+    # gather ceiling: uniformly random rows of the workload's row width from tables of
+    # growing size (L2-, MALL- and HBM-resident), the memory hierarchy's gather rate
+    ceiling = None
+    row_bytes = H * d * b
+    if args.ceiling_gathers > 0 and row_bytes in (64, 128, 256, 512, 1024):
+        sizes = [2 << 20, 64 << 20, 512 << 20, 2 << 30, 8 << 30]
+        table = torch.zeros(sizes[-1], dtype=torch.uint8, device="cuda")
+        ceiling = {"row_bytes": row_bytes, "gathers": args.ceiling_gathers, "tables": []}
+        for sz in sizes:
+            fn = lambda: ga.gather_probe_random(table, row_bytes, args.ceiling_gathers,
+                                                table_rows=sz // row_bytes, sink=sink)
+            fn()
+            pm, _ = timed(fn, 5)
+            gbps = args.ceiling_gathers * row_bytes / (pm * 1e-3) / 1e9
+            ceiling["tables"].append({"table_bytes": sz, "ms": pm, "GBps": gbps})
+        del table
+    torch.cuda.synchronize()
+    if int(sink.sum()) != 0:
+        raise RuntimeError("a probe wrote its sink")
+
+    main_fwd = "reduce_fwd_main" if red else "fwd_main"
+    node_order = args.order
     kernels = {}
     for name, (launches, tot) in kt.items():
         per = tot / launches
-        ab = algorithmic_bytes(name, N, E, H, d, b, w.score)
         kernels[name] = {"launches_per_step": launches / args.steps, "avg_ms": per,
                          "share": tot / (ms_step * args.steps)}
-        if ab is not None:
-            kernels[name].update(algorithmic_bytes=ab, GBps=ab / (per * 1e-3) / 1e9)
-    dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
+        lb = algorithmic_bytes(name, N, E, H, d, b, w.score)
+        cb = compulsory_bytes(name, N, E, H, d, b, w.score)
+        tb = measured_traffic(w.name, name, info, node_order)
+        if lb is not None:
+            kernels[name].update(logical_bytes=lb, logical_GBps=_rates(lb, per),
+                                 compulsory_bytes=cb, compulsory_GBps=_rates(cb, per))
+        if tb is not None:
+            kernels[name].update(l2_miss_bytes=tb, l2_miss_GBps=_rates(tb, per))
+        if name in floor_ms:
+            kernels[name].update(floor_ms=floor_ms[name], over_floor=per / floor_ms[name])
+    dom = max((k for k in kernels if "logical_bytes" in kernels[k]),
               key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches_per_step"])
     dk_ = kernels[dom]
-    ach = dk_["GBps"]
-    traffic = measured_traffic(w.name, dom)
-    fwd_bytes = step_bytes(N, E, H, d, b, False, w.score)
+    up = dk_.get("l2_miss_GBps")
+
+    def bracket(names, ms):
+        """Compulsory (lower) and L2-miss (upper) bounds of the HBM rate of the kernels
+        `names` over `ms` per step, and their fractions of the peak (None when a kernel's
+        counters are not on record)."""
+        comp = sum(compulsory_bytes(k, N, E, H, d, b, w.score) or 0 for k in names
+                   if k in kernels)
+        miss = [kernels[k].get("l2_miss_bytes") for k in names if k in kernels]
+        lo = _rates(comp, ms)
+        hi = _rates(sum(miss), ms) if miss and None not in miss else None
+        return {"hbm_GBps_lower": lo, "frac_lower": lo / HBM_PEAK_GBPS,
+                "hbm_GBps_upper": hi, "frac_upper": None if hi is None else hi / HBM_PEAK_GBPS}
+
+    fwd_names = [k for k in kt_fwd]
     tot_bytes = step_bytes(N, E, H, d, b, w.backward, w.score)
+    fwd_bytes = step_bytes(N, E, H, d, b, False, w.score)
     fwd_main_ms = kt_fwd[main_fwd][1] / kt_fwd[main_fwd][0]
     rec = {
         "metric": "fused graph-attn fwd/bwd edges/sec + achieved HBM GB/s (% of MI355X peak)",
@@ -503,41 +817,48 @@ def main():
             "workload": w.name,
             "graph": w.graph, "nodes": N, "edges": E, "heads": H, "dim": d,
             "score": w.score, "step": "forward+backward" if w.backward else "forward",
-            "node_order": args.order,
-            "plan": {k: info[k] for k in ("light_max_deg", "hub_min_deg_exclusive", "hub_chunk",
-                                          "n_row_light", "n_row_medium", "n_row_hub",
-                                          "n_row_chunks", "n_col_hub", "n_col_chunks",
-                                          "max_in_degree", "max_out_degree", "rows_sorted",
-                                          "feature_slices", "col_hub_min_deg_exclusive",
-                                          "col_hub_chunk", "xcd_split_min_deg_exclusive",
-                                          "col_xcd_split_min_deg_exclusive", "n_row_sched",
-                                          "n_col_sched")},
+            "node_order": node_order,
+            "plan": {k: info[k] for k in PLAN_KEYS},
             "parallelism": "single GPU",
         },
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic},
+        "roofline": {
+            "bound": "hbm", "kernel": dom, "achieved": up, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": None if up is None else up / HBM_PEAK_GBPS,
+            "traffic": dk_.get("l2_miss_bytes"),
+            "basis": "achieved = the kernel's L2-miss bytes per launch (rocprofv3 FETCH_SIZE "
+                     "and WRITE_SIZE, calibrated on the copy kernel; committed counter runs of "
+                     "these kernel sources and this plan) / its average launch time here: an "
+                     "upper bound on its HBM rate, as the MALL may serve misses",
+            "compulsory_GBps": dk_["compulsory_GBps"],
+            "frac_compulsory": dk_["compulsory_GBps"] / HBM_PEAK_GBPS,
+            "compulsory_basis": "every operand and output row moved once: a lower bound on "
+                                "its HBM rate",
+            "logical_GBps": dk_["logical_GBps"],
+            "logical_basis": "one read of every gathered row per edge (re-gathers served by "
+                             "L2 and MALL included): a work rate, not a memory fraction",
+            "floor_ms": dk_.get("floor_ms"), "over_floor": dk_.get("over_floor"),
+        },
         "cpu_baseline": cpu,
-        "step_GBps_algorithmic": tot_bytes / (ms_step * 1e-3) / 1e9,
-        "step_frac_of_peak": tot_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "step_frac_of_copy_probe": tot_bytes / (ms_step * 1e-3) / 1e9 / copy_gbps,
-        "fwd": {"ms": ms_fwd, "ms_distribution": dist_fwd, "edges_per_s": E / (ms_fwd * 1e-3),
-                "GBps_algorithmic": fwd_bytes / (ms_fwd * 1e-3) / 1e9,
-                "frac_of_peak": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                "frac_of_copy_probe": fwd_bytes / (ms_fwd * 1e-3) / 1e9 / copy_gbps,
-                "fwd_main_ms": fwd_main_ms},
-        "bwd": ({"ms": ms_bwd, "ms_distribution": dist_bwd, "edges_per_s": E / (ms_bwd * 1e-3),
-                 "GBps_algorithmic": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9,
-                 "frac_of_peak": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                 "frac_of_copy_probe": (tot_bytes - fwd_bytes) / (ms_bwd * 1e-3) / 1e9 / copy_gbps,
-                 "note": "the backward alone, timed after a forward"}
+        "step": dict(bracket(list(kt), ms_step),
+                     logical_GBps=_rates(tot_bytes, ms_step),
+                     frac_of_copy_probe_logical=_rates(tot_bytes, ms_step) / copy_gbps),
+        "fwd": dict({"ms": ms_fwd, "ms_distribution": dist_fwd,
+                     "edges_per_s": E / (ms_fwd * 1e-3), "main_ms": fwd_main_ms,
+                     "logical_GBps": _rates(fwd_bytes, ms_fwd)},
+                    **bracket(fwd_names, ms_fwd),
+                    note="the forward alone; the bracket is its HBM rate between the "
+                         "compulsory bytes and the L2-miss bytes of its kernels"),
+        "bwd": (dict({"ms": ms_bwd, "ms_distribution": dist_bwd,
+                      "edges_per_s": E / (ms_bwd * 1e-3),
+                      "logical_GBps": _rates(tot_bytes - fwd_bytes, ms_bwd)},
+                     **bracket([k for k in kt if k not in kt_fwd], ms_bwd),
+                     note="the backward alone, timed after a forward")
                 if w.backward else None),
-        "gather_floor": {
-            "ms": ms_gather, "GBps_algorithmic": gather_bytes / (ms_gather * 1e-3) / 1e9,
-            "fwd_main_frac_of_floor": ms_gather / fwd_main_ms,
-            "rows_per_edge": rows_per_edge,
-            "note": "the source rows of every edge gathered with the forward's lane pattern "
-                    "and no arithmetic (graph_attn_gather_probe); the memory system's floor "
-                    "for the forward's gathers on this graph"},
+        "floors": {k: {"probe_ms": floor_ms[k], "kernel_ms": kernels[k]["avg_ms"],
+                       "kernel_over_floor": kernels[k]["avg_ms"] / floor_ms[k],
+                       "probe": probes[k][0]}
+                   for k in floor_ms if k in kernels},
+        "gather_ceiling": ceiling,
         "kernels": kernels,
         "copy_probe_GBps": copy_gbps,
         "plan_build_s": plan_host_s, "plan_build_and_upload_s": plan_s,

@@ -112,3 +112,75 @@ def test_xcd_split_defaults_of_the_workloads():
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 0) == (0, 0)
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 2048) == (2048, 2048)
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 128, 0) == (128, 0)
+
+
+def _fake_run(tmp, workload="chunglu1m_train_bf16", fetch_copy=524288, write_copy=1048576,
+              fetch_k=1_000_000, write_k=20_000):
+    """A directory shaped like the rocprofv3 runs of bench.py: the kernel-trace run's log
+    and stats, and two counter passes (FETCH_SIZE, WRITE_SIZE) with the copy kernel."""
+    import json
+    run = tmp / "run"
+    plan = {k: i for i, k in enumerate(bench.PLAN_KEYS)}
+    line = {"ms_per_step": 10.0, "value": 1e9, "dtype": "bf16",
+            "config": {"workload": workload, "nodes": 1000, "edges": 5000, "heads": 8,
+                       "dim": 32, "score": "dot", "step": "forward+backward",
+                       "node_order": "as-generated", "plan": plan},
+            "kernels": {"fwd_main": {"avg_ms": 0.5}}}
+    (run / "kt" / "host").mkdir(parents=True)
+    (run / "kt.log").write_text("[bench] noise\n" + json.dumps(line) + "\n")
+    name_k = "void ga::(anonymous namespace)::fwd_main<unsigned short, 32, 4, 0, 8>(ga::FwdArgs)"
+    (run / "kt" / "host" / "kt_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        f'"{name_k}",10,5000000,500000,90.0,490000,510000,1.0\n'
+        '"void ga::(anonymous namespace)::copy_probe(HIP_vector_type<unsigned int, 4u>*)",'
+        '3,1200000,400000,10.0,390000,410000,1.0\n')
+    for k, (ctr, vcopy, vk) in enumerate((("FETCH_SIZE", fetch_copy, fetch_k),
+                                          ("WRITE_SIZE", write_copy, write_k)), 1):
+        d = run / f"p{k}" / "host"
+        d.mkdir(parents=True)
+        rows = ['"Kernel_Name","Counter_Name","Counter_Value"']
+        rows += [f'"{name_k}","{ctr}",{vk}', f'"{name_k}","{ctr}",{vk}',
+                 f'"copy_probe","{ctr}",{vcopy}']
+        (d / f"p{k}_counter_collection.csv").write_text("\n".join(rows) + "\n")
+        (run / f"p{k}.counters").write_text(ctr + "\n")
+    return run, plan
+
+
+def test_counter_ingest_calibrates_on_the_copy_kernel(tmp_path):
+    """FETCH_SIZE counts 64 bytes per 128-byte request on this part: the copy kernel moving
+    1 GiB each way reads 524,288 KiB fetched and 1,048,576 KiB written, so the factors are
+    2 and 1, and a kernel reading 1,000,000 KiB fetched and 20,000 KiB written moves
+    (2 * 1,000,000 + 20,000) * 1024 bytes per launch."""
+    run, plan = _fake_run(tmp_path)
+    prof = tmp_path / "profiles"
+    tpath = prof / "traffic.json"
+    recs = bench.ingest_counters(str(run), "chunglu1m_train_bf16", profiles_dir=str(prof),
+                                 traffic_path=str(tpath))
+    r = recs["fwd_main"]
+    assert r["fetch_factor"] == pytest.approx(2.0) and r["write_factor"] == pytest.approx(1.0)
+    assert r["bytes_per_launch"] == pytest.approx((2 * 1_000_000 + 20_000) * 1024)
+    assert "copy_probe" not in recs
+    assert (prof / "chunglu1m_train_bf16.kernel_trace.txt").read_text().count("fwd_main") >= 1
+    assert "fetch factor 2.0000" in (prof / "chunglu1m_train_bf16.counters.txt").read_text()
+    # read back only for the same sources, plan and node order
+    info = dict(plan)
+    got = bench.measured_traffic("chunglu1m_train_bf16", "fwd_main", info, "as-generated",
+                                 path=str(tpath))
+    assert got == pytest.approx(r["bytes_per_launch"])
+    info["n_row_sched"] += 1
+    assert bench.measured_traffic("chunglu1m_train_bf16", "fwd_main", info, "as-generated",
+                                  path=str(tpath)) is None
+    assert bench.measured_traffic("chunglu1m_train_bf16", "fwd_main", plan, "rcm",
+                                  path=str(tpath)) is None
+
+
+def test_compulsory_bytes_bound_the_logical_bytes():
+    """Every operand row once is never more than one read per gathered edge (E >= N), and
+    the dot forward's compulsory bytes are the CSR plus five [N, H, d] / [N, H] arrays."""
+    N, E, H, d, b = 1000, 50_000, 8, 32, 2
+    for k in ("fwd_main", "bwd_dq_main", "bwd_dkdv_main", "reduce_fwd_main"):
+        assert bench.compulsory_bytes(k, N, E, H, d, b) <= bench.algorithmic_bytes(k, N, E, H, d, b)
+    assert bench.compulsory_bytes("fwd_main", N, E, H, d, b) == \
+        4 * (N + 1) + 4 * E + 4 * N * H * d * b + 4 * N * H
+    assert bench.compulsory_bytes("fwd_main", 1_000_000, 50_997_829, 8, 32, 2) == \
+        pytest.approx(2.29e9, rel=0.01)
