@@ -292,13 +292,33 @@ def xcd_split_of(w, rows=None, cols=None):
     return rows, cols
 
 
-def source_digest():
-    """Digest of the device sources (kernels and the headers they include): counters
-    taken on other kernel sources do not describe these kernels."""
+# the device source file of each kernel family; every kernel also includes the shared
+# device and internal headers
+KERNEL_SOURCES = (("fwd_", "fwd.hip"), ("bwd_dq_", "bwd.hip"), ("bwd_dkdv_", "bwd.hip"),
+                  ("bwd_gat_", "bwd_gat.hip"), ("bwd_gatv2_", "bwd_gatv2.hip"),
+                  ("reduce_", "reduce.hip"), ("gather_probe", "probe.hip"),
+                  ("copy_probe", "probe.hip"))
+SHARED_HEADERS = ("ga_device.h", "ga_internal.h")
+
+
+def kernel_source(kernel):
+    """The .hip file that defines `kernel` (None if unknown)."""
+    for prefix, src in KERNEL_SOURCES:
+        if kernel.startswith(prefix):
+            return src
+    return None
+
+
+def source_digest(kernel=None):
+    """Digest of the device sources a kernel is built from (its .hip file and the shared
+    headers; every device source when `kernel` is None or unknown): counters taken on
+    other sources do not describe that kernel."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_graph_attention_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    src = kernel_source(kernel) if kernel else None
+    files = sorted(os.listdir(csrc)) if src is None else sorted((src,) + SHARED_HEADERS)
+    for f in files:
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
@@ -323,7 +343,7 @@ def measured_traffic(workload, kernel, plan, node_order, path=None):
     except (OSError, ValueError):
         return None
     rec = t.get(workload, {}).get(kernel)
-    if not rec or rec.get("source_digest") != source_digest():
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     if rec.get("plan") != {k: plan[k] for k in PLAN_KEYS} or \
             rec.get("node_order", "as-generated") != node_order:
@@ -397,7 +417,7 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
           for r in csv.DictReader(open(stats[0]))]
     lib = {k: v["avg_ms"] for k, v in bl["kernels"].items()}
     cmd_kt = ("rocprofv3 --kernel-trace --stats --output-format csv -d <run>/kt -o kt -- "
-              f"python3 bench.py --cpu-budget 0 --workload {workload}")
+              f"python3 bench.py --cpu-budget 0 --ceiling-gathers 0 --workload {workload}")
     if cfg.get("node_order", "as-generated") != "as-generated":
         cmd_kt += f" --order {cfg['node_order']}"
     out = [f"# rocprofv3 kernel trace: {desc}",
@@ -437,8 +457,8 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
     o = [f"# rocprofv3 counters: {desc}", f"# plan: {split}",
          "# one run per pass (repo root):"]
     o += [f"#   timeout -s KILL 240 rocprofv3 --pmc {p} --output-format csv -d <run>/p{k + 1} "
-          f"-o p{k + 1} -- python3 bench.py --cpu-budget 0 --workload {workload}{order_arg} "
-          "--steps 1 --warmup 1" for k, p in enumerate(passes)]
+          f"-o p{k + 1} -- python3 bench.py --cpu-budget 0 --ceiling-gathers 0 --workload "
+          f"{workload}{order_arg} --steps 1 --warmup 1" for k, p in enumerate(passes)]
     o += [f"# written by: python3 bench.py --ingest-counters <run> --workload {workload}",
           "#", "# calibration with the library copy kernel (1 GiB read + 1 GiB written per "
           "launch, in every run):",
@@ -451,7 +471,6 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
     b = 2 if bl["dtype"] == "bf16" else 4
     score = cfg["score"]
     recs = {}
-    dig = source_digest()
     for k in sorted(cnt):
         c = cnt[k]
         kb = _kernel_base(k)
@@ -496,7 +515,8 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
         if kb not in ("copy_probe", "__amd_rocclr_copyBuffer") and not kb.startswith("__amd"):
             recs[kb] = {"bytes_per_launch": t, "fetch_bytes": fb, "write_bytes": wb,
                         "fetch_factor": ff, "write_factor": wf, "l2_hit_rate": hr,
-                        "source_digest": dig, "plan": {q: plan[q] for q in PLAN_KEYS},
+                        "source_digest": source_digest(kb),
+                        "plan": {q: plan[q] for q in PLAN_KEYS},
                         "node_order": cfg.get("node_order", "as-generated")}
     open(os.path.join(prof, f"{workload}.counters.txt"), "w").write("\n".join(o))
     try:

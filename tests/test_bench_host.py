@@ -184,3 +184,18 @@ def test_compulsory_bytes_bound_the_logical_bytes():
         4 * (N + 1) + 4 * E + 4 * N * H * d * b + 4 * N * H
     assert bench.compulsory_bytes("fwd_main", 1_000_000, 50_997_829, 8, 32, 2) == \
         pytest.approx(2.29e9, rel=0.01)
+
+
+def test_kernel_digests_follow_their_own_sources():
+    """A counter record is tied to the source file of its kernel and the shared headers,
+    so editing one kernel family's file leaves the other families' records valid."""
+    assert bench.kernel_source("fwd_main") == "fwd.hip"
+    assert bench.kernel_source("bwd_dkdv_merge") == "bwd.hip"
+    assert bench.kernel_source("bwd_gat_cols_main") == "bwd_gat.hip"
+    assert bench.kernel_source("bwd_gatv2_rows_main") == "bwd_gatv2.hip"
+    assert bench.kernel_source("reduce_bwd_main") == "reduce.hip"
+    assert bench.kernel_source("gather_probe_cols") == "probe.hip"
+    assert bench.source_digest("fwd_main") == bench.source_digest("fwd_hub_merge")
+    assert bench.source_digest("fwd_main") != bench.source_digest("bwd_dq_main")
+    csrc = os.path.join(ROOT, "sparse_graph_attention_02_amd", "csrc")
+    assert all(os.path.exists(os.path.join(csrc, f)) for _, f in bench.KERNEL_SOURCES)
