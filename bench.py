@@ -430,6 +430,7 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
            f"# written by: python3 bench.py --ingest-counters <run> --workload {workload}",
            "", f"{'kernel':52s} {'calls':>6s} {'avg_ms':>9s} {'min_ms':>9s} {'max_ms':>9s} "
            f"{'pct':>6s}"]
+    st = [x for x in st if kernel_source(_kernel_base(x[0]))]   # the library's kernels
     for n, c, a, mn, mx, pc in st:
         out.append(f"{n:52s} {c:6d} {a:9.4f} {mn:9.4f} {mx:9.4f} {pc:6.2f}")
     os.makedirs(prof, exist_ok=True)
@@ -474,7 +475,7 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
     for k in sorted(cnt):
         c = cnt[k]
         kb = _kernel_base(k)
-        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c or not kernel_source(kb):
             continue
         fb, wb = c["FETCH_SIZE"] * 1024 * ff, c["WRITE_SIZE"] * 1024 * wf
         t = fb + wb
@@ -512,7 +513,7 @@ def ingest_counters(run_dir, workload, profiles_dir=None, traffic_path=None):
             if "SQ_INSTS_VALU" in c and logical and E:
                 o.append(f"   VALU wave-instructions per edge {c['SQ_INSTS_VALU'] / E:.2f}")
         o.append("")
-        if kb not in ("copy_probe", "__amd_rocclr_copyBuffer") and not kb.startswith("__amd"):
+        if kb != "copy_probe":
             recs[kb] = {"bytes_per_launch": t, "fetch_bytes": fb, "write_bytes": wb,
                         "fetch_factor": ff, "write_factor": wf, "l2_hit_rate": hr,
                         "source_digest": source_digest(kb),

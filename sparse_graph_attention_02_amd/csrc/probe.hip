@@ -99,7 +99,7 @@ __device__ __forceinline__ void probe_edges(const ProbeArgs& a, int e0, int e1, 
 // wavefront each), then light items (one G-lane group each). Rows run in feature slices
 // as the forward does.
 template <int G, int U, bool COLS>
-__global__ __launch_bounds__(kBlock) void gather_probe_items(ProbeArgs a0) {
+__device__ __forceinline__ void probe_items(const ProbeArgs& a0) {
   constexpr int NG = kWave / G;
   const int lane = threadIdx.x & (kWave - 1);
   const SliceItem si = slice_of(a0.slices);
@@ -144,6 +144,16 @@ __global__ __launch_bounds__(kBlock) void gather_probe_items(ProbeArgs a0) {
   else
     probe_edges<G, U, 1, COLS>(a, e0, e1, g * G, 0, r, h, acc);
   probe_sink(a, acc, lane);
+}
+
+template <int G, int U>
+__global__ __launch_bounds__(kBlock) void gather_probe_rows(ProbeArgs a) {
+  probe_items<G, U, false>(a);
+}
+
+template <int G, int U>
+__global__ __launch_bounds__(kBlock) void gather_probe_cols(ProbeArgs a) {
+  probe_items<G, U, true>(a);
 }
 
 // Uniformly random rows of a table: gather k of a launch reads row
@@ -212,8 +222,12 @@ int launch_items(const ProbeLaunch& p, void* stream, TimerHook hook) {
   switch (GS) {
 #define GA_G(GG)                                                                        \
   case GG:                                                                              \
-    hipLaunchKernelGGL((gather_probe_items<GG, kProbeUnroll, COLS>),                    \
-                       dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);     \
+    if (COLS)                                                                           \
+      hipLaunchKernelGGL((gather_probe_cols<GG, kProbeUnroll>),                         \
+                         dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);   \
+    else                                                                                \
+      hipLaunchKernelGGL((gather_probe_rows<GG, kProbeUnroll>),                         \
+                         dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);   \
     break;
     GA_G(4) GA_G(8) GA_G(16) GA_G(32) GA_G(64)
 #undef GA_G
