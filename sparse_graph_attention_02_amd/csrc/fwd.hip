@@ -33,6 +33,17 @@
 namespace ga {
 namespace {
 
+// LeakyReLU with slope s as alpha z + beta |z|, alpha = (1 + s) / 2, beta = (1 - s) / 2: the
+// two forms agree for either sign of z and any s, so a . LeakyReLU(z) is alpha a . z +
+// beta a . |z|, two FMAs per element (|z| is a free source modifier) and no compare or
+// select.
+struct LeakySplit {
+  float alpha, beta;
+};
+__device__ __forceinline__ LeakySplit leaky_split(float slope) {
+  return {0.5f * (1.f + slope), 0.5f * (1.f - slope)};
+}
+
 template <typename T, int G, int LH, int MODE, int U>
 struct Fwd {
   static constexpr bool GAT = MODE == kModeGat;
@@ -57,12 +68,14 @@ struct Fwd {
   }
 
   // Row-side operand of the score: the query row slice (dot), s[i, h] (gat), or the
-  // destination projection xd_i plus the lane's slice of the attention vector (gatv2).
+  // destination projection xd_i plus the lane's slice of the attention vector and the two
+  // halves of the LeakyReLU split (gatv2; see leaky_split).
   struct RowOp {
     raw_t q;
     float si;
     float xd[GATV2 ? VEC : 1];
     float av[GATV2 ? VEC : 1];
+    LeakySplit ls;
   };
 
   __device__ __forceinline__ static void load_row(const FwdArgs& a, int row, int r, int h,
@@ -74,6 +87,7 @@ struct Fwd {
     }
     if constexpr (GATV2) {
       L16::unpack(q.q, q.xd);
+      q.ls = leaky_split(a.neg_slope);
       const f32x4* ap = reinterpret_cast<const f32x4*>(a.attn + r * VEC);
 #pragma unroll
       for (int k = 0; k < VEC / 4; ++k) {
@@ -134,13 +148,15 @@ struct Fwd {
           } else if constexpr (GATV2) {
             float xs[VEC];
             L16::unpack(kr[u], xs);
-            float e = 0.f;
+            // a . LeakyReLU(z) = alpha a . z + beta a . |z|: two FMAs per element
+            float e1 = 0.f, e2 = 0.f;
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {
               const float z = q.xd[c] + xs[c];
-              e = fmaf(q.av[c], z >= 0.f ? z : z * a.neg_slope, e);
+              e1 = fmaf(q.av[c], z, e1);
+              e2 = fmaf(q.av[c], fabsf(z), e2);
             }
-            x = head_sum<LH>(e) * a.sc2;
+            x = head_sum<LH>(fmaf(q.ls.alpha, e1, q.ls.beta * e2)) * a.sc2;
           } else {
             x = head_sum<LH>(L16::dot(q.q, kr[u])) * a.sc2;
           }
