@@ -176,9 +176,10 @@ struct Bwd : RowIO<T, G, LH> {
 // (a.dq_stride floats per chunk, a multiple of 4 so the 16-byte stores stay aligned). The
 // main kernel works on a feature slice of G lanes (whole heads; see fwd_main); each slice
 // writes its part of A, B, D and L.
-template <typename T, int G, int LH, int U>
+template <typename T, int G, int LH, int U, int UL>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
   using K = Bwd<T, G, LH, U>;
+  using KL = Bwd<T, G, LH, UL>;  // light rows
   using raw_t = typename K::raw_t;
   constexpr int NG = K::NG, VEC = K::VEC, H = K::H;
   const int lane = threadIdx.x & (kWave - 1);
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dq_main(BwdArgs a0) {
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
   K::row_prologue(a, row, r, h, qr, dor, lse2);
-  K::template run_dq<1>(a, e0, e1, g * G, 0, r, qr, dor, lse2, A, Bk, D, Lp);
+  KL::template run_dq<1>(a, e0, e1, g * G, 0, r, qr, dor, lse2, A, Bk, D, Lp);
   K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
 }
 
@@ -275,9 +276,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_merge(BwdArgs a) {
   K::finish_row(a, row, r, h, lse2, A, Bk, D, Lp);
 }
 
-template <typename T, int G, int LH, int U>
+template <typename T, int G, int LH, int U, int UL>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) {
   using K = Bwd<T, G, LH, U>;
+  using KL = Bwd<T, G, LH, UL>;  // light columns
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
   const int lane = threadIdx.x & (kWave - 1);
   const int item = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_dkdv_main(BwdArgs a) 
   const size_t off = static_cast<size_t>(col) * G + r;
   kr = ld_stream(K::R(a.k) + off);
   vr = ld_stream(K::R(a.v) + off);
-  K::template run_dkdv<1>(a, e0, e1, g * G, 0, r, h, kr, vr, dk, dv);
+  KL::template run_dkdv<1>(a, e0, e1, g * G, 0, r, h, kr, vr, dk, dv);
   K::store(a.dk, col, r, dk, a.scale);
   K::store(a.dv, col, r, dv, 1.f);
 }
@@ -376,7 +378,7 @@ struct Launcher {
   static int dq_main(const BwdArgs& a, void* stream, TimerHook hook) {
     const int64_t items = items_of(a.rows);
     if (items <= 0) return 0;
-    return go("bwd_dq_main", bwd_dq_main<T, G, LH, GA_UNROLL_DQ>,
+    return go("bwd_dq_main", bwd_dq_main<T, G, LH, GA_UNROLL_DQ, GA_UNROLL_DQ_LIGHT>,
               slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices), a, stream,
               hook);
   }
@@ -386,7 +388,7 @@ struct Launcher {
     if ((e = go("bwd_dq_merge", bwd_dq_merge<T, G, LH>,
                 (a.rows.n_hub + kWavesPerBlock - 1) / kWavesPerBlock, a, stream, hook)))
       return e;
-    if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, GA_UNROLL_DKDV>,
+    if ((e = go("bwd_dkdv_main", bwd_dkdv_main<T, G, LH, GA_UNROLL_DKDV, GA_UNROLL_DKDV_LIGHT>,
                 (items_of(a.cols) + kWavesPerBlock - 1) / kWavesPerBlock, a, stream, hook)))
       return e;
     return go("bwd_dkdv_merge", bwd_dkdv_merge<T, G, LH>,

@@ -235,9 +235,10 @@ struct Fwd {
 // geometry is the slice's. slice_of() deals slices to XCDs (see ga_device.h); each wave
 // moves its operand pointers to its slice, after which row strides (a.ld lanes, a.hf
 // heads) address the full rows.
-template <typename T, int G, int LH, int MODE, int U>
+template <typename T, int G, int LH, int MODE, int U, int UL>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   using K = Fwd<T, G, LH, MODE, U>;
+  using KL = Fwd<T, G, LH, MODE, UL>;  // light rows
   using raw_t = typename K::raw_t;
   constexpr int NG = K::NG, H = K::H, VEC = K::VEC;
   const int lane = threadIdx.x & (kWave - 1);
@@ -262,10 +263,10 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   }
   const int g = lane / G, r = lane % G, h = r / LH;
   const DevBins& B = a.bins;
-  typename K::State st;
-  typename K::RowOp q;
-  K::init(st);
   if (item < B.n_sched + B.n_medium) {
+    typename K::State st;
+    typename K::RowOp q;
+    K::init(st);
     int row, e0, e1, c = 0;
     const bool chunk = item < B.n_sched;
     if (chunk) {
@@ -293,9 +294,12 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   if (li >= B.n_light) return;
   const int row = B.light[li];
   const int e0 = a.indptr[row], e1 = a.indptr[row + 1];
-  K::load_row(a, row, r, h, q);
-  K::template run<1>(a, e0, e1, g * G, 0, r, h, q, st);
-  K::write_row(a, row, r, h, st);
+  typename KL::State st;
+  typename KL::RowOp q;
+  KL::init(st);
+  KL::load_row(a, row, r, h, q);
+  KL::template run<1>(a, e0, e1, g * G, 0, r, h, q, st);
+  KL::write_row(a, row, r, h, st);
 }
 
 // One wavefront per hub row: lane group g folds chunks c0+g, c0+g+NG, ... in ascending
@@ -341,14 +345,14 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
 // Main kernel on the slice geometry (G lanes per slice), a.slices slices.
 template <typename T, int G, int LH, int MODE>
 int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
-  constexpr int U = GA_UNROLL_FWD;
+  constexpr int U = GA_UNROLL_FWD, UL = GA_UNROLL_FWD_LIGHT;
   constexpr int NG = kWave / G;
   const DevBins& B = a.bins;
   const int64_t items = int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
   if (items <= 0) return 0;
   const int64_t blocks = slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices);
   if (hook) hook("fwd_main", stream, 1);
-  hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U>), dim3(static_cast<unsigned>(blocks)),
+  hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U, UL>), dim3(static_cast<unsigned>(blocks)),
                      dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
   if (hook) hook("fwd_main", stream, 0);
   return static_cast<int>(hipGetLastError());

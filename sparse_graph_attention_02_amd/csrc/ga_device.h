@@ -53,6 +53,18 @@ __device__ __forceinline__ void st_stream(V* p, V x) {
 #ifndef GA_UNROLL_DKDV
 #define GA_UNROLL_DKDV 4
 #endif
+// The same for light rows and columns (at most light_max_deg edges, on power-law graphs
+// mostly a few): fewer slots per step, as masked slots still pay for the score and the
+// exponential.
+#ifndef GA_UNROLL_FWD_LIGHT
+#define GA_UNROLL_FWD_LIGHT 2
+#endif
+#ifndef GA_UNROLL_DQ_LIGHT
+#define GA_UNROLL_DQ_LIGHT 4
+#endif
+#ifndef GA_UNROLL_DKDV_LIGHT
+#define GA_UNROLL_DKDV_LIGHT 4
+#endif
 // Minimum waves per SIMD requested from the register allocator for the main kernels
 // (0 = compiler default).
 #ifndef GA_WAVES_PER_EU

@@ -28,9 +28,11 @@ __global__ __launch_bounds__(kBlock) void copy_probe(u32x4* __restrict__ dst,
 
 // Gather-only probes: the memory traffic of a pass with its arithmetic taken out. Each
 // loads what the pass it stands beside loads, in the same order, with the same lanes
-// (16 bytes per lane, G lanes per row), the same work items and the same edges in flight,
-// and folds the loaded words into an XOR that keeps the loads live; none writes anything
-// but an improbable sink store. Their durations are floors for those passes' times on the
+// (16 bytes per lane, G lanes per row), the same work items and index batches, and folds
+// the loaded words into an XOR that keeps the loads live; none writes anything but an
+// improbable sink store. Every item keeps 8 edges in flight per lane group, at least as
+// many as the passes (a pass with fewer, and arithmetic between its loads, measured no
+// faster than a probe with 8). Their durations are floors for those passes' times on the
 // same graph and plan: what the memory system takes to deliver their reads.
 struct ProbeArgs {
   const int32_t* ptr;     // indptr (rows) or colptr (columns)
@@ -98,7 +100,7 @@ __device__ __forceinline__ void probe_edges(const ProbeArgs& a, int e0, int e1, 
 // [0, n_sched) chunk slots (the plan's XCD schedule, -1 = unused), then medium items (one
 // wavefront each), then light items (one G-lane group each). Rows run in feature slices
 // as the forward does.
-template <int G, int U, bool COLS>
+template <int G, int U, int UL, bool COLS>
 __device__ __forceinline__ void probe_items(const ProbeArgs& a0) {
   constexpr int NG = kWave / G;
   const int lane = threadIdx.x & (kWave - 1);
@@ -142,18 +144,20 @@ __device__ __forceinline__ void probe_items(const ProbeArgs& a0) {
   if (wide)
     probe_edges<G, U, NG, COLS>(a, e0, e1, 0, g, r, h, acc);
   else
-    probe_edges<G, U, 1, COLS>(a, e0, e1, g * G, 0, r, h, acc);
+    probe_edges<G, UL, 1, COLS>(a, e0, e1, g * G, 0, r, h, acc);
   probe_sink(a, acc, lane);
 }
 
-template <int G, int U>
+constexpr int kProbeUnroll = 8;
+
+template <int G>
 __global__ __launch_bounds__(kBlock) void gather_probe_rows(ProbeArgs a) {
-  probe_items<G, U, false>(a);
+  probe_items<G, kProbeUnroll, kProbeUnroll, false>(a);
 }
 
-template <int G, int U>
+template <int G>
 __global__ __launch_bounds__(kBlock) void gather_probe_cols(ProbeArgs a) {
-  probe_items<G, U, true>(a);
+  probe_items<G, kProbeUnroll, kProbeUnroll, true>(a);
 }
 
 // Uniformly random rows of a table: gather k of a launch reads row
@@ -191,7 +195,6 @@ __global__ __launch_bounds__(kBlock) void gather_probe_random(const u32x4* __res
 }  // namespace
 
 namespace {
-constexpr int kProbeUnroll = 8;
 
 template <bool COLS>
 int launch_items(const ProbeLaunch& p, void* stream, TimerHook hook) {
@@ -223,10 +226,10 @@ int launch_items(const ProbeLaunch& p, void* stream, TimerHook hook) {
 #define GA_G(GG)                                                                        \
   case GG:                                                                              \
     if (COLS)                                                                           \
-      hipLaunchKernelGGL((gather_probe_cols<GG, kProbeUnroll>),                         \
+      hipLaunchKernelGGL((gather_probe_cols<GG>),                                       \
                          dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);   \
     else                                                                                \
-      hipLaunchKernelGGL((gather_probe_rows<GG, kProbeUnroll>),                         \
+      hipLaunchKernelGGL((gather_probe_rows<GG>),                                       \
                          dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, s, a);   \
     break;
     GA_G(4) GA_G(8) GA_G(16) GA_G(32) GA_G(64)
