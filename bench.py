@@ -49,6 +49,10 @@ XCD_SPLIT_ROWS, XCD_SPLIT_COLS = 256, 1024
 # the min / max reduction's chunk partials (value, id, edge) are larger, so its merge is
 # dearer: 7.85 ms unsplit, 7.56 ms at 256 / 1024, 7.40 ms at 512 / 512 on the 1M max step
 XCD_SPLIT_REDUCE = 512
+# column chunk of the dot-score workloads' split plans: a sweep on the 1M training step
+# (columns split above 1024) gave 17.57 ms at the automatic 512-edge chunk, 17.52-17.53 ms
+# at 1024 (and 537 instead of 556 MB of backward workspace), 17.56 ms at 2048, 17.55 at 4096
+XCD_SPLIT_COL_CHUNK = 1024
 
 
 # ---------------------------------------------------------------- algorithmic bytes
@@ -307,6 +311,19 @@ def kernel_source(kernel):
         if kernel.startswith(prefix):
             return src
     return None
+
+
+def bench_plan_kw(w, rows=None, cols=None, col_chunk=None):
+    """The XCD-split plan options bench.py runs workload w with (rows / columns split
+    thresholds as in xcd_split_of; the dot-score workloads' split transpose also takes
+    1024-edge column chunks unless a chunk is given)."""
+    rows, cols = xcd_split_of(w, rows, cols)
+    kw = dict(xcd_split_min_deg_exclusive=rows, col_xcd_split_min_deg_exclusive=cols)
+    if col_chunk is None and cols > 0 and w.score == "dot":
+        col_chunk = XCD_SPLIT_COL_CHUNK
+    if col_chunk is not None:
+        kw["col_hub_chunk"] = col_chunk
+    return kw
 
 
 def source_digest(kernel=None):
@@ -580,7 +597,10 @@ def main():
         return
 
     w = gg.WORKLOADS[args.workload]
-    args.xcd_split, args.col_xcd_split = xcd_split_of(w, args.xcd_split, args.col_xcd_split)
+    pkw = bench_plan_kw(w, args.xcd_split, args.col_xcd_split, args.col_chunk)
+    args.xcd_split = pkw["xcd_split_min_deg_exclusive"]
+    args.col_xcd_split = pkw["col_xcd_split_min_deg_exclusive"]
+    args.col_chunk = pkw.get("col_hub_chunk")
     t0 = time.perf_counter()
     ip, ix = gg.make_graph(w)
     feats = gg.make_features(w)
@@ -701,6 +721,10 @@ def main():
         kt = ga.timers(enable=False, reset=True)
         return ms, kt
 
+    # the library's kernel timers take their hipEvents from a pool that grows on first use;
+    # one untimed pass with the timers on fills it, so that no timed region pays for event
+    # creation (which short kernels cannot hide)
+    timed(step, args.steps)
     ms_step, kt = timed(step, args.steps)
     ms_fwd, kt_fwd = timed(lambda: step(False), args.steps)
 

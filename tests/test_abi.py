@@ -522,3 +522,28 @@ def test_xcd_split_defaults_and_info():
     al = lambda x: (x + 255) // 256 * 256
     nc = info["n_row_chunks"]
     assert p.fwd_workspace_bytes(8, 32) == al(nc * 8 * 2 * 4) + al(nc * 256 * 4)
+
+
+@pytest.mark.parametrize("tx,c", [(16, 4), (32, 16), (256, 2048), (64, 64)])
+def test_split_chunk_count_bound(tx, c):
+    """Upper bound on a split plan's chunks, hence on the hub workspaces: a split row of d
+    edges (d > T_X) gives at most d / C + 8 chunks (eight residue groups, each cut into
+    C-edge chunks), an unsplit hub row at most d / C + 1, and at most E / (T_X + 1) rows
+    are split, so chunks <= E / C + 8 E / (T_X + 1) + E / (T_H + 1). Checked on a power-law
+    graph and on the adversarial one where every row has T_X + 1 edges."""
+    rng = np.random.default_rng(tx)
+    graphs = [gg.make_graph(gg.WORKLOADS["chunglu1m_dot_bf16"], n=4000)]
+    n = 600
+    src = rng.integers(0, n, n * (tx + 1))
+    dst = np.repeat(np.arange(n), tx + 1)
+    graphs.append(gg.csr_from_edges(n, src, dst))
+    for ip, ix in graphs:
+        E = ix.size
+        p = Plan(ip, ix, light_max_deg=min(16, tx), hub_min_deg_exclusive=max(tx, 16) * 4,
+                 hub_chunk=c, xcd_split_min_deg_exclusive=tx, col_xcd_split_min_deg_exclusive=tx,
+                 col_hub_chunk=c)
+        info = p.info()
+        for side, th in (("row", info["hub_min_deg_exclusive"]),
+                         ("col", info["col_hub_min_deg_exclusive"])):
+            bound = E / c + 8 * E / (tx + 1) + E / (th + 1)
+            assert info[f"n_{side}_chunks"] <= bound, (side, info[f"n_{side}_chunks"], bound)

@@ -112,6 +112,14 @@ def test_xcd_split_defaults_of_the_workloads():
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 0) == (0, 0)
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 2048) == (2048, 2048)
     assert bench.xcd_split_of(W["chunglu1m_train_bf16"], 128, 0) == (128, 0)
+    # the plan options: dot-score split transposes take 1024-edge column chunks
+    assert bench.bench_plan_kw(W["chunglu1m_train_bf16"]) == dict(
+        xcd_split_min_deg_exclusive=256, col_xcd_split_min_deg_exclusive=1024, col_hub_chunk=1024)
+    assert bench.bench_plan_kw(W["chunglu1m_gatv2_train_bf16"]) == dict(
+        xcd_split_min_deg_exclusive=256, col_xcd_split_min_deg_exclusive=1024)
+    assert bench.bench_plan_kw(W["chunglu1m_train_bf16"], 0) == dict(
+        xcd_split_min_deg_exclusive=0, col_xcd_split_min_deg_exclusive=0)
+    assert bench.bench_plan_kw(W["chunglu1m_train_bf16"], col_chunk=512)["col_hub_chunk"] == 512
 
 
 def _fake_run(tmp, workload="chunglu1m_train_bf16", fetch_copy=524288, write_copy=1048576,

@@ -27,8 +27,6 @@ from tests.gpu_util import dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SPLIT = dict(xcd_split_min_deg_exclusive=bench.XCD_SPLIT_ROWS,
-             col_xcd_split_min_deg_exclusive=bench.XCD_SPLIT_COLS)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -89,18 +87,20 @@ def _check_on_host(d, spec):
 @pytest.mark.timeout(900)
 def test_full_training_step_every_element_bench_plan(work_dir):
     w = gg.WORKLOADS["chunglu1m_train_bf16"]
+    plan_kw = bench.bench_plan_kw(w)
     ip, ix = gg.make_graph(w)
     q, k, v = gg.make_features(w)
     dout = gg.make_dout(w)
     scale = float(np.float32(1 / math.sqrt(w.dim)))
-    say("full chunglu1m training step, every element, plan", SPLIT, "E", ix.size)
-    plan = Plan(ip, ix, **SPLIT).upload()
+    say("full chunglu1m training step, every element, plan", plan_kw, "E", ix.size)
+    plan = Plan(ip, ix, **plan_kw).upload()
     assert plan.info()["n_row_sched"] > 0 and plan.info()["n_col_sched"] > 0
     tq, tk, tv, td = dev(q), dev(k), dev(v), dev(dout)
     out, lse = fwd(plan, tq, tk, tv, scale=scale)
     dq, dk, dv = bwd(plan, tq, tk, tv, td, lse, scale=scale)
     # the 1M forward workload runs on a plan of the same split without the transpose
-    plan_fwd = Plan(ip, ix, build_csc=False, **SPLIT).upload()
+    plan_fwd = Plan(ip, ix, build_csc=False,
+                    **bench.bench_plan_kw(gg.WORKLOADS["chunglu1m_dot_bf16"])).upload()
     out2, lse2 = fwd(plan_fwd, tq, tk, tv, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
@@ -116,11 +116,12 @@ def test_full_training_step_every_element_bench_plan(work_dir):
 @pytest.mark.timeout(900)
 def test_full_rmat21_forward_every_row_bench_plan(work_dir):
     w = gg.WORKLOADS["rmat21_dot_bf16"]
+    plan_kw = bench.bench_plan_kw(w)
     ip, ix = gg.make_graph(w)
     q, k, v = gg.make_features(w)
     scale = float(np.float32(1 / math.sqrt(w.dim)))
-    say("full rmat21 forward, every row, plan", SPLIT, "E", ix.size)
-    plan = Plan(ip, ix, build_csc=False, **SPLIT).upload()
+    say("full rmat21 forward, every row, plan", plan_kw, "E", ix.size)
+    plan = Plan(ip, ix, build_csc=False, **plan_kw).upload()
     assert plan.info()["max_in_degree"] > 100_000 and plan.info()["n_row_sched"] > 0
     out, lse = fwd(plan, dev(q), dev(k), dev(v), scale=scale)
     torch.cuda.synchronize()

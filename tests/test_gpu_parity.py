@@ -395,17 +395,18 @@ def test_no_edge_sized_allocation():
 # ------------------------------------------------------------------ full workload sizes
 
 # Plans of the full-size tests: the library default, and the XCD split bench.py uses for
-# the attention workloads (rows above 256 and columns above 1024 edges regrouped)
+# the dot-score workloads (rows above 256 and columns above 1024 edges regrouped, columns
+# in 1024-edge chunks)
 FULL_PLANS = [pytest.param({}, id="default-plan"),
               pytest.param(dict(xcd_split_min_deg_exclusive=256,
-                                col_xcd_split_min_deg_exclusive=1024), id="bench-split-plan")]
+                                col_xcd_split_min_deg_exclusive=1024, col_hub_chunk=1024),
+                           id="bench-split-plan")]
 
 
 def test_full_plans_match_the_bench():
     import bench
-    assert FULL_PLANS[1].values[0] == dict(
-        xcd_split_min_deg_exclusive=bench.XCD_SPLIT_ROWS,
-        col_xcd_split_min_deg_exclusive=bench.XCD_SPLIT_COLS)
+    for name in ("chunglu1m_train_bf16", "chunglu1m_dot_bf16", "rmat21_dot_bf16"):
+        assert FULL_PLANS[1].values[0] == bench.bench_plan_kw(gg.WORKLOADS[name])
 
 
 # The 1M training step (and so the 1M forward) and the R-MAT forward are checked on every
