@@ -48,7 +48,8 @@ __all__ = [
     "backward_gat", "grad_s_rows", "grad_tv_cols", "gatv2_row_scores", "forward_gatv2",
     "forward_gatv2_rows", "backward_gatv2", "grad_gatv2_rows", "grad_gatv2_cols",
     "train_step_rows_gatv2", "forward_online_chunked", "train_step_rows_gat", "row_pass",
-    "transpose_order", "column_pass",
+    "transpose_order", "column_pass", "row_pass_gat", "column_pass_gat", "row_pass_gatv2",
+    "column_pass_gatv2",
 ]
 
 
@@ -437,6 +438,59 @@ def train_step_rows_gat(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slo
     return out, lse, ds, cols, dt, dv
 
 
+def row_pass_gat(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slope=0.2):
+    """The row half of the GAT-style training step for the listed rows: out [R,H,d],
+    lse [R,H] and ds [R,H] of each row, and alpha [M,H] and dS [M,H] of each of its edges,
+    the rows' edges concatenated in the order of ``rows``.  With ``column_pass_gat`` over
+    every column this is ``forward`` plus ``backward_gat``."""
+    sc = float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = v.shape[1], v.shape[2]
+    deg = (indptr[rows + 1] - indptr[rows]).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(deg)])
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    ds = np.zeros((rows.size, H))
+    e_alpha = np.zeros((int(start[-1]), H))
+    e_ds = np.zeros((int(start[-1]), H))
+    for r, i in enumerate(rows):
+        if deg[r] == 0:
+            continue
+        J = _neighbours(indptr, indices, i)
+        e = row_scores(i, indptr, indices, s, t, "gat", sc, neg_slope)
+        alpha, lse[r] = row_softmax(e)
+        vj = widen(v[J])
+        out[r] = np.einsum("kh,khc->hc", alpha, vj)
+        dp = np.einsum("hc,khc->kh", widen(dout[i]), vj)
+        D = (alpha * dp).sum(axis=0)
+        dS = alpha * (dp - D[None, :])
+        g = leaky_relu_grad(widen(s[i])[None, :] + widen(t[J]), float(neg_slope))
+        ds[r] = sc * (dS * g).sum(axis=0)
+        e_alpha[start[r]:start[r + 1]] = alpha
+        e_ds[start[r]:start[r + 1]] = dS
+    return out, lse, ds, e_alpha, e_ds
+
+
+def column_pass_gat(s, t, dout, e_alpha, e_ds, order, col_start, edge_row, cols, scale=1.0,
+                    neg_slope=0.2):
+    """dt [C,H] and dv [C,H,d] of the listed source columns from every edge's alpha and dS
+    (by CSR position, over the transpose of ``transpose_order``): for column j and each
+    edge (i -> j), dt_j += scale dS LeakyReLU'(s_i + t_j) and dv_j += alpha dout_i."""
+    sc = float(scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    dt = np.zeros((cols.size,) + tuple(t.shape[1:]))
+    dv = np.zeros((cols.size,) + tuple(dout.shape[1:]))
+    for c, j in enumerate(cols):
+        es = order[col_start[j]:col_start[j + 1]]
+        if es.size == 0:
+            continue
+        rows = edge_row[es]
+        g = leaky_relu_grad(widen(s[rows]) + widen(t[j])[None, :], float(neg_slope))
+        dt[c] = sc * (e_ds[es] * g).sum(axis=0)
+        dv[c] = np.einsum("eh,ehc->hc", e_alpha[es], widen(dout[rows]))
+    return dt, dv
+
+
 def grad_s_rows(indptr, indices, s, t, v, dout, rows, scale=1.0, neg_slope=0.2):
     """ds [R, H] for the listed rows only."""
     sc = float(scale)
@@ -563,6 +617,59 @@ def backward_gatv2(indptr, indices, xd, xs, attn, dout, scale=1.0, neg_slope=0.2
         np.add.at(dxs, J, w + alpha[:, :, None] * widen(dout[i])[None])
         da += sc * np.einsum("kh,khc->hc", dS, lz)
     return dxd, dxs, da
+
+
+def row_pass_gatv2(indptr, indices, xd, xs, attn, dout, rows, scale=1.0, neg_slope=0.2):
+    """The row half of the GATv2 training step for the listed rows: out [R,H,d], lse [R,H]
+    and dxd [R,H,d] of each row, alpha [M,H] and dS [M,H] of each of its edges (the rows'
+    edges concatenated in the order of ``rows``), and the rows' share of dattn [H,d].
+    With ``column_pass_gatv2`` over every column this is ``forward_gatv2`` plus
+    ``backward_gatv2`` (dattn = the sum of the shares)."""
+    sc = float(scale)
+    a = widen(attn)
+    rows = np.asarray(rows, dtype=np.int64)
+    H, d = xs.shape[1], xs.shape[2]
+    deg = (indptr[rows + 1] - indptr[rows]).astype(np.int64)
+    start = np.concatenate([[0], np.cumsum(deg)])
+    out = np.zeros((rows.size, H, d))
+    lse = np.full((rows.size, H), -np.inf)
+    dxd = np.zeros((rows.size, H, d))
+    da = np.zeros((H, d))
+    e_alpha = np.zeros((int(start[-1]), H))
+    e_ds = np.zeros((int(start[-1]), H))
+    for r, i in enumerate(rows):
+        if deg[r] == 0:
+            continue
+        e = gatv2_row_scores(i, indptr, indices, xd, xs, attn, scale, neg_slope)
+        _, lse[r] = row_softmax(e)
+        J, alpha, dS, g, lz = _row_backward_gatv2(i, indptr, indices, xd, xs, attn, dout, sc,
+                                                  neg_slope)
+        out[r] = np.einsum("kh,khc->hc", alpha, widen(xs[J]))
+        dxd[r] = (sc * dS[:, :, None] * g * a[None]).sum(axis=0)
+        da += sc * np.einsum("kh,khc->hc", dS, lz)
+        e_alpha[start[r]:start[r + 1]] = alpha
+        e_ds[start[r]:start[r + 1]] = dS
+    return out, lse, dxd, e_alpha, e_ds, da
+
+
+def column_pass_gatv2(xd, xs, attn, dout, e_alpha, e_ds, order, col_start, edge_row, cols,
+                      scale=1.0, neg_slope=0.2):
+    """dxs [C,H,d] of the listed source columns from every edge's alpha and dS (by CSR
+    position, over the transpose of ``transpose_order``): for column j and each edge
+    (i -> j), dxs_j += scale dS (attn * LeakyReLU'(xd_i + xs_j)) + alpha dout_i."""
+    sc = float(scale)
+    a = widen(attn)
+    cols = np.asarray(cols, dtype=np.int64)
+    dxs = np.zeros((cols.size,) + tuple(xs.shape[1:]))
+    for c, j in enumerate(cols):
+        es = order[col_start[j]:col_start[j + 1]]
+        if es.size == 0:
+            continue
+        rows = edge_row[es]
+        g = leaky_relu_grad(widen(xd[rows]) + widen(xs[j])[None], float(neg_slope))
+        dxs[c] = (sc * e_ds[es][:, :, None] * g * a[None]).sum(axis=0) + \
+            np.einsum("eh,ehc->hc", e_alpha[es], widen(dout[rows]))
+    return dxs
 
 
 def grad_gatv2_rows(indptr, indices, xd, xs, attn, dout, rows, scale=1.0, neg_slope=0.2):

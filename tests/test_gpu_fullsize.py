@@ -1,8 +1,10 @@
 """GPU parity on every element at full workload sizes, in the launch configuration bench.py
 times (its XCD-split plans): the 1M-node Chung-Lu training step (out, lse, dq, dk, dv over
 all 1M rows and columns; its forward is also the 1M forward workload's, checked bit for
-bit on that workload's transpose-less plan) and the R-MAT 2^21 forward (out, lse over all
-2M rows).
+bit on that workload's transpose-less plan), the R-MAT 2^21 forward (out, lse over all
+2M rows), the 100k GAT-style fp32 training step (out, lse, ds, dt, dv), the 1M GATv2
+training step (out, lse, dxd, dxs and the summed dattn) and the 1M max-pooling training
+step (out, arg and slot exactly, dx).
 
 The GPU results are saved to a directory and compared by a child process
 (tests/fullsize.py) that runs the fp64 oracle over every row and column in forked worker
@@ -22,7 +24,8 @@ import torch
 
 import bench
 import graphgen as gg
-from sparse_graph_attention_02_amd import Plan, bwd, fwd
+from sparse_graph_attention_02_amd import (Plan, bwd, bwd_gatv2, fwd, fwd_gatv2, reduce_bwd,
+                                           reduce_fwd)
 from tests.gpu_util import dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -130,3 +133,78 @@ def test_full_rmat21_forward_every_row_bench_plan(work_dir):
     torch.cuda.empty_cache()
     _check_on_host(work_dir, {"workload": w.name, "graph_cache": os.environ["GRAPHGEN_CACHE"],
                               "scale": scale, "train": False, "gpu": files})
+
+
+@pytest.mark.timeout(900)
+def test_full_gat_training_step_every_element_bench_plan(work_dir):
+    w = gg.WORKLOADS["chunglu100k_gat_train_f32"]
+    plan_kw = bench.bench_plan_kw(w)
+    ip, ix = gg.make_graph(w)
+    s, t, v = gg.make_features(w)
+    dout = gg.make_dout(w)
+    slope = float(np.float32(0.2))
+    say("full chunglu100k GAT-style fp32 training step, every element, plan", plan_kw,
+        "E", ix.size)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    ts, tt, tv, td = dev(s), dev(t), dev(v), dev(dout)
+    out, lse = fwd(plan, ts, tt, tv, score="gat", scale=1.0, neg_slope=slope)
+    ds, dt, dv = bwd(plan, ts, tt, tv, td, lse, score="gat", scale=1.0, neg_slope=slope)
+    torch.cuda.synchronize()
+    files = {n: _save(work_dir, n, x) for n, x in (("out", out), ("lse", lse), ("ds", ds),
+                                                    ("dt", dt), ("dv", dv))}
+    del ts, tt, tv, td, out, lse, ds, dt, dv, plan
+    torch.cuda.empty_cache()
+    _check_on_host(work_dir, {"workload": w.name, "graph_cache": os.environ["GRAPHGEN_CACHE"],
+                              "scale": 1.0, "slope": slope, "train": True, "gpu": files})
+
+
+@pytest.mark.timeout(900)
+def test_full_gatv2_training_step_every_element_bench_plan(work_dir):
+    w = gg.WORKLOADS["chunglu1m_gatv2_train_bf16"]
+    plan_kw = bench.bench_plan_kw(w)
+    ip, ix = gg.make_graph(w)
+    xd, xs, a = gg.make_features(w)
+    dout = gg.make_dout(w)
+    slope = float(np.float32(0.2))
+    say("full chunglu1m GATv2 training step, every element, plan", plan_kw, "E", ix.size)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    assert plan.info()["n_row_sched"] > 0 and plan.info()["n_col_sched"] > 0
+    txd, txs, ta, td = dev(xd), dev(xs), dev(a), dev(dout)
+    out, lse = fwd_gatv2(plan, txd, txs, ta, scale=1.0, neg_slope=slope)
+    dxd, dxs, dattn = bwd_gatv2(plan, txd, txs, ta, td, lse, scale=1.0, neg_slope=slope)
+    torch.cuda.synchronize()
+    files = {n: _save(work_dir, n, x) for n, x in (("out", out), ("lse", lse), ("dxd", dxd),
+                                                    ("dxs", dxs), ("dattn", dattn))}
+    del txd, txs, ta, td, out, lse, dxd, dxs, dattn, plan
+    torch.cuda.empty_cache()
+    _check_on_host(work_dir, {"workload": w.name, "graph_cache": os.environ["GRAPHGEN_CACHE"],
+                              "scale": 1.0, "slope": slope, "train": True, "gpu": files})
+
+
+@pytest.mark.timeout(900)
+def test_full_max_pooling_training_step_every_element_bench_plan(work_dir):
+    w = gg.WORKLOADS["chunglu1m_max_train_bf16"]
+    plan_kw = bench.bench_plan_kw(w)
+    ip, ix = gg.make_graph(w)
+    (x,) = gg.make_features(w)
+    dout = gg.make_dout(w)
+    say("full chunglu1m max-pooling training step, every element, plan", plan_kw,
+        "E", ix.size)
+    plan = Plan(ip, ix, **plan_kw).upload()
+    assert plan.info()["n_row_sched"] > 0
+    tx, td = dev(x), dev(dout)
+    out, arg, slot = reduce_fwd(plan, tx, op="max")
+    dx = reduce_bwd(plan, None, td, slot=slot)
+    torch.cuda.synchronize()
+    files = {n: _save(work_dir, n, t) for n, t in (("out", out), ("arg", arg), ("dx", dx))}
+    # 16-bit slots are unsigned positions (all ones: the row is empty)
+    sl = slot.cpu().numpy()
+    files["slot"] = os.path.join(work_dir, "gpu_slot.npy")
+    np.save(files["slot"], sl.view(np.uint16) if sl.dtype == np.int16 else sl,
+            allow_pickle=False)
+    pix = os.path.join(work_dir, "plan_indices.npy")
+    np.save(pix, plan.array("indices"), allow_pickle=False)
+    del tx, td, out, arg, slot, dx, plan
+    torch.cuda.empty_cache()
+    _check_on_host(work_dir, {"workload": w.name, "graph_cache": os.environ["GRAPHGEN_CACHE"],
+                              "train": True, "gpu": files, "plan_indices": pix})

@@ -302,3 +302,42 @@ def test_row_and_column_passes_in_blocks_are_the_plain_step(seed):
         np.testing.assert_allclose(dk, dk0[c0:c1], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dv, dv0[c0:c1], rtol=1e-12, atol=1e-12)
     assert np.all(dk0[11] == 0) and np.all(dq0[9] == 0)
+
+
+def _blocky_graph(seed, n=70):
+    rng = np.random.default_rng(seed)
+    ip, ix = gg.random_multigraph(n, 900, rng, self_loops=False, hub_rows=(4,), hub_deg=120)
+    dst = np.repeat(np.arange(n), np.diff(ip))
+    keep = (dst != 9) & (ix != 11)                      # row 9 and column 11 empty
+    ip, ix = gg.csr_from_edges(n, ix[keep], dst[keep])
+    return rng, ip, ix
+
+
+@pytest.mark.parametrize("slope", [0.2, -0.3])
+def test_gat_row_and_column_passes_in_blocks_are_the_plain_step(slope):
+    """The GAT-style halves run over random blocks of rows and columns reproduce forward
+    and backward_gat (pinned above by finite differences and dense autograd)."""
+    rng, ip, ix = _blocky_graph(33)
+    n, H, d = 70, 3, 5
+    s, t = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    v, do = rng.standard_normal((n, H, d)), rng.standard_normal((n, H, d))
+    fo, fl = A.forward(ip, ix, s, t, v, "gat", 1.3, slope)
+    ds0, dt0, dv0 = A.backward_gat(ip, ix, s, t, v, do, 1.3, slope)
+    ea, ed = np.full((ix.size, H), np.nan), np.full((ix.size, H), np.nan)
+    cuts = np.unique(np.r_[0, rng.choice(n, 5), n])
+    for r0, r1 in zip(cuts[:-1], cuts[1:]):
+        out, lse, ds, a, e = A.row_pass_gat(ip, ix, s, t, v, do, np.arange(r0, r1), 1.3, slope)
+        np.testing.assert_allclose(out, fo[r0:r1], rtol=1e-13, atol=1e-14)
+        fin = ~np.isneginf(fl[r0:r1])
+        np.testing.assert_array_equal(np.isneginf(lse), ~fin)
+        np.testing.assert_allclose(lse[fin], fl[r0:r1][fin], rtol=1e-13)
+        np.testing.assert_allclose(ds, ds0[r0:r1], rtol=1e-12, atol=1e-12)
+        ea[ip[r0]:ip[r1]], ed[ip[r0]:ip[r1]] = a, e
+    assert not np.isnan(ea).any() and not np.isnan(ed).any()
+    order, col_start, edge_row = A.transpose_order(ip, ix)
+    for c0, c1 in ((0, 11), (11, 12), (12, n)):
+        dt, dv = A.column_pass_gat(s, t, do, ea, ed, order, col_start, edge_row,
+                                   np.arange(c0, c1), 1.3, slope)
+        np.testing.assert_allclose(dt, dt0[c0:c1], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dv, dv0[c0:c1], rtol=1e-12, atol=1e-12)
+    assert np.all(dt0[11] == 0) and np.all(ds0[9] == 0)

@@ -122,3 +122,40 @@ def test_train_step_rows_gatv2_is_the_plain_step():
     o3, _, dxd3, _, _, _ = A.train_step_rows_gatv2(ip, ix, xd, xs, a, do, rows, 0.8, 0.15)
     np.testing.assert_allclose(o3, out[rows], atol=1e-13)
     np.testing.assert_allclose(dxd3, dxd[rows], atol=1e-12)
+
+
+@pytest.mark.parametrize("slope", [0.2, 1.7])
+def test_gatv2_row_and_column_passes_in_blocks_are_the_plain_step(slope):
+    """The GATv2 halves run over random blocks of rows and columns reproduce forward_gatv2
+    and backward_gatv2 (pinned above by dense autograd and finite differences); the
+    blocks' dattn shares sum to dattn."""
+    rng = np.random.default_rng(41)
+    n, H, d = 60, 2, 4
+    ip, ix = gg.random_multigraph(n, 700, rng, self_loops=False, hub_rows=(5,), hub_deg=90)
+    dst = np.repeat(np.arange(n), np.diff(ip))
+    keep = (dst != 7) & (ix != 13)                      # row 7 and column 13 empty
+    ip, ix = gg.csr_from_edges(n, ix[keep], dst[keep])
+    xd, xs, do = (rng.standard_normal((n, H, d)) for _ in range(3))
+    attn = rng.standard_normal((H, d))
+    fo, fl = A.forward_gatv2(ip, ix, xd, xs, attn, 0.8, slope)
+    dxd0, dxs0, da0 = A.backward_gatv2(ip, ix, xd, xs, attn, do, 0.8, slope)
+    ea, ed = np.full((ix.size, H), np.nan), np.full((ix.size, H), np.nan)
+    da = np.zeros((H, d))
+    cuts = np.unique(np.r_[0, rng.choice(n, 5), n])
+    for r0, r1 in zip(cuts[:-1], cuts[1:]):
+        out, lse, dxd, a, e, dap = A.row_pass_gatv2(ip, ix, xd, xs, attn, do,
+                                                   np.arange(r0, r1), 0.8, slope)
+        np.testing.assert_allclose(out, fo[r0:r1], rtol=1e-13, atol=1e-14)
+        fin = ~np.isneginf(fl[r0:r1])
+        np.testing.assert_allclose(lse[fin], fl[r0:r1][fin], rtol=1e-13)
+        np.testing.assert_allclose(dxd, dxd0[r0:r1], rtol=1e-12, atol=1e-12)
+        ea[ip[r0]:ip[r1]], ed[ip[r0]:ip[r1]] = a, e
+        da += dap
+    assert not np.isnan(ea).any() and not np.isnan(ed).any()
+    np.testing.assert_allclose(da, da0, rtol=1e-12, atol=1e-12)
+    order, col_start, edge_row = A.transpose_order(ip, ix)
+    for c0, c1 in ((0, 13), (13, 14), (14, n)):
+        dxs = A.column_pass_gatv2(xd, xs, attn, do, ea, ed, order, col_start, edge_row,
+                                  np.arange(c0, c1), 0.8, slope)
+        np.testing.assert_allclose(dxs, dxs0[c0:c1], rtol=1e-12, atol=1e-12)
+    assert np.all(dxs0[13] == 0) and np.all(dxd0[7] == 0)
