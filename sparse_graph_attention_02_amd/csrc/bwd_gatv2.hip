@@ -125,10 +125,14 @@ struct BwdV2 : RowIO<T, G, LH> {
                                                   float lse2, RowAcc& s) {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
-    const raw_t* __restrict__ Xs = R(a.k);
+    const rows_t Xd = node_rows(a.k, G * int(sizeof(raw_t)), a.n);
+    const int roff = r * int(sizeof(raw_t));
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
+      // lanes past the batch's edges hold node 0; a step's spare slots read those lanes (or,
+      // past the segment, another lane's node), so they load rows already in L2, and their
+      // weight is masked out
       const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
@@ -137,11 +141,11 @@ struct BwdV2 : RowIO<T, G, LH> {
         for (int u = 0; u < U; ++u) {
           const int pos = t + u * NGS + gs;
           ok[u] = pos < nb;
-          jj[u] = __shfl(my_j, seg0 + (ok[u] ? pos : t));
+          jj[u] = __builtin_amdgcn_ds_bpermute((seg0 + pos) << 2, my_j);
         }
         raw_t xr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[u] = Xs[static_cast<size_t>(jj[u]) * G + r];
+        for (int u = 0; u < U; ++u) xr[u] = ld_row<raw_t>(Xd, jj[u], roff);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float xs[VEC];

@@ -107,12 +107,18 @@ struct Fwd {
                                              int r, int h, const RowOp& q, State& st) {
     constexpr int L = NGS * G;  // lanes of the segment = indices fetched per batch
     const int lane = threadIdx.x & (kWave - 1);
-    const raw_t* __restrict__ Kr = static_cast<const raw_t*>(a.b);
+    // K and V rows through structured buffers; GAT's t entries (4 bytes per head, read by
+    // every lane of the head) by plain loads, which serve that pattern faster
+    const rows_t Kd = node_rows(a.b, a.ld * int(sizeof(raw_t)), a.n);
+    const rows_t Vd = node_rows(a.v, a.ld * int(sizeof(raw_t)), a.n);
+    const int roff = r * int(sizeof(raw_t));
     const float* __restrict__ Tt = static_cast<const float*>(a.b);
-    const raw_t* __restrict__ Vr = static_cast<const raw_t*>(a.v);
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
+      // lanes past the batch's edges hold node 0; a step's spare slots read those lanes (or,
+      // past the segment, another lane's node), so they load rows already in L2, and the
+      // softmax below masks them out
       const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
@@ -121,9 +127,7 @@ struct Fwd {
         for (int u = 0; u < U; ++u) {
           const int pos = t + u * NGS + gs;
           ok[u] = pos < nb;
-          // out-of-range slots re-read this step's first edge (valid, cached) and are
-          // masked out of the softmax below
-          jj[u] = __shfl(my_j, seg0 + (ok[u] ? pos : t));
+          jj[u] = __builtin_amdgcn_ds_bpermute((seg0 + pos) << 2, my_j);
         }
         raw_t kr[U], vr[U];
         float tv[U];
@@ -132,11 +136,11 @@ struct Fwd {
           if constexpr (GAT)
             tv[u] = Tt[static_cast<size_t>(jj[u]) * a.hf + h];
           else
-            kr[u] = Kr[static_cast<size_t>(jj[u]) * a.ld + r];
+            kr[u] = ld_row<raw_t>(Kd, jj[u], roff);
           if constexpr (GATV2)
             vr[u] = kr[u];  // the message is the gathered source projection
           else
-            vr[u] = Vr[static_cast<size_t>(jj[u]) * a.ld + r];
+            vr[u] = ld_row<raw_t>(Vd, jj[u], roff);
         }
         float s[U];
 #pragma unroll

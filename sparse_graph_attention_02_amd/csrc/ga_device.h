@@ -43,6 +43,31 @@ __device__ __forceinline__ void st_stream(V* p, V x) {
   __builtin_nontemporal_store(x, p);
 }
 
+// Gathered neighbour rows are read through a structured buffer: one descriptor per tensor
+// (base, row stride in bytes, number of rows), and each load names a node id and this lane's
+// byte offset within the row. The memory unit forms base + id * stride + offset in 64 bits,
+// so no address arithmetic runs on the vector ALU, and an id outside [0, rows) reads zeros.
+// The fourth descriptor word selects 32-bit untyped data (the gfx9 buffer format).
+constexpr int kBufWord3 = 0x00020000;
+using rows_t = __amdgpu_buffer_rsrc_t;
+__device__ __forceinline__ rows_t node_rows(const void* base, int row_bytes, int n_rows) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base),
+                                           static_cast<short>(row_bytes), n_rows, kBufWord3);
+}
+__device__ u32x4 ga_sbuf_ld_v4(rows_t rows, int index, int offset, int soffset, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+__device__ float ga_sbuf_ld_f32(rows_t rows, int index, int offset, int soffset, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.f32");
+template <typename V>
+__device__ __forceinline__ V ld_row(rows_t rows, int node, int offset) {
+  if constexpr (sizeof(V) == 16) {
+    return __builtin_bit_cast(V, ga_sbuf_ld_v4(rows, node, offset, 0, 0));
+  } else {
+    static_assert(sizeof(V) == 4, "16- or 4-byte row elements");
+    return __builtin_bit_cast(V, ga_sbuf_ld_f32(rows, node, offset, 0, 0));
+  }
+}
+
 // Edges folded per lane group per step (independent gathers in flight per lane), per pass.
 #ifndef GA_UNROLL_FWD
 #define GA_UNROLL_FWD 8

@@ -136,6 +136,7 @@ struct FwdArgs {
   int ld;         // feature row stride in 16-byte lanes (the full row)
   int hf;         // heads per node (stride of lse / s / t / partial (m, l))
   int slices;     // feature slices of the main kernel (1, 2, 4 or 8)
+  int n;          // nodes (rows of every node-indexed tensor)
 };
 
 // Backward kernels (bwd.hip).
@@ -163,6 +164,7 @@ struct BwdArgs {
   int hf;            // heads per node (stride of lse and of the records)
   int slices;        // feature slices of the dQ pass (1, 2, 4 or 8)
   int dq_stride;     // floats per dQ chunk partial of the full row (dq_partial_floats)
+  int n;             // nodes (rows of every node-indexed tensor)
   // GATv2 only
   const float* attn;  // attention vector [H*d]
   float* dattn;       // its gradient [H*d]
@@ -218,6 +220,7 @@ struct RedArgs {
   bool rows_sorted;        // host-side: every row's neighbour ids non-decreasing
   int ld;                  // feature row stride in 16-byte lanes (the full row)
   int slices;              // feature slices of the main kernels (1, 2, 4 or 8)
+  int n;                   // nodes (rows of every node-indexed tensor)
   // forward
   const void* x;     // [N, F]
   void* out;         // [N, F]
