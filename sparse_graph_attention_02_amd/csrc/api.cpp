@@ -246,6 +246,7 @@ ga_status fwd_enqueue(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t 
   args.ld = g.G;
   args.hf = g.heads;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
   // GAT-style scores gather t_j per head, a partial line per slice: not sliced; nor are
   // plans whose chunk slots are scheduled to XCDs
   args.slices = score == GA_SCORE_DOT && p->rows.sched.empty()
@@ -497,6 +498,7 @@ ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.ld = g.G;
   args.hf = g.heads;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
   args.slices = p->rows.sched.empty()
                     ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices, 0)
                     : 1;
@@ -559,6 +561,7 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.neg_slope = neg_slope;
   args.ld = g.G;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
   args.hf = g.heads;
   args.slices = p->rows.sched.empty()
                     ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
@@ -630,6 +633,7 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(g.G) * 16);
   const int rc = ga::launch_bwd_gatv2(dtype, g, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
@@ -685,6 +689,7 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   args.rows_sorted = p->rows_sorted;
   args.ld = G;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
   args.slices = p->rows.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   if (need > 0) {
     args.ws_val = static_cast<float*>(ws);
@@ -725,6 +730,7 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.ld = G;
   args.n = static_cast<int>(p->n);
+  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
   args.slices = p->cols.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   args.dout = dout;
   args.dx = dx;

@@ -117,8 +117,9 @@ struct BwdV2 : RowIO<T, G, LH> {
     return head_sum<LH>(e) * a.sc2;
   }
 
-  // Row pass over edges [e0, e1) of a row (xd, dout held by the lane).
-  template <int NGS>
+  // Row pass over edges [e0, e1) of a row (xd, dout held by the lane). WIDE: the xs table
+  // is larger than one 4 GiB buffer window (BwdArgs::wide).
+  template <int NGS, bool WIDE>
   __device__ __forceinline__ static void run_rows(const BwdArgs& a, int e0, int e1, int seg0,
                                                   int gs, int r, const float* xd,
                                                   const raw_t& dor, const float* av,
@@ -126,7 +127,7 @@ struct BwdV2 : RowIO<T, G, LH> {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
     const rows_t Xd = node_rows(a.k, G * int(sizeof(raw_t)), a.n);
-    const int roff = r * int(sizeof(raw_t));
+    const raw_t* __restrict__ Xs = R(a.k);
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
@@ -145,7 +146,7 @@ struct BwdV2 : RowIO<T, G, LH> {
         }
         raw_t xr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[u] = ld_row<raw_t>(Xd, jj[u], roff);
+        for (int u = 0; u < U; ++u) xr[u] = ld_node<WIDE>(Xd, Xs, jj[u], G, r);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float xs[VEC];
@@ -296,7 +297,7 @@ struct BwdV2 : RowIO<T, G, LH> {
   }
 };
 
-template <typename T, int G, int LH, int U>
+template <typename T, int G, int LH, int U, bool WIDE>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdArgs a) {
   using K = BwdV2<T, G, LH, U>;
   constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdAr
       K::L16::unpack(ld_stream(K::R(a.q) + off), xd);
       dor = ld_stream(K::R(a.dout) + off);
       lse2 = ld_stream(a.lse + static_cast<size_t>(row) * K::H + h) * kLog2e;
-      K::template run_rows<NG>(a, e0, e1, 0, g, r, xd, dor, av, lse2, s);
+      K::template run_rows<NG, WIDE>(a, e0, e1, 0, g, r, xd, dor, av, lse2, s);
       K::template combine<NG>(s);
       if (g == 0) {
         if (chunk)
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void bwd_gatv2_rows_main(BwdAr
         K::L16::unpack(ld_stream(K::R(a.q) + off), xd);
         dor = ld_stream(K::R(a.dout) + off);
         lse2 = ld_stream(a.lse + static_cast<size_t>(row) * K::H + h) * kLog2e;
-        K::template run_rows<1>(a, e0, e1, g * G, 0, r, xd, dor, av, lse2, s);
+        K::template run_rows<1, WIDE>(a, e0, e1, g * G, 0, r, xd, dor, av, lse2, s);
         K::finish_row(a, row, r, h, lse2, av, xd, s, da);
       }
     }
@@ -560,8 +561,12 @@ int launch(const BwdArgs& a, void* stream, TimerHook hook) {
   };
   if (row_waves > 0) {
     if (hook) hook("bwd_gatv2_rows_main", stream, 1);
-    hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, rows_unroll<G, LH>()>), blocks(row_waves),
-                       dim3(kBlock), 0, s, a);
+    if (a.wide)
+      hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, rows_unroll<G, LH>(), true>),
+                         blocks(row_waves), dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_gatv2_rows_main<T, G, LH, rows_unroll<G, LH>(), false>),
+                         blocks(row_waves), dim3(kBlock), 0, s, a);
     if ((e = done("bwd_gatv2_rows_main"))) return e;
   }
   if (a.rows.n_hub > 0) {

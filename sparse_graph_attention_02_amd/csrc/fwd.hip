@@ -101,17 +101,20 @@ struct Fwd {
   }
 
   // Stream edges [e0, e1) through the state with NGS lane groups cooperating. seg0 is the
-  // segment's first lane in the wave, gs this lane's group within the segment.
-  template <int NGS>
+  // segment's first lane in the wave, gs this lane's group within the segment. WIDE: the
+  // gathered tables are larger than one 4 GiB buffer window (FwdArgs::wide).
+  template <int NGS, bool WIDE>
   __device__ __forceinline__ static void run(const FwdArgs& a, int e0, int e1, int seg0, int gs,
                                              int r, int h, const RowOp& q, State& st) {
     constexpr int L = NGS * G;  // lanes of the segment = indices fetched per batch
     const int lane = threadIdx.x & (kWave - 1);
-    // K and V rows through structured buffers; GAT's t entries (4 bytes per head, read by
-    // every lane of the head) by plain loads, which serve that pattern faster
+    // K and V rows through structured buffers (plain loads for tables past 4 GiB); GAT's t
+    // entries (4 bytes per head, read by every lane of the head) by plain loads, which serve
+    // that pattern faster
     const rows_t Kd = node_rows(a.b, a.ld * int(sizeof(raw_t)), a.n);
     const rows_t Vd = node_rows(a.v, a.ld * int(sizeof(raw_t)), a.n);
-    const int roff = r * int(sizeof(raw_t));
+    const raw_t* __restrict__ Kr = static_cast<const raw_t*>(a.b);
+    const raw_t* __restrict__ Vr = static_cast<const raw_t*>(a.v);
     const float* __restrict__ Tt = static_cast<const float*>(a.b);
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
@@ -136,11 +139,11 @@ struct Fwd {
           if constexpr (GAT)
             tv[u] = Tt[static_cast<size_t>(jj[u]) * a.hf + h];
           else
-            kr[u] = ld_row<raw_t>(Kd, jj[u], roff);
+            kr[u] = ld_node<WIDE>(Kd, Kr, jj[u], a.ld, r);
           if constexpr (GATV2)
             vr[u] = kr[u];  // the message is the gathered source projection
           else
-            vr[u] = ld_row<raw_t>(Vd, jj[u], roff);
+            vr[u] = ld_node<WIDE>(Vd, Vr, jj[u], a.ld, r);
         }
         float s[U];
 #pragma unroll
@@ -239,7 +242,7 @@ struct Fwd {
 // geometry is the slice's. slice_of() deals slices to XCDs (see ga_device.h); each wave
 // moves its operand pointers to its slice, after which row strides (a.ld lanes, a.hf
 // heads) address the full rows.
-template <typename T, int G, int LH, int MODE, int U, int UL>
+template <typename T, int G, int LH, int MODE, int U, int UL, bool WIDE>
 __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   using K = Fwd<T, G, LH, MODE, U>;
   using KL = Fwd<T, G, LH, MODE, UL>;  // light rows
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
       e1 = a.indptr[row + 1];
     }
     K::load_row(a, row, r, h, q);
-    K::template run<NG>(a, e0, e1, 0, g, r, h, q, st);
+    K::template run<NG, WIDE>(a, e0, e1, 0, g, r, h, q, st);
     K::template combine<NG>(st);
     if (g != 0) return;
     if (chunk)
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
   typename KL::RowOp q;
   KL::init(st);
   KL::load_row(a, row, r, h, q);
-  KL::template run<1>(a, e0, e1, g * G, 0, r, h, q, st);
+  KL::template run<1, WIDE>(a, e0, e1, g * G, 0, r, h, q, st);
   KL::write_row(a, row, r, h, st);
 }
 
@@ -356,8 +359,14 @@ int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
   if (items <= 0) return 0;
   const int64_t blocks = slice_blocks((items + kWavesPerBlock - 1) / kWavesPerBlock, a.slices);
   if (hook) hook("fwd_main", stream, 1);
-  hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U, UL>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kBlock), 0, static_cast<hipStream_t>(stream), a);
+  if (a.wide)
+    hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U, UL, true>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
+  else
+    hipLaunchKernelGGL((fwd_main<T, G, LH, MODE, U, UL, false>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), a);
   if (hook) hook("fwd_main", stream, 0);
   return static_cast<int>(hipGetLastError());
 }

@@ -45,9 +45,11 @@ __device__ __forceinline__ void st_stream(V* p, V x) {
 
 // Gathered neighbour rows are read through a structured buffer: one descriptor per tensor
 // (base, row stride in bytes, number of rows), and each load names a node id and this lane's
-// byte offset within the row. The memory unit forms base + id * stride + offset in 64 bits,
-// so no address arithmetic runs on the vector ALU, and an id outside [0, rows) reads zeros.
-// The fourth descriptor word selects 32-bit untyped data (the gfx9 buffer format).
+// byte offset within the row. The memory unit forms the address (id * stride + offset, a
+// 32-bit byte offset from the base), so no address arithmetic runs on the vector ALU, and an
+// id outside [0, rows) reads zeros. A table larger than 4 GiB does not fit one descriptor;
+// kernels read those with plain 64-bit loads (ld_node below, `wide`). The fourth
+// descriptor word selects 32-bit untyped data (the gfx9 buffer format).
 constexpr int kBufWord3 = 0x00020000;
 using rows_t = __amdgpu_buffer_rsrc_t;
 __device__ __forceinline__ rows_t node_rows(const void* base, int row_bytes, int n_rows) {
@@ -66,6 +68,16 @@ __device__ __forceinline__ V ld_row(rows_t rows, int node, int offset) {
     static_assert(sizeof(V) == 4, "16- or 4-byte row elements");
     return __builtin_bit_cast(V, ga_sbuf_ld_f32(rows, node, offset, 0, 0));
   }
+}
+// Element r (16-byte lanes) of row `node` of a table with rows of ld lanes: through the
+// descriptor, or (WIDE: a table past 4 GiB) by a plain load. Callers pick WIDE once per
+// step from the kernel argument, so the branch is uniform and outside the loads.
+template <bool WIDE, typename V>
+__device__ __forceinline__ V ld_node(rows_t rows, const V* base, int node, int ld, int r) {
+  if constexpr (WIDE)
+    return base[static_cast<size_t>(static_cast<uint32_t>(node)) * ld + r];
+  else
+    return ld_row<V>(rows, node, r * int(sizeof(V)));
 }
 
 // Edges folded per lane group per step (independent gathers in flight per lane), per pass.

@@ -118,6 +118,11 @@ inline int feature_slices(int G, int LH, int requested, int auto_lanes) {
 }
 constexpr int kAutoSliceLanesTwoRows = 16;  // auto slices of the dot forward / dQ pass
 
+// A buffer descriptor addresses its table with a 32-bit byte offset, so gathers read
+// through one only while n rows of row_bytes fit in 4 GiB; larger tables take plain
+// 64-bit loads.
+inline int rows_wide(int64_t n, int64_t row_bytes) { return n * row_bytes > (int64_t(1) << 32); }
+
 // Forward kernels (fwd.hip).
 struct FwdArgs {
   const int32_t* indptr;
@@ -137,6 +142,7 @@ struct FwdArgs {
   int hf;         // heads per node (stride of lse / s / t / partial (m, l))
   int slices;     // feature slices of the main kernel (1, 2, 4 or 8)
   int n;          // nodes (rows of every node-indexed tensor)
+  int wide;       // gathered tables span more than one 4 GiB buffer window (rows_wide)
 };
 
 // Backward kernels (bwd.hip).
@@ -165,6 +171,7 @@ struct BwdArgs {
   int slices;        // feature slices of the dQ pass (1, 2, 4 or 8)
   int dq_stride;     // floats per dQ chunk partial of the full row (dq_partial_floats)
   int n;             // nodes (rows of every node-indexed tensor)
+  int wide;          // gathered tables span more than one 4 GiB buffer window (rows_wide)
   // GATv2 only
   const float* attn;  // attention vector [H*d]
   float* dattn;       // its gradient [H*d]
@@ -221,6 +228,7 @@ struct RedArgs {
   int ld;                  // feature row stride in 16-byte lanes (the full row)
   int slices;              // feature slices of the main kernels (1, 2, 4 or 8)
   int n;                   // nodes (rows of every node-indexed tensor)
+  int wide;                // gathered tables span more than one 4 GiB buffer window
   // forward
   const void* x;     // [N, F]
   void* out;         // [N, F]

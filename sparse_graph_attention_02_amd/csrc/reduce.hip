@@ -121,7 +121,7 @@ struct Red : RowIO<T, G, G> {
     constexpr int L = NGS * G;
     const int lane = threadIdx.x & (kWave - 1);
     const rows_t Xd = node_rows(a.x, a.ld * int(sizeof(raw_t)), a.n);
-    const int roff = r * int(sizeof(raw_t));
+    const raw_t* __restrict__ X = IO::R(a.x);
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
@@ -139,8 +139,15 @@ struct Red : RowIO<T, G, G> {
           jj[u] = __builtin_amdgcn_ds_bpermute((seg0 + pos) << 2, my_j);
         }
         raw_t xr[U];
+        auto gather = [&](auto wide) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) xr[u] = ld_row<raw_t>(Xd, jj[u], roff);
+          for (int u = 0; u < U; ++u)
+            xr[u] = ld_node<decltype(wide)::value>(Xd, X, jj[u], a.ld, r);
+        };
+        if (a.wide)
+          gather(std::true_type{});
+        else
+          gather(std::false_type{});
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float xf[VEC];
