@@ -352,7 +352,9 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
 // Main kernel on the slice geometry (G lanes per slice), a.slices slices.
 template <typename T, int G, int LH, int MODE>
 int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
-  constexpr int U = GA_UNROLL_FWD, UL = GA_UNROLL_FWD_LIGHT;
+  // light rows: the GATv2 score's longer per-edge arithmetic pays for 4 edges in flight,
+  // the dot and GAT-style scores keep GA_UNROLL_FWD_LIGHT
+  constexpr int U = GA_UNROLL_FWD, UL = MODE == kModeGatV2 ? 4 : GA_UNROLL_FWD_LIGHT;
   constexpr int NG = kWave / G;
   const DevBins& B = a.bins;
   const int64_t items = int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;
