@@ -70,8 +70,8 @@ __device__ __forceinline__ V ld_row(rows_t rows, int node, int offset) {
   }
 }
 // Element r (16-byte lanes) of row `node` of a table with rows of ld lanes: through the
-// descriptor, or (WIDE: a table past 4 GiB) by a plain load. Callers pick WIDE once per
-// step from the kernel argument, so the branch is uniform and outside the loads.
+// descriptor, or (WIDE: a table past 4 GiB) by a plain load. WIDE is a kernel template
+// parameter, or a uniform branch taken once per step around a step's loads.
 template <bool WIDE, typename V>
 __device__ __forceinline__ V ld_node(rows_t rows, const V* base, int node, int ld, int r) {
   if constexpr (WIDE)
