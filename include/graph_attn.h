@@ -43,6 +43,11 @@
  *     Argument checks run before any HIP call, so an invalid call enqueues nothing.
  *   Determinism: no atomics anywhere; partial states merge in a fixed order, so two runs
  *     on the same inputs are bitwise identical.
+ *   Gathers: the forward, the GATv2 row pass and the min / max forward read neighbour
+ *     rows through buffer descriptors while N * row bytes <= 2^32, and with plain 64-bit
+ *     loads past that (results are the same either way). Setting the environment
+ *     variable GRAPH_ATTN_WIDE_LOADS=1 makes every call take the 64-bit path (read at
+ *     each call; a testing aid).
  */
 #ifndef GRAPH_ATTN_H
 #define GRAPH_ATTN_H

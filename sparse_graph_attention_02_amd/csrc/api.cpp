@@ -3,6 +3,7 @@
 // call, so a rejected call enqueues nothing.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -18,6 +19,13 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Gathers from tables of n rows of row_bytes: through buffer descriptors unless the table
+// passes 4 GiB, or GRAPH_ATTN_WIDE_LOADS=1 asks for the 64-bit path everywhere.
+int wide_loads(int64_t n, int64_t row_bytes) {
+  const char* e = std::getenv("GRAPH_ATTN_WIDE_LOADS");
+  return ga::rows_wide(n, row_bytes) || (e && e[0] == '1' && e[1] == 0);
+}
 
 // ---------------------------------------------------------------- timers
 struct TimerRec {
@@ -246,7 +254,7 @@ ga_status fwd_enqueue(const ga_plan* p, ga_score score, ga_dtype dtype, int32_t 
   args.ld = g.G;
   args.hf = g.heads;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
+  args.wide = wide_loads(p->n, int64_t(args.ld) * 16);
   // GAT-style scores gather t_j per head, a partial line per slice: not sliced; nor are
   // plans whose chunk slots are scheduled to XCDs
   args.slices = score == GA_SCORE_DOT && p->rows.sched.empty()
@@ -498,7 +506,7 @@ ga_status graph_attn_fwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.ld = g.G;
   args.hf = g.heads;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
+  args.wide = wide_loads(p->n, int64_t(args.ld) * 16);
   args.slices = p->rows.sched.empty()
                     ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices, 0)
                     : 1;
@@ -561,7 +569,7 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.neg_slope = neg_slope;
   args.ld = g.G;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
+  args.wide = wide_loads(p->n, int64_t(args.ld) * 16);
   args.hf = g.heads;
   args.slices = p->rows.sched.empty()
                     ? ga::feature_slices(g.G, g.LH, p->opts.feature_slices,
@@ -633,7 +641,7 @@ ga_status graph_attn_bwd_gatv2(const ga_plan* p, ga_dtype dtype, int32_t heads, 
   args.sc2 = scale * 1.4426950408889634f;
   args.neg_slope = neg_slope;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(g.G) * 16);
+  args.wide = wide_loads(p->n, int64_t(g.G) * 16);
   const int rc = ga::launch_bwd_gatv2(dtype, g, args, stream, active_hook());
   return rc == 0 ? GA_OK : (rc < 0 ? GA_ERR_UNSUPPORTED : GA_ERR_HIP);
 }
@@ -689,7 +697,7 @@ ga_status graph_attn_reduce_fwd(const ga_plan* p, ga_reduce op, ga_dtype dtype,
   args.rows_sorted = p->rows_sorted;
   args.ld = G;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
+  args.wide = wide_loads(p->n, int64_t(args.ld) * 16);
   args.slices = p->rows.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   if (need > 0) {
     args.ws_val = static_cast<float*>(ws);
@@ -730,7 +738,7 @@ ga_status graph_attn_reduce_bwd(const ga_plan* p, ga_dtype dtype, int32_t featur
   args.slot_bytes = ga::reduce_slot_bytes(p->max_in);
   args.ld = G;
   args.n = static_cast<int>(p->n);
-  args.wide = ga::rows_wide(p->n, int64_t(args.ld) * 16);
+  args.wide = wide_loads(p->n, int64_t(args.ld) * 16);
   args.slices = p->cols.sched.empty() ? ga::feature_slices(G, 1, p->opts.feature_slices, 0) : 1;
   args.dout = dout;
   args.dx = dx;
