@@ -111,9 +111,11 @@ struct Red : RowIO<T, G, G> {
   }
 
   // Edges [e0, e1) of a row through the state; NGS lane groups share the edges. The loop
-  // counter runs forward; with SORTED it maps to the edges in reverse (k = e0 + e1 - 1 - n).
+  // counter runs forward; with SORTED it maps to the edges in reverse (k = e1 - 1 - (n - e0),
+  // written so that no intermediate passes 2^31 when the row lies near the end of a graph
+  // of 2^31 - 2^16 edges).
   __device__ __forceinline__ static int edge_of(int e0, int e1, int n) {
-    return SORTED ? e0 + e1 - 1 - n : n;
+    return SORTED ? e1 - 1 - (n - e0) : n;
   }
   template <int NGS>
   __device__ __forceinline__ static void run(const RedArgs& a, int e0, int e1, int seg0, int gs,
