@@ -131,6 +131,35 @@ def test_dot_training_step_past_4gib(graph, split):
 
 
 @pytest.mark.timeout(600)
+def test_gat_training_step_past_4gib(graph):
+    """GAT-style scores: s, t per node and head (fp32), V rows past 4 GiB."""
+    (dt, N, H, D, HIGH), ip, ix, S, ipc, ixc = graph
+    plan = Plan(ip, ix).upload()
+    rng = np.random.default_rng(14)
+    s_, t_ = (rng.standard_normal((S.size, H), dtype=np.float32) for _ in range(2))
+    v, dout = (_rows(rng, S.size, (H, D), dt) for _ in range(2))
+    slope = float(np.float32(0.2))
+    ts, tt = _scatter(N, S, s_), _scatter(N, S, t_)
+    tv, td = _scatter(N, S, v), _scatter(N, S, dout)
+    out, lse = fwd(plan, ts, tt, tv, score="gat", scale=1.0, neg_slope=slope)
+    ds, dtt, dv = bwd(plan, ts, tt, tv, td, lse, score="gat", scale=1.0, neg_slope=slope)
+    torch.cuda.synchronize()
+    del ts, tt, tv, td
+    ro, rl = A.forward(ipc, ixc, s_, t_, v, "gat", 1.0, slope)
+    rs, rt_, rv = A.backward_gat(ipc, ixc, s_, t_, v, dout, 1.0, slope)
+    St = torch.from_numpy(S).cuda()
+    for name, g, r, kind in (("out", out, ro, dt), ("ds", ds, rs, "f32"), ("dt", dtt, rt_, "f32"),
+                             ("dv", dv, rv, dt)):
+        say(name, check(name, host64(g[St]), r, kind))
+    check_lse("lse", host64(lse[St]), rl)
+    o = _others(N, HIGH, S)
+    for name, t in (("out", out), ("ds", ds), ("dt", dtt), ("dv", dv)):
+        _empty_rows(name, t, o)
+    del out, lse, ds, dtt, dv, plan
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
 def test_gatv2_training_step_past_4gib(graph):
     (dt, N, H, D, HIGH), ip, ix, S, ipc, ixc = graph
     plan = Plan(ip, ix).upload()
