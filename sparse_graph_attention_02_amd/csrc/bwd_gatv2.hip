@@ -14,8 +14,9 @@
 //   dattn = scale sum_ij dS_ij LeakyReLU(z_ij) = scale (sum_i xd_i R_i + sum_j xs_j C_j),
 // the last because LeakyReLU(z) = g z and z_ij = xd_i + xs_j: the attention gradient costs
 // one product per node instead of two per edge.
-//   bwd_gatv2_rows_main   over CSR rows: per lane element A1 = sum P dp g, B1 = sum P g,
-//                         R_i = (A1 - D^ B1) / L; writes dxd, the record
+//   bwd_gatv2_rows_main   over CSR rows (xs rows by structured buffer loads, or plain 64-bit
+//                         loads for tables past 4 GiB): per lane element A1 = sum P dp g,
+//                         B1 = sum P g, R_i = (A1 - D^ B1) / L; writes dxd, the record
 //                         (lse_i log2 e + log2 L_i, D^_i) for the column pass, and
 //                         scale xd_i R_i into the wave's dattn partial. Each of the W
 //                         wavefronts runs kItemsPerWave work items dealt in snake order (pass

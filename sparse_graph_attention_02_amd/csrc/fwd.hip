@@ -23,10 +23,11 @@
 // GATv2 edge gathers one row instead of two).
 //
 // Per edge a lane group gathers the neighbour's K and V rows with 16-byte loads per lane
-// (coalesced across the group), reduces the per-head dot product with DPP adds, and folds
-// U edges at a time into the running (m, l, acc) state: one rescale per U edges. Scores
-// are kept in log2 units (scale * log2 e folded into one multiplier) so every exponential
-// is a single v_exp_f32. No atomics: results are bitwise reproducible.
+// (coalesced across the group; structured buffer loads that take the node id, or plain
+// 64-bit loads for tables past 4 GiB), reduces the per-head dot product with DPP adds,
+// and folds U edges at a time into the running (m, l, acc) state: one rescale per U
+// edges. Scores are kept in log2 units (scale * log2 e folded into one multiplier) so every
+// exponential is a single v_exp_f32. No atomics: results are bitwise reproducible.
 #include "ga_device.h"
 #include "ga_internal.h"
 

@@ -15,7 +15,8 @@
 //
 // Forward (one launch over every row, the plan's row bins, like the attention forward):
 //   reduce_fwd_main   hub chunks -> (value, index) partials; medium rows one wavefront each;
-//                     light rows one G-lane group each (16 bytes of the row per lane)
+//                     light rows one G-lane group each (16 bytes of the row per lane, by
+//                     structured buffer loads, or plain 64-bit loads for tables past 4 GiB)
 //   reduce_fwd_merge  one wavefront per hub row folds its chunk partials with the same
 //                     (value, index) rule (exact: the rule is a total order, so the merge
 //                     order does not matter; it is fixed anyway)
