@@ -59,7 +59,10 @@ void timer_hook(const char* name, void* stream, int begin) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   hipEvent_t e = pool_get();
   if (!e) return;
-  hipEventRecord(e, static_cast<hipStream_t>(stream));
+  if (hipEventRecord(e, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    g_pool.push_back(e);  // timers are best effort: this launch goes untimed
+    return;
+  }
   if (begin) {
     g_recs.push_back(TimerRec{name, e, nullptr});
   } else {
@@ -557,7 +560,6 @@ ga_status graph_attn_bwd(const ga_plan* p, ga_score score, ga_dtype dtype, int32
   args.dq = dq;
   args.dk = dk;
   args.dv = dv;
-  const size_t F = size_t(heads) * dim;
   char* w = static_cast<char*>(ws);
   args.ws_ld = reinterpret_cast<float*>(w);
   w += align_up(size_t(p->n) * heads * 2 * sizeof(float));

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
 template <typename T, int G, int LH>
 __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
   using K = Fwd<T, G, LH, kModeDot, 1>;
-  constexpr int H = K::H, F = K::F, VEC = K::VEC, NG = K::NG;
+  constexpr int VEC = K::VEC, NG = K::NG;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane / G, r = lane % G, h = r / LH;

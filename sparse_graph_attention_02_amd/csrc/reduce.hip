@@ -525,7 +525,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_main(RedArgs a0) {
 template <typename T, int G>
 __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
   using K = Red<T, G, kReduceMax, 1>;
-  constexpr int NG = K::NG, VEC = K::VEC, F = K::F;
+  constexpr int NG = K::NG, VEC = K::VEC;
   const int hub = wave_uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane / G, r = lane % G;
