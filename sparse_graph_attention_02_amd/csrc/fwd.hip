@@ -239,12 +239,34 @@ struct Fwd {
   }
 };
 
+// The GATv2 score gathers one row per edge and is paced by its per-edge arithmetic and the
+// latency of the gathers that feed it; it trades edges per step for waves per SIMD:
+// 4 edges per step (2 in light rows) fit in at most 80 VGPRs, six waves, with no spills.
+#ifndef GA_UNROLL_FWD_GATV2
+#define GA_UNROLL_FWD_GATV2 4
+#endif
+#ifndef GA_UNROLL_FWD_GATV2_LIGHT
+#define GA_UNROLL_FWD_GATV2_LIGHT 2
+#endif
+#ifndef GA_WAVES_FWD_GATV2
+#define GA_WAVES_FWD_GATV2 6
+#endif
+
+// Waves per SIMD the register allocator must make room for: GA_WAVES_FWD_GATV2 for the
+// GATv2 score; the dot and GAT-style scores take GA_WAVES_PER_EU, or the compiler's own
+// choice (1 sets no floor).
+template <int MODE>
+constexpr int fwd_min_waves() {
+  return MODE == kModeGatV2 ? GA_WAVES_FWD_GATV2 : (GA_WAVES_PER_EU > 0 ? GA_WAVES_PER_EU : 1);
+}
+
 // A "slice" is G lanes (whole heads) of a feature row of a.ld lanes; the kernel's template
 // geometry is the slice's. slice_of() deals slices to XCDs (see ga_device.h); each wave
 // moves its operand pointers to its slice, after which row strides (a.ld lanes, a.hf
 // heads) address the full rows.
 template <typename T, int G, int LH, int MODE, int U, int UL, bool WIDE>
-__global__ __launch_bounds__(kBlock) GA_OCCUPANCY void fwd_main(FwdArgs a0) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(fwd_min_waves<MODE>())))
+void fwd_main(FwdArgs a0) {
   using K = Fwd<T, G, LH, MODE, U>;
   using KL = Fwd<T, G, LH, MODE, UL>;  // light rows
   using raw_t = typename K::raw_t;
@@ -353,9 +375,9 @@ __global__ __launch_bounds__(kBlock) void fwd_hub_merge(FwdArgs a) {
 // Main kernel on the slice geometry (G lanes per slice), a.slices slices.
 template <typename T, int G, int LH, int MODE>
 int launch_main(const FwdArgs& a, void* stream, TimerHook hook) {
-  // light rows: the GATv2 score's longer per-edge arithmetic pays for 4 edges in flight,
-  // the dot and GAT-style scores keep GA_UNROLL_FWD_LIGHT
-  constexpr int U = GA_UNROLL_FWD, UL = MODE == kModeGatV2 ? 4 : GA_UNROLL_FWD_LIGHT;
+  constexpr bool V2 = MODE == kModeGatV2;
+  constexpr int U = V2 ? GA_UNROLL_FWD_GATV2 : GA_UNROLL_FWD;
+  constexpr int UL = V2 ? GA_UNROLL_FWD_GATV2_LIGHT : GA_UNROLL_FWD_LIGHT;
   constexpr int NG = kWave / G;
   const DevBins& B = a.bins;
   const int64_t items = int64_t(B.n_sched) + B.n_medium + (int64_t(B.n_light) + NG - 1) / NG;

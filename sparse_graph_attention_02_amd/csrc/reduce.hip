@@ -542,7 +542,10 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_merge(RedArgs a) {
   if (g == 0) K::store(a.dx, col, r, s, 1.f);
 }
 
-constexpr int kUnrollRed = 8;
+// Edges per step of the forward: 2 keeps the kernel at 52 VGPRs (bf16, 32-lane rows), eight
+// waves per SIMD, whose loads hide each other's latency better than deeper unrolls at
+// fewer waves (8 edges: 82 VGPRs, five waves).
+constexpr int kUnrollRed = 2;
 #ifndef GA_UNROLL_RED_BWD
 #define GA_UNROLL_RED_BWD 4
 #endif
