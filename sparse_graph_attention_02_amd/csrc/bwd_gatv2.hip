@@ -125,17 +125,25 @@ struct BwdV2 : RowIO<T, G, LH> {
                                                   int gs, int r, const float* xd,
                                                   const raw_t& dor, const float* av,
                                                   float lse2, RowAcc& s) {
-    constexpr int L = NGS * G;
+    // index batches of whole steps, so that no step of a full batch is part empty (every
+    // slot costs its arithmetic here); a step longer than the segment keeps the segment
+    constexpr int L = NGS * G, S = NGS * U;
+    constexpr int LB = S <= L ? L / S * S : L;
+    static_assert(LB > 0 && LB <= L, "index batch");
     const int lane = threadIdx.x & (kWave - 1);
     const rows_t Xd = node_rows(a.k, G * int(sizeof(raw_t)), a.n);
     const raw_t* __restrict__ Xs = R(a.k);
-    for (int base = e0; base < e1; base += L) {
-      const int nb = min(L, e1 - base);
+    for (int base = e0; base < e1; base += LB) {
+      const int nb = min(LB, e1 - base);
       const int li = lane - seg0;
-      // lanes past the batch's edges hold node 0; a step's spare slots read those lanes (or,
-      // past the segment, another lane's node), so they load rows already in L2, and their
-      // weight is masked out
-      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
+      // lanes past the batch's edges name node n, one past the table: a structured buffer
+      // load out of range returns zeros without touching memory. A step's spare slots read
+      // those lanes or, where a step is longer than a batch, lanes of the same batch (edges
+      // of this row, weighted zero), so what a table holds outside this row's neighbours
+      // never enters the sums. Plain 64-bit loads have no range check; there the spare
+      // lanes name the batch's first edge, a neighbour of the same row.
+      const int my_j = WIDE ? ld_stream(a.indices + base + (li < nb ? li : 0))
+                            : (li < nb ? ld_stream(a.indices + base + li) : a.n);
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
@@ -143,7 +151,10 @@ struct BwdV2 : RowIO<T, G, LH> {
         for (int u = 0; u < U; ++u) {
           const int pos = t + u * NGS + gs;
           ok[u] = pos < nb;
-          jj[u] = __builtin_amdgcn_ds_bpermute((seg0 + pos) << 2, my_j);
+          // a step longer than a lane group's own segment (light rows of 4-lane groups)
+          // wraps within that segment, not into the next group's row
+          const int src = (S > L && L < kWave) ? (pos & (L - 1)) : pos;
+          jj[u] = __builtin_amdgcn_ds_bpermute((seg0 + src) << 2, my_j);
         }
         raw_t xr[U];
 #pragma unroll

@@ -120,10 +120,14 @@ struct Fwd {
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      // lanes past the batch's edges hold node 0; a step's spare slots read those lanes (or,
-      // past the segment, another lane's node), so they load rows already in L2, and the
-      // softmax below masks them out
-      const int my_j = (li < nb) ? ld_stream(a.indices + base + li) : 0;
+      // lanes past the batch's edges name node n, one past the table: a structured buffer
+      // load out of range returns zeros without touching memory. A step's spare slots read
+      // those lanes or, where a step is longer than a batch, lanes of the same batch (edges
+      // of this row, weighted zero), so what a table holds outside this row's neighbours
+      // never enters the sums. Plain 64-bit loads have no range check; there the spare
+      // lanes name the batch's first edge, a neighbour of the same row.
+      const int my_j = WIDE ? ld_stream(a.indices + base + (li < nb ? li : 0))
+                            : (li < nb ? ld_stream(a.indices + base + li) : a.n);
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
@@ -138,7 +142,7 @@ struct Fwd {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if constexpr (GAT)
-            tv[u] = Tt[static_cast<size_t>(jj[u]) * a.hf + h];
+            tv[u] = Tt[static_cast<size_t>(min(jj[u], a.n - 1)) * a.hf + h];  // plain load: in range
           else
             kr[u] = ld_node<WIDE>(Kd, Kr, jj[u], a.ld, r);
           if constexpr (GATV2)
