@@ -48,6 +48,11 @@
  *     loads past that (results are the same either way). Setting the environment
  *     variable GRAPH_ATTN_WIDE_LOADS=1 makes every call take the 64-bit path (read at
  *     each call; a testing aid).
+ *   Non-finite inputs: a NaN or infinity in node j's features reaches only the rows
+ *     that list j (and, in the backward, what those rows feed), as in the plain
+ *     definition. A step folds several edges; its unused slots read zeros (a buffer
+ *     record past the table, which loads nothing) or an edge of the same row, with a
+ *     zero weight, never another node's row.
  */
 #ifndef GRAPH_ATTN_H
 #define GRAPH_ATTN_H

@@ -58,7 +58,8 @@ __device__ __forceinline__ void probe_sink(const ProbeArgs& a, const u32x4& acc,
 // Edges [e0, e1) of one work item, NGS lane groups cooperating (the attention passes'
 // index batch: one index per lane, broadcast by shuffles, U edges per group per step;
 // masked slots re-read the step's first edge, as the dQ and column passes do; the
-// buffer-fed passes point them at node 0 instead, a row that likewise stays in L2).
+// buffer-fed passes give them a record past the table instead, which loads nothing, so
+// there the probe's masked slots are L2 hits the pass does not make).
 template <int G, int U, int NGS, bool COLS>
 __device__ __forceinline__ void probe_edges(const ProbeArgs& a, int e0, int e1, int seg0, int gs,
                                             int r, int h, u32x4& acc) {
