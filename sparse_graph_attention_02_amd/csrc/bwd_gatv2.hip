@@ -144,13 +144,16 @@ struct BwdV2 : RowIO<T, G, LH> {
       // lanes name the batch's first edge, a neighbour of the same row.
       const int my_j = WIDE ? ld_stream(a.indices + base + (li < nb ? li : 0))
                             : (li < nb ? ld_stream(a.indices + base + li) : a.n);
-      for (int t = 0; t < nb; t += NGS * U) {
+      // full steps take every slot unmasked; the item's last, partial step skips the slots
+      // no lane group of the segment uses (their loads read nothing)
+      auto step = [&](int t, auto full) {
+        constexpr bool FULL = decltype(full)::value;
         int jj[U];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int pos = t + u * NGS + gs;
-          ok[u] = pos < nb;
+          ok[u] = FULL || pos < nb;
           // a step longer than a lane group's own segment (light rows of 4-lane groups)
           // wraps within that segment, not into the next group's row
           const int src = (S > L && L < kWave) ? (pos & (L - 1)) : pos;
@@ -161,6 +164,9 @@ struct BwdV2 : RowIO<T, G, LH> {
         for (int u = 0; u < U; ++u) xr[u] = ld_node<WIDE>(Xd, Xs, jj[u], G, r);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          if constexpr (!FULL) {
+            if (t + u * NGS >= nb) continue;
+          }
           float xs[VEC];
           L16::unpack(xr[u], xs);
           // g = LeakyReLU'(z) by one select, LeakyReLU(z) = z g exactly (g is 1 or the slope)
@@ -183,7 +189,10 @@ struct BwdV2 : RowIO<T, G, LH> {
             s.B1[c] = fma(static_cast<acc_t>(p), static_cast<acc_t>(g[c]), s.B1[c]);
           }
         }
-      }
+      };
+      int t = 0;
+      for (; t + S <= nb; t += S) step(t, std::true_type{});
+      if (t < nb) step(t, std::false_type{});
     }
   }
 
