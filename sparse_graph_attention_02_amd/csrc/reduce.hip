@@ -128,10 +128,13 @@ struct Red : RowIO<T, G, G> {
     for (int base = e0; base < e1; base += L) {
       const int nb = min(L, e1 - base);
       const int li = lane - seg0;
-      // lanes past the batch's edges hold node 0; a step's spare slots read those lanes (or,
-      // past the segment, another lane's node), so they load rows already in L2, and the
-      // fold skips them
-      const int my_j = (li < nb) ? ld_stream(a.indices + edge_of(e0, e1, base + li)) : 0;
+      // lanes past the batch's edges name node n, one record past the table, which a
+      // structured buffer load reads as zeros without touching memory; with plain 64-bit
+      // loads (no range check) they name the batch's first edge, of the same row. A step's
+      // spare slots read those lanes or, where a step is longer than a batch, edges of the
+      // same batch, and the fold skips them either way
+      const int jb = ld_stream(a.indices + edge_of(e0, e1, base + (li < nb ? li : 0)));
+      const int my_j = (li < nb || a.wide) ? jb : a.n;
       for (int t = 0; t < nb; t += NGS * U) {
         int jj[U];
         bool ok[U];
